@@ -1,0 +1,18 @@
+"""Plain CPU fp64 oracle of the KV-cache correction hot path (test infrastructure).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may import
+this package.  The product path (the HIP library and its Python binding) never does.
+"""
+from .kvc_oracle import (  # noqa: F401
+    chain,
+    correct,
+    cosine_scores,
+    effective_rank,
+    fit_anchor,
+    pool,
+    reliability,
+    rel_frobenius,
+    round_to_bf16,
+    round_to_dtype,
+    softmax_weights,
+)

@@ -1,0 +1,294 @@
+"""fp64 CPU oracle of KVCMAS's online KV-cache correction and its rank-r anchor fit.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this module; the HIP library never calls it and shares no
+code, table or constant with it.
+
+Source: "KVCMAS: Efficient KV cache Correction for Shared Context in Multi-Agent Systems"
+(arXiv:2609.34060), as shown on the thelatestinai listing (captions of Figs. 1, 2, 3, 7, 13
+and Tables 3, 6, 13) and the metraipolis abstract.  The pages describe the method in prose
+only; every formula below is the plainest reading of that prose, and each function says
+which.
+
+Conventions
+* Caches K, V: [L, H, T, d] (layer, kv-head, token, channel); one (l, h) is a segment.
+* Descriptors: [L, H, A, 2d]; anchor factors U: [2, L, H, A, T, r], W: [2, L, H, A, r, d]
+  (index 0 = K, 1 = V).  Fit input delta: [M, T, d].
+* All arithmetic is float64.  Cache values given in bf16 / fp32 are widened exactly.
+  Outputs stored in the cache dtype are rounded ONCE from the float64 value.
+
+Parity pins: every function is checked in ``tests/test_oracle_*.py`` against closed forms,
+hand-worked fixtures (``tests/golden``), brute force on tiny inputs and invariants.  The
+reading of the method itself (mean-pooled descriptor, cosine, softmax with temperature 1,
+max-cosine reliability) is not pinned by any number on the pages: parity with the
+authors' own implementation is unpinned; parity of the GPU path with this oracle is.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------------------
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as float64.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and float32's exponent
+    range: normal numbers down to 2^-126, subnormals in steps of 2^-133, overflow to inf
+    at (2 - 2^-8) * 2^127 and above.  The rounding is done directly from float64, so a
+    value is rounded exactly once.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    v = x[fin]
+    _, e = np.frexp(v)  # |v| = m * 2^e with m in [0.5, 1)
+    # quantum of the 8-bit significand at this binade; below 2^-126 the spacing is fixed
+    q_exp = np.maximum(e - 8, -133)
+    scaled = np.ldexp(v, -q_exp)  # exact: power-of-two scaling
+    y = np.ldexp(np.rint(scaled), q_exp)  # np.rint rounds half to even
+    y = np.where(np.abs(y) >= 2.0 ** 128, np.copysign(np.inf, v), y)
+    out[fin] = y
+    return out
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Store float64 values in the cache dtype ("bf16" or "f32") once, back as float64."""
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# --------------------------------------------------------------------------------------
+# matching: descriptor, cosine, softmax, reliability
+# --------------------------------------------------------------------------------------
+
+
+def pool(K, V) -> np.ndarray:
+    """Pooled descriptor of a cache segment: q = [mean_t K ; mean_t V], shape [..., 2d].
+
+    Fig. 1(b): the current cache representation is matched against the segment's
+    online anchors.  Reading: the representation is the token mean of the segment's
+    keys followed by the token mean of its values.  An empty segment (T = 0) pools to 0.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    T = K.shape[-2]
+    if T == 0:
+        return np.zeros(K.shape[:-2] + (2 * K.shape[-1],), dtype=np.float64)
+    return np.concatenate([K.sum(axis=-2) / T, V.sum(axis=-2) / T], axis=-1)
+
+
+def cosine_scores(q, desc) -> np.ndarray:
+    """s_a = <q, desc_a> / (||q|| ||desc_a||), and 0 when either norm is 0. Shape [..., A].
+
+    Fig. 1(b): similarity between the current representation and each online anchor.
+    Reading: cosine similarity; a zero vector has no direction and scores 0; a NaN in
+    either vector gives a NaN score (which then falls back, see ``reliability``).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    desc = np.asarray(desc, dtype=np.float64)
+    dots = np.einsum("...k,...ak->...a", q, desc)
+    nq = np.sqrt(np.einsum("...k,...k->...", q, q))[..., None]
+    nd = np.sqrt(np.einsum("...ak,...ak->...a", desc, desc))
+    den = nq * nd
+    with np.errstate(invalid="ignore", divide="ignore"):
+        s = np.where(den == 0, 0.0, dots / np.where(den == 0, 1.0, den))
+    return s
+
+
+def softmax_weights(s) -> np.ndarray:
+    """w_a = exp(s_a - max s) / sum_b exp(s_b - max s) over the anchors (last axis).
+
+    Fig. 1(b): anchor corrections are combined with similarity-based weights.
+    Reading: a softmax of the cosines with temperature 1 over all A anchors.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def reliability(s, tau):
+    """score = max_a s_a; fallback mask = score < tau, or score not a number.
+
+    Fig. 1(a): a shared segment's cache is reused when its correction is reliable and
+    falls back to dense prefill otherwise; Table 3 gives one threshold tau per workload.
+    Reading: the reliability score is the best anchor cosine and the comparison is
+    strict (score == tau reuses).  The decision is taken in float32, the precision in
+    which the GPU kernel holds the score and tau: the float64 score is rounded to float32
+    and compared with float32(tau).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    score = np.max(s, axis=-1)  # NaN propagates
+    s32 = score.astype(np.float32)
+    t32 = np.float32(tau)
+    mask = ~(s32 >= t32)
+    return score, mask.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------------------
+# correction
+# --------------------------------------------------------------------------------------
+
+
+def correct(K, V, desc, U, W, tau, dtype, K_fb=None, V_fb=None, q=None) -> dict:
+    """Correct a reused cache with the similarity-weighted sum of the anchors' low-rank deltas.
+
+    For every segment (l, h) and X in {K, V}:
+        X' = X + sum_a w_a U^X_a W^X_a        if the segment is reliable,
+        X' = X_fb (dense-prefill stand-in) or X   if it falls back,
+    then X' is stored once in ``dtype``.  The weights w are shared by K and V.
+
+    Figs. 1(a) and 1(b); the abstract (cross-agent deviations kept as compact low-rank
+    states).  Inputs: K, V [L, H, T, d]; desc [L, H, A, 2d]; U [2, L, H, A, T, r];
+    W [2, L, H, A, r, d]; optional fallback caches and a precomputed pooled query q.
+    Returns float64 arrays: K_out, V_out (stored values), K_exact, V_exact (before
+    storage rounding), and q, s, w, score, mask.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    if q is None:
+        q = pool(K, V)
+    q = np.asarray(q, dtype=np.float64)
+    s = cosine_scores(q, desc)
+    w = softmax_weights(s)
+    score, mask = reliability(s, tau)
+    outs = []
+    for x, (X, X_fb) in enumerate(((K, K_fb), (V, V_fb))):
+        delta = np.zeros_like(X)
+        for a in range(U.shape[3]):
+            delta += w[..., a, None, None] * np.matmul(U[x, :, :, a], W[x, :, :, a])
+        corrected = X + delta
+        keep = X if X_fb is None else np.asarray(X_fb, dtype=np.float64)
+        exact = np.where(mask[..., None, None].astype(bool), keep, corrected)
+        outs.append(exact)
+    return {
+        "K_exact": outs[0],
+        "V_exact": outs[1],
+        "K_out": round_to_dtype(outs[0], dtype),
+        "V_out": round_to_dtype(outs[1], dtype),
+        "q": q,
+        "s": s,
+        "w": w,
+        "score": score,
+        "mask": mask,
+    }
+
+
+def chain(K0, V0, edges, tau, dtype) -> list:
+    """Chained correction along a workflow A0 -> A1 -> ... (Fig. 1(c), Fig. 3(b)).
+
+    Agent A0's cache is exact and is the first edge's source, untouched.  Edge i
+    corrects its source and stores the result in ``dtype``; that stored cache is the
+    source of edge i+1, with no separate reference prefill.  ``edges`` is a list of
+    dicts with keys desc, U, W and optionally K_fb, V_fb (agent i+1's dense-prefill
+    cache, used where the segment falls back) and q (a precomputed pooled query).
+    Returns the per-edge outputs of ``correct``; each also carries its source.
+    """
+    srcK = np.asarray(K0, dtype=np.float64)
+    srcV = np.asarray(V0, dtype=np.float64)
+    res = []
+    for ed in edges:
+        out = correct(srcK, srcV, ed["desc"], ed["U"], ed["W"], tau, dtype,
+                      K_fb=ed.get("K_fb"), V_fb=ed.get("V_fb"), q=ed.get("q"))
+        out["K_src"], out["V_src"] = srcK, srcV
+        res.append(out)
+        srcK, srcV = out["K_out"], out["V_out"]
+    return res
+
+
+# --------------------------------------------------------------------------------------
+# anchor fit
+# --------------------------------------------------------------------------------------
+
+
+def effective_rank(lam, energy: float = 0.9) -> np.ndarray:
+    """Smallest k >= 1 whose top-k eigenvalues hold at least ``energy`` of the total.
+
+    Figs. 2 and 7(a): effective rank is the minimum rank that retains 90% of the
+    singular-value energy.  Reading: energy of singular value sigma_i is sigma_i^2 = lambda_i
+    (eigenvalue of delta^T delta), summed over all of them; values are sorted descending and
+    negative round-off is clamped to 0; a zero matrix has effective rank 0.  The running
+    sum and the comparison are float64.  ``lam``: [..., n]; returns int32 [...].
+    """
+    lam = np.asarray(lam, dtype=np.float64)
+    lam = np.clip(-np.sort(-lam, axis=-1), 0.0, None)
+    flat = lam.reshape(-1, lam.shape[-1])
+    out = np.zeros(flat.shape[0], dtype=np.int32)
+    for i, row in enumerate(flat):
+        total = 0.0
+        for v in row:
+            total += v
+        if total == 0.0:
+            continue
+        need = energy * total
+        run = 0.0
+        for k, v in enumerate(row, start=1):
+            run += v
+            if run >= need:
+                out[i] = k
+                break
+        else:
+            out[i] = row.shape[0]
+    return out.reshape(lam.shape[:-1])
+
+
+def _canonical_rows(Wr: np.ndarray) -> np.ndarray:
+    """Flip each row so that its largest-magnitude entry (first one on ties) is positive."""
+    Wr = np.array(Wr, copy=True)
+    for i in range(Wr.shape[0]):
+        j = int(np.argmax(np.abs(Wr[i])))
+        if Wr[i, j] < 0:
+            Wr[i] = -Wr[i]
+    return Wr
+
+
+def fit_anchor(delta, r: int, energy: float = 0.9) -> dict:
+    """Rank-r anchor of a cache delta: the truncated SVD written out.
+
+    delta = exact - reused (one [T, d] matrix per (K|V, layer, head)).  The compact
+    low-rank state of the abstract is read as the best rank-r approximation of delta
+    (Eckart-Young), with r = r_delta = 32 by default (Fig. 13 caption); its eigenvalues
+    lambda_i = sigma_i^2 give the effective rank (Figs. 2, 7).  Factors:
+        W = top-r right singular vectors as rows (orthonormal), each row's
+            largest-magnitude entry made positive;
+        U = delta W^T, so U W is the truncation and U's columns carry sigma.
+    delta: [M, T, d].  Returns U [M, T, r], W [M, r, d], k_eff int32 [M],
+    eig [M, d] (descending, zero-padded when T < d).
+    """
+    delta = np.asarray(delta, dtype=np.float64)
+    M, T, d = delta.shape
+    U = np.zeros((M, T, r))
+    W = np.zeros((M, r, d))
+    eig = np.zeros((M, d))
+    for m in range(M):
+        if T == 0:
+            continue
+        _, sv, vt = np.linalg.svd(delta[m], full_matrices=False)
+        k = sv.shape[0]
+        eig[m, :k] = sv * sv
+        rr = min(r, k)
+        W[m, :rr] = _canonical_rows(vt[:rr])
+        U[m] = delta[m] @ W[m].T
+    return {"U": U, "W": W, "k_eff": effective_rank(eig, energy), "eig": eig}
+
+
+# --------------------------------------------------------------------------------------
+# metrics
+# --------------------------------------------------------------------------------------
+
+
+def rel_frobenius(x, ref) -> float:
+    """||x - ref||_F / ||ref||_F: the error normalised by the target (Fig. 3 caption)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    return float(num / den) if den > 0 else float(num)
