@@ -1,0 +1,280 @@
+"""Python binding of libkvc, the gfx950 HIP library for KVCMAS's online KV-cache correction.
+
+Argument marshalling only: torch tensors supply device memory and the current stream;
+every step of the computation runs in the library's HIP kernels.  The library is loaded
+from this directory (built by ``agent_kv_cache_kvc_amd/build.py``); when it is missing
+every call raises -- there is no fallback implementation.
+
+Entry points (same names as the C ABI in include/kvc.h):
+    pool_descriptor(K, V)                               -> q
+    correct(K, V, desc, U, W, tau, ...)                 -> CorrectResult
+    correct_chain(K0, V0, edges, tau)                   -> list[CorrectResult]
+    fit_anchor(delta, r=32, energy=0.9)                 -> FitResult
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "KvcError",
+    "CorrectResult",
+    "FitResult",
+    "lib",
+    "lib_path",
+    "pool_descriptor",
+    "correct",
+    "correct_chain",
+    "fit_anchor",
+    "correct_workspace_bytes",
+    "fit_workspace_bytes",
+    "KVC_BF16",
+    "KVC_F32",
+]
+
+KVC_BF16 = 0
+KVC_F32 = 1
+_STATUS = {0: "KVC_OK", 1: "KVC_ERR_ARG", 2: "KVC_ERR_UNSUPPORTED", 3: "KVC_ERR_HIP",
+           4: "KVC_ERR_WORKSPACE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libkvc.so")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_SIGS = {
+    "kvc_version": (ctypes.c_char_p, []),
+    "kvc_last_error": (ctypes.c_char_p, []),
+    "kvc_pool_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "kvc_pool_descriptor": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "kvc_correct_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "kvc_correct": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, ctypes.c_float,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "kvc_correct_chain": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
+                               ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_fit_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "kvc_fit_anchor": (_i, [_vp, _i, _i, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
+                            _sz, _vp]),
+}
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvc.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is missing: build it with agent_kv_cache_kvc_amd/build.py")
+        h = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = h
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KvcError(status, lib().kvc_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError(f"cache dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def correct_workspace_bytes(L, H, T, d, A, r) -> int:
+    return int(lib().kvc_correct_workspace_bytes(L, H, T, d, A, r))
+
+
+def fit_workspace_bytes(M, T, d, r) -> int:
+    return int(lib().kvc_fit_workspace_bytes(M, T, d, r))
+
+
+def pool_descriptor(K: torch.Tensor, V: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q[l, h] = [mean_t K[l, h] ; mean_t V[l, h]] (float32) for K, V of shape [L, H, T, d]."""
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    _need(V, "V", K.shape, K.dtype, dev)
+    _need(K, "K", K.shape, K.dtype, dev)
+    q = out if out is not None else torch.empty(L, H, 2 * d, dtype=torch.float32, device=dev)
+    _need(q, "q_out", (L, H, 2 * d), torch.float32, dev)
+    nb = int(lib().kvc_pool_workspace_bytes(L, H, T, d))
+    ws = workspace if workspace is not None else _workspace(nb, dev)
+    _check(lib().kvc_pool_descriptor(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(q), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    return q
+
+
+@dataclasses.dataclass
+class CorrectResult:
+    K: torch.Tensor
+    V: torch.Tensor
+    mask: torch.Tensor  # uint8 [L, H], 1 = fall back to dense prefill
+    score: Optional[torch.Tensor] = None  # float32 [L, H]
+    w: Optional[torch.Tensor] = None  # float32 [L, H, A]
+    q_next: Optional[torch.Tensor] = None  # float32 [L, H, 2d]
+
+
+def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tensor,
+            W: torch.Tensor, tau: float, *, q_in: Optional[torch.Tensor] = None,
+            K_fb: Optional[torch.Tensor] = None, V_fb: Optional[torch.Tensor] = None,
+            K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
+            want_score: bool = True, want_w: bool = True, want_q_next: bool = False,
+            workspace: Optional[torch.Tensor] = None) -> CorrectResult:
+    """Correct a reused cache with its segments' anchors (see kvc_correct in include/kvc.h).
+
+    K, V: [L, H, T, d]; desc: [L, H, A, 2d] float32; U: [2, L, H, A, T, r];
+    W: [2, L, H, A, r, d] (cache dtype).  Pass K_out=K, V_out=V to correct in place.
+    """
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    A = desc.shape[2]
+    r = U.shape[-1]
+    _need(K, "K", (L, H, T, d), K.dtype, dev)
+    _need(V, "V", (L, H, T, d), K.dtype, dev)
+    _need(desc, "desc", (L, H, A, 2 * d), torch.float32, dev)
+    _need(U, "U", (2, L, H, A, T, r), K.dtype, dev)
+    _need(W, "W", (2, L, H, A, r, d), K.dtype, dev)
+    if q_in is not None:
+        _need(q_in, "q_in", (L, H, 2 * d), torch.float32, dev)
+    for name, t in (("K_fb", K_fb), ("V_fb", V_fb)):
+        if t is not None:
+            _need(t, name, (L, H, T, d), K.dtype, dev)
+    Ko = K_out if K_out is not None else torch.empty_like(K)
+    Vo = V_out if V_out is not None else torch.empty_like(V)
+    _need(Ko, "K_out", (L, H, T, d), K.dtype, dev)
+    _need(Vo, "V_out", (L, H, T, d), K.dtype, dev)
+    mask = torch.empty(L, H, dtype=torch.uint8, device=dev)
+    score = torch.empty(L, H, dtype=torch.float32, device=dev) if want_score else None
+    w = torch.empty(L, H, A, dtype=torch.float32, device=dev) if want_w else None
+    qn = torch.empty(L, H, 2 * d, dtype=torch.float32, device=dev) if want_q_next else None
+    ws = workspace if workspace is not None else _workspace(correct_workspace_bytes(L, H, T, d, A, r), dev)
+    _check(lib().kvc_correct(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(desc), _ptr(U), _ptr(W), A,
+                             r, float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
+                             _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(qn), _ptr(ws),
+                             ws.numel(), _stream(dev)))
+    return CorrectResult(Ko, Vo, mask, score, w, qn)
+
+
+def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau: float, *,
+                  outputs: Optional[Sequence[tuple]] = None,
+                  workspace: Optional[torch.Tensor] = None) -> list:
+    """Chained correction A0 -> A1 -> ... (see kvc_correct_chain in include/kvc.h).
+
+    ``edges``: one dict per edge with desc, U, W and optionally K_fb, V_fb.  ``outputs``:
+    optional preallocated (K_out, V_out) per edge.  Returns one CorrectResult per edge.
+    """
+    L, H, T, d = K0.shape
+    dev = K0.device
+    dt = _dtype_code(K0)
+    n = len(edges)
+    if n < 1:
+        raise ValueError("need at least one edge")
+    A = edges[0]["desc"].shape[2]
+    r = edges[0]["U"].shape[-1]
+    _need(V0, "V0", K0.shape, K0.dtype, dev)
+    res = []
+    for e, ed in enumerate(edges):
+        _need(ed["desc"], f"desc[{e}]", (L, H, A, 2 * d), torch.float32, dev)
+        _need(ed["U"], f"U[{e}]", (2, L, H, A, T, r), K0.dtype, dev)
+        _need(ed["W"], f"W[{e}]", (2, L, H, A, r, d), K0.dtype, dev)
+        for name in ("K_fb", "V_fb"):
+            if ed.get(name) is not None:
+                _need(ed[name], f"{name}[{e}]", K0.shape, K0.dtype, dev)
+        if outputs is not None:
+            Ko, Vo = outputs[e]
+        else:
+            Ko, Vo = torch.empty_like(K0), torch.empty_like(V0)
+        res.append(CorrectResult(Ko, Vo, torch.empty(L, H, dtype=torch.uint8, device=dev),
+                                 torch.empty(L, H, dtype=torch.float32, device=dev)))
+    has_fb = [ed.get("K_fb") is not None for ed in edges]
+    ws = workspace if workspace is not None else _workspace(
+        int(lib().kvc_chain_workspace_bytes(L, H, T, d, A, r)), dev)
+    _check(lib().kvc_correct_chain(
+        _ptr(K0), _ptr(V0), L, H, T, d, dt, n,
+        _ptr_array([ed["desc"] for ed in edges]), _ptr_array([ed["U"] for ed in edges]),
+        _ptr_array([ed["W"] for ed in edges]), A, r, float(tau),
+        _ptr_array([ed.get("K_fb") for ed in edges]) if any(has_fb) else None,
+        _ptr_array([ed.get("V_fb") for ed in edges]) if any(has_fb) else None,
+        _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
+        _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return res
+
+
+@dataclasses.dataclass
+class FitResult:
+    U: torch.Tensor  # float32 [M, T, r]
+    W: torch.Tensor  # float32 [M, r, d]
+    k_eff: torch.Tensor  # int32 [M]
+    eig: Optional[torch.Tensor] = None  # float32 [M, d], descending
+
+
+def fit_anchor(delta: torch.Tensor, r: int = 32, energy: float = 0.9, *, want_eig: bool = True,
+               workspace: Optional[torch.Tensor] = None) -> FitResult:
+    """Rank-r anchor of delta [M, T, d] (see kvc_fit_anchor in include/kvc.h)."""
+    M, T, d = delta.shape
+    dev = delta.device
+    dt = _dtype_code(delta)
+    _need(delta, "delta", (M, T, d), delta.dtype, dev)
+    U = torch.empty(M, T, r, dtype=torch.float32, device=dev)
+    W = torch.empty(M, r, d, dtype=torch.float32, device=dev)
+    k = torch.empty(M, dtype=torch.int32, device=dev)
+    eig = torch.empty(M, d, dtype=torch.float32, device=dev) if want_eig else None
+    ws = workspace if workspace is not None else _workspace(fit_workspace_bytes(M, T, d, r), dev)
+    _check(lib().kvc_fit_anchor(_ptr(delta), M, T, d, dt, int(r), float(energy), _ptr(U),
+                                _ptr(W), _ptr(k), _ptr(eig), _ptr(ws), ws.numel(), _stream(dev)))
+    return FitResult(U, W, k, eig)

@@ -1,0 +1,304 @@
+// C ABI of libkvc: argument validation (before any HIP call), workspace sizing, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvc_status ok() {
+  g_err[0] = '\0';
+  return KVC_OK;
+}
+
+kvc_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr long long kMaxElems = 1ll << 62;
+
+int elem_size(int dtype) { return dtype == KVC_BF16 ? 2 : 4; }
+
+// Shape of a cache.  Returns KVC_OK or the failing status (message set).
+kvc_status check_cache_shape(int L, int H, int T, int d, int dtype) {
+  if (L < 0 || H < 0 || T < 0) return fail(KVC_ERR_ARG, "negative size (L=%d H=%d T=%d)", L, H, T);
+  if (d <= 0) return fail(KVC_ERR_ARG, "d must be positive (d=%d)", d);
+  if (dtype != KVC_BF16 && dtype != KVC_F32) return fail(KVC_ERR_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(KVC_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", d);
+  const long long S = (long long)L * H;
+  if (S > 65535) return fail(KVC_ERR_UNSUPPORTED, "L*H=%lld exceeds 65535 segments", S);
+  if (S * T > kMaxElems / (2ll * d)) return fail(KVC_ERR_ARG, "cache too large");
+  return KVC_OK;
+}
+
+kvc_status check_tensor(const void* p, const char* name, size_t align = 16) {
+  if (p == nullptr) return fail(KVC_ERR_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(KVC_ERR_ARG, "%s is not %zu-byte aligned", name, align);
+  return KVC_OK;
+}
+
+kvc_status check_anchors(int A, int r, int dtype) {
+  if (A < 1) return fail(KVC_ERR_ARG, "A=%d (need >= 1)", A);
+  if (r < 1) return fail(KVC_ERR_ARG, "r=%d (need >= 1)", r);
+  if (A > kvc::kMaxA) return fail(KVC_ERR_UNSUPPORTED, "A=%d exceeds %d anchors", A, kvc::kMaxA);
+  if (r > kvc::kMaxR) return fail(KVC_ERR_UNSUPPORTED, "r=%d exceeds %d", r, kvc::kMaxR);
+  if (dtype == KVC_BF16) {
+    const int rp = (r + 15) / 16 * 16;
+    if (A * rp > kvc::kMaxKSlots)
+      return fail(KVC_ERR_UNSUPPORTED, "A*ceil16(r)=%d exceeds %d", A * rp, kvc::kMaxKSlots);
+  } else {
+    const int rp = (r + 7) / 8 * 8;
+    if (A * rp > 64) return fail(KVC_ERR_UNSUPPORTED, "fp32: A*ceil8(r)=%d exceeds 64", A * rp);
+  }
+  return KVC_OK;
+}
+
+#define KVC_TRY(x)                       \
+  do {                                   \
+    kvc_status _s = (x);                 \
+    if (_s != KVC_OK) return _s;         \
+  } while (0)
+
+#define KVC_HIP(call, what)                          \
+  do {                                               \
+    hipError_t _e = (call);                          \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_version(void) { return "kvc 0.1.0 gfx950"; }
+
+const char* kvc_last_error(void) { return g_err; }
+
+// --------------------------------------------------------------------------- pooling
+size_t kvc_pool_workspace_bytes(int L, int H, int T, int d) {
+  if (L < 0 || H < 0 || T < 0 || d <= 0) return 0;
+  return kvc::correct_layout(L, H, T, d, 1).off_next;  // the pooling partials only
+}
+
+kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, float* q_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  const int S = L * H;
+  if (S == 0) return ok();
+  if (T > 0) {
+    KVC_TRY(check_tensor(K, "K"));
+    KVC_TRY(check_tensor(V, "V"));
+  }
+  KVC_TRY(check_tensor(q_out, "q_out", 4));
+  const size_t need = kvc_pool_workspace_bytes(L, H, T, d);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, 1);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_pool);
+  if (T > 0) KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, part, c.n_pool_tiles, st), "pool");
+  KVC_HIP(kvc::launch_reduce_pool(part, T > 0 ? c.n_pool_tiles : 0, T, S, d, q_out, st),
+          "pool reduce");
+  return ok();
+}
+
+// --------------------------------------------------------------------------- correction
+size_t kvc_correct_workspace_bytes(int L, int H, int T, int d, int A, int r) {
+  (void)r;
+  if (L < 0 || H < 0 || T < 0 || d <= 0 || A < 1) return 0;
+  return kvc::correct_layout(L, H, T, d, A).bytes;
+}
+
+static kvc_status validate_correct(const void* K, const void* V, int L, int H, int T, int d,
+                                   int dtype, const float* desc, const void* U, const void* W,
+                                   int A, int r, const float* q_in, const void* K_fb,
+                                   const void* V_fb, void* K_out, void* V_out,
+                                   uint8_t* mask_out, void* ws, size_t ws_bytes) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  KVC_TRY(check_anchors(A, r, dtype));
+  if (L * H == 0) return KVC_OK;
+  if (T > 0) {
+    KVC_TRY(check_tensor(K, "K"));
+    KVC_TRY(check_tensor(V, "V"));
+    KVC_TRY(check_tensor(U, "U"));
+    KVC_TRY(check_tensor(K_out, "K_out"));
+    KVC_TRY(check_tensor(V_out, "V_out"));
+  }
+  KVC_TRY(check_tensor(desc, "desc", 4));
+  KVC_TRY(check_tensor(W, "W"));
+  KVC_TRY(check_tensor(mask_out, "mask_out", 1));
+  if (q_in != nullptr) KVC_TRY(check_tensor(q_in, "q_in", 4));
+  if ((K_fb == nullptr) != (V_fb == nullptr))
+    return fail(KVC_ERR_ARG, "K_fb and V_fb must both be given or both be NULL");
+  if (K_fb != nullptr && T > 0) {
+    KVC_TRY(check_tensor(K_fb, "K_fb"));
+    KVC_TRY(check_tensor(V_fb, "V_fb"));
+  }
+  const size_t need = kvc_correct_workspace_bytes(L, H, T, d, A, r);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  return KVC_OK;
+}
+
+static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, int T, int d,
+                                  int dtype, const float* desc, const void* U, const void* W,
+                                  int A, int r, float tau, const float* q_in,
+                                  const float* next_partials_in, const void* K_fb,
+                                  const void* V_fb, void* K_out, void* V_out,
+                                  uint8_t* mask_out, float* score_out, float* w_out,
+                                  bool want_next, void* ws, hipStream_t st) {
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  const int S = c.S;
+  char* base = static_cast<char*>(ws);
+  float* pool = reinterpret_cast<float*>(base + c.off_pool);
+  float* next = reinterpret_cast<float*>(base + c.off_next);
+  float* wv = reinterpret_cast<float*>(base + c.off_w);
+  float* sc = reinterpret_cast<float*>(base + c.off_score);
+  uint8_t* mk = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  const float* partials = pool;
+  int n_tiles = c.n_pool_tiles;
+  if (q_in == nullptr && next_partials_in != nullptr) {
+    partials = next_partials_in;
+    n_tiles = c.n_corr_tiles;
+  } else if (q_in == nullptr && T > 0) {
+    KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, pool, c.n_pool_tiles, st), "pool");
+  }
+  if (T == 0) n_tiles = 0;
+  KVC_HIP(kvc::launch_score(partials, n_tiles, T, q_in, desc, S, d, A, tau, nullptr, wv, sc, mk,
+                            nullptr, score_out, w_out, mask_out, st),
+          "score");
+  KVC_HIP(kvc::launch_correct(K, V, S, T, d, dtype, U, W, A, r, wv, mk, K_fb, V_fb, K_out, V_out,
+                              want_next ? next : nullptr, st),
+          "correct");
+  return KVC_OK;
+}
+
+kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d, int dtype,
+                       const float* desc, const void* U, const void* W, int A, int r,
+                       float tau, const float* q_in, const void* K_fb, const void* V_fb,
+                       void* K_out, void* V_out, uint8_t* mask_out, float* score_out,
+                       float* w_out, float* q_next_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  KVC_TRY(validate_correct(K, V, L, H, T, d, dtype, desc, U, W, A, r, q_in, K_fb, V_fb, K_out,
+                           V_out, mask_out, ws, ws_bytes));
+  if (score_out) KVC_TRY(check_tensor(score_out, "score_out", 4));
+  if (w_out) KVC_TRY(check_tensor(w_out, "w_out", 4));
+  if (q_next_out) KVC_TRY(check_tensor(q_next_out, "q_next_out", 4));
+  if (L * H == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  KVC_TRY(enqueue_correct(K, V, L, H, T, d, dtype, desc, U, W, A, r, tau, q_in, nullptr, K_fb,
+                          V_fb, K_out, V_out, mask_out, score_out, w_out, q_next_out != nullptr,
+                          ws, st));
+  if (q_next_out) {
+    const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+    float* next = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_next);
+    KVC_HIP(kvc::launch_reduce_pool(next, T > 0 ? c.n_corr_tiles : 0, T, c.S, d, q_next_out, st),
+            "q_next");
+  }
+  return ok();
+}
+
+// --------------------------------------------------------------------------- chain
+size_t kvc_chain_workspace_bytes(int L, int H, int T, int d, int A, int r) {
+  return kvc_correct_workspace_bytes(L, H, T, d, A, r);
+}
+
+kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T, int d,
+                             int dtype, int n_edges, const float* const* desc,
+                             const void* const* U, const void* const* W, int A, int r,
+                             float tau, const void* const* K_fb, const void* const* V_fb,
+                             void* const* K_out, void* const* V_out,
+                             uint8_t* const* mask_out, float* const* score_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (n_edges < 1) return fail(KVC_ERR_ARG, "n_edges=%d (need >= 1)", n_edges);
+  if (!desc || !U || !W || !K_out || !V_out || !mask_out)
+    return fail(KVC_ERR_ARG, "desc, U, W, K_out, V_out and mask_out arrays are required");
+  if ((K_fb == nullptr) != (V_fb == nullptr))
+    return fail(KVC_ERR_ARG, "K_fb and V_fb arrays must both be given or both be NULL");
+  for (int e = 0; e < n_edges; ++e) {
+    const void* src_k = e == 0 ? K0 : K_out[e - 1];
+    const void* src_v = e == 0 ? V0 : V_out[e - 1];
+    const void* kf = K_fb ? K_fb[e] : nullptr;
+    const void* vf = V_fb ? V_fb[e] : nullptr;
+    kvc_status s = validate_correct(src_k, src_v, L, H, T, d, dtype, desc[e], U[e], W[e], A, r,
+                                    nullptr, kf, vf, K_out[e], V_out[e], mask_out[e], ws,
+                                    ws_bytes);
+    if (s != KVC_OK) {
+      char tmp[512];
+      snprintf(tmp, sizeof(tmp), "edge %d: %s", e, g_err);
+      return fail(s, "%s", tmp);
+    }
+    if (score_out && score_out[e]) KVC_TRY(check_tensor(score_out[e], "score_out[e]", 4));
+    if (T > 0 && (K_out[e] == src_k || V_out[e] == src_v))
+      return fail(KVC_ERR_ARG, "edge %d writes over its own source", e);
+  }
+  if (L * H == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  const float* next = reinterpret_cast<const float*>(static_cast<char*>(ws) + c.off_next);
+  for (int e = 0; e < n_edges; ++e) {
+    const void* src_k = e == 0 ? K0 : K_out[e - 1];
+    const void* src_v = e == 0 ? V0 : V_out[e - 1];
+    const void* kf = K_fb ? K_fb[e] : nullptr;
+    const void* vf = V_fb ? V_fb[e] : nullptr;
+    KVC_TRY(enqueue_correct(src_k, src_v, L, H, T, d, dtype, desc[e], U[e], W[e], A, r, tau,
+                            nullptr, e == 0 ? nullptr : next, kf, vf, K_out[e], V_out[e],
+                            mask_out[e], score_out ? score_out[e] : nullptr, nullptr,
+                            e + 1 < n_edges, ws, st));
+  }
+  return ok();
+}
+
+// --------------------------------------------------------------------------- fit
+size_t kvc_fit_workspace_bytes(int M, int T, int d, int r) {
+  if (M < 0 || T < 0 || d <= 0 || r < 1) return 0;
+  return kvc::fit_layout(M, T, d, r).bytes;
+}
+
+kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int r,
+                          double energy, float* U_out, float* W_out, int32_t* k_eff_out,
+                          float* eig_out, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || T < 0) return fail(KVC_ERR_ARG, "negative size (M=%d T=%d)", M, T);
+  if (d <= 0) return fail(KVC_ERR_ARG, "d must be positive (d=%d)", d);
+  if (dtype != KVC_BF16 && dtype != KVC_F32) return fail(KVC_ERR_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(KVC_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", d);
+  if (r < 1 || r > d) return fail(KVC_ERR_ARG, "r=%d (need 1 <= r <= d)", r);
+  if (!(energy > 0.0 && energy <= 1.0)) return fail(KVC_ERR_ARG, "energy must be in (0, 1]");
+  if (M > 65535) return fail(KVC_ERR_UNSUPPORTED, "M=%d exceeds 65535 matrices", M);
+  if ((long long)M * T > kMaxElems / (2ll * d)) return fail(KVC_ERR_ARG, "delta too large");
+  if (M == 0) return ok();
+  if (T > 0) {
+    KVC_TRY(check_tensor(delta, "delta"));
+    KVC_TRY(check_tensor(U_out, "U_out"));
+  }
+  KVC_TRY(check_tensor(W_out, "W_out"));
+  KVC_TRY(check_tensor(k_eff_out, "k_eff_out", 4));
+  if (eig_out) KVC_TRY(check_tensor(eig_out, "eig_out", 4));
+  const size_t need = kvc_fit_workspace_bytes(M, T, d, r);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  const kvc::FitLayout f = kvc::fit_layout(M, T, d, r);
+  KVC_HIP(kvc::launch_fit(delta, f, dtype, energy, U_out, W_out, k_eff_out, eig_out,
+                          static_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream)),
+          "fit");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,517 @@
+// Online correction of a reused shared-context KV cache on gfx950.
+//
+// KVCMAS, thelatestinai listing, Fig. 1: the reused cache of a shared segment is matched
+// against the segment's online anchors (pooled descriptor vs. anchor descriptors, cosine),
+// the anchors' low-rank corrections are combined with similarity weights (softmax) and
+// added to K and V; a segment whose best match is below tau falls back to dense prefill.
+//
+// Kernels (all deterministic: fixed-order reductions, no floating-point atomics)
+//   pool_partials_kernel  token sums of K and V per 256-token tile          (HBM stream)
+//   score_kernel          tile sums -> q, cosines, softmax, score, mask     (one wave/segment)
+//   correct_kernel        X' = X + sum_a w_a U_a W_a on MFMA, or copy-through (HBM stream)
+//   reduce_pool_kernel    tile sums -> q (the pooling entry point)
+#include <hip/hip_runtime.h>
+
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// ------------------------------------------------------------------------- dtype traits
+struct TrBF16 {
+  using elem = uint16_t;
+  using frag = u32x4;
+  static constexpr int VEC = 8;    // elements per 16-byte access
+  static constexpr int SLOT = 8;   // consecutive k per lane per MFMA
+  static constexpr int MAXF = 16;  // register-resident U fragments per 32-token tile
+  static constexpr int RPAD = 16;  // r is padded to a multiple of this
+  __device__ static float f(elem e) { return bf16_to_f32(e); }
+  __device__ static elem e(float v) { return f32_to_bf16(v); }
+  __device__ static floatx16 mma(const frag& a, const frag& b, const floatx16& c) {
+    return mfma_bf16(a, b, c);
+  }
+};
+
+struct TrF32 {
+  using elem = float;
+  using frag = float;
+  static constexpr int VEC = 4;
+  static constexpr int SLOT = 1;
+  static constexpr int MAXF = 32;
+  static constexpr int RPAD = 8;
+  __device__ static float f(elem e) { return e; }
+  __device__ static elem e(float v) { return v; }
+  __device__ static floatx16 mma(const frag& a, const frag& b, const floatx16& c) {
+    return mfma_f32(a, b, c);
+  }
+};
+
+template <class Tr>
+__device__ __forceinline__ void load16(const typename Tr::elem* p, float (&v)[Tr::VEC]) {
+  u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+  if constexpr (Tr::VEC == 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(raw[j] << 16);
+      v[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(raw[j]);
+  }
+}
+
+// ------------------------------------------------------------------------- pooling
+// grid (n_tiles, S, 2); each workgroup sums kPoolRows tokens of one segment's K or V.
+template <class Tr, int D>
+__global__ __launch_bounds__(kBlock) void pool_partials_kernel(
+    const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V, int T,
+    float* __restrict__ partials, int n_tiles) {
+  using elem = typename Tr::elem;
+  constexpr int VEC = Tr::VEC;
+  constexpr int LPR = D / VEC;       // lanes per token row
+  constexpr int RPP = kBlock / LPR;  // rows per pass
+  __shared__ float red[RPP][D + 1];
+  const int tile = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
+  const elem* src = (x == 0 ? K : V) + (size_t)s * T * D;
+  const int tid = threadIdx.x;
+  const int cg = tid % LPR, rs = tid / LPR;
+  float acc[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
+  const int t0 = tile * kPoolRows;
+  const int t1 = min(T, t0 + kPoolRows);
+#pragma unroll 4
+  for (int t = t0 + rs; t < t1; t += RPP) {
+    float v[VEC];
+    load16<Tr>(src + (size_t)t * D + cg * VEC, v);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[j] += v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) red[rs][cg * VEC + j] = acc[j];
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.f;
+    for (int i = 0; i < RPP; ++i) sum += red[i][tid];
+    partials[(((size_t)x * S + s) * n_tiles + tile) * D + tid] = sum;
+  }
+}
+
+// tile sums -> pooled descriptor, one wave per segment.
+template <int D>
+__device__ __forceinline__ void pooled_query(const float* __restrict__ partials, int n_tiles,
+                                             int T, int s, int S, int lane,
+                                             float (&q)[2 * D / kWave]) {
+  constexpr int PER = 2 * D / kWave;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = lane + kWave * i;
+    const int x = c / D, ch = c % D;
+    const float* p = partials + ((size_t)x * S + s) * n_tiles * D + ch;
+    float sum = 0.f;
+    for (int tt = 0; tt < n_tiles; ++tt) sum += p[(size_t)tt * D];
+    q[i] = T > 0 ? sum / (float)T : 0.f;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave) void reduce_pool_kernel(const float* __restrict__ partials,
+                                                            int n_tiles, int T,
+                                                            float* __restrict__ q_out) {
+  constexpr int PER = 2 * D / kWave;
+  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  float q[PER];
+  pooled_query<D>(partials, n_tiles, T, s, S, lane, q);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
+}
+
+// ------------------------------------------------------------------------- matching
+// One wave per segment: q, s_a = cos(q, desc_a), w = softmax(s), score = max s, mask.
+template <int D>
+__global__ __launch_bounds__(kWave) void score_kernel(
+    const float* __restrict__ partials, int n_tiles, int T, const float* __restrict__ q_in,
+    const float* __restrict__ desc, int A, float tau, float* __restrict__ w_ws,
+    uint8_t* __restrict__ mask_ws, float* __restrict__ q_out, float* __restrict__ score_out,
+    float* __restrict__ w_out, uint8_t* __restrict__ mask_out) {
+  constexpr int PER = 2 * D / kWave;
+  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  float q[PER];
+  if (q_in != nullptr) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
+  } else {
+    pooled_query<D>(partials, n_tiles, T, s, S, lane, q);
+  }
+  float qq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
+  qq = wave_sum(qq);
+  const float nq = sqrtf(qq);
+  float sc[kMaxA];
+  float best = -INFINITY;
+  bool nan = false;
+#pragma unroll
+  for (int a = 0; a < kMaxA; ++a) {
+    sc[a] = 0.f;
+    if (a < A) {
+      const float* da = desc + ((size_t)s * A + a) * 2 * D;
+      float dd = 0.f, dq = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const float v = da[lane + kWave * i];
+        dd += v * v;
+        dq += v * q[i];
+      }
+      dd = wave_sum(dd);
+      dq = wave_sum(dq);
+      const float den = nq * sqrtf(dd);
+      const float c = (den == 0.f) ? 0.f : dq / den;
+      sc[a] = c;
+      nan |= (c != c);
+      best = fmaxf(best, c);
+    }
+  }
+  const float score = nan ? __uint_as_float(0x7fc00000u) : best;
+  float z = 0.f;
+  float ex[kMaxA];
+#pragma unroll
+  for (int a = 0; a < kMaxA; ++a) {
+    ex[a] = 0.f;
+    if (a < A) {
+      ex[a] = expf(sc[a] - score);
+      z += ex[a];
+    }
+  }
+  const uint8_t fall = !(score >= tau);
+  if (lane < A) {
+    float wv = 0.f;
+#pragma unroll
+    for (int a = 0; a < kMaxA; ++a)
+      if (a == lane) wv = ex[a] / z;
+    w_ws[(size_t)s * A + lane] = wv;
+    if (w_out) w_out[(size_t)s * A + lane] = wv;
+  }
+  if (lane == 0) {
+    mask_ws[s] = fall;
+    if (mask_out) mask_out[s] = fall;
+    if (score_out) score_out[s] = score;
+  }
+  if (q_out) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
+  }
+}
+
+// ------------------------------------------------------------------------- correction
+// grid (n_corr_tiles, S, 2): workgroup = 4 waves, each wave owns 32 tokens per iteration
+// and all d channels.  The MFMA computes (delta X)^T = W^T U^T per 32-channel block:
+// A operand = W_a^T staged in LDS (rows permuted by cmap32), B operand = U_a rows
+// (8 consecutive k per lane, straight from HBM), result register i of lane l =
+// (token l % 32, channel 16 (l / 32) + i).  Each anchor's product is finished in float32
+// and then scaled by its weight, so w never passes through bf16.
+//
+// k layout: r is padded to rp (multiple of 2*SLOT); lane half g covers k in
+// [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.
+template <class Tr, int D, int NF, bool POOL_OUT>
+__global__ __launch_bounds__(kBlock, 2) void correct_kernel(
+    const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V,
+    const typename Tr::elem* __restrict__ U, const typename Tr::elem* __restrict__ W,
+    const float* __restrict__ w_all, const uint8_t* __restrict__ mask,
+    const typename Tr::elem* __restrict__ K_fb, const typename Tr::elem* __restrict__ V_fb,
+    typename Tr::elem* K_out, typename Tr::elem* V_out, float* __restrict__ next_partials,
+    int T, int A, int r, int rp) {
+  using elem = typename Tr::elem;
+  using frag = typename Tr::frag;
+  constexpr int VEC = Tr::VEC;
+  constexpr int SLOT = Tr::SLOT;
+  constexpr int NCB = D / 32;
+  constexpr int PADK = 16 / sizeof(elem);
+  constexpr int NCH = 16 / VEC;  // 16-byte chunks holding a lane's 16 channels of a block
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  elem* wt = reinterpret_cast<elem*>(smem_raw);  // [A][D][rp + PADK]
+  __shared__ float wsh[kMaxA];
+  __shared__ float red[4][D];
+
+  const int tile = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, ln = lane & 31;
+  const size_t seg = (size_t)s * T * D;
+  const elem* X = (x == 0 ? K : V) + seg;
+  elem* Y = (x == 0 ? K_out : V_out) + seg;
+  const elem* Xfb = (x == 0 ? K_fb : V_fb);
+  const bool masked = mask[s] != 0;
+  const int tbase = tile * kCorrRowsPerIter * kCorrIters;
+
+  float qacc[POOL_OUT ? NCB : 1][16];
+  if constexpr (POOL_OUT) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qacc[cb][i] = 0.f;
+  }
+
+  if (masked) {
+    // dense-prefill stand-in: copy the fallback cache (or the source) bit for bit
+    const elem* src = Xfb ? Xfb + seg : X;
+    for (int it = 0; it < kCorrIters; ++it) {
+      const int t = tbase + it * kCorrRowsPerIter + wave * 32 + ln;
+      if (t < T) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const size_t off = (size_t)t * D + cb * 32 + 16 * g;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            u32x4 raw = *reinterpret_cast<const u32x4*>(src + off + c * VEC);
+            *reinterpret_cast<u32x4*>(Y + off + c * VEC) = raw;
+            if constexpr (POOL_OUT) {
+              const elem* v = reinterpret_cast<const elem*>(&raw);
+#pragma unroll
+              for (int j = 0; j < VEC; ++j) qacc[cb][c * VEC + j] += Tr::f(v[j]);
+            }
+          }
+        }
+      }
+    }
+  } else {
+    const int RS = rp + PADK;
+    const int half = rp / 2;
+    const int KS = half / SLOT;  // MFMA steps per anchor
+    const int nfrag = A * KS;
+    const bool uvec = (r % VEC) == 0;
+    // ---- stage W_a^T of this segment in LDS (zero for k >= r)
+    const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
+    const int chunks = A * r * (D / VEC);
+    for (int q = tid; q < chunks; q += kBlock) {
+      const int c0 = (q % (D / VEC)) * VEC;
+      const int ak = q / (D / VEC);  // a * r + k
+      const int a = ak / r, k = ak % r;
+      const elem* src = Wseg + (size_t)ak * D + c0;
+      elem v[VEC];
+      *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) wt[((size_t)a * D + c0 + j) * RS + k] = v[j];
+    }
+    if (rp > r) {
+      const int pad = rp - r;
+      for (int q = tid; q < A * D * pad; q += kBlock) {
+        const int k = r + q % pad;
+        const int ac = q / pad;
+        wt[(size_t)ac * RS + k] = Tr::e(0.f);
+      }
+    }
+    if (tid < A) wsh[tid] = w_all[(size_t)s * A + tid];
+    __syncthreads();
+
+    const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
+    for (int it = 0; it < kCorrIters; ++it) {
+      const int t0 = tbase + it * kCorrRowsPerIter + wave * 32;
+      if (t0 >= T) break;
+      const int t = t0 + ln;
+      const bool valid = t < T;
+      // ---- this lane's 16 channels of every block, issued before the MFMA work
+      u32x4 xr[NCB][NCH];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          xr[cb][c] = valid ? *reinterpret_cast<const u32x4*>(X + (size_t)t * D + cb * 32 +
+                                                              16 * g + c * VEC)
+                            : u32x4{0u, 0u, 0u, 0u};
+      // ---- U fragments of this lane's token, all anchors (register resident)
+      frag bf[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f < nfrag) {
+          const int a = f / KS, ks = f - a * KS;
+          const int k0 = g * half + ks * SLOT;
+          const elem* up = Useg + ((size_t)a * T + t) * r + k0;
+          if constexpr (SLOT == 8) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (valid && k0 < r) {
+              if (uvec) {
+                v = *reinterpret_cast<const u32x4*>(up);
+              } else {
+                uint16_t tmp[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) tmp[j] = (k0 + j < r) ? up[j] : (uint16_t)0;
+                v = *reinterpret_cast<u32x4*>(tmp);
+              }
+            }
+            bf[f] = v;
+          } else {
+            bf[f] = (valid && k0 < r) ? Tr::f(*up) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const elem* ap = wt + (size_t)(cb * 32 + cmap32(ln)) * RS + g * half;
+        floatx16 acc, tmp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { acc[i] = 0.f; tmp[i] = 0.f; }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f < nfrag) {
+            const int a = f / KS, ks = f - a * KS;
+            frag af;
+            if constexpr (SLOT == 8) {
+              af = *reinterpret_cast<const u32x4*>(ap + (size_t)a * D * RS + ks * SLOT);
+            } else {
+              af = ap[(size_t)a * D * RS + ks];
+            }
+            tmp = Tr::mma(af, bf[f], tmp);
+            if (ks == KS - 1) {
+              const float wa = wsh[a];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) { acc[i] += wa * tmp[i]; tmp[i] = 0.f; }
+            }
+          }
+        }
+        if (valid) {
+          const size_t off = (size_t)t * D + cb * 32 + 16 * g;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const elem* xv = reinterpret_cast<const elem*>(&xr[cb][c]);
+            elem ov[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+              ov[j] = Tr::e(Tr::f(xv[j]) + acc[c * VEC + j]);
+              if constexpr (POOL_OUT) qacc[cb][c * VEC + j] += Tr::f(ov[j]);
+            }
+            *reinterpret_cast<u32x4*>(Y + off + c * VEC) = *reinterpret_cast<u32x4*>(ov);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (POOL_OUT) {
+    // token sums of the stored output: lanes -> half-wave sums -> waves in fixed order
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = half_wave_sum(qacc[cb][i]);
+        if (ln == 0) red[wave][cb * 32 + 16 * g + i] = v;
+      }
+    __syncthreads();
+    if (tid < D) {
+      const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      next_partials[(((size_t)x * S + s) * gridDim.x + tile) * D + tid] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- launchers
+template <class Tr, int D>
+static hipError_t pool_partials_t(const void* K, const void* V, int S, int T, float* partials,
+                                  int n_tiles, hipStream_t st) {
+  dim3 grid(n_tiles, S, 2);
+  hipLaunchKernelGGL((pool_partials_kernel<Tr, D>), grid, dim3(kBlock), 0, st,
+                     (const typename Tr::elem*)K, (const typename Tr::elem*)V, T, partials,
+                     n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_partials(const void* K, const void* V, int S, int T, int d, int dtype,
+                                float* partials, int n_tiles, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  if (dtype == KVC_BF16)
+    return d == 128 ? pool_partials_t<TrBF16, 128>(K, V, S, T, partials, n_tiles, st)
+                    : pool_partials_t<TrBF16, 64>(K, V, S, T, partials, n_tiles, st);
+  return d == 128 ? pool_partials_t<TrF32, 128>(K, V, S, T, partials, n_tiles, st)
+                  : pool_partials_t<TrF32, 64>(K, V, S, T, partials, n_tiles, st);
+}
+
+hipError_t launch_reduce_pool(const float* partials, int n_tiles, int T, int S, int d,
+                              float* q_out, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL((reduce_pool_kernel<128>), dim3(S), dim3(kWave), 0, st, partials,
+                       n_tiles, T, q_out);
+  else
+    hipLaunchKernelGGL((reduce_pool_kernel<64>), dim3(S), dim3(kWave), 0, st, partials,
+                       n_tiles, T, q_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const float* partials, int n_tiles, int T, const float* q_in,
+                        const float* desc, int S, int d, int A, float tau, float* q_ws,
+                        float* w_ws, float* score_ws, uint8_t* mask_ws, float* q_out,
+                        float* score_out, float* w_out, uint8_t* mask_out, hipStream_t st) {
+  (void)q_ws;
+  if (S == 0) return hipSuccess;
+  float* so = score_out ? score_out : score_ws;
+  if (d == 128)
+    hipLaunchKernelGGL((score_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
+                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out);
+  else
+    hipLaunchKernelGGL((score_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
+                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out);
+  return hipGetLastError();
+}
+
+template <class Tr, int D, int NF>
+static hipError_t correct_nf(const void* K, const void* V, int S, int T, const void* U,
+                             const void* W, int A, int r, int rp, const float* w,
+                             const uint8_t* mask, const void* K_fb, const void* V_fb,
+                             void* K_out, void* V_out, float* next_partials, hipStream_t st) {
+  using elem = typename Tr::elem;
+  const int PADK = 16 / (int)sizeof(elem);
+  const size_t lds = (size_t)A * D * (rp + PADK) * sizeof(elem);
+  const int n_tiles = T > 0 ? ceil_div(T, kCorrRowsPerIter * kCorrIters) : 1;
+  dim3 grid(n_tiles, S, 2);
+  auto k_pool = correct_kernel<Tr, D, NF, true>;
+  auto k_plain = correct_kernel<Tr, D, NF, false>;
+  if (lds > 48 * 1024) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pool),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plain),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }
+  hipLaunchKernelGGL(next_partials ? k_pool : k_plain, grid, dim3(kBlock), lds, st,
+                     (const elem*)K, (const elem*)V, (const elem*)U, (const elem*)W, w, mask,
+                     (const elem*)K_fb, (const elem*)V_fb, (elem*)K_out, (elem*)V_out,
+                     next_partials, T, A, r, rp);
+  return hipGetLastError();
+}
+
+// Picks the smallest register-resident fragment count that holds A * (rp / 2 / SLOT).
+template <class Tr, int D>
+static hipError_t correct_t(const void* K, const void* V, int S, int T, const void* U,
+                            const void* W, int A, int r, const float* w, const uint8_t* mask,
+                            const void* K_fb, const void* V_fb, void* K_out, void* V_out,
+                            float* next_partials, hipStream_t st) {
+  const int rp = (r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
+  const int nfrag = A * (rp / 2 / Tr::SLOT);
+  constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
+  if (nfrag <= F0)
+    return correct_nf<Tr, D, F0>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
+                                 next_partials, st);
+  if (nfrag <= F1)
+    return correct_nf<Tr, D, F1>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
+                                 next_partials, st);
+  return correct_nf<Tr, D, F2>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
+                               next_partials, st);
+}
+
+hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
+                          const void* U, const void* W, int A, int r, const float* w,
+                          const uint8_t* mask, const void* K_fb, const void* V_fb, void* K_out,
+                          void* V_out, float* next_partials, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  if (dtype == KVC_BF16)
+    return d == 128 ? correct_t<TrBF16, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
+                                             V_out, next_partials, st)
+                    : correct_t<TrBF16, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
+                                            V_out, next_partials, st);
+  return d == 128 ? correct_t<TrF32, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
+                                          V_out, next_partials, st)
+                  : correct_t<TrF32, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
+                                         V_out, next_partials, st);
+}
+
+}  // namespace kvc

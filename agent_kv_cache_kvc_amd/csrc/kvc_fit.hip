@@ -1,0 +1,541 @@
+// Rank-r anchor fit of a cache delta on gfx950.
+//
+// KVCMAS (thelatestinai listing): cross-agent cache deviations are kept as compact
+// low-rank states (abstract) of rank r_delta = 32 by default (Fig. 13); Figs. 2 and 7(a)
+// measure a delta's effective rank as the minimum rank holding 90% of the singular-value
+// energy.  The anchor is the best rank-r approximation of delta = exact - reused, found
+// through the eigen-decomposition of its Gram matrix:
+//   gram_kernel     G partials = delta_chunk^T delta_chunk on MFMA (upper 32x32 blocks)
+//   jacobi_kernel   sum partials in fixed order, one-sided Jacobi on G in LDS, sort,
+//                   effective rank (float64 running sum), canonical signs, W, bf16 hi/lo W
+//   project_kernel  U = delta W^T on MFMA (W split into bf16 hi + lo for bf16 deltas)
+#include <hip/hip_runtime.h>
+
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// Upper-triangular block (I, J), I <= J, of an nb x nb grid of 32x32 blocks -> index.
+__host__ __device__ constexpr int blk_index(int I, int J, int nb) {
+  return I * nb - I * (I - 1) / 2 + (J - I);
+}
+
+// Which Gram blocks each of the 4 waves owns.  d = 128 (10 blocks): 3, 3, 2, 2 blocks;
+// d = 64 (3 blocks): one each for waves 0..2.  {I, J} pairs, -1 = none.
+__constant__ int c_blk128[4][3][2] = {
+    {{0, 0}, {0, 1}, {1, 1}}, {{2, 2}, {2, 3}, {3, 3}}, {{0, 2}, {0, 3}, {-1, -1}},
+    {{1, 2}, {1, 3}, {-1, -1}}};
+__constant__ int c_blk64[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
+                                      {{0, 1}, {-1, -1}, {-1, -1}},
+                                      {{1, 1}, {-1, -1}, {-1, -1}},
+                                      {{-1, -1}, {-1, -1}, {-1, -1}}};
+
+// ------------------------------------------------------------------------- Gram, bf16
+// grid (nsplit, M).  Each slab of SLAB = 16384/D tokens is loaded as 8x8 bf16 blocks
+// (one per thread, 8 rows x 16 bytes, coalesced), transposed in registers and stored
+// channel-major in LDS, so an MFMA fragment (8 consecutive tokens of one channel) is a
+// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator.
+template <int D>
+__global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __restrict__ delta,
+                                                              int T, int chunk,
+                                                              float* __restrict__ partials) {
+  constexpr int SLAB = 16384 / D;
+  constexpr int SR = SLAB + 8;  // LDS row stride (bf16 elements), 16-byte pad
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  constexpr int CG = D / 8;  // 8-channel groups per row
+  __shared__ __align__(16) uint16_t lt[D * SR];
+  const int split = blockIdx.x, m = blockIdx.y, nsplit = gridDim.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, ln = lane & 31;
+  const uint16_t* src = delta + (size_t)m * T * D;
+  const int t_begin = split * chunk;
+  const int t_end = min(T, t_begin + chunk);
+  const int rg = tid / CG, cg = tid % CG;
+
+  int I[3], J[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    I[b] = D == 128 ? c_blk128[wave][b][0] : c_blk64[wave][b][0];
+    J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
+  }
+  floatx16 acc[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+
+  for (int ts = t_begin; ts < t_end; ts += SLAB) {
+    // ---- load an 8x8 block: rows ts + 8 rg + i, channels 8 cg .. 8 cg + 7
+    u32x4 in[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = ts + 8 * rg + i;
+      in[i] = (t < t_end) ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * cg)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();  // previous slab's fragments are consumed
+    // ---- transpose: out[j] = channel 8 cg + j, tokens 8 rg .. 8 rg + 7
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = in[2 * k][j >> 1], b = in[2 * k + 1][j >> 1];
+        o[k] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      *reinterpret_cast<u32x4*>(&lt[(8 * cg + j) * SR + 8 * rg]) = o;
+    }
+    __syncthreads();
+    // ---- MFMA over the slab's k-steps of 16 tokens
+#pragma unroll 2
+    for (int ks = 0; ks < SLAB / 16; ++ks) {
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        if (I[b] >= 0) {
+          const u32x4 fa =
+              *reinterpret_cast<const u32x4*>(&lt[(I[b] * 32 + ln) * SR + 16 * ks + 8 * g]);
+          const u32x4 fb =
+              *reinterpret_cast<const u32x4*>(&lt[(J[b] * 32 + ln) * SR + 16 * ks + 8 * g]);
+          acc[b] = mfma_bf16(fa, fb, acc[b]);
+        }
+      }
+    }
+  }
+  // ---- write this workgroup's blocks: [m][split][blk][reg][lane]
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    if (I[b] >= 0) {
+      float* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = acc[b][i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- Gram, fp32
+// Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2.
+template <int D>
+__global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __restrict__ delta,
+                                                             int T, int chunk,
+                                                             float* __restrict__ partials) {
+  constexpr int SLAB = 8192 / D;
+  constexpr int SR = D + 4;
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  constexpr int C4 = D / 4;
+  __shared__ __align__(16) float lt[SLAB * SR];
+  const int split = blockIdx.x, m = blockIdx.y, nsplit = gridDim.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, ln = lane & 31;
+  const float* src = delta + (size_t)m * T * D;
+  const int t_begin = split * chunk;
+  const int t_end = min(T, t_begin + chunk);
+  int I[3], J[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    I[b] = D == 128 ? c_blk128[wave][b][0] : c_blk64[wave][b][0];
+    J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
+  }
+  floatx16 acc[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+  for (int ts = t_begin; ts < t_end; ts += SLAB) {
+    __syncthreads();
+    for (int q = tid; q < SLAB * C4; q += kBlock) {
+      const int row = q / C4, c4 = q % C4;
+      const int t = ts + row;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (t < t_end) v = *reinterpret_cast<const floatx4*>(src + (size_t)t * D + 4 * c4);
+      *reinterpret_cast<floatx4*>(&lt[row * SR + 4 * c4]) = v;
+    }
+    __syncthreads();
+    for (int ks = 0; ks < SLAB / 2; ++ks) {
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        if (I[b] >= 0) {
+          const float fa = lt[(2 * ks + g) * SR + I[b] * 32 + ln];
+          const float fb = lt[(2 * ks + g) * SR + J[b] * 32 + ln];
+          acc[b] = mfma_f32(fa, fb, acc[b]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    if (I[b] >= 0) {
+      float* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = acc[b][i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- Jacobi
+// One workgroup per matrix.  LDS holds A (starts as G) and V (starts as I), both
+// column-major with a padded column stride.  Each step of a sweep rotates d/2 disjoint
+// column pairs (round-robin "circle" ordering, every pair once per sweep); a pair is
+// owned by 256/(d/2) adjacent lanes that each hold d/(that) rows.  For columns a_i, a_j:
+//   alpha = |a_i|^2, beta = |a_j|^2, gamma = a_i . a_j,
+//   zeta = (beta - alpha) / (2 gamma), t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
+//   c = 1 / sqrt(1 + t^2), s = c t,  a_i <- c a_i - s a_j,  a_j <- s a_i + c a_j,
+// which makes the pair orthogonal; V gets the same rotation.  At convergence A = G V has
+// orthogonal columns, so V holds eigenvectors and lambda_i = |a_i|.  A pair is left alone
+// when |gamma| <= max(tol sqrt(alpha beta), eta |G|_F^2); the loop ends after a sweep
+// without rotations or after kJacobiMaxSweeps sweeps (uniform across the workgroup).
+__device__ __forceinline__ void rr_pair(int p, int step, int n, int& i, int& j) {
+  const int a = (p == 0) ? 0 : ((p - 1 + step) % (n - 1)) + 1;
+  const int b = ((n - 2 - p + step) % (n - 1)) + 1;
+  i = min(a, b);
+  j = max(a, b);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
+    const float* __restrict__ partials, int nsplit, int r, double energy, float tol, float eta,
+    float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
+    uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad,
+    int* __restrict__ sweeps_out) {
+  constexpr int CS = D + 4;           // column stride (floats)
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  constexpr int TPP = kBlock / (D / 2);  // threads per pair: 4 (d=128) or 8 (d=64)
+  constexpr int RPT = D / TPP;           // rows per thread: 32 or 8
+  extern __shared__ __align__(16) float smem[];
+  float* Am = smem;           // [D][CS]
+  float* Vm = smem + D * CS;  // [D][CS]
+  __shared__ float lam[D];
+  __shared__ int order[D];
+  __shared__ float redf[kBlock / kWave];
+  __shared__ int redi[kBlock / kWave];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+
+  // ---- G = sum of the partials (fixed order), mirrored to a full symmetric matrix
+  const float* P = partials + (size_t)m * nsplit * NBLK * 1024;
+  float fro = 0.f;
+  for (int e = tid; e < NBLK * 1024; e += kBlock) {
+    const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += P[(size_t)sp * NBLK * 1024 + e];
+    int I = 0, rem = blk;
+    while (rem >= NB - I) { rem -= NB - I; ++I; }
+    const int J = I + rem;
+    const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
+    const int col = J * 32 + (l % 32);
+    if (row > col) continue;  // a diagonal block's lower half: its mirror writes it
+    Am[col * CS + row] = v;
+    Am[row * CS + col] = v;
+    fro += (row == col) ? v * v : 2.f * v * v;
+  }
+  for (int e = tid; e < D * D; e += kBlock) {
+    const int c = e / D, rr = e % D;
+    Vm[c * CS + rr] = (c == rr) ? 1.f : 0.f;
+  }
+  fro = wave_sum(fro);
+  if (lane == 0) redf[wave] = fro;
+  __syncthreads();
+  const float f2 = ((redf[0] + redf[1]) + redf[2]) + redf[3];
+  const float abs_floor = eta * f2;
+
+  // ---- sweeps
+  const int p = tid / TPP, sub = tid % TPP;
+  int sweep = 0;
+  for (; sweep < kJacobiMaxSweeps; ++sweep) {
+    int rotated = 0;
+    for (int step = 0; step < D - 1; ++step) {
+      int ci, cj;
+      rr_pair(p, step, D, ci, cj);
+      float* ai = Am + ci * CS + sub * RPT;
+      float* aj = Am + cj * CS + sub * RPT;
+      float xi[RPT], xj[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; k += 4) {
+        *reinterpret_cast<floatx4*>(&xi[k]) = *reinterpret_cast<const floatx4*>(ai + k);
+        *reinterpret_cast<floatx4*>(&xj[k]) = *reinterpret_cast<const floatx4*>(aj + k);
+      }
+      float al = 0.f, be = 0.f, ga = 0.f;
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        al += xi[k] * xi[k];
+        be += xj[k] * xj[k];
+        ga += xi[k] * xj[k];
+      }
+#pragma unroll
+      for (int off = 1; off < TPP; off <<= 1) {
+        al += __shfl_xor(al, off, 64);
+        be += __shfl_xor(be, off, 64);
+        ga += __shfl_xor(ga, off, 64);
+      }
+      const float lim = fmaxf(tol * sqrtf(al) * sqrtf(be), abs_floor);
+      if (fabsf(ga) > lim) {
+        rotated = 1;
+        const float zeta = (be - al) / (2.f * ga);
+        const float t = copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
+        const float c = 1.f / sqrtf(1.f + t * t);
+        const float s = c * t;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+          const float u = xi[k], v = xj[k];
+          xi[k] = c * u - s * v;
+          xj[k] = s * u + c * v;
+        }
+#pragma unroll
+        for (int k = 0; k < RPT; k += 4) {
+          *reinterpret_cast<floatx4*>(ai + k) = *reinterpret_cast<floatx4*>(&xi[k]);
+          *reinterpret_cast<floatx4*>(aj + k) = *reinterpret_cast<floatx4*>(&xj[k]);
+        }
+        float* vi = Vm + ci * CS + sub * RPT;
+        float* vj = Vm + cj * CS + sub * RPT;
+#pragma unroll
+        for (int k = 0; k < RPT; k += 4) {
+          floatx4 u = *reinterpret_cast<const floatx4*>(vi + k);
+          floatx4 v = *reinterpret_cast<const floatx4*>(vj + k);
+          floatx4 nu, nv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            nu[q] = c * u[q] - s * v[q];
+            nv[q] = s * u[q] + c * v[q];
+          }
+          *reinterpret_cast<floatx4*>(vi + k) = nu;
+          *reinterpret_cast<floatx4*>(vj + k) = nv;
+        }
+      }
+      __syncthreads();
+    }
+    // uniform convergence test
+    const int any = __any(rotated) ? 1 : 0;
+    if (lane == 0) redi[wave] = any;
+    __syncthreads();
+    const int tot = redi[0] | redi[1] | redi[2] | redi[3];
+    __syncthreads();
+    if (!tot) { ++sweep; break; }
+  }
+
+  // ---- eigenvalues = column norms of A; order by descending value (ties: lower index)
+  if (tid < D) {
+    const float* a = Am + tid * CS;
+    float ss = 0.f;
+    for (int k = 0; k < D; ++k) ss += a[k] * a[k];
+    lam[tid] = sqrtf(ss);
+  }
+  __syncthreads();
+  if (tid < D) {
+    const float li = lam[tid];
+    int rank = 0;
+    for (int k = 0; k < D; ++k) {
+      const float lk = lam[k];
+      rank += (lk > li) || (lk == li && k < tid);
+    }
+    order[rank] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    for (int k = 0; k < D; ++k) total += (double)lam[order[k]];
+    int ke = 0;
+    if (total > 0.0) {
+      const double need = energy * total;
+      double run = 0.0;
+      ke = D;
+      for (int k = 0; k < D; ++k) {
+        run += (double)lam[order[k]];
+        if (run >= need) { ke = k + 1; break; }
+      }
+    }
+    k_eff_out[m] = ke;
+    if (sweeps_out) sweeps_out[m] = sweep;
+  }
+  if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = lam[order[tid]];
+  // ---- canonical sign of each kept eigenvector: largest |entry| (first on ties) positive
+  __shared__ float sgn[D];
+  if (tid < r) {
+    const float* v = Vm + order[tid] * CS;
+    float best = -1.f, bv = 0.f;
+    for (int k = 0; k < D; ++k) {
+      const float av = fabsf(v[k]);
+      if (av > best) { best = av; bv = v[k]; }
+    }
+    sgn[tid] = bv < 0.f ? -1.f : 1.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < rpad * D; e += kBlock) {
+    const int k = e / D, c = e % D;
+    float wv = 0.f;
+    if (k < r) {
+      wv = sgn[k] * Vm[order[k] * CS + c];
+      W_out[((size_t)m * r + k) * D + c] = wv;
+    }
+    if (w_hi) {
+      const uint16_t hi = f32_to_bf16(wv);
+      const uint16_t lo = f32_to_bf16(wv - bf16_to_f32(hi));
+      w_hi[((size_t)m * rpad + k) * D + c] = hi;
+      w_lo[((size_t)m * rpad + k) * D + c] = lo;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- projection
+// grid (n_tiles, M): U[t, j] = sum_c delta[t, c] W[j, c].  Orientation U^T = W delta^T:
+// A operand = W rows (row m of a 32-block = component 32 mb + cmap32(m)), B operand =
+// delta rows; result register i of lane l = (token l % 32, component 32 mb + 16 (l/32) + i).
+// k layout: lane half g covers channels [g D/2, (g+1) D/2), SLOT consecutive per MFMA.
+constexpr int kProjIters = 4;
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
+    const uint16_t* __restrict__ delta, const uint16_t* __restrict__ w_hi,
+    const uint16_t* __restrict__ w_lo, int T, int r, int rpad, float* __restrict__ U_out) {
+  constexpr int KS = D / 16;  // MFMA steps over d
+  const int tile = blockIdx.x, m = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, ln = lane & 31;
+  const uint16_t* src = delta + (size_t)m * T * D;
+  const bool uvec = (r % 4) == 0;
+  for (int mb = 0; mb < rpad / 32; ++mb) {
+    const int jrow = mb * 32 + cmap32(ln);
+    u32x4 ah[KS], al[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = ((size_t)m * rpad + jrow) * D + g * (D / 2) + 8 * ks;
+      ah[ks] = *reinterpret_cast<const u32x4*>(w_hi + off);
+      al[ks] = *reinterpret_cast<const u32x4*>(w_lo + off);
+    }
+    for (int it = 0; it < kProjIters; ++it) {
+      const int t0 = (tile * kProjIters + it) * kCorrRowsPerIter + wave * 32;
+      if (t0 >= T) break;
+      const int t = t0 + ln;
+      const bool valid = t < T;
+      u32x4 b[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        b[ks] = valid ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + g * (D / 2) + 8 * ks)
+                      : u32x4{0u, 0u, 0u, 0u};
+      floatx16 acc0, acc1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc0 = mfma_bf16(ah[ks], b[ks], acc0);
+        acc1 = mfma_bf16(al[ks], b[ks], acc1);
+      }
+      if (valid) {
+        float* dst = U_out + ((size_t)m * T + t) * r + mb * 32 + 16 * g;
+        const int jb = mb * 32 + 16 * g;
+        if (uvec && jb + 16 <= r) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            floatx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc0[4 * q + e] + acc1[4 * q + e];
+            *reinterpret_cast<floatx4*>(dst + 4 * q) = o;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (jb + i < r) dst[i] = acc0[i] + acc1[i];
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 2) void project_f32_kernel(const float* __restrict__ delta,
+                                                                const float* __restrict__ W,
+                                                                int T, int r, int rpad,
+                                                                float* __restrict__ U_out) {
+  constexpr int KH = D / 2;  // MFMA steps over d (one k per lane half)
+  const int tile = blockIdx.x, m = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, ln = lane & 31;
+  const float* src = delta + (size_t)m * T * D;
+  for (int mb = 0; mb < rpad / 32; ++mb) {
+    const int j = mb * 32 + cmap32(ln);
+    float a[KH];
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+      a[ks] = (j < r) ? W[((size_t)m * r + j) * D + g * KH + ks] : 0.f;
+    for (int it = 0; it < kProjIters; ++it) {
+      const int t0 = (tile * kProjIters + it) * kCorrRowsPerIter + wave * 32;
+      if (t0 >= T) break;
+      const int t = t0 + ln;
+      const bool valid = t < T;
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < KH / 4; ++k4) {
+        floatx4 bv = {0.f, 0.f, 0.f, 0.f};
+        if (valid) bv = *reinterpret_cast<const floatx4*>(src + (size_t)t * D + g * KH + 4 * k4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(a[4 * k4 + e], bv[e], acc);
+      }
+      if (valid) {
+        float* dst = U_out + ((size_t)m * T + t) * r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int jj = mb * 32 + 16 * g + i;
+          if (jj < r) dst[jj] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- launcher
+template <typename K>
+static void allow_dynamic_lds(K kernel, size_t bytes) {
+  if (bytes > 48 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int D>
+static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double energy,
+                        float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
+                        hipStream_t st) {
+  float* partials = reinterpret_cast<float*>(ws + f.off_gram);
+  uint16_t* whi = reinterpret_cast<uint16_t*>(ws + f.off_whi);
+  uint16_t* wlo = reinterpret_cast<uint16_t*>(ws + f.off_wlo);
+  int* sweeps = reinterpret_cast<int*>(ws + f.off_sweeps);
+  const dim3 g1(f.nsplit, f.M);
+  if (dtype == KVC_BF16)
+    hipLaunchKernelGGL((gram_bf16_kernel<D>), g1, dim3(kBlock), 0, st,
+                       (const uint16_t*)delta, f.T, f.chunk, partials);
+  else
+    hipLaunchKernelGGL((gram_f32_kernel<D>), g1, dim3(kBlock), 0, st, (const float*)delta,
+                       f.T, f.chunk, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = 2ull * D * (D + 4) * sizeof(float);
+  allow_dynamic_lds(jacobi_kernel<D>, lds);
+  const float tol = 2e-6f, eta = 1e-12f;
+  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kBlock), lds, st, partials, f.nsplit,
+                     f.r, energy, tol, eta, W_out, eig, k_eff,
+                     dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
+                     f.rpad, sweeps);
+  e = hipGetLastError();
+  if (e != hipSuccess || f.T == 0) return e;
+  const int n_tiles = ceil_div(f.T, kCorrRowsPerIter * kProjIters);
+  const dim3 g3(n_tiles, f.M);
+  if (dtype == KVC_BF16)
+    hipLaunchKernelGGL((project_bf16_kernel<D>), g3, dim3(kBlock), 0, st,
+                       (const uint16_t*)delta, whi, wlo, f.T, f.r, f.rpad, U_out);
+  else
+    hipLaunchKernelGGL((project_f32_kernel<D>), g3, dim3(kBlock), 0, st, (const float*)delta,
+                       W_out, f.T, f.r, f.rpad, U_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
+                      float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
+                      hipStream_t st) {
+  if (f.M == 0) return hipSuccess;
+  return f.d == 128 ? fit_t<128>(delta, f, dtype, energy, U_out, W_out, k_eff, eig, ws, st)
+                    : fit_t<64>(delta, f, dtype, energy, U_out, W_out, k_eff, eig, ws, st);
+}
+
+}  // namespace kvc

@@ -1,0 +1,152 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) library for KVCMAS's online KV-cache correction.
+ *
+ * Method: "KVCMAS: Efficient KV cache Correction for Shared Context in Multi-Agent
+ * Systems" (arXiv:2609.34060).  Fig. 1 of the thelatestinai listing: a shared-context
+ * (PH) segment's cache, reused from the preceding agent, is matched against the segment's
+ * online anchors; their low-rank corrections are combined with similarity-based weights;
+ * an unreliable segment falls back to dense prefill; the corrected cache becomes the next
+ * workflow edge's reference (chaining).  Figs. 2 and 7 define the effective rank at 90% of
+ * the singular-value energy; Fig. 13 sets the delta rank (default 32).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers (HIP global memory), dense, row-major,
+ *    with the shapes given below.  The caller owns every buffer, including the workspace;
+ *    the library allocates nothing and keeps no state between calls.
+ *  - Caches K, V (and fallbacks, outputs): [L, H, T, d] = (layer, kv-head, token,
+ *    channel).  One (l, h) pair is a segment; S = L*H.
+ *  - dtype: KVC_BF16 (bfloat16) or KVC_F32 (float32) for caches, anchor factors and the
+ *    fit input.  Descriptors, weights and fit outputs are float32.
+ *  - d must be 64 or 128.  Sizes are int; every element count must fit in 2^62.
+ *  - Pointers to caches, factors and float outputs must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
+ *    on it and return; results are valid once the stream has been synchronised.
+ *  - Arguments are validated before any HIP call: a bad argument returns KVC_ERR_ARG
+ *    (or KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE) and enqueues nothing.  A failing HIP
+ *    launch returns KVC_ERR_HIP.  kvc_last_error() then describes the failure.
+ *  - Calls that overlap in time on different streams must not share a workspace.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
+
+typedef enum {
+    KVC_OK = 0,
+    KVC_ERR_ARG = 1,         /* null / misaligned pointer, negative size, bad shape    */
+    KVC_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement           */
+    KVC_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed             */
+    KVC_ERR_WORKSPACE = 4    /* workspace pointer null or smaller than required        */
+} kvc_status;
+
+/* Library version string, static storage. */
+const char* kvc_version(void);
+
+/* Message for the last non-OK status returned on the calling thread (thread-local,
+ * valid until that thread's next call); "" if none. */
+const char* kvc_last_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Pooled descriptor (Fig. 1(b): the current cache representation that is matched
+ * against the online anchors).  Read here as the token mean of K followed by the token
+ * mean of V:  q[l,h,0:d] = (1/T) sum_t K[l,h,t,:],  q[l,h,d:2d] = (1/T) sum_t V[l,h,t,:].
+ * T = 0 gives q = 0.  Summation is float32 in a fixed order (deterministic).
+ *   K, V   : [L,H,T,d] dtype, read only
+ *   q_out  : [L,H,2d] float32, written
+ *   ws     : workspace of at least kvc_pool_workspace_bytes(L,H,T,d) bytes
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_pool_workspace_bytes(int L, int H, int T, int d);
+kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, float* q_out, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Correction of a reused shared-context cache (Figs. 1(a), 1(b); the abstract's compact
+ * low-rank states).  Per segment (l,h), with q the pooled descriptor of (K, V):
+ *   s_a   = cos(q, desc[l,h,a])  (0 if either vector is zero)          a = 0..A-1
+ *   w     = softmax(s)           (temperature 1)
+ *   score = max_a s_a;  fallback = !(score >= tau)   (float32 compare; NaN falls back)
+ *   reliable segment:  X' = X + sum_a w_a U[x,l,h,a] W[x,l,h,a]   for X in {K, V}
+ *                      (x = 0 for K, 1 for V; products accumulated in float32 and the
+ *                      sum stored once in dtype, round-to-nearest-even)
+ *   fallback segment:  X' = X_fb (dense-prefill stand-in) if given, else X, bit exact;
+ *                      U and W are not read.
+ *   K, V        : [L,H,T,d] dtype                      (source cache, read only)
+ *   desc        : [L,H,A,2d] float32                   (anchor descriptors)
+ *   U           : [2,L,H,A,T,r] dtype                  (left factors, index 0 = K)
+ *   W           : [2,L,H,A,r,d] dtype                  (right factors)
+ *   A, r        : 1 <= A, 1 <= r <= 64, A * ceil(r/16)*16 <= 256
+ *   tau         : reliability threshold (+inf: every segment falls back; -inf: none)
+ *   q_in        : [L,H,2d] float32 or NULL: a precomputed pooled descriptor of (K, V);
+ *                 when NULL it is computed here (one extra read of K and V)
+ *   K_fb, V_fb  : [L,H,T,d] dtype or NULL (both or neither)
+ *   K_out, V_out: [L,H,T,d] dtype, written; may equal K / V (in place); must not
+ *                 otherwise overlap any input
+ *   mask_out    : [L,H] uint8, 1 = fall back, written
+ *   score_out   : [L,H] float32 or NULL;  w_out: [L,H,A] float32 or NULL
+ *   q_next_out  : [L,H,2d] float32 or NULL: pooled descriptor of (K_out, V_out)
+ *   ws          : at least kvc_correct_workspace_bytes(L,H,T,d,A,r) bytes
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_correct_workspace_bytes(int L, int H, int T, int d, int A, int r);
+kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d, int dtype,
+                       const float* desc, const void* U, const void* W, int A, int r,
+                       float tau, const float* q_in, const void* K_fb, const void* V_fb,
+                       void* K_out, void* V_out, uint8_t* mask_out, float* score_out,
+                       float* w_out, float* q_next_out, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Chained correction along a workflow A0 -> A1 -> ... (Fig. 1(c); Fig. 3(b): A0's cache
+ * is exact).  Edge e corrects its source with its own anchors; the stored result is the
+ * source of edge e+1; edge 0's source is (K0, V0), which is not modified.  The pooled
+ * descriptor of every edge >= 1 is taken from the previous edge's output pass, so each
+ * source is read from memory once.
+ *   n_edges >= 1.  Every array below is a HOST array of n_edges DEVICE pointers, laid
+ *   out as for kvc_correct: desc[e], U[e], W[e], K_out[e], V_out[e], mask_out[e]
+ *   required; K_fb / V_fb (the array itself or an entry, both or neither per edge) and
+ *   score_out may be NULL.  K_out[e] must not overlap K_out[e-1] or the edge's inputs.
+ *   ws: at least kvc_chain_workspace_bytes(L,H,T,d,A,r) bytes.
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_chain_workspace_bytes(int L, int H, int T, int d, int A, int r);
+kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T, int d,
+                             int dtype, int n_edges, const float* const* desc,
+                             const void* const* U, const void* const* W, int A, int r,
+                             float tau, const void* const* K_fb, const void* const* V_fb,
+                             void* const* K_out, void* const* V_out,
+                             uint8_t* const* mask_out, float* const* score_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Rank-r anchor fit of a cache delta (delta = exact - reused, one [T,d] matrix per
+ * (K|V, layer, head)).  The anchor is the best rank-r approximation U W of delta (the
+ * compact low-rank state of the abstract; r = r_delta of Fig. 13), computed as
+ *   G = delta^T delta (float32 accumulation of exact bf16 products, fixed order),
+ *   G = Q diag(lambda) Q^T by one-sided Jacobi (float32), lambda sorted descending,
+ *   W = first r columns of Q, as rows, each row's largest-|.| entry positive,
+ *   U = delta W^T (float32 accumulation),
+ * and the effective rank k = min{k >= 1 : sum_{i<k} lambda_i >= energy * sum lambda}
+ * (0 for a zero delta), the running sum and compare in float64 (Figs. 2, 7(a)).
+ *   delta    : [M,T,d] dtype, read only
+ *   r        : 1 <= r <= d
+ *   energy   : in (0, 1], 0.9 in the pages
+ *   U_out    : [M,T,r] float32;  W_out: [M,r,d] float32;  k_eff_out: [M] int32
+ *   eig_out  : [M,d] float32 (lambda, descending) or NULL
+ *   ws       : at least kvc_fit_workspace_bytes(M,T,d,r) bytes
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_fit_workspace_bytes(int M, int T, int d, int r);
+kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int r,
+                          double energy, float* U_out, float* W_out, int32_t* k_eff_out,
+                          float* eig_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

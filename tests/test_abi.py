@@ -1,0 +1,119 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and rejects bad
+arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import agent_kv_cache_kvc_amd as kvc
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    lib = kvc.lib()
+    names = _declared()
+    assert "kvc_correct" in names and "kvc_fit_anchor" in names and "kvc_correct_chain" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_the_abi():
+    for n in ("pool_descriptor", "correct", "correct_chain", "fit_anchor"):
+        assert callable(getattr(kvc, n))
+    assert set(kvc._SIGS) == set(_declared())
+
+
+def test_version_and_empty_error():
+    assert kvc.lib().kvc_version().startswith(b"kvc")
+
+
+def _correct(**kw):
+    args = dict(K=FAKE, V=FAKE, L=2, H=2, T=64, d=128, dtype=0, desc=FAKE, U=FAKE, W=FAKE, A=4,
+                r=32, tau=0.3, q_in=None, K_fb=None, V_fb=None, K_out=FAKE, V_out=FAKE,
+                mask=FAKE, score=None, w=None, qn=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    st = kvc.lib().kvc_correct(*args.values())
+    return st, kvc.lib().kvc_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=None), 1, "K is NULL"),
+    (dict(V=FAKE + 4), 1, "aligned"),
+    (dict(T=-1), 1, "negative"),
+    (dict(d=96), 2, "d=96"),
+    (dict(d=0), 1, "positive"),
+    (dict(dtype=7), 1, "dtype"),
+    (dict(A=0), 1, "A=0"),
+    (dict(A=17), 2, "A=17"),
+    (dict(r=0), 1, "r=0"),
+    (dict(r=65), 2, "r=65"),
+    (dict(A=8, r=48), 2, "A*ceil16"),
+    (dict(dtype=1, A=2, r=40), 2, "fp32"),
+    (dict(K_fb=FAKE), 1, "both"),
+    (dict(mask=None), 1, "mask_out"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(ws=FAKE, ws_bytes=16), 4, "workspace"),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), 4, "aligned"),
+    (dict(L=70000, H=1), 2, "segments"),
+])
+def test_correct_rejects_bad_arguments(kw, status, msg):
+    st, err = _correct(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_empty_cache_is_a_no_op():
+    # L*H == 0: nothing to do, no pointer is needed and no HIP call is made
+    st, err = _correct(L=0, K=None, V=None, U=None, W=None, desc=None, K_out=None, V_out=None,
+                       mask=None)
+    # desc/W/mask are still required pointers only when there are segments
+    assert st == 0, err
+
+
+def test_fit_rejects_bad_arguments():
+    lib = kvc.lib()
+    base = dict(delta=FAKE, M=4, T=64, d=128, dtype=0, r=32, energy=0.9, U=FAKE, W=FAKE,
+                k=FAKE, eig=None, ws=None, nb=0, st=None)
+    for kw, status in [(dict(r=0), 1), (dict(r=129), 1), (dict(energy=0.0), 1),
+                       (dict(energy=1.5), 1), (dict(energy=float("nan")), 1), (dict(d=32), 2),
+                       (dict(delta=None), 1), (dict(M=-1), 1), (dict(), 4),
+                       (dict(U=FAKE + 8), 1)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_fit_anchor(*a.values()) == status, (kw, lib.kvc_last_error())
+    a = dict(base, M=0, delta=None, U=None, W=None, k=None)
+    assert lib.kvc_fit_anchor(*a.values()) == 0
+
+
+def test_chain_rejects_bad_arguments():
+    lib = kvc.lib()
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE + 256)
+    st = lib.kvc_correct_chain(FAKE, FAKE, 1, 1, 64, 128, 0, 0, arr, arr, arr, 4, 32, 0.3, None,
+                               None, arr, arr, arr, None, None, 0, None)
+    assert st == 1 and b"n_edges" in lib.kvc_last_error()
+    st = lib.kvc_correct_chain(FAKE, FAKE, 1, 1, 64, 128, 0, 2, None, arr, arr, 4, 32, 0.3, None,
+                               None, arr, arr, arr, None, None, 0, None)
+    assert st == 1
+    # an edge whose output aliases its source
+    outs = (ctypes.c_void_p * 2)(FAKE, FAKE + 4096)
+    st = lib.kvc_correct_chain(FAKE, FAKE, 1, 1, 64, 128, 0, 2, arr, arr, arr, 4, 32, 0.3, None,
+                               None, outs, outs, arr, None, FAKE, 1 << 30, None)
+    assert st == 1 and b"source" in lib.kvc_last_error()
+
+
+def test_workspace_sizes_are_monotone():
+    a = kvc.correct_workspace_bytes(32, 8, 2048, 128, 4, 32)
+    b = kvc.correct_workspace_bytes(32, 8, 8192, 128, 4, 32)
+    assert 0 < a < b
+    assert kvc.fit_workspace_bytes(512, 8192, 128, 32) >= kvc.fit_workspace_bytes(512, 2048, 128, 32) > 0
+    assert kvc.fit_workspace_bytes(1, 8192, 128, 32) > kvc.fit_workspace_bytes(1, 128, 128, 32) > 0

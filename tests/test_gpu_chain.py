@@ -1,0 +1,104 @@
+"""GPU parity of the chained correction A0 -> A1 -> A2 -> A3 (kvc_correct_chain) against the
+oracle chain, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import agent_kv_cache_kvc_amd as kvc
+import oracle
+import synth
+from gpu_helpers import check_close, dev, pool_all, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_small_chain_every_segment():
+    cfg = synth.CONFIGS["chain_t32768"].replace(L=2, H=3, T=600, seed=31, fallback_prob=0.3)
+    say(f"[chain] L={cfg.L} H={cfg.H} T={cfg.T} edges={cfg.n_edges}")
+    case = synth.generate(cfg)
+    # descriptors of edge e are built on the oracle's pooled query of edge e's source, so the
+    # +-guard band around tau holds on every edge
+    edges_o, edges_g = [], []
+    srcK, srcV = synth.to_f64(case.K0), synth.to_f64(case.V0)
+    refs = []
+    for e, ed in enumerate(case.edges):
+        q = oracle.pool(srcK, srcV)
+        desc = synth.build_descriptors(case, e, q)
+        eo = {"desc": synth.to_f64(desc), "U": synth.to_f64(ed.U), "W": synth.to_f64(ed.W),
+              "K_fb": synth.to_f64(ed.exact_K), "V_fb": synth.to_f64(ed.exact_V)}
+        out = oracle.correct(srcK, srcV, eo["desc"], eo["U"], eo["W"], cfg.tau, cfg.dtype,
+                             K_fb=eo["K_fb"], V_fb=eo["V_fb"])
+        refs.append(out)
+        srcK, srcV = out["K_out"], out["V_out"]
+        d = dev()
+        edges_g.append({"desc": desc.to(d), "U": ed.U.to(d), "W": ed.W.to(d),
+                        "K_fb": ed.exact_K.to(d), "V_fb": ed.exact_V.to(d)})
+        edges_o.append(eo)
+    # the oracle's chain gives the same per-edge results as the edge-by-edge loop
+    ch = oracle.chain(synth.to_f64(case.K0), synth.to_f64(case.V0), edges_o, cfg.tau, cfg.dtype)
+    for a, b in zip(ch, refs):
+        np.testing.assert_array_equal(a["K_out"], b["K_out"])
+    K0, V0 = case.K0.to(dev()), case.V0.to(dev())
+    K0c, V0c = K0.clone(), V0.clone()
+    res = kvc.correct_chain(K0, V0, edges_g, cfg.tau)
+    torch.cuda.synchronize()
+    assert torch.equal(K0, K0c) and torch.equal(V0, V0c)  # A0's exact cache is untouched
+    for e, (g, r) in enumerate(zip(res, refs)):
+        np.testing.assert_array_equal(g.mask.cpu().numpy(), r["mask"], err_msg=f"edge {e}")
+        eK = check_close(f"K'[{e}]", synth.to_f64(g.K), r["K_out"])
+        eV = check_close(f"V'[{e}]", synth.to_f64(g.V), r["V_out"])
+        fin = np.isfinite(r["score"])
+        np.testing.assert_allclose(g.score.cpu().numpy()[fin], r["score"][fin], atol=2e-6)
+        err = oracle.rel_frobenius(synth.to_f64(g.K), synth.to_f64(case.edges[e].exact_K))
+        say(f"  edge {e}: mask {g.mask.cpu().numpy().ravel().tolist()} parity K' {eK:.1e} "
+            f"V' {eV:.1e}; error vs exact {err:.3e}")
+
+
+def test_chain_t32768_full_size():
+    cfg = synth.CONFIGS["chain_t32768"]
+    say(f"[chain-full] L={cfg.L} H={cfg.H} T={cfg.T} edges={cfg.n_edges}")
+    d = dev()
+    case = synth.generate(cfg, d)
+    edges_g = []
+    for e, ed in enumerate(case.edges):
+        srcK = case.K0 if e == 0 else case.edges[e - 1].exact_K
+        srcV = case.V0 if e == 0 else case.edges[e - 1].exact_V
+        q = pool_all(srcK, srcV)  # descriptors built on agent e's exact cache
+        edges_g.append({"desc": synth.build_descriptors(case, e, q), "U": ed.U, "W": ed.W,
+                        "K_fb": ed.exact_K, "V_fb": ed.exact_V})
+        if e == 0:
+            q0 = q
+    res = kvc.correct_chain(case.K0, case.V0, edges_g, cfg.tau)
+    torch.cuda.synchronize()
+    # edge 0: its source is A0's exact cache, so every segment's decision is checked
+    s0 = oracle.cosine_scores(q0, synth.to_f64(edges_g[0]["desc"]))
+    _, m0 = oracle.reliability(s0, cfg.tau)
+    np.testing.assert_array_equal(res[0].mask.cpu().numpy(), m0)
+    for e in range(cfg.n_edges):
+        err = torch.linalg.vector_norm((res[e].K.double() - case.edges[e].exact_K.double())) / \
+            torch.linalg.vector_norm(case.edges[e].exact_K.double())
+        say(f"  edge {e}: reuse ratio {1 - res[e].mask.double().mean().item():.3f}, "
+            f"K' error vs exact {err.item():.3e}")
+    # sampled segments: the oracle chain of each, skipping near-ties of score and tau
+    rng = np.random.default_rng(1)
+    cand = [(int(l), int(h)) for l, h in zip(rng.integers(0, cfg.L, 16), rng.integers(0, cfg.H, 16))]
+    checked = 0
+    for l, h in cand:
+        if checked == 5:
+            break
+        edges_o = []
+        for e, ed in enumerate(edges_g):
+            edges_o.append({k: synth.to_f64(v[l, h])[None, None] if k in ("desc", "K_fb", "V_fb")
+                            else synth.to_f64(v[:, l, h])[:, None, None] for k, v in ed.items()})
+        ch = oracle.chain(synth.to_f64(case.K0[l, h])[None, None],
+                          synth.to_f64(case.V0[l, h])[None, None], edges_o, cfg.tau, cfg.dtype)
+        if any(abs(float(c["score"][0, 0]) - cfg.tau) < 1e-4 for c in ch):
+            say(f"  segment ({l},{h}) has a near-tie score; skipped")
+            continue
+        for e, c in enumerate(ch):
+            assert int(res[e].mask[l, h]) == int(c["mask"][0, 0]), (l, h, e)
+            check_close(f"K'[{e}]({l},{h})", synth.to_f64(res[e].K[l, h]), c["K_out"][0, 0])
+            check_close(f"V'[{e}]({l},{h})", synth.to_f64(res[e].V[l, h]), c["V_out"][0, 0])
+        checked += 1
+    assert checked >= 3
+    say(f"  {checked} sampled segments match the oracle chain on all edges")
