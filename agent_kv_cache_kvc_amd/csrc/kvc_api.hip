@@ -172,6 +172,7 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
   float* wv = reinterpret_cast<float*>(base + c.off_w);
   float* sc = reinterpret_cast<float*>(base + c.off_score);
   uint8_t* mk = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  int* ctr = reinterpret_cast<int*>(base + c.off_ctr);
   const float* partials = pool;
   int n_tiles = c.n_pool_tiles;
   if (q_in == nullptr && next_partials_in != nullptr) {
@@ -182,10 +183,10 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
   }
   if (T == 0) n_tiles = 0;
   KVC_HIP(kvc::launch_score(partials, n_tiles, T, q_in, desc, S, d, A, tau, nullptr, wv, sc, mk,
-                            nullptr, score_out, w_out, mask_out, st),
+                            nullptr, score_out, w_out, mask_out, ctr, st),
           "score");
   KVC_HIP(kvc::launch_correct(K, V, S, T, d, dtype, U, W, A, r, wv, mk, K_fb, V_fb, K_out, V_out,
-                              want_next ? next : nullptr, st),
+                              want_next ? next : nullptr, ctr, st),
           "correct");
   return KVC_OK;
 }

@@ -25,6 +25,7 @@ struct TrBF16 {
   static constexpr int SLOT = 8;   // consecutive k per lane per MFMA
   static constexpr int MAXF = 16;  // register-resident U fragments per 32-token tile
   static constexpr int RPAD = 16;  // r is padded to a multiple of this
+  static constexpr int LPT = 8;    // lanes per 64-channel half row (16 bytes each)
   __device__ static float f(elem e) { return bf16_to_f32(e); }
   __device__ static elem e(float v) { return f32_to_bf16(v); }
   __device__ static floatx16 mma(const frag& a, const frag& b, const floatx16& c) {
@@ -39,6 +40,7 @@ struct TrF32 {
   static constexpr int SLOT = 1;
   static constexpr int MAXF = 32;
   static constexpr int RPAD = 8;
+  static constexpr int LPT = 16;
   __device__ static float f(elem e) { return e; }
   __device__ static elem e(float v) { return v; }
   __device__ static floatx16 mma(const frag& a, const frag& b, const floatx16& c) {
@@ -134,9 +136,10 @@ __global__ __launch_bounds__(kWave) void score_kernel(
     const float* __restrict__ partials, int n_tiles, int T, const float* __restrict__ q_in,
     const float* __restrict__ desc, int A, float tau, float* __restrict__ w_ws,
     uint8_t* __restrict__ mask_ws, float* __restrict__ q_out, float* __restrict__ score_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ mask_out) {
+    float* __restrict__ w_out, uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
   constexpr int PER = 2 * D / kWave;
   const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  if (s == 0 && lane == 0) *ctr = 0;  // work counter of the correction pass that follows
   float q[PER];
   if (q_in != nullptr) {
 #pragma unroll
@@ -205,15 +208,32 @@ __global__ __launch_bounds__(kWave) void score_kernel(
 }
 
 // ------------------------------------------------------------------------- correction
-// grid (n_corr_tiles, S, 2): workgroup = 4 waves, each wave owns 32 tokens per iteration
-// and all d channels.  The MFMA computes (delta X)^T = W^T U^T per 32-channel block:
-// A operand = W_a^T staged in LDS (rows permuted by cmap32), B operand = U_a rows
-// (8 consecutive k per lane, straight from HBM), result register i of lane l =
-// (token l % 32, channel 16 (l / 32) + i).  Each anchor's product is finished in float32
-// and then scaled by its weight, so w never passes through bf16.
+// Persistent workgroups (4 waves) take work items (segment, K|V, 512-token chunk) from a
+// counter that the score kernel resets.  A wave owns 32 tokens per tile and all d channels.
 //
+// MFMA: (delta X)^T = W^T U^T per 32-channel block; A operand = W_a^T staged in LDS (rows
+// permuted by cmap32), B operand = U_a rows (8 consecutive k per lane, straight from HBM);
+// result register i of lane l = (token l % 32, channel 16 (l / 32) + i).  Each anchor's
+// product is finished in float32 and scaled by its weight, so w never passes through bf16.
 // k layout: r is padded to rp (multiple of 2*SLOT); lane half g covers k in
 // [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.
+//
+// Memory: X is loaded and X' stored with coalesced 16-byte accesses (lane l of an access
+// covers token l / LPT of the group, channels 8 (l % LPT) ... of a 64-channel half row);
+// the MFMA result goes through a per-wave LDS tile [32][64 + 4] floats to meet that layout.
+// The next tile's U is requested as soon as the MFMAs have consumed the current one, and
+// each half of the next tile's X as soon as the epilogue has consumed that half.
+constexpr int kChunk = kCorrRowsPerIter * kCorrIters;  // tokens per work item
+constexpr int kStageRow = 68;                          // floats per staged token row
+
+template <class Tr, int D, int NF>
+struct CorrTile {
+  static constexpr int NH = D / 64;        // 64-channel halves
+  static constexpr int JN = Tr::LPT / 2;   // coalesced accesses per half per 32 tokens
+  u32x4 x[NH][JN];                         // X of the tile in flight (coalesced layout)
+  typename Tr::frag u[NF];                 // U fragments of the tile in flight
+};
+
 template <class Tr, int D, int NF, bool POOL_OUT>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
     const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V,
@@ -221,188 +241,258 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
     const float* __restrict__ w_all, const uint8_t* __restrict__ mask,
     const typename Tr::elem* __restrict__ K_fb, const typename Tr::elem* __restrict__ V_fb,
     typename Tr::elem* K_out, typename Tr::elem* V_out, float* __restrict__ next_partials,
-    int T, int A, int r, int rp) {
+    int T, int S, int A, int r, int rp, int n_chunks, int n_items, int* __restrict__ ctr) {
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
+  using Tile = CorrTile<Tr, D, NF>;
   constexpr int VEC = Tr::VEC;
   constexpr int SLOT = Tr::SLOT;
-  constexpr int NCB = D / 32;
+  constexpr int LPT = Tr::LPT;
+  constexpr int TPI = kWave / LPT;  // tokens per coalesced access
+  constexpr int NH = Tile::NH, JN = Tile::JN;
   constexpr int PADK = 16 / sizeof(elem);
-  constexpr int NCH = 16 / VEC;  // 16-byte chunks holding a lane's 16 channels of a block
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  elem* wt = reinterpret_cast<elem*>(smem_raw);  // [A][D][rp + PADK]
   __shared__ float wsh[kMaxA];
   __shared__ float red[4][D];
+  __shared__ int s_item;
 
-  const int tile = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, ln = lane & 31;
-  const size_t seg = (size_t)s * T * D;
-  const elem* X = (x == 0 ? K : V) + seg;
-  elem* Y = (x == 0 ? K_out : V_out) + seg;
-  const elem* Xfb = (x == 0 ? K_fb : V_fb);
-  const bool masked = mask[s] != 0;
-  const int tbase = tile * kCorrRowsPerIter * kCorrIters;
+  float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
+  elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * kStageRow * sizeof(float));
+  const int RS = rp + PADK;
+  const int half = rp / 2;
+  const int KS = half / SLOT;  // MFMA steps per anchor
+  const int nfrag = A * KS;
+  const bool uvec = (r % VEC) == 0;
+  const int lrow = lane / LPT;               // token within a coalesced access
+  const int lcol = VEC * (lane % LPT);       // channel offset within a half row
 
-  float qacc[POOL_OUT ? NCB : 1][16];
-  if constexpr (POOL_OUT) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qacc[cb][i] = 0.f;
-  }
-
-  if (masked) {
-    // dense-prefill stand-in: copy the fallback cache (or the source) bit for bit
-    const elem* src = Xfb ? Xfb + seg : X;
-    for (int it = 0; it < kCorrIters; ++it) {
-      const int t = tbase + it * kCorrRowsPerIter + wave * 32 + ln;
-      if (t < T) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const size_t off = (size_t)t * D + cb * 32 + 16 * g;
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            u32x4 raw = *reinterpret_cast<const u32x4*>(src + off + c * VEC);
-            *reinterpret_cast<u32x4*>(Y + off + c * VEC) = raw;
-            if constexpr (POOL_OUT) {
-              const elem* v = reinterpret_cast<const elem*>(&raw);
-#pragma unroll
-              for (int j = 0; j < VEC; ++j) qacc[cb][c * VEC + j] += Tr::f(v[j]);
-            }
-          }
-        }
-      }
-    }
-  } else {
-    const int RS = rp + PADK;
-    const int half = rp / 2;
-    const int KS = half / SLOT;  // MFMA steps per anchor
-    const int nfrag = A * KS;
-    const bool uvec = (r % VEC) == 0;
-    // ---- stage W_a^T of this segment in LDS (zero for k >= r)
-    const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
-    const int chunks = A * r * (D / VEC);
-    for (int q = tid; q < chunks; q += kBlock) {
-      const int c0 = (q % (D / VEC)) * VEC;
-      const int ak = q / (D / VEC);  // a * r + k
-      const int a = ak / r, k = ak % r;
-      const elem* src = Wseg + (size_t)ak * D + c0;
-      elem v[VEC];
-      *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) wt[((size_t)a * D + c0 + j) * RS + k] = v[j];
-    }
-    if (rp > r) {
-      const int pad = rp - r;
-      for (int q = tid; q < A * D * pad; q += kBlock) {
-        const int k = r + q % pad;
-        const int ac = q / pad;
-        wt[(size_t)ac * RS + k] = Tr::e(0.f);
-      }
-    }
-    if (tid < A) wsh[tid] = w_all[(size_t)s * A + tid];
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(ctr, 1);
     __syncthreads();
+    const int item = s_item;
+    if (item >= n_items) break;
+    const int chunk = item % n_chunks;
+    const int sx = item / n_chunks;
+    const int x = sx & 1, s = sx >> 1;
+    const size_t seg = (size_t)s * T * D;
+    const elem* X = (x == 0 ? K : V) + seg;
+    elem* Y = (x == 0 ? K_out : V_out) + seg;
+    const elem* Xfb = (x == 0 ? K_fb : V_fb);
+    const int tb = chunk * kChunk;
 
-    const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
-    for (int it = 0; it < kCorrIters; ++it) {
-      const int t0 = tbase + it * kCorrRowsPerIter + wave * 32;
-      if (t0 >= T) break;
-      const int t = t0 + ln;
-      const bool valid = t < T;
-      // ---- this lane's 16 channels of every block, issued before the MFMA work
-      u32x4 xr[NCB][NCH];
+    float qs[POOL_OUT ? NH : 1][VEC];
+    if constexpr (POOL_OUT) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-          xr[cb][c] = valid ? *reinterpret_cast<const u32x4*>(X + (size_t)t * D + cb * 32 +
-                                                              16 * g + c * VEC)
-                            : u32x4{0u, 0u, 0u, 0u};
-      // ---- U fragments of this lane's token, all anchors (register resident)
-      frag bf[NF];
+        for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+    }
+
+    if (mask[s]) {
+      // dense-prefill stand-in: copy the fallback cache (or the source) bit for bit
+      const elem* src = Xfb ? Xfb + seg : X;
+      for (int it = 0; it < kCorrIters; ++it) {
+        const int t0 = tb + it * kCorrRowsPerIter + wave * 32;
+        if (t0 >= T) break;
+        u32x4 v[NH][JN];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (f < nfrag) {
-          const int a = f / KS, ks = f - a * KS;
-          const int k0 = g * half + ks * SLOT;
-          const elem* up = Useg + ((size_t)a * T + t) * r + k0;
-          if constexpr (SLOT == 8) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid && k0 < r) {
-              if (uvec) {
-                v = *reinterpret_cast<const u32x4*>(up);
-              } else {
-                uint16_t tmp[8];
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) tmp[j] = (k0 + j < r) ? up[j] : (uint16_t)0;
-                v = *reinterpret_cast<u32x4*>(tmp);
+          for (int j = 0; j < JN; ++j) {
+            const int tok = t0 + TPI * j + lrow;
+            v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(src + (size_t)tok * D + 64 * h + lcol)
+                              : u32x4{0u, 0u, 0u, 0u};
+          }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const int tok = t0 + TPI * j + lrow;
+            if (tok < T) {
+              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = v[h][j];
+              if constexpr (POOL_OUT) {
+                const elem* ev = reinterpret_cast<const elem*>(&v[h][j]);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) qs[h][e] += Tr::f(ev[e]);
               }
             }
-            bf[f] = v;
-          } else {
-            bf[f] = (valid && k0 < r) ? Tr::f(*up) : 0.f;
           }
+      }
+    } else {
+      // ---- stage W_a^T of this segment in LDS (zero for k >= r) and the weights
+      const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
+      const int chunks = A * r * (D / VEC);
+      for (int q = tid; q < chunks; q += kBlock) {
+        const int c0 = (q % (D / VEC)) * VEC;
+        const int ak = q / (D / VEC);  // a * r + k
+        const int a = ak / r, k = ak % r;
+        elem v[VEC];
+        *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(Wseg + (size_t)ak * D + c0);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) wt[((size_t)a * D + c0 + j) * RS + k] = v[j];
+      }
+      if (rp > r) {
+        const int pad = rp - r;
+        for (int q = tid; q < A * D * pad; q += kBlock) {
+          const int k = r + q % pad;
+          const int ac = q / pad;
+          wt[(size_t)ac * RS + k] = Tr::e(0.f);
         }
       }
+      if (tid < A) wsh[tid] = w_all[(size_t)s * A + tid];
+      __syncthreads();
+
+      const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
+      const int first = tb + wave * 32;
+      const int n_my = first < T ? min(kCorrIters, (T - first + kCorrRowsPerIter - 1) / kCorrRowsPerIter) : 0;
+
+      Tile b;
+      auto load_x = [&](int h, int t0) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const elem* ap = wt + (size_t)(cb * 32 + cmap32(ln)) * RS + g * half;
-        floatx16 acc, tmp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { acc[i] = 0.f; tmp[i] = 0.f; }
+        for (int j = 0; j < JN; ++j) {
+          const int tok = t0 + TPI * j + lrow;
+          b.x[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+      };
+      auto load_u = [&](int t0) {
+        const int t = t0 + ln;
+        const bool valid = t < T;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           if (f < nfrag) {
             const int a = f / KS, ks = f - a * KS;
-            frag af;
+            const int k0 = g * half + ks * SLOT;
+            const elem* up = Useg + ((size_t)a * T + t) * r + k0;
             if constexpr (SLOT == 8) {
-              af = *reinterpret_cast<const u32x4*>(ap + (size_t)a * D * RS + ks * SLOT);
-            } else {
-              af = ap[(size_t)a * D * RS + ks];
-            }
-            tmp = Tr::mma(af, bf[f], tmp);
-            if (ks == KS - 1) {
-              const float wa = wsh[a];
+              u32x4 v = {0u, 0u, 0u, 0u};
+              if (valid && k0 < r) {
+                if (uvec) {
+                  v = *reinterpret_cast<const u32x4*>(up);
+                } else {
+                  uint16_t tmp[8];
 #pragma unroll
-              for (int i = 0; i < 16; ++i) { acc[i] += wa * tmp[i]; tmp[i] = 0.f; }
+                  for (int jj = 0; jj < 8; ++jj) tmp[jj] = (k0 + jj < r) ? up[jj] : (uint16_t)0;
+                  v = *reinterpret_cast<u32x4*>(tmp);
+                }
+              }
+              b.u[f] = v;
+            } else {
+              b.u[f] = (valid && k0 < r) ? Tr::f(*up) : 0.f;
             }
           }
         }
-        if (valid) {
-          const size_t off = (size_t)t * D + cb * 32 + 16 * g;
+      };
+
+      if (n_my > 0) {
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            const elem* xv = reinterpret_cast<const elem*>(&xr[cb][c]);
+        for (int h = 0; h < NH; ++h) load_x(h, first);
+        load_u(first);
+      }
+      for (int it = 0; it < n_my; ++it) {
+        const int t0 = first + it * kCorrRowsPerIter;
+        const int tn = t0 + kCorrRowsPerIter;
+        const bool more = it + 1 < n_my;
+        // ---- per 64-channel half: two 32-channel MFMA blocks into the staging tile, then
+        //      add X, round, coalesced store
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+#pragma unroll 1
+          for (int cbl = 0; cbl < 2; ++cbl) {
+            const int cb = 2 * h + cbl;
+            const elem* ap = wt + (size_t)(cb * 32 + cmap32(ln)) * RS + g * half;
+            floatx16 acc, tmp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { acc[i] = 0.f; tmp[i] = 0.f; }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              if (f < nfrag) {
+                const int a = f / KS, ks = f - a * KS;
+                frag af;
+                if constexpr (SLOT == 8) {
+                  af = *reinterpret_cast<const u32x4*>(ap + (size_t)a * D * RS + ks * SLOT);
+                } else {
+                  af = ap[(size_t)a * D * RS + ks];
+                }
+                tmp = Tr::mma(af, b.u[f], tmp);
+                if (ks == KS - 1) {
+                  const float wa = wsh[a];
+#pragma unroll
+                  for (int i = 0; i < 16; ++i) { acc[i] += wa * tmp[i]; tmp[i] = 0.f; }
+                }
+              }
+            }
+            float* sp = stage + ln * kStageRow + cbl * 32 + 16 * g;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<floatx4*>(sp + 4 * q) =
+                  floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          }
+          if (h == NH - 1 && more) load_u(tn);  // U of this tile is consumed
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const int row = TPI * j + lrow;
+            const int tok = t0 + row;
+            float dv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+              *reinterpret_cast<floatx4*>(&dv[e]) =
+                  *reinterpret_cast<const floatx4*>(stage + row * kStageRow + lcol + e);
+            const elem* xv = reinterpret_cast<const elem*>(&b.x[h][j]);
             elem ov[VEC];
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-              ov[j] = Tr::e(Tr::f(xv[j]) + acc[c * VEC + j]);
-              if constexpr (POOL_OUT) qacc[cb][c * VEC + j] += Tr::f(ov[j]);
+            for (int e = 0; e < VEC; ++e) ov[e] = Tr::e(Tr::f(xv[e]) + dv[e]);
+            if (tok < T) {
+              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) =
+                  *reinterpret_cast<const u32x4*>(ov);
+              if constexpr (POOL_OUT) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) qs[h][e] += Tr::f(ov[e]);
+              }
             }
-            *reinterpret_cast<u32x4*>(Y + off + c * VEC) = *reinterpret_cast<u32x4*>(ov);
           }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          if (more) load_x(h, tn);  // this half of X is consumed
         }
       }
     }
-  }
 
-  if constexpr (POOL_OUT) {
-    // token sums of the stored output: lanes -> half-wave sums -> waves in fixed order
+    if constexpr (POOL_OUT) {
+      // token sums of the stored output: lanes sharing a channel -> waves in fixed order
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = half_wave_sum(qacc[cb][i]);
-        if (ln == 0) red[wave][cb * 32 + 16 * g + i] = v;
+        for (int e = 0; e < VEC; ++e) {
+          float v = qs[h][e];
+#pragma unroll
+          for (int off = LPT; off < kWave; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (lane < LPT) red[wave][64 * h + lcol + e] = v;
+        }
+      __syncthreads();
+      if (tid < D) {
+        const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
       }
-    __syncthreads();
-    if (tid < D) {
-      const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-      next_partials[(((size_t)x * S + s) * gridDim.x + tile) * D + tid] = v;
     }
+    __syncthreads();  // LDS (W^T, weights, staging, item id) is free for the next item
   }
+}
+
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 // ------------------------------------------------------------------------- launchers
@@ -441,16 +531,17 @@ hipError_t launch_reduce_pool(const float* partials, int n_tiles, int T, int S, 
 hipError_t launch_score(const float* partials, int n_tiles, int T, const float* q_in,
                         const float* desc, int S, int d, int A, float tau, float* q_ws,
                         float* w_ws, float* score_ws, uint8_t* mask_ws, float* q_out,
-                        float* score_out, float* w_out, uint8_t* mask_out, hipStream_t st) {
+                        float* score_out, float* w_out, uint8_t* mask_out, int* ctr,
+                        hipStream_t st) {
   (void)q_ws;
   if (S == 0) return hipSuccess;
   float* so = score_out ? score_out : score_ws;
   if (d == 128)
     hipLaunchKernelGGL((score_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
-                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out);
+                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out, ctr);
   else
     hipLaunchKernelGGL((score_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
-                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out);
+                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out, ctr);
   return hipGetLastError();
 }
 
@@ -458,12 +549,15 @@ template <class Tr, int D, int NF>
 static hipError_t correct_nf(const void* K, const void* V, int S, int T, const void* U,
                              const void* W, int A, int r, int rp, const float* w,
                              const uint8_t* mask, const void* K_fb, const void* V_fb,
-                             void* K_out, void* V_out, float* next_partials, hipStream_t st) {
+                             void* K_out, void* V_out, float* next_partials, int* ctr,
+                             hipStream_t st) {
   using elem = typename Tr::elem;
   const int PADK = 16 / (int)sizeof(elem);
-  const size_t lds = (size_t)A * D * (rp + PADK) * sizeof(elem);
-  const int n_tiles = T > 0 ? ceil_div(T, kCorrRowsPerIter * kCorrIters) : 1;
-  dim3 grid(n_tiles, S, 2);
+  const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
+                     (size_t)A * D * (rp + PADK) * sizeof(elem);
+  const int n_chunks = T > 0 ? ceil_div(T, kChunk) : 1;
+  const int n_items = S * 2 * n_chunks;
+  const int grid = n_items < 2 * device_cus() ? n_items : 2 * device_cus();
   auto k_pool = correct_kernel<Tr, D, NF, true>;
   auto k_plain = correct_kernel<Tr, D, NF, false>;
   if (lds > 48 * 1024) {
@@ -472,10 +566,10 @@ static hipError_t correct_nf(const void* K, const void* V, int S, int T, const v
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plain),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   }
-  hipLaunchKernelGGL(next_partials ? k_pool : k_plain, grid, dim3(kBlock), lds, st,
+  hipLaunchKernelGGL(next_partials ? k_pool : k_plain, dim3(grid), dim3(kBlock), lds, st,
                      (const elem*)K, (const elem*)V, (const elem*)U, (const elem*)W, w, mask,
                      (const elem*)K_fb, (const elem*)V_fb, (elem*)K_out, (elem*)V_out,
-                     next_partials, T, A, r, rp);
+                     next_partials, T, S, A, r, rp, n_chunks, n_items, ctr);
   return hipGetLastError();
 }
 
@@ -484,34 +578,34 @@ template <class Tr, int D>
 static hipError_t correct_t(const void* K, const void* V, int S, int T, const void* U,
                             const void* W, int A, int r, const float* w, const uint8_t* mask,
                             const void* K_fb, const void* V_fb, void* K_out, void* V_out,
-                            float* next_partials, hipStream_t st) {
+                            float* next_partials, int* ctr, hipStream_t st) {
   const int rp = (r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
   const int nfrag = A * (rp / 2 / Tr::SLOT);
   constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
   if (nfrag <= F0)
     return correct_nf<Tr, D, F0>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                                 next_partials, st);
+                                 next_partials, ctr, st);
   if (nfrag <= F1)
     return correct_nf<Tr, D, F1>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                                 next_partials, st);
+                                 next_partials, ctr, st);
   return correct_nf<Tr, D, F2>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                               next_partials, st);
+                               next_partials, ctr, st);
 }
 
 hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
                           const void* U, const void* W, int A, int r, const float* w,
                           const uint8_t* mask, const void* K_fb, const void* V_fb, void* K_out,
-                          void* V_out, float* next_partials, hipStream_t st) {
+                          void* V_out, float* next_partials, int* ctr, hipStream_t st) {
   if (S == 0) return hipSuccess;
   if (dtype == KVC_BF16)
     return d == 128 ? correct_t<TrBF16, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                             V_out, next_partials, st)
+                                             V_out, next_partials, ctr, st)
                     : correct_t<TrBF16, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                            V_out, next_partials, st);
+                                            V_out, next_partials, ctr, st);
   return d == 128 ? correct_t<TrF32, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                          V_out, next_partials, st)
+                                          V_out, next_partials, ctr, st)
                   : correct_t<TrF32, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                         V_out, next_partials, st);
+                                         V_out, next_partials, ctr, st);
 }
 
 }  // namespace kvc

@@ -66,15 +66,19 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 
-  for (int ts = t_begin; ts < t_end; ts += SLAB) {
-    // ---- load an 8x8 block: rows ts + 8 rg + i, channels 8 cg .. 8 cg + 7
-    u32x4 in[8];
+  // ---- 8x8 block of this thread: rows ts + 8 rg + i, channels 8 cg .. 8 cg + 7; the next
+  //      slab's block is requested before the current slab's MFMAs
+  u32x4 in[8];
+  auto load_block = [&](int ts) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = ts + 8 * rg + i;
       in[i] = (t < t_end) ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * cg)
                           : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  if (t_begin < t_end) load_block(t_begin);
+  for (int ts = t_begin; ts < t_end; ts += SLAB) {
     __syncthreads();  // previous slab's fragments are consumed
     // ---- transpose: out[j] = channel 8 cg + j, tokens 8 rg .. 8 rg + 7
 #pragma unroll
@@ -88,6 +92,7 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
       *reinterpret_cast<u32x4*>(&lt[(8 * cg + j) * SR + 8 * rg]) = o;
     }
     __syncthreads();
+    if (ts + SLAB < t_end) load_block(ts + SLAB);
     // ---- MFMA over the slab's k-steps of 16 tokens
 #pragma unroll 2
     for (int ks = 0; ks < SLAB / 16; ++ks) {
@@ -175,17 +180,23 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
 }
 
 // ------------------------------------------------------------------------- Jacobi
-// One workgroup per matrix.  LDS holds A (starts as G) and V (starts as I), both
-// column-major with a padded column stride.  Each step of a sweep rotates d/2 disjoint
-// column pairs (round-robin "circle" ordering, every pair once per sweep); a pair is
-// owned by 256/(d/2) adjacent lanes that each hold d/(that) rows.  For columns a_i, a_j:
+// One 512-thread workgroup per matrix; LDS holds A (starts as G), column-major, column
+// stride d + 4 floats, 16-byte chunks of a column swizzled (bit 1 flipped in the upper half)
+// so that the 8 lanes of a pair read distinct banks.  Each step of a sweep rotates d/2
+// disjoint column pairs (round-robin "circle" ordering, every pair once per sweep); a pair
+// is owned by 512/(d/2) adjacent lanes, each holding d/(that) rows.  For columns a_i, a_j:
 //   alpha = |a_i|^2, beta = |a_j|^2, gamma = a_i . a_j,
 //   zeta = (beta - alpha) / (2 gamma), t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
 //   c = 1 / sqrt(1 + t^2), s = c t,  a_i <- c a_i - s a_j,  a_j <- s a_i + c a_j,
-// which makes the pair orthogonal; V gets the same rotation.  At convergence A = G V has
-// orthogonal columns, so V holds eigenvectors and lambda_i = |a_i|.  A pair is left alone
-// when |gamma| <= max(tol sqrt(alpha beta), eta |G|_F^2); the loop ends after a sweep
-// without rotations or after kJacobiMaxSweeps sweeps (uniform across the workgroup).
+// which makes the pair orthogonal.  At convergence A = G V with V orthogonal and A's
+// columns orthogonal, so a_j = lambda_j v_j: lambda_j = |a_j| and v_j = a_j / |a_j| (no V is
+// kept).  A pair is left alone when |gamma| <= max(tol sqrt(alpha beta), eta |G|_F^2); the
+// loop ends after a sweep without rotations or after kJacobiMaxSweeps sweeps (the decision
+// is uniform across the workgroup).  The kept vectors are re-orthonormalised by two passes
+// of Gram-Schmidt in descending order, which also completes null directions (a zero or
+// noise-level column) with canonical basis vectors.
+constexpr int kJacobiBlock = 512;
+
 __device__ __forceinline__ void rr_pair(int p, int step, int n, int& i, int& j) {
   const int a = (p == 0) ? 0 : ((p - 1 + step) % (n - 1)) + 1;
   const int b = ((n - 2 - p + step) % (n - 1)) + 1;
@@ -193,51 +204,65 @@ __device__ __forceinline__ void rr_pair(int p, int step, int n, int& i, int& j) 
   j = max(a, b);
 }
 
+// float index of element `row` inside a column (swizzled 16-byte chunks)
+__device__ __forceinline__ int jrow(int row) {
+  const int c = row >> 2;
+  return ((c ^ (((c >> 4) & 1) << 1)) << 2) | (row & 3);
+}
+
 template <int D>
-__global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  // deterministic sum over the workgroup: waves in fixed order
+  v = wave_sum(v);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < kJacobiBlock / kWave; ++w) s += red[w];
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
     const float* __restrict__ partials, int nsplit, int r, double energy, float tol, float eta,
     float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
     uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad,
     int* __restrict__ sweeps_out) {
-  constexpr int CS = D + 4;           // column stride (floats)
+  constexpr int CS = D + 4;                     // column stride (floats)
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
-  constexpr int TPP = kBlock / (D / 2);  // threads per pair: 4 (d=128) or 8 (d=64)
-  constexpr int RPT = D / TPP;           // rows per thread: 32 or 8
-  extern __shared__ __align__(16) float smem[];
-  float* Am = smem;           // [D][CS]
-  float* Vm = smem + D * CS;  // [D][CS]
+  constexpr int TPP = kJacobiBlock / (D / 2);   // lanes per pair: 8 (d = 128) or 16 (d = 64)
+  constexpr int RPT = D / TPP;                  // rows per lane: 16 or 4
+  constexpr int NW = kJacobiBlock / kWave;
+  extern __shared__ __align__(16) float Am[];   // [D][CS]
   __shared__ float lam[D];
   __shared__ int order[D];
-  __shared__ float redf[kBlock / kWave];
-  __shared__ int redi[kBlock / kWave];
+  __shared__ float redf[NW];
+  __shared__ int redi[NW];
+  __shared__ float coef[D];
+  __shared__ float xs[D];
+  __shared__ float sgn[D];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
   // ---- G = sum of the partials (fixed order), mirrored to a full symmetric matrix
   const float* P = partials + (size_t)m * nsplit * NBLK * 1024;
   float fro = 0.f;
-  for (int e = tid; e < NBLK * 1024; e += kBlock) {
+  for (int e = tid; e < NBLK * 1024; e += kJacobiBlock) {
     const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
-    float v = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) v += P[(size_t)sp * NBLK * 1024 + e];
     int I = 0, rem = blk;
     while (rem >= NB - I) { rem -= NB - I; ++I; }
     const int J = I + rem;
     const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
     const int col = J * 32 + (l % 32);
     if (row > col) continue;  // a diagonal block's lower half: its mirror writes it
-    Am[col * CS + row] = v;
-    Am[row * CS + col] = v;
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += P[(size_t)sp * NBLK * 1024 + e];
+    Am[col * CS + jrow(row)] = v;
+    Am[row * CS + jrow(col)] = v;
     fro += (row == col) ? v * v : 2.f * v * v;
   }
-  for (int e = tid; e < D * D; e += kBlock) {
-    const int c = e / D, rr = e % D;
-    Vm[c * CS + rr] = (c == rr) ? 1.f : 0.f;
-  }
-  fro = wave_sum(fro);
-  if (lane == 0) redf[wave] = fro;
-  __syncthreads();
-  const float f2 = ((redf[0] + redf[1]) + redf[2]) + redf[3];
+  const float f2 = block_sum<D>(fro, redf);
   const float abs_floor = eta * f2;
 
   // ---- sweeps
@@ -248,13 +273,14 @@ __global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
     for (int step = 0; step < D - 1; ++step) {
       int ci, cj;
       rr_pair(p, step, D, ci, cj);
-      float* ai = Am + ci * CS + sub * RPT;
-      float* aj = Am + cj * CS + sub * RPT;
+      float* ai = Am + ci * CS;
+      float* aj = Am + cj * CS;
       float xi[RPT], xj[RPT];
 #pragma unroll
       for (int k = 0; k < RPT; k += 4) {
-        *reinterpret_cast<floatx4*>(&xi[k]) = *reinterpret_cast<const floatx4*>(ai + k);
-        *reinterpret_cast<floatx4*>(&xj[k]) = *reinterpret_cast<const floatx4*>(aj + k);
+        const int o = jrow(sub * RPT + k);
+        *reinterpret_cast<floatx4*>(&xi[k]) = *reinterpret_cast<const floatx4*>(ai + o);
+        *reinterpret_cast<floatx4*>(&xj[k]) = *reinterpret_cast<const floatx4*>(aj + o);
       }
       float al = 0.f, be = 0.f, ga = 0.f;
 #pragma unroll
@@ -284,23 +310,9 @@ __global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
         }
 #pragma unroll
         for (int k = 0; k < RPT; k += 4) {
-          *reinterpret_cast<floatx4*>(ai + k) = *reinterpret_cast<floatx4*>(&xi[k]);
-          *reinterpret_cast<floatx4*>(aj + k) = *reinterpret_cast<floatx4*>(&xj[k]);
-        }
-        float* vi = Vm + ci * CS + sub * RPT;
-        float* vj = Vm + cj * CS + sub * RPT;
-#pragma unroll
-        for (int k = 0; k < RPT; k += 4) {
-          floatx4 u = *reinterpret_cast<const floatx4*>(vi + k);
-          floatx4 v = *reinterpret_cast<const floatx4*>(vj + k);
-          floatx4 nu, nv;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            nu[q] = c * u[q] - s * v[q];
-            nv[q] = s * u[q] + c * v[q];
-          }
-          *reinterpret_cast<floatx4*>(vi + k) = nu;
-          *reinterpret_cast<floatx4*>(vj + k) = nv;
+          const int o = jrow(sub * RPT + k);
+          *reinterpret_cast<floatx4*>(ai + o) = *reinterpret_cast<floatx4*>(&xi[k]);
+          *reinterpret_cast<floatx4*>(aj + o) = *reinterpret_cast<floatx4*>(&xj[k]);
         }
       }
       __syncthreads();
@@ -309,7 +321,8 @@ __global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
     const int any = __any(rotated) ? 1 : 0;
     if (lane == 0) redi[wave] = any;
     __syncthreads();
-    const int tot = redi[0] | redi[1] | redi[2] | redi[3];
+    int tot = 0;
+    for (int w = 0; w < NW; ++w) tot |= redi[w];
     __syncthreads();
     if (!tot) { ++sweep; break; }
   }
@@ -349,23 +362,73 @@ __global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
     if (sweeps_out) sweeps_out[m] = sweep;
   }
   if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = lam[order[tid]];
-  // ---- canonical sign of each kept eigenvector: largest |entry| (first on ties) positive
-  __shared__ float sgn[D];
+
+  // ---- kept vectors: two-pass classical Gram-Schmidt in descending order, written back
+  // into the kept columns (column order[k] holds w_k afterwards)
+  for (int k = 0; k < r; ++k) {
+    const int ck = order[k];
+    int cand = -1;  // -1: the Jacobi column itself, else canonical basis vector e_cand
+    for (;;) {
+      if (tid < D) xs[tid] = (cand < 0) ? Am[ck * CS + jrow(tid)] : (tid == cand ? 1.f : 0.f);
+      __syncthreads();
+      float n0 = 0.f;
+      if (tid < D) n0 = xs[tid] * xs[tid];
+      n0 = block_sum<D>(n0, redf);
+      for (int pass = 0; pass < 2; ++pass) {
+        // coef_i = w_i . x for i < k  (8 lanes per coefficient, fixed-order butterfly)
+        for (int i0 = 0; i0 < k; i0 += kJacobiBlock / 8) {
+          const int i = i0 + tid / 8, part = tid % 8;
+          float cdot = 0.f;
+          if (i < k) {
+            const float* w = Am + order[i] * CS;
+            for (int q = part; q < D; q += 8) cdot += w[jrow(q)] * xs[q];
+          }
+          cdot += __shfl_xor(cdot, 1, 64);
+          cdot += __shfl_xor(cdot, 2, 64);
+          cdot += __shfl_xor(cdot, 4, 64);
+          if (i < k && part == 0) coef[i] = cdot;
+        }
+        __syncthreads();
+        if (tid < D) {
+          float v = xs[tid];
+          for (int i = 0; i < k; ++i) v -= coef[i] * Am[order[i] * CS + jrow(tid)];
+          xs[tid] = v;
+        }
+        __syncthreads();
+      }
+      float n1 = 0.f;
+      if (tid < D) n1 = xs[tid] * xs[tid];
+      n1 = block_sum<D>(n1, redf);
+      // accept: a column that keeps most of its length (noise-level columns included) or,
+      // for a completion, a basis vector with a clear residual
+      const bool ok = (cand < 0) ? (n0 > 0.f && n1 > 1e-4f * n0)
+                                 : (n1 > 1.f / (4.f * D));
+      if (ok || cand == D - 1) {
+        const float inv = n1 > 0.f ? 1.f / sqrtf(n1) : 0.f;
+        if (tid < D) Am[ck * CS + jrow(tid)] = xs[tid] * inv;
+        __syncthreads();
+        break;
+      }
+      ++cand;
+      __syncthreads();
+    }
+  }
+  // ---- canonical sign: largest |entry| (first on ties) positive
   if (tid < r) {
-    const float* v = Vm + order[tid] * CS;
+    const float* v = Am + order[tid] * CS;
     float best = -1.f, bv = 0.f;
     for (int k = 0; k < D; ++k) {
-      const float av = fabsf(v[k]);
-      if (av > best) { best = av; bv = v[k]; }
+      const float av = fabsf(v[jrow(k)]);
+      if (av > best) { best = av; bv = v[jrow(k)]; }
     }
     sgn[tid] = bv < 0.f ? -1.f : 1.f;
   }
   __syncthreads();
-  for (int e = tid; e < rpad * D; e += kBlock) {
+  for (int e = tid; e < rpad * D; e += kJacobiBlock) {
     const int k = e / D, c = e % D;
     float wv = 0.f;
     if (k < r) {
-      wv = sgn[k] * Vm[order[k] * CS + c];
+      wv = sgn[k] * Am[order[k] * CS + jrow(c)];
       W_out[((size_t)m * r + k) * D + c] = wv;
     }
     if (w_hi) {
@@ -384,60 +447,98 @@ __global__ __launch_bounds__(kBlock, 1) void jacobi_kernel(
 // k layout: lane half g covers channels [g D/2, (g+1) D/2), SLOT consecutive per MFMA.
 constexpr int kProjIters = 4;
 
+// bf16 delta: per iteration the workgroup loads a 128-token tile with coalesced 16-byte
+// accesses into LDS (row stride d + 8 bf16); each wave reads its B fragments (token l % 32,
+// channels 16 ks + 8 (l / 32) ...) from there; W is split as W = hi + lo in bf16 and both
+// halves are multiplied (float32 accumulation).  U is staged per wave in LDS and written
+// with coalesced 16-byte stores.  The next tile is requested before the current one is
+// computed.
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
     const uint16_t* __restrict__ delta, const uint16_t* __restrict__ w_hi,
     const uint16_t* __restrict__ w_lo, int T, int r, int rpad, float* __restrict__ U_out) {
-  constexpr int KS = D / 16;  // MFMA steps over d
+  constexpr int KS = D / 16;            // MFMA steps over d
+  constexpr int DR = D + 8;             // LDS row stride of the delta tile (bf16)
+  constexpr int UR = 36;                // LDS row stride of the U staging tile (floats)
+  constexpr int CPR = D / 8;            // 16-byte chunks per token row
+  constexpr int LD = kCorrRowsPerIter * CPR / kBlock;  // chunks per thread per tile
+  __shared__ __align__(16) uint16_t dt[kCorrRowsPerIter * DR];
+  __shared__ __align__(16) float us[4][32 * UR];
   const int tile = blockIdx.x, m = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, ln = lane & 31;
   const uint16_t* src = delta + (size_t)m * T * D;
   const bool uvec = (r % 4) == 0;
+  const int t_first = tile * kProjIters * kCorrRowsPerIter;
+  const int n_it = min(kProjIters, (T - t_first + kCorrRowsPerIter - 1) / kCorrRowsPerIter);
+  float* ust = us[wave];
   for (int mb = 0; mb < rpad / 32; ++mb) {
     const int jrow = mb * 32 + cmap32(ln);
     u32x4 ah[KS], al[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const size_t off = ((size_t)m * rpad + jrow) * D + g * (D / 2) + 8 * ks;
+      const size_t off = ((size_t)m * rpad + jrow) * D + 16 * ks + 8 * g;
       ah[ks] = *reinterpret_cast<const u32x4*>(w_hi + off);
       al[ks] = *reinterpret_cast<const u32x4*>(w_lo + off);
     }
-    for (int it = 0; it < kProjIters; ++it) {
-      const int t0 = (tile * kProjIters + it) * kCorrRowsPerIter + wave * 32;
-      if (t0 >= T) break;
-      const int t = t0 + ln;
-      const bool valid = t < T;
-      u32x4 b[KS];
+    u32x4 ld[LD];
+    auto load_tile = [&](int t0) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        b[ks] = valid ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + g * (D / 2) + 8 * ks)
+      for (int q = 0; q < LD; ++q) {
+        const int c = tid + q * kBlock;
+        const int t = t0 + c / CPR;
+        ld[q] = t < T ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * (c % CPR))
                       : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    if (n_it > 0) load_tile(t_first);
+    for (int it = 0; it < n_it; ++it) {
+      const int t0 = t_first + it * kCorrRowsPerIter;
+      __syncthreads();  // previous tile's fragments are consumed
+#pragma unroll
+      for (int q = 0; q < LD; ++q) {
+        const int c = tid + q * kBlock;
+        *reinterpret_cast<u32x4*>(&dt[(c / CPR) * DR + 8 * (c % CPR)]) = ld[q];
+      }
+      __syncthreads();
+      if (it + 1 < n_it) load_tile(t0 + kCorrRowsPerIter);
       floatx16 acc0, acc1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
+      const uint16_t* brow = &dt[(wave * 32 + ln) * DR + 8 * g];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        acc0 = mfma_bf16(ah[ks], b[ks], acc0);
-        acc1 = mfma_bf16(al[ks], b[ks], acc1);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(brow + 16 * ks);
+        acc0 = mfma_bf16(ah[ks], b, acc0);
+        acc1 = mfma_bf16(al[ks], b, acc1);
       }
-      if (valid) {
-        float* dst = U_out + ((size_t)m * T + t) * r + mb * 32 + 16 * g;
-        const int jb = mb * 32 + 16 * g;
-        if (uvec && jb + 16 <= r) {
+      // stage: lane (token ln, half g) holds components 32 mb + 16 g + i
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            floatx4 o;
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<floatx4*>(&ust[ln * UR + 16 * g + 4 * q]) =
+            floatx4{acc0[4 * q] + acc1[4 * q], acc0[4 * q + 1] + acc1[4 * q + 1],
+                    acc0[4 * q + 2] + acc1[4 * q + 2], acc0[4 * q + 3] + acc1[4 * q + 3]};
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      // coalesced store: 8 lanes per token (32 floats), 8 tokens per access
+      const int tw = t0 + wave * 32;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc0[4 * q + e] + acc1[4 * q + e];
-            *reinterpret_cast<floatx4*>(dst + 4 * q) = o;
+      for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + lane / 8;
+        const int t = tw + row;
+        const int jb = mb * 32 + 4 * (lane % 8);
+        const floatx4 v = *reinterpret_cast<const floatx4*>(&ust[row * UR + 4 * (lane % 8)]);
+        if (t < T) {
+          float* dst = U_out + ((size_t)m * T + t) * r + jb;
+          if (uvec && jb + 4 <= r) {
+            *reinterpret_cast<floatx4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (jb + e < r) dst[e] = v[e];
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (jb + i < r) dst[i] = acc0[i] + acc1[i];
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
   }
 }
@@ -510,10 +611,10 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
                        f.T, f.chunk, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = 2ull * D * (D + 4) * sizeof(float);
+  const size_t lds = (size_t)D * (D + 4) * sizeof(float);
   allow_dynamic_lds(jacobi_kernel<D>, lds);
   const float tol = 2e-6f, eta = 1e-12f;
-  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kBlock), lds, st, partials, f.nsplit,
+  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials, f.nsplit,
                      f.r, energy, tol, eta, W_out, eig, k_eff,
                      dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
                      f.rpad, sweeps);

@@ -34,6 +34,7 @@ struct CorrectLayout {
   size_t off_w;       // float [S][A]
   size_t off_score;   // float [S]
   size_t off_mask;    // uint8 [S]
+  size_t off_ctr;     // int [1]: work counter of the correction pass
   size_t bytes;
 };
 
@@ -52,6 +53,7 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_w = o;     o = align_up(o + sizeof(float) * (size_t)c.S * A, 256);
   c.off_score = o; o = align_up(o + sizeof(float) * (size_t)c.S, 256);
   c.off_mask = o;  o = align_up(o + (size_t)c.S, 256);
+  c.off_ctr = o;   o = align_up(o + sizeof(int), 256);
   c.bytes = o;
   return c;
 }
@@ -99,11 +101,12 @@ hipError_t launch_pool_partials(const void* K, const void* V, int S, int T, int 
 hipError_t launch_score(const float* partials, int n_tiles, int T, const float* q_in,
                         const float* desc, int S, int d, int A, float tau, float* q_ws,
                         float* w_ws, float* score_ws, uint8_t* mask_ws, float* q_out,
-                        float* score_out, float* w_out, uint8_t* mask_out, hipStream_t st);
+                        float* score_out, float* w_out, uint8_t* mask_out, int* ctr,
+                        hipStream_t st);
 hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
                           const void* U, const void* W, int A, int r, const float* w,
                           const uint8_t* mask, const void* K_fb, const void* V_fb, void* K_out,
-                          void* V_out, float* next_partials, hipStream_t st);
+                          void* V_out, float* next_partials, int* ctr, hipStream_t st);
 hipError_t launch_reduce_pool(const float* partials, int n_tiles, int T, int S, int d,
                               float* q_out, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
