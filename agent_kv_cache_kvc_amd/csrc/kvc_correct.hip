@@ -106,15 +106,30 @@ __device__ __forceinline__ void pooled_query(const float* __restrict__ partials,
                                              int T, int s, int S, int lane,
                                              float (&q)[2 * D / kWave]) {
   constexpr int PER = 2 * D / kWave;
+  // tile sums are added in tile order; loads are issued 8 tiles at a time
+  float sum[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = lane + kWave * i;
-    const int x = c / D, ch = c % D;
-    const float* p = partials + ((size_t)x * S + s) * n_tiles * D + ch;
-    float sum = 0.f;
-    for (int tt = 0; tt < n_tiles; ++tt) sum += p[(size_t)tt * D];
-    q[i] = T > 0 ? sum / (float)T : 0.f;
+  for (int i = 0; i < PER; ++i) sum[i] = 0.f;
+  for (int t0 = 0; t0 < n_tiles; t0 += 8) {
+    float v[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = lane + kWave * i;
+        const int x = c / D, ch = c % D;
+        v[u][i] = (t0 + u < n_tiles)
+                      ? partials[(((size_t)x * S + s) * n_tiles + t0 + u) * D + ch]
+                      : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (t0 + u < n_tiles) sum[i] += v[u][i];
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) q[i] = T > 0 ? sum[i] / (float)T : 0.f;
 }
 
 template <int D>
@@ -221,10 +236,48 @@ __global__ __launch_bounds__(kWave) void score_kernel(
 // Memory: X is loaded and X' stored with coalesced 16-byte accesses (lane l of an access
 // covers token l / LPT of the group, channels 8 (l % LPT) ... of a 64-channel half row);
 // the MFMA result goes through a per-wave LDS tile [32][64 + 4] floats to meet that layout.
-// The next tile's U is requested as soon as the MFMAs have consumed the current one, and
+// The next tile's U (double-buffered) is requested before the current tile's MFMAs, and
 // each half of the next tile's X as soon as the epilogue has consumed that half.
 constexpr int kChunk = kCorrRowsPerIter * kCorrIters;  // tokens per work item
 constexpr int kStageRow = 68;                          // floats per staged token row
+
+// Inverse of cmap32: channel within a 32-block -> MFMA operand row.  W^T rows are stored in
+// LDS in operand-row order, so the 16 lanes of a quarter wave read 16 consecutive rows.
+__device__ __forceinline__ int cinv32(int c) {
+  return 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
+}
+
+// VEC float32 results -> VEC stored elements (bf16: hardware round-to-nearest-even pairs)
+template <class Tr>
+__device__ __forceinline__ u32x4 pack_out(const float* v) {
+  u32x4 o;
+  if constexpr (Tr::VEC == 8) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = __builtin_bit_cast(uint32_t,
+                                __builtin_convertvector(f2_t{v[2 * j], v[2 * j + 1]}, bf16x2_t));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(v[j]);
+  }
+  return o;
+}
+
+template <class Tr>
+__device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
+  if constexpr (Tr::VEC == 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(raw[j] << 16);
+      v[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(raw[j]);
+  }
+}
 
 template <class Tr, int D, int NF>
 struct CorrTile {
@@ -234,16 +287,21 @@ struct CorrTile {
   typename Tr::frag u[NF];                 // U fragments of the tile in flight
 };
 
-template <class Tr, int D, int NF, bool POOL_OUT>
+// NA > 0: compile-time anchor count NA and MFMA steps per anchor KSC (r = 2 KSC SLOT);
+// NA == 0: runtime A and r with up to NFG register-resident fragments.
+template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
     const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V,
     const typename Tr::elem* __restrict__ U, const typename Tr::elem* __restrict__ W,
     const float* __restrict__ w_all, const uint8_t* __restrict__ mask,
     const typename Tr::elem* __restrict__ K_fb, const typename Tr::elem* __restrict__ V_fb,
     typename Tr::elem* K_out, typename Tr::elem* V_out, float* __restrict__ next_partials,
-    int T, int S, int A, int r, int rp, int n_chunks, int n_items, int* __restrict__ ctr) {
+    int T, int S, int A_rt, int r_rt, int rp_rt, int n_chunks, int n_items,
+    int* __restrict__ ctr) {
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
+  constexpr bool FIX = NA > 0;
+  constexpr int NF = FIX ? NA * KSC : NFG;
   using Tile = CorrTile<Tr, D, NF>;
   constexpr int VEC = Tr::VEC;
   constexpr int SLOT = Tr::SLOT;
@@ -257,22 +315,26 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
   __shared__ float red[4][D];
   __shared__ int s_item;
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 5, ln = lane & 31;
   float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
   elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * kStageRow * sizeof(float));
+  const int A = FIX ? NA : A_rt;
+  const int r = FIX ? 2 * KSC * SLOT : r_rt;
+  const int rp = FIX ? 2 * KSC * SLOT : rp_rt;
   const int RS = rp + PADK;
   const int half = rp / 2;
-  const int KS = half / SLOT;  // MFMA steps per anchor
+  const int KS = FIX ? KSC : half / SLOT;  // MFMA steps per anchor
   const int nfrag = A * KS;
-  const bool uvec = (r % VEC) == 0;
+  const bool uvec = FIX || (r % VEC) == 0;
   const int lrow = lane / LPT;               // token within a coalesced access
   const int lcol = VEC * (lane % LPT);       // channel offset within a half row
 
   for (;;) {
     if (tid == 0) s_item = atomicAdd(ctr, 1);
     __syncthreads();
-    const int item = s_item;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= n_items) break;
     const int chunk = item % n_chunks;
     const int sx = item / n_chunks;
@@ -303,7 +365,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
 #pragma unroll
           for (int j = 0; j < JN; ++j) {
             const int tok = t0 + TPI * j + lrow;
-            v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(src + (size_t)tok * D + 64 * h + lcol)
+            v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(src + tok * D + 64 * h + lcol)
                               : u32x4{0u, 0u, 0u, 0u};
           }
 #pragma unroll
@@ -312,34 +374,42 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
           for (int j = 0; j < JN; ++j) {
             const int tok = t0 + TPI * j + lrow;
             if (tok < T) {
-              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = v[h][j];
+              *reinterpret_cast<u32x4*>(Y + tok * D + 64 * h + lcol) = v[h][j];
               if constexpr (POOL_OUT) {
-                const elem* ev = reinterpret_cast<const elem*>(&v[h][j]);
+                float fv[VEC];
+                unpack_in<Tr>(v[h][j], fv);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) qs[h][e] += Tr::f(ev[e]);
+                for (int e = 0; e < VEC; ++e) qs[h][e] += fv[e];
               }
             }
           }
       }
     } else {
-      // ---- stage W_a^T of this segment in LDS (zero for k >= r) and the weights
+      // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for
+      //      k >= r), and the weights
       const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
       const int chunks = A * r * (D / VEC);
       for (int q = tid; q < chunks; q += kBlock) {
-        const int c0 = (q % (D / VEC)) * VEC;
-        const int ak = q / (D / VEC);  // a * r + k
-        const int a = ak / r, k = ak % r;
+        // k varies fastest across lanes, so the transposed LDS writes are contiguous
+        const int k = q % r;
+        const int rest = q / r;
+        const int c0 = (rest % (D / VEC)) * VEC;
+        const int a = rest / (D / VEC);
         elem v[VEC];
-        *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(Wseg + (size_t)ak * D + c0);
+        *reinterpret_cast<u32x4*>(v) =
+            *reinterpret_cast<const u32x4*>(Wseg + ((size_t)a * r + k) * D + c0);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) wt[((size_t)a * D + c0 + j) * RS + k] = v[j];
+        for (int j = 0; j < VEC; ++j) {
+          const int c = c0 + j;
+          wt[(a * D + (c & ~31) + cinv32(c & 31)) * RS + k] = v[j];
+        }
       }
-      if (rp > r) {
+      if (!FIX && rp > r) {
         const int pad = rp - r;
         for (int q = tid; q < A * D * pad; q += kBlock) {
           const int k = r + q % pad;
           const int ac = q / pad;
-          wt[(size_t)ac * RS + k] = Tr::e(0.f);
+          wt[ac * RS + k] = Tr::e(0.f);
         }
       }
       if (tid < A) wsh[tid] = w_all[(size_t)s * A + tid];
@@ -350,23 +420,40 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
       const int n_my = first < T ? min(kCorrIters, (T - first + kCorrRowsPerIter - 1) / kCorrRowsPerIter) : 0;
 
       Tile b;
+      frag u2[NF];
       auto load_x = [&](int h, int t0) {
+        if (t0 + 32 <= T) {
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
-          const int tok = t0 + TPI * j + lrow;
-          b.x[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
-                              : u32x4{0u, 0u, 0u, 0u};
+          for (int j = 0; j < JN; ++j)
+            b.x[h][j] = *reinterpret_cast<const u32x4*>(X + (t0 + TPI * j + lrow) * D + 64 * h + lcol);
+        } else {
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const int tok = t0 + TPI * j + lrow;
+            b.x[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + tok * D + 64 * h + lcol)
+                                : u32x4{0u, 0u, 0u, 0u};
+          }
         }
       };
-      auto load_u = [&](int t0) {
+      auto load_u = [&](frag (&dst)[NF], int t0) {
         const int t = t0 + ln;
+        if (FIX && t0 + 32 <= T) {
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const int a = f / KS, ks = f - a * KS;
+            const elem* up = Useg + (a * T + t) * r + g * half + ks * SLOT;
+            if constexpr (SLOT == 8) dst[f] = *reinterpret_cast<const u32x4*>(up);
+            else dst[f] = Tr::f(*up);
+          }
+          return;
+        }
         const bool valid = t < T;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           if (f < nfrag) {
             const int a = f / KS, ks = f - a * KS;
             const int k0 = g * half + ks * SLOT;
-            const elem* up = Useg + ((size_t)a * T + t) * r + k0;
+            const elem* up = Useg + (a * T + t) * r + k0;
             if constexpr (SLOT == 8) {
               u32x4 v = {0u, 0u, 0u, 0u};
               if (valid && k0 < r) {
@@ -379,49 +466,53 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
                   v = *reinterpret_cast<u32x4*>(tmp);
                 }
               }
-              b.u[f] = v;
+              dst[f] = v;
             } else {
-              b.u[f] = (valid && k0 < r) ? Tr::f(*up) : 0.f;
+              dst[f] = (valid && k0 < r) ? Tr::f(*up) : 0.f;
             }
           }
         }
       };
 
-      if (n_my > 0) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) load_x(h, first);
-        load_u(first);
-      }
-      for (int it = 0; it < n_my; ++it) {
+      // one tile: MFMAs on `cu`; the next tile's U goes to `nu` before the MFMAs start
+      auto run_tile = [&](int it, frag (&cu)[NF], frag (&nu)[NF]) {
         const int t0 = first + it * kCorrRowsPerIter;
         const int tn = t0 + kCorrRowsPerIter;
         const bool more = it + 1 < n_my;
-        // ---- per 64-channel half: two 32-channel MFMA blocks into the staging tile, then
-        //      add X, round, coalesced store
+        if (more) load_u(nu, tn);
+        const bool full = t0 + 32 <= T;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
+          // ---- two 32-channel MFMA blocks of this half into the staging tile
 #pragma unroll 1
           for (int cbl = 0; cbl < 2; ++cbl) {
             const int cb = 2 * h + cbl;
-            const elem* ap = wt + (size_t)(cb * 32 + cmap32(ln)) * RS + g * half;
+            const elem* ap = wt + (cb * 32 + ln) * RS + g * half;
             floatx16 acc, tmp;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) { acc[i] = 0.f; tmp[i] = 0.f; }
+            for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-              if (f < nfrag) {
+              if (FIX || f < nfrag) {
                 const int a = f / KS, ks = f - a * KS;
                 frag af;
                 if constexpr (SLOT == 8) {
-                  af = *reinterpret_cast<const u32x4*>(ap + (size_t)a * D * RS + ks * SLOT);
+                  af = *reinterpret_cast<const u32x4*>(ap + a * D * RS + ks * SLOT);
                 } else {
-                  af = ap[(size_t)a * D * RS + ks];
+                  af = ap[a * D * RS + ks];
                 }
-                tmp = Tr::mma(af, b.u[f], tmp);
+                if (ks == 0) {
+                  floatx16 z;
+#pragma unroll
+                  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+                  tmp = Tr::mma(af, cu[f], z);
+                } else {
+                  tmp = Tr::mma(af, cu[f], tmp);
+                }
                 if (ks == KS - 1) {
                   const float wa = wsh[a];
 #pragma unroll
-                  for (int i = 0; i < 16; ++i) { acc[i] += wa * tmp[i]; tmp[i] = 0.f; }
+                  for (int i = 0; i < 16; ++i) acc[i] += wa * tmp[i];
                 }
               }
             }
@@ -431,33 +522,44 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
               *reinterpret_cast<floatx4*>(sp + 4 * q) =
                   floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
           }
-          if (h == NH - 1 && more) load_u(tn);  // U of this tile is consumed
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          // ---- add X, round once, coalesced store
 #pragma unroll
           for (int j = 0; j < JN; ++j) {
             const int row = TPI * j + lrow;
             const int tok = t0 + row;
-            float dv[VEC];
+            float dv[VEC], xv[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
               *reinterpret_cast<floatx4*>(&dv[e]) =
                   *reinterpret_cast<const floatx4*>(stage + row * kStageRow + lcol + e);
-            const elem* xv = reinterpret_cast<const elem*>(&b.x[h][j]);
-            elem ov[VEC];
+            unpack_in<Tr>(b.x[h][j], xv);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) ov[e] = Tr::e(Tr::f(xv[e]) + dv[e]);
-            if (tok < T) {
-              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) =
-                  *reinterpret_cast<const u32x4*>(ov);
+            for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
+            const u32x4 o = pack_out<Tr>(dv);
+            if (full || tok < T) {
+              *reinterpret_cast<u32x4*>(Y + tok * D + 64 * h + lcol) = o;
               if constexpr (POOL_OUT) {
+                float fo[VEC];
+                unpack_in<Tr>(o, fo);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) qs[h][e] += Tr::f(ov[e]);
+                for (int e = 0; e < VEC; ++e) qs[h][e] += fo[e];
               }
             }
           }
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
           if (more) load_x(h, tn);  // this half of X is consumed
         }
+      };
+
+      if (n_my > 0) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) load_x(h, first);
+        load_u(b.u, first);
+      }
+      for (int it = 0; it < n_my; it += 2) {
+        run_tile(it, b.u, u2);
+        if (it + 1 < n_my) run_tile(it + 1, u2, b.u);
       }
     }
 
@@ -545,12 +647,12 @@ hipError_t launch_score(const float* partials, int n_tiles, int T, const float* 
   return hipGetLastError();
 }
 
-template <class Tr, int D, int NF>
-static hipError_t correct_nf(const void* K, const void* V, int S, int T, const void* U,
-                             const void* W, int A, int r, int rp, const float* w,
-                             const uint8_t* mask, const void* K_fb, const void* V_fb,
-                             void* K_out, void* V_out, float* next_partials, int* ctr,
-                             hipStream_t st) {
+template <class Tr, int D, int NA, int KSC, int NFG>
+static hipError_t correct_v(const void* K, const void* V, int S, int T, const void* U,
+                            const void* W, int A, int r, int rp, const float* w,
+                            const uint8_t* mask, const void* K_fb, const void* V_fb,
+                            void* K_out, void* V_out, float* next_partials, int* ctr,
+                            hipStream_t st) {
   using elem = typename Tr::elem;
   const int PADK = 16 / (int)sizeof(elem);
   const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
@@ -558,8 +660,8 @@ static hipError_t correct_nf(const void* K, const void* V, int S, int T, const v
   const int n_chunks = T > 0 ? ceil_div(T, kChunk) : 1;
   const int n_items = S * 2 * n_chunks;
   const int grid = n_items < 2 * device_cus() ? n_items : 2 * device_cus();
-  auto k_pool = correct_kernel<Tr, D, NF, true>;
-  auto k_plain = correct_kernel<Tr, D, NF, false>;
+  auto k_pool = correct_kernel<Tr, D, NA, KSC, NFG, true>;
+  auto k_plain = correct_kernel<Tr, D, NA, KSC, NFG, false>;
   if (lds > 48 * 1024) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pool),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -573,23 +675,36 @@ static hipError_t correct_nf(const void* K, const void* V, int S, int T, const v
   return hipGetLastError();
 }
 
-// Picks the smallest register-resident fragment count that holds A * (rp / 2 / SLOT).
+// Compile-time variants for the common anchor shapes (bf16, r = 32 with A in {1, 2, 4, 6, 8},
+// r = 16 or 64 with A = 4); every other shape takes the runtime-general kernel with the
+// smallest register-resident fragment count that holds A * (rp / 2 / SLOT).
 template <class Tr, int D>
 static hipError_t correct_t(const void* K, const void* V, int S, int T, const void* U,
                             const void* W, int A, int r, const float* w, const uint8_t* mask,
                             const void* K_fb, const void* V_fb, void* K_out, void* V_out,
                             float* next_partials, int* ctr, hipStream_t st) {
   const int rp = (r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
+#define KVC_ARGS K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out, next_partials, ctr, st
+  if constexpr (Tr::SLOT == 8 && D == 128) {
+    if (r == 32) {
+      switch (A) {
+        case 1: return correct_v<Tr, D, 1, 2, 0>(KVC_ARGS);
+        case 2: return correct_v<Tr, D, 2, 2, 0>(KVC_ARGS);
+        case 4: return correct_v<Tr, D, 4, 2, 0>(KVC_ARGS);
+        case 6: return correct_v<Tr, D, 6, 2, 0>(KVC_ARGS);
+        case 8: return correct_v<Tr, D, 8, 2, 0>(KVC_ARGS);
+        default: break;
+      }
+    }
+    if (r == 16 && A == 4) return correct_v<Tr, D, 4, 1, 0>(KVC_ARGS);
+    if (r == 64 && A == 4) return correct_v<Tr, D, 4, 4, 0>(KVC_ARGS);
+  }
   const int nfrag = A * (rp / 2 / Tr::SLOT);
   constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
-  if (nfrag <= F0)
-    return correct_nf<Tr, D, F0>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                                 next_partials, ctr, st);
-  if (nfrag <= F1)
-    return correct_nf<Tr, D, F1>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                                 next_partials, ctr, st);
-  return correct_nf<Tr, D, F2>(K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out,
-                               next_partials, ctr, st);
+  if (nfrag <= F0) return correct_v<Tr, D, 0, 0, F0>(KVC_ARGS);
+  if (nfrag <= F1) return correct_v<Tr, D, 0, 0, F1>(KVC_ARGS);
+  return correct_v<Tr, D, 0, 0, F2>(KVC_ARGS);
+#undef KVC_ARGS
 }
 
 hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
