@@ -113,9 +113,8 @@ kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, 1);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_pool);
-  if (T > 0) KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, part, c.n_pool_tiles, st), "pool");
-  KVC_HIP(kvc::launch_reduce_pool(part, T > 0 ? c.n_pool_tiles : 0, T, S, d, q_out, st),
-          "pool reduce");
+  KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, part, c.n_chunks, st), "pool");
+  KVC_HIP(kvc::launch_reduce_pool(part, c.n_chunks, T, S, d, q_out, st), "pool reduce");
   return ok();
 }
 
@@ -157,6 +156,9 @@ static kvc_status validate_correct(const void* K, const void* V, int L, int H, i
   return KVC_OK;
 }
 
+// One correction pass.  Without q_in or earlier chunk sums, pooling, matching and correction
+// run as one fused launch; otherwise the matching kernel reads q_in (or the chunk sums that the
+// previous pass of a chain left in the workspace) and the correction kernel follows it.
 static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, int T, int d,
                                   int dtype, const float* desc, const void* U, const void* W,
                                   int A, int r, float tau, const float* q_in,
@@ -165,29 +167,43 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
                                   uint8_t* mask_out, float* score_out, float* w_out,
                                   bool want_next, void* ws, hipStream_t st) {
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
-  const int S = c.S;
   char* base = static_cast<char*>(ws);
-  float* pool = reinterpret_cast<float*>(base + c.off_pool);
-  float* next = reinterpret_cast<float*>(base + c.off_next);
-  float* wv = reinterpret_cast<float*>(base + c.off_w);
-  float* sc = reinterpret_cast<float*>(base + c.off_score);
-  uint8_t* mk = reinterpret_cast<uint8_t*>(base + c.off_mask);
-  int* ctr = reinterpret_cast<int*>(base + c.off_ctr);
-  const float* partials = pool;
-  int n_tiles = c.n_pool_tiles;
-  if (q_in == nullptr && next_partials_in != nullptr) {
-    partials = next_partials_in;
-    n_tiles = c.n_corr_tiles;
-  } else if (q_in == nullptr && T > 0) {
-    KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, pool, c.n_pool_tiles, st), "pool");
+  kvc::CorrectLaunch cl{};
+  cl.K = K;
+  cl.V = V;
+  cl.S = c.S;
+  cl.T = T;
+  cl.d = d;
+  cl.dtype = dtype;
+  cl.U = U;
+  cl.W = W;
+  cl.A = A;
+  cl.r = r;
+  cl.w_ws = reinterpret_cast<float*>(base + c.off_w);
+  cl.mask_ws = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  cl.K_fb = K_fb;
+  cl.V_fb = V_fb;
+  cl.K_out = K_out;
+  cl.V_out = V_out;
+  cl.next_partials = want_next ? reinterpret_cast<float*>(base + c.off_next) : nullptr;
+  cl.ctr = reinterpret_cast<int*>(base + c.off_ctr);
+  cl.fused = q_in == nullptr && next_partials_in == nullptr;
+  if (cl.fused) {
+    cl.pool_partials = reinterpret_cast<float*>(base + c.off_pool);
+    cl.done = reinterpret_cast<int*>(base + c.off_done);
+    cl.desc = desc;
+    cl.tau = tau;
+    cl.mask_out = mask_out;
+    cl.score_out = score_out;
+    cl.w_out = w_out;
+  } else {
+    KVC_HIP(kvc::launch_score(next_partials_in, c.n_chunks, T, q_in, desc, c.S, d, A, tau,
+                              reinterpret_cast<float*>(base + c.off_w),
+                              reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
+                              mask_out, cl.ctr, st),
+            "score");
   }
-  if (T == 0) n_tiles = 0;
-  KVC_HIP(kvc::launch_score(partials, n_tiles, T, q_in, desc, S, d, A, tau, nullptr, wv, sc, mk,
-                            nullptr, score_out, w_out, mask_out, ctr, st),
-          "score");
-  KVC_HIP(kvc::launch_correct(K, V, S, T, d, dtype, U, W, A, r, wv, mk, K_fb, V_fb, K_out, V_out,
-                              want_next ? next : nullptr, ctr, st),
-          "correct");
+  KVC_HIP(kvc::launch_correct(cl, st), "correct");
   return KVC_OK;
 }
 
@@ -210,8 +226,7 @@ kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d,
   if (q_next_out) {
     const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
     float* next = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_next);
-    KVC_HIP(kvc::launch_reduce_pool(next, T > 0 ? c.n_corr_tiles : 0, T, c.S, d, q_next_out, st),
-            "q_next");
+    KVC_HIP(kvc::launch_reduce_pool(next, c.n_chunks, T, c.S, d, q_next_out, st), "q_next");
   }
   return ok();
 }

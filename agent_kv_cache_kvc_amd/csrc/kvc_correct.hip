@@ -6,10 +6,13 @@
 // added to K and V; a segment whose best match is below tau falls back to dense prefill.
 //
 // Kernels (all deterministic: fixed-order reductions, no floating-point atomics)
-//   pool_partials_kernel  token sums of K and V per 256-token tile          (HBM stream)
-//   score_kernel          tile sums -> q, cosines, softmax, score, mask     (one wave/segment)
-//   correct_kernel        X' = X + sum_a w_a U_a W_a on MFMA, or copy-through (HBM stream)
-//   reduce_pool_kernel    tile sums -> q (the pooling entry point)
+//   pool_partials_kernel  token sums of K and V per 512-token chunk          (HBM stream)
+//   reduce_pool_kernel    chunk sums -> q (the pooling entry point)
+//   score_kernel          chunk sums or q -> cosines, softmax, score, mask  (one wave/segment)
+//   correct_kernel        X' = X + sum_a w_a U_a W_a on MFMA, or copy-through (HBM stream);
+//                         its fused form also carries the pooling and the matching of every
+//                         segment in the same work queue (one launch for the whole step)
+//   reset_kernel          zeroes the counters of the fused form
 #include <hip/hip_runtime.h>
 
 #include "kvc_device.h"
@@ -48,198 +51,7 @@ struct TrF32 {
   }
 };
 
-template <class Tr>
-__device__ __forceinline__ void load16(const typename Tr::elem* p, float (&v)[Tr::VEC]) {
-  u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-  if constexpr (Tr::VEC == 8) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(raw[j] << 16);
-      v[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(raw[j]);
-  }
-}
-
-// ------------------------------------------------------------------------- pooling
-// grid (n_tiles, S, 2); each workgroup sums kPoolRows tokens of one segment's K or V.
-template <class Tr, int D>
-__global__ __launch_bounds__(kBlock) void pool_partials_kernel(
-    const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V, int T,
-    float* __restrict__ partials, int n_tiles) {
-  using elem = typename Tr::elem;
-  constexpr int VEC = Tr::VEC;
-  constexpr int LPR = D / VEC;       // lanes per token row
-  constexpr int RPP = kBlock / LPR;  // rows per pass
-  __shared__ float red[RPP][D + 1];
-  const int tile = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
-  const elem* src = (x == 0 ? K : V) + (size_t)s * T * D;
-  const int tid = threadIdx.x;
-  const int cg = tid % LPR, rs = tid / LPR;
-  float acc[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
-  const int t0 = tile * kPoolRows;
-  const int t1 = min(T, t0 + kPoolRows);
-#pragma unroll 4
-  for (int t = t0 + rs; t < t1; t += RPP) {
-    float v[VEC];
-    load16<Tr>(src + (size_t)t * D + cg * VEC, v);
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) acc[j] += v[j];
-  }
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) red[rs][cg * VEC + j] = acc[j];
-  __syncthreads();
-  if (tid < D) {
-    float sum = 0.f;
-    for (int i = 0; i < RPP; ++i) sum += red[i][tid];
-    partials[(((size_t)x * S + s) * n_tiles + tile) * D + tid] = sum;
-  }
-}
-
-// tile sums -> pooled descriptor, one wave per segment.
-template <int D>
-__device__ __forceinline__ void pooled_query(const float* __restrict__ partials, int n_tiles,
-                                             int T, int s, int S, int lane,
-                                             float (&q)[2 * D / kWave]) {
-  constexpr int PER = 2 * D / kWave;
-  // tile sums are added in tile order; loads are issued 8 tiles at a time
-  float sum[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) sum[i] = 0.f;
-  for (int t0 = 0; t0 < n_tiles; t0 += 8) {
-    float v[8][PER];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int c = lane + kWave * i;
-        const int x = c / D, ch = c % D;
-        v[u][i] = (t0 + u < n_tiles)
-                      ? partials[(((size_t)x * S + s) * n_tiles + t0 + u) * D + ch]
-                      : 0.f;
-      }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (t0 + u < n_tiles) sum[i] += v[u][i];
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) q[i] = T > 0 ? sum[i] / (float)T : 0.f;
-}
-
-template <int D>
-__global__ __launch_bounds__(kWave) void reduce_pool_kernel(const float* __restrict__ partials,
-                                                            int n_tiles, int T,
-                                                            float* __restrict__ q_out) {
-  constexpr int PER = 2 * D / kWave;
-  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
-  float q[PER];
-  pooled_query<D>(partials, n_tiles, T, s, S, lane, q);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
-}
-
-// ------------------------------------------------------------------------- matching
-// One wave per segment: q, s_a = cos(q, desc_a), w = softmax(s), score = max s, mask.
-template <int D>
-__global__ __launch_bounds__(kWave) void score_kernel(
-    const float* __restrict__ partials, int n_tiles, int T, const float* __restrict__ q_in,
-    const float* __restrict__ desc, int A, float tau, float* __restrict__ w_ws,
-    uint8_t* __restrict__ mask_ws, float* __restrict__ q_out, float* __restrict__ score_out,
-    float* __restrict__ w_out, uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
-  constexpr int PER = 2 * D / kWave;
-  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
-  if (s == 0 && lane == 0) *ctr = 0;  // work counter of the correction pass that follows
-  float q[PER];
-  if (q_in != nullptr) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
-  } else {
-    pooled_query<D>(partials, n_tiles, T, s, S, lane, q);
-  }
-  float qq = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
-  qq = wave_sum(qq);
-  const float nq = sqrtf(qq);
-  float sc[kMaxA];
-  float best = -INFINITY;
-  bool nan = false;
-#pragma unroll
-  for (int a = 0; a < kMaxA; ++a) {
-    sc[a] = 0.f;
-    if (a < A) {
-      const float* da = desc + ((size_t)s * A + a) * 2 * D;
-      float dd = 0.f, dq = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const float v = da[lane + kWave * i];
-        dd += v * v;
-        dq += v * q[i];
-      }
-      dd = wave_sum(dd);
-      dq = wave_sum(dq);
-      const float den = nq * sqrtf(dd);
-      const float c = (den == 0.f) ? 0.f : dq / den;
-      sc[a] = c;
-      nan |= (c != c);
-      best = fmaxf(best, c);
-    }
-  }
-  const float score = nan ? __uint_as_float(0x7fc00000u) : best;
-  float z = 0.f;
-  float ex[kMaxA];
-#pragma unroll
-  for (int a = 0; a < kMaxA; ++a) {
-    ex[a] = 0.f;
-    if (a < A) {
-      ex[a] = expf(sc[a] - score);
-      z += ex[a];
-    }
-  }
-  const uint8_t fall = !(score >= tau);
-  if (lane < A) {
-    float wv = 0.f;
-#pragma unroll
-    for (int a = 0; a < kMaxA; ++a)
-      if (a == lane) wv = ex[a] / z;
-    w_ws[(size_t)s * A + lane] = wv;
-    if (w_out) w_out[(size_t)s * A + lane] = wv;
-  }
-  if (lane == 0) {
-    mask_ws[s] = fall;
-    if (mask_out) mask_out[s] = fall;
-    if (score_out) score_out[s] = score;
-  }
-  if (q_out) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
-  }
-}
-
-// ------------------------------------------------------------------------- correction
-// Persistent workgroups (4 waves) take work items (segment, K|V, 512-token chunk) from a
-// counter that the score kernel resets.  A wave owns 32 tokens per tile and all d channels.
-//
-// MFMA: (delta X)^T = W^T U^T per 32-channel block; A operand = W_a^T staged in LDS (rows
-// permuted by cmap32), B operand = U_a rows (8 consecutive k per lane, straight from HBM);
-// result register i of lane l = (token l % 32, channel 16 (l / 32) + i).  Each anchor's
-// product is finished in float32 and scaled by its weight, so w never passes through bf16.
-// k layout: r is padded to rp (multiple of 2*SLOT); lane half g covers k in
-// [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.
-//
-// Memory: X is loaded and X' stored with coalesced 16-byte accesses (lane l of an access
-// covers token l / LPT of the group, channels 8 (l % LPT) ... of a 64-channel half row);
-// the MFMA result goes through a per-wave LDS tile [32][64 + 4] floats to meet that layout.
-// The next tile's U (double-buffered) is requested before the current tile's MFMAs, and
-// each half of the next tile's X as soon as the epilogue has consumed that half.
-constexpr int kChunk = kCorrRowsPerIter * kCorrIters;  // tokens per work item
-constexpr int kStageRow = 68;                          // floats per staged token row
+constexpr int kStageRow = 68;  // floats per staged token row (64 + 4: conflict-free rows)
 
 // Inverse of cmap32: channel within a 32-block -> MFMA operand row.  W^T rows are stored in
 // LDS in operand-row order, so the 16 lanes of a quarter wave read 16 consecutive rows.
@@ -279,6 +91,260 @@ __device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
   }
 }
 
+// ------------------------------------------------------------------------- chunk sums
+// Coalesced layout of a 32-token wave tile: access j of lane l covers token TPI j + l / LPT
+// and channels 64 h + VEC (l % LPT) ... of half h.  A lane adds its tokens in (tile, access)
+// order, then the lanes sharing a channel are added by a butterfly and the 4 waves in fixed
+// order.  Every pooled sum in this file (inputs, fused pooling items, outputs) takes this
+// order, so the pooled descriptor of a cache does not depend on which pass computed it.
+template <class Tr, int D>
+__device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
+                                             int tid) {
+  constexpr int NH = D / 64, VEC = Tr::VEC, LPT = Tr::LPT;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int lcol = VEC * (lane % LPT);
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float v = qs[h][e];
+#pragma unroll
+      for (int off = LPT; off < kWave; off <<= 1) v += __shfl_xor(v, off, 64);
+      if (lane < LPT) red[wave][64 * h + lcol + e] = v;
+    }
+  __syncthreads();
+  float out = 0.f;
+  if (tid < D) out = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  return out;  // valid for tid < D; the caller synchronises before `red` is written again
+}
+
+// Token sums of the chunk [tb, min(T, tb + kChunk)) of one [T, D] segment.
+template <class Tr, int D>
+__device__ __forceinline__ float chunk_sums(const typename Tr::elem* __restrict__ X, int tb,
+                                            int T, float (*red)[D], int tid) {
+  constexpr int NH = D / 64, VEC = Tr::VEC, LPT = Tr::LPT, TPI = kWave / LPT;
+  constexpr int JN = LPT / 2;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int lrow = lane / LPT, lcol = VEC * (lane % LPT);
+  float qs[NH][VEC];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+#pragma unroll 2
+  for (int it = 0; it < kCorrIters; ++it) {
+    const int t0 = tb + it * kCorrRowsPerIter + wave * 32;
+    u32x4 v[NH][JN];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        const int tok = t0 + TPI * j + lrow;
+        v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
+                          : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        float fv[VEC];
+        unpack_in<Tr>(v[h][j], fv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qs[h][e] += fv[e];
+      }
+  }
+  return finish_sums<Tr, D>(qs, red, tid);
+}
+
+// grid (n_chunks, S, 2): chunk sums of K (z = 0) and V (z = 1).
+template <class Tr, int D>
+__global__ __launch_bounds__(kBlock) void pool_partials_kernel(
+    const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V, int T,
+    float* __restrict__ partials, int n_chunks) {
+  __shared__ float red[4][D];
+  const int chunk = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
+  const typename Tr::elem* X = (x == 0 ? K : V) + (size_t)s * T * D;
+  const float v = chunk_sums<Tr, D>(X, chunk * kChunk, T, red, threadIdx.x);
+  if (threadIdx.x < D) partials[(((size_t)x * S + s) * n_chunks + chunk) * D + threadIdx.x] = v;
+}
+
+// ------------------------------------------------------------------------- matching
+// Chunk sums written by other workgroups of the running kernel are read through the
+// device-coherent path (agent-scope atomic loads); sums from earlier launches with plain loads.
+template <bool COHERENT>
+__device__ __forceinline__ float load_sum(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+// Chunk sums -> pooled descriptor [mean K ; mean V]; one wave, lane holds channels
+// lane + 64 i.  The sums are added in chunk order; loads go out 8 chunks at a time.
+template <int D, bool COHERENT>
+__device__ __forceinline__ void pooled_query(const float* __restrict__ partials, int n_chunks,
+                                             int T, int s, int S, int lane,
+                                             float (&q)[2 * D / kWave]) {
+  constexpr int PER = 2 * D / kWave;
+  float sum[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum[i] = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+    float v[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = lane + kWave * i;
+        const int x = c / D, ch = c % D;
+        v[u][i] = (c0 + u < n_chunks)
+                      ? load_sum<COHERENT>(partials +
+                                           (((size_t)x * S + s) * n_chunks + c0 + u) * D + ch)
+                      : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (c0 + u < n_chunks) sum[i] += v[u][i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) q[i] = T > 0 ? sum[i] / (float)T : 0.f;
+}
+
+// One wave: s_a = cos(q, desc_a) (0 when a norm is 0), w = softmax(s), score = max_a s_a
+// (NaN if any s_a is NaN), fallback = !(score >= tau).  Lane a < A returns w_a.
+template <int D>
+__device__ __forceinline__ float segment_weights(const float (&q)[2 * D / kWave],
+                                                 const float* __restrict__ desc, int s, int A,
+                                                 float tau, int lane, float& score,
+                                                 uint8_t& fall) {
+  constexpr int PER = 2 * D / kWave;
+  float qq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
+  qq = wave_sum(qq);
+  const float nq = sqrtf(qq);
+  float sc[kMaxA];
+  float best = -INFINITY;
+  bool nan = false;
+#pragma unroll
+  for (int a = 0; a < kMaxA; ++a) {
+    sc[a] = 0.f;
+    if (a < A) {
+      const float* da = desc + ((size_t)s * A + a) * 2 * D;
+      float dd = 0.f, dq = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const float v = da[lane + kWave * i];
+        dd += v * v;
+        dq += v * q[i];
+      }
+      dd = wave_sum(dd);
+      dq = wave_sum(dq);
+      const float den = nq * sqrtf(dd);
+      const float c = (den == 0.f) ? 0.f : dq / den;
+      sc[a] = c;
+      nan |= (c != c);
+      best = fmaxf(best, c);
+    }
+  }
+  score = nan ? __uint_as_float(0x7fc00000u) : best;
+  float z = 0.f;
+  float ex[kMaxA];
+#pragma unroll
+  for (int a = 0; a < kMaxA; ++a) {
+    ex[a] = 0.f;
+    if (a < A) {
+      ex[a] = expf(sc[a] - score);
+      z += ex[a];
+    }
+  }
+  fall = !(score >= tau);
+  float wv = 0.f;
+#pragma unroll
+  for (int a = 0; a < kMaxA; ++a)
+    if (a == lane) wv = ex[a] / z;
+  return wv;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave) void reduce_pool_kernel(const float* __restrict__ partials,
+                                                            int n_chunks, int T,
+                                                            float* __restrict__ q_out) {
+  constexpr int PER = 2 * D / kWave;
+  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  float q[PER];
+  pooled_query<D, false>(partials, n_chunks, T, s, S, lane, q);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
+}
+
+// One wave per segment; also resets the work counter of the correction pass that follows.
+template <int D>
+__global__ __launch_bounds__(kWave) void score_kernel(
+    const float* __restrict__ partials, int n_chunks, int T, const float* __restrict__ q_in,
+    const float* __restrict__ desc, int A, float tau, float* __restrict__ w_ws,
+    uint8_t* __restrict__ mask_ws, float* __restrict__ score_out, float* __restrict__ w_out,
+    uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
+  constexpr int PER = 2 * D / kWave;
+  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  if (s == 0 && lane == 0) *ctr = 0;
+  float q[PER];
+  if (q_in != nullptr) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
+  } else {
+    pooled_query<D, false>(partials, n_chunks, T, s, S, lane, q);
+  }
+  float score;
+  uint8_t fall;
+  const float wv = segment_weights<D>(q, desc, s, A, tau, lane, score, fall);
+  if (lane < A) {
+    w_ws[(size_t)s * A + lane] = wv;
+    if (w_out) w_out[(size_t)s * A + lane] = wv;
+  }
+  if (lane == 0) {
+    mask_ws[s] = fall;
+    mask_out[s] = fall;
+    if (score_out) score_out[s] = score;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
+                                                       int* __restrict__ done, int S) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ctr = 0;
+  for (int i = blockIdx.x * kBlock + threadIdx.x; i < S; i += gridDim.x * kBlock) done[i] = 0;
+}
+
+// ------------------------------------------------------------------------- correction
+// Persistent workgroups (4 waves) take work items from a counter.  A correction item is
+// (segment, K|V, 512-token chunk); a wave owns 32 tokens per tile and all d channels.
+//
+// MFMA: (delta X)^T = W^T U^T per 32-channel block; A operand = W_a^T staged in LDS (rows in
+// operand order, see cinv32), B operand = U_a rows (8 consecutive k per lane, straight from
+// HBM); result register i of lane l = (token l % 32, channel 16 (l / 32) + i).  Each anchor's
+// product is finished in float32 and scaled by its weight, so w never passes through bf16.
+// k layout: r is padded to rp (multiple of 2*SLOT); lane half g covers k in
+// [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.
+//
+// Memory: X is loaded and X' stored with coalesced 16-byte accesses; the MFMA result goes
+// through a per-wave LDS tile [32][64 + 4] floats to meet that layout.  The next tile's U
+// (double-buffered) is requested before the current tile's MFMAs, and each half of the next
+// tile's X as soon as the epilogue has consumed that half.
+//
+// FUSED: the queue also holds pooling items (segment, K|V, chunk) that publish chunk sums and
+// count them per segment.  Items are ordered by batches of `batch` segments as
+//   P0, P1, C0, P2, C1, ..., P(nb-1), C(nb-2), C(nb-1)
+// (P = pooling items of a batch, C = its correction items), so a correction item only waits
+// for pooling items taken from the queue before it: each of those is held by a running
+// workgroup that does not wait, so every wait ends.  A batch's correction re-reads K and V
+// shortly after its pooling read them.  The last pooling item of a segment (the one whose
+// count increment completes the set) computes q, the weights and the fallback flag, publishes
+// them and moves the count past n_ci; correction items wait for that.  Published values are
+// written with device-coherent stores whose completion is awaited before the count moves, and
+// read with device-coherent loads (device-scope release/acquire fences would write back or
+// invalidate the whole L2 at every item on this target).  The step needs one launch.
 template <class Tr, int D, int NF>
 struct CorrTile {
   static constexpr int NH = D / 64;        // 64-channel halves
@@ -287,17 +353,39 @@ struct CorrTile {
   typename Tr::frag u[NF];                 // U fragments of the tile in flight
 };
 
+struct CorrectArgs {
+  const void* K;
+  const void* V;
+  const void* U;
+  const void* W;
+  float* w_ws;             // [S][A] weights (from score_kernel, or published when fused)
+  const uint8_t* mask;     // [S] fallback flags from score_kernel (not fused)
+  const void* K_fb;
+  const void* V_fb;
+  void* K_out;
+  void* V_out;
+  float* next_partials;    // chunk sums of the output, or null
+  int* ctr;                // work counter
+  float* pool_partials;    // fused: [2][S][n_chunks][D] chunk sums of the source
+  int* done;               // fused: [S] pooling items finished per segment, then n_ci + 1
+                           //        (matched) or n_ci + 2 (matched, fallback)
+  const float* desc;       // fused: [S][A][2D] anchor descriptors
+  uint8_t* mask_out;       // fused outputs
+  float* score_out;
+  float* w_out;
+  float tau;
+  int T, S, A, r, rp, n_chunks, n_items, batch;
+};
+
+// Bounded wait of a correction item: 0.2 s of the 100 MHz constant clock.  A safety net that
+// the queue order above never reaches; if it were reached the segment is flagged with
+// mask value 2 and its output is the copy-through.
+constexpr long long kWaitTicks = 20000000ll;
+
 // NA > 0: compile-time anchor count NA and MFMA steps per anchor KSC (r = 2 KSC SLOT);
 // NA == 0: runtime A and r with up to NFG register-resident fragments.
-template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT>
-__global__ __launch_bounds__(kBlock, 2) void correct_kernel(
-    const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V,
-    const typename Tr::elem* __restrict__ U, const typename Tr::elem* __restrict__ W,
-    const float* __restrict__ w_all, const uint8_t* __restrict__ mask,
-    const typename Tr::elem* __restrict__ K_fb, const typename Tr::elem* __restrict__ V_fb,
-    typename Tr::elem* K_out, typename Tr::elem* V_out, float* __restrict__ next_partials,
-    int T, int S, int A_rt, int r_rt, int rp_rt, int n_chunks, int n_items,
-    int* __restrict__ ctr) {
+template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED>
+__global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
   constexpr bool FIX = NA > 0;
@@ -309,43 +397,157 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
   constexpr int TPI = kWave / LPT;  // tokens per coalesced access
   constexpr int NH = Tile::NH, JN = Tile::JN;
   constexpr int PADK = 16 / sizeof(elem);
+  constexpr int PER = 2 * D / kWave;
+
+  const elem* __restrict__ K = static_cast<const elem*>(args.K);
+  const elem* __restrict__ V = static_cast<const elem*>(args.V);
+  const elem* __restrict__ U = static_cast<const elem*>(args.U);
+  const elem* __restrict__ W = static_cast<const elem*>(args.W);
+  const elem* K_fb = static_cast<const elem*>(args.K_fb);
+  const elem* V_fb = static_cast<const elem*>(args.V_fb);
+  elem* K_out = static_cast<elem*>(args.K_out);
+  elem* V_out = static_cast<elem*>(args.V_out);
+  const int T = args.T, S = args.S, n_chunks = args.n_chunks;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float wsh[kMaxA];
   __shared__ float red[4][D];
   __shared__ int s_item;
+  __shared__ int s_mask;
+  __shared__ int s_last;
 
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int g = lane >> 5, ln = lane & 31;
-  float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
   elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * kStageRow * sizeof(float));
-  const int A = FIX ? NA : A_rt;
-  const int r = FIX ? 2 * KSC * SLOT : r_rt;
-  const int rp = FIX ? 2 * KSC * SLOT : rp_rt;
+  const int A = FIX ? NA : args.A;
+  const int r = FIX ? 2 * KSC * SLOT : args.r;
+  const int rp = FIX ? 2 * KSC * SLOT : args.rp;
   const int RS = rp + PADK;
   const int half = rp / 2;
   const int KS = FIX ? KSC : half / SLOT;  // MFMA steps per anchor
   const int nfrag = A * KS;
   const bool uvec = FIX || (r % VEC) == 0;
-  const int lrow = lane / LPT;               // token within a coalesced access
-  const int lcol = VEC * (lane % LPT);       // channel offset within a half row
+  const int n_ci = 2 * n_chunks;             // items per segment and kind
 
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(ctr, 1);
+    // lane-derived values are recomputed per item (kept out of the loop-carried registers)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane >> 5, ln = lane & 31;
+    float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
+    const int lrow = lane / LPT;               // token within a coalesced access
+    const int lcol = VEC * (lane % LPT);       // channel offset within a half row
+    if (tid == 0) s_item = atomicAdd(args.ctr, 1);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= n_items) break;
-    const int chunk = item % n_chunks;
-    const int sx = item / n_chunks;
-    const int x = sx & 1, s = sx >> 1;
+    if (item >= args.n_items) break;
+
+    // ---- decode the item
+    bool pool_item = false;
+    int s, ci;
+    if constexpr (FUSED) {
+      const int per_slot = args.batch * n_ci;
+      const int k = item / per_slot, o = item - k * per_slot;
+      const int nb = (S + args.batch - 1) / args.batch;
+      int b;
+      if (k == 0) {
+        pool_item = true;
+        b = 0;
+      } else if (k == 2 * nb - 1) {
+        b = nb - 1;
+      } else if (k & 1) {
+        pool_item = true;
+        b = (k + 1) / 2;
+      } else {
+        b = k / 2 - 1;
+      }
+      s = b * args.batch + o / n_ci;
+      ci = o % n_ci;
+      if (s >= S) {  // padding of the last batch
+        __syncthreads();
+        continue;
+      }
+    } else {
+      s = item / n_ci;
+      ci = item % n_ci;
+    }
+    const int x = ci / n_chunks, chunk = ci % n_chunks;
     const size_t seg = (size_t)s * T * D;
     const elem* X = (x == 0 ? K : V) + seg;
     elem* Y = (x == 0 ? K_out : V_out) + seg;
     const elem* Xfb = (x == 0 ? K_fb : V_fb);
     const int tb = chunk * kChunk;
 
-    float qs[POOL_OUT ? NH : 1][VEC];
+    if constexpr (FUSED) {
+      if (pool_item) {
+        // fields used only here are read through an opaque pointer to the kernel arguments,
+        // so they are loaded per item instead of holding scalar registers for the whole kernel
+        const __attribute__((address_space(4))) CorrectArgs* pa =
+            (const __attribute__((address_space(4))) CorrectArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(pa));
+        // ---- pooling item: chunk sums of the source, published, then counted
+        const float v = chunk_sums<Tr, D>(X, tb, T, red, tid);
+        if (tid < D)
+          __hip_atomic_store(pa->pool_partials + (((size_t)x * S + s) * n_chunks + chunk) * D + tid,
+                             v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // order only: the stores are complete before the barrier, the count after it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+        __syncthreads();
+        if (tid == 0)
+          s_last = __hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == n_ci - 1;
+        __syncthreads();
+        if (s_last && wave == 0) {
+          // the segment's last pooling item matches it: q from all chunk sums, weights and
+          // flag published, then the count moves past n_ci (by 1, or by 2 for a fallback)
+          __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          float q[PER];
+          pooled_query<D, true>(pa->pool_partials, n_chunks, T, s, S, lane, q);
+          float score;
+          uint8_t fall;
+          const float wv = segment_weights<D>(q, pa->desc, s, A, pa->tau, lane, score, fall);
+          if (lane < A) {
+            __hip_atomic_store(pa->w_ws + (size_t)s * A + lane, wv, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (pa->w_out) pa->w_out[(size_t)s * A + lane] = wv;
+          }
+          if (lane == 0) {
+            pa->mask_out[s] = fall;
+            if (pa->score_out) pa->score_out[s] = score;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+          if (lane == 0)
+            __hip_atomic_fetch_add(pa->done + s, 1 + (int)fall, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();  // `red`, s_last and the item id are free for the next item
+        continue;
+      }
+      // ---- correction item: wait until the segment is matched
+      if (tid == 0) {
+        int v = __hip_atomic_load(args.done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v <= n_ci) {
+          const long long t_end = wall_clock64() + kWaitTicks;
+          do {
+            __builtin_amdgcn_s_sleep(2);
+            v = __hip_atomic_load(args.done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } while (v <= n_ci && wall_clock64() < t_end);
+          if (v <= n_ci) args.mask_out[s] = 2;
+        }
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        s_mask = v != n_ci + 1;
+      }
+    } else {
+      if (tid == 0) s_mask = args.mask[s];
+    }
+    __syncthreads();
+    const bool masked = s_mask != 0;
+
+    float qs[NH][VEC];
     if constexpr (POOL_OUT) {
 #pragma unroll
       for (int h = 0; h < NH; ++h)
@@ -353,7 +555,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
         for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
     }
 
-    if (mask[s]) {
+    if (masked) {
       // dense-prefill stand-in: copy the fallback cache (or the source) bit for bit
       const elem* src = Xfb ? Xfb + seg : X;
       for (int it = 0; it < kCorrIters; ++it) {
@@ -385,11 +587,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
           }
       }
     } else {
+      if (tid < A) wsh[tid] = load_sum<FUSED>(args.w_ws + (size_t)s * A + tid);
       // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for
-      //      k >= r), and the weights
+      //      k >= r)
       const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
-      const int chunks = A * r * (D / VEC);
-      for (int q = tid; q < chunks; q += kBlock) {
+      const int n_w = A * r * (D / VEC);
+      for (int q = tid; q < n_w; q += kBlock) {
         // k varies fastest across lanes, so the transposed LDS writes are contiguous
         const int k = q % r;
         const int rest = q / r;
@@ -412,12 +615,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
           wt[ac * RS + k] = Tr::e(0.f);
         }
       }
-      if (tid < A) wsh[tid] = w_all[(size_t)s * A + tid];
       __syncthreads();
 
       const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
       const int first = tb + wave * 32;
-      const int n_my = first < T ? min(kCorrIters, (T - first + kCorrRowsPerIter - 1) / kCorrRowsPerIter) : 0;
+      const int n_my =
+          first < T ? min(kCorrIters, (T - first + kCorrRowsPerIter - 1) / kCorrRowsPerIter) : 0;
 
       Tile b;
       frag u2[NF];
@@ -425,7 +628,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
         if (t0 + 32 <= T) {
 #pragma unroll
           for (int j = 0; j < JN; ++j)
-            b.x[h][j] = *reinterpret_cast<const u32x4*>(X + (t0 + TPI * j + lrow) * D + 64 * h + lcol);
+            b.x[h][j] =
+                *reinterpret_cast<const u32x4*>(X + (t0 + TPI * j + lrow) * D + 64 * h + lcol);
         } else {
 #pragma unroll
           for (int j = 0; j < JN; ++j) {
@@ -564,21 +768,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(
     }
 
     if constexpr (POOL_OUT) {
-      // token sums of the stored output: lanes sharing a channel -> waves in fixed order
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float v = qs[h][e];
-#pragma unroll
-          for (int off = LPT; off < kWave; off <<= 1) v += __shfl_xor(v, off, 64);
-          if (lane < LPT) red[wave][64 * h + lcol + e] = v;
-        }
-      __syncthreads();
-      if (tid < D) {
-        const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-        next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
-      }
+      // token sums of the stored output, in the order of chunk_sums
+      const float v = finish_sums<Tr, D>(qs, red, tid);
+      if (tid < D) args.next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
     }
     __syncthreads();  // LDS (W^T, weights, staging, item id) is free for the next item
   }
@@ -590,7 +782,8 @@ static int device_cus() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cache[dev] == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
       n = 256;
     cache[dev] = n;
   }
@@ -600,78 +793,106 @@ static int device_cus() {
 // ------------------------------------------------------------------------- launchers
 template <class Tr, int D>
 static hipError_t pool_partials_t(const void* K, const void* V, int S, int T, float* partials,
-                                  int n_tiles, hipStream_t st) {
-  dim3 grid(n_tiles, S, 2);
+                                  int n_chunks, hipStream_t st) {
+  dim3 grid(n_chunks, S, 2);
   hipLaunchKernelGGL((pool_partials_kernel<Tr, D>), grid, dim3(kBlock), 0, st,
                      (const typename Tr::elem*)K, (const typename Tr::elem*)V, T, partials,
-                     n_tiles);
+                     n_chunks);
   return hipGetLastError();
 }
 
 hipError_t launch_pool_partials(const void* K, const void* V, int S, int T, int d, int dtype,
-                                float* partials, int n_tiles, hipStream_t st) {
+                                float* partials, int n_chunks, hipStream_t st) {
   if (S == 0) return hipSuccess;
   if (dtype == KVC_BF16)
-    return d == 128 ? pool_partials_t<TrBF16, 128>(K, V, S, T, partials, n_tiles, st)
-                    : pool_partials_t<TrBF16, 64>(K, V, S, T, partials, n_tiles, st);
-  return d == 128 ? pool_partials_t<TrF32, 128>(K, V, S, T, partials, n_tiles, st)
-                  : pool_partials_t<TrF32, 64>(K, V, S, T, partials, n_tiles, st);
+    return d == 128 ? pool_partials_t<TrBF16, 128>(K, V, S, T, partials, n_chunks, st)
+                    : pool_partials_t<TrBF16, 64>(K, V, S, T, partials, n_chunks, st);
+  return d == 128 ? pool_partials_t<TrF32, 128>(K, V, S, T, partials, n_chunks, st)
+                  : pool_partials_t<TrF32, 64>(K, V, S, T, partials, n_chunks, st);
 }
 
-hipError_t launch_reduce_pool(const float* partials, int n_tiles, int T, int S, int d,
+hipError_t launch_reduce_pool(const float* partials, int n_chunks, int T, int S, int d,
                               float* q_out, hipStream_t st) {
   if (S == 0) return hipSuccess;
   if (d == 128)
     hipLaunchKernelGGL((reduce_pool_kernel<128>), dim3(S), dim3(kWave), 0, st, partials,
-                       n_tiles, T, q_out);
+                       n_chunks, T, q_out);
   else
     hipLaunchKernelGGL((reduce_pool_kernel<64>), dim3(S), dim3(kWave), 0, st, partials,
-                       n_tiles, T, q_out);
+                       n_chunks, T, q_out);
   return hipGetLastError();
 }
 
-hipError_t launch_score(const float* partials, int n_tiles, int T, const float* q_in,
-                        const float* desc, int S, int d, int A, float tau, float* q_ws,
-                        float* w_ws, float* score_ws, uint8_t* mask_ws, float* q_out,
-                        float* score_out, float* w_out, uint8_t* mask_out, int* ctr,
-                        hipStream_t st) {
-  (void)q_ws;
+hipError_t launch_score(const float* partials, int n_chunks, int T, const float* q_in,
+                        const float* desc, int S, int d, int A, float tau, float* w_ws,
+                        uint8_t* mask_ws, float* score_out, float* w_out, uint8_t* mask_out,
+                        int* ctr, hipStream_t st) {
   if (S == 0) return hipSuccess;
-  float* so = score_out ? score_out : score_ws;
   if (d == 128)
-    hipLaunchKernelGGL((score_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
-                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out, ctr);
+    hipLaunchKernelGGL((score_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_chunks,
+                       T, q_in, desc, A, tau, w_ws, mask_ws, score_out, w_out, mask_out, ctr);
   else
-    hipLaunchKernelGGL((score_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_tiles, T,
-                       q_in, desc, A, tau, w_ws, mask_ws, q_out, so, w_out, mask_out, ctr);
+    hipLaunchKernelGGL((score_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_chunks,
+                       T, q_in, desc, A, tau, w_ws, mask_ws, score_out, w_out, mask_out, ctr);
   return hipGetLastError();
 }
 
 template <class Tr, int D, int NA, int KSC, int NFG>
-static hipError_t correct_v(const void* K, const void* V, int S, int T, const void* U,
-                            const void* W, int A, int r, int rp, const float* w,
-                            const uint8_t* mask, const void* K_fb, const void* V_fb,
-                            void* K_out, void* V_out, float* next_partials, int* ctr,
-                            hipStream_t st) {
+static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   using elem = typename Tr::elem;
   const int PADK = 16 / (int)sizeof(elem);
   const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
-                     (size_t)A * D * (rp + PADK) * sizeof(elem);
-  const int n_chunks = T > 0 ? ceil_div(T, kChunk) : 1;
-  const int n_items = S * 2 * n_chunks;
-  const int grid = n_items < 2 * device_cus() ? n_items : 2 * device_cus();
-  auto k_pool = correct_kernel<Tr, D, NA, KSC, NFG, true>;
-  auto k_plain = correct_kernel<Tr, D, NA, KSC, NFG, false>;
-  if (lds > 48 * 1024) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_pool),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plain),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                     (size_t)L.A * D * (L.rp + PADK) * sizeof(elem);
+  CorrectArgs a{};
+  a.K = L.K;
+  a.V = L.V;
+  a.U = L.U;
+  a.W = L.W;
+  a.w_ws = L.w_ws;
+  a.mask = L.mask_ws;
+  a.K_fb = L.K_fb;
+  a.V_fb = L.V_fb;
+  a.K_out = L.K_out;
+  a.V_out = L.V_out;
+  a.next_partials = L.next_partials;
+  a.ctr = L.ctr;
+  a.pool_partials = L.pool_partials;
+  a.done = L.done;
+  a.desc = L.desc;
+  a.mask_out = L.mask_out;
+  a.score_out = L.score_out;
+  a.w_out = L.w_out;
+  a.tau = L.tau;
+  a.T = L.T;
+  a.S = L.S;
+  a.A = L.A;
+  a.r = L.r;
+  a.rp = L.rp;
+  a.n_chunks = chunks_of(L.T);
+  const int per_kind = L.S * 2 * a.n_chunks;  // correction (or pooling) items
+  if (L.fused) {
+    a.batch = fused_batch(a.n_chunks);
+    a.n_items = 2 * ceil_div(L.S, a.batch) * a.batch * 2 * a.n_chunks;
+  } else {
+    a.batch = 0;
+    a.n_items = per_kind;
   }
-  hipLaunchKernelGGL(next_partials ? k_pool : k_plain, dim3(grid), dim3(kBlock), lds, st,
-                     (const elem*)K, (const elem*)V, (const elem*)U, (const elem*)W, w, mask,
-                     (const elem*)K_fb, (const elem*)V_fb, (elem*)K_out, (elem*)V_out,
-                     next_partials, T, S, A, r, rp, n_chunks, n_items, ctr);
+  const int want = L.fused ? 2 * per_kind : per_kind;
+  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
+  const bool pool = L.next_partials != nullptr;
+  auto k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
+                           : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
+                : (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, false, true>
+                           : correct_kernel<Tr, D, NA, KSC, NFG, false, false>);
+  if (lds > 48 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (L.fused) {
+    hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(kBlock), 0, st, L.ctr, L.done, L.S);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
@@ -679,48 +900,34 @@ static hipError_t correct_v(const void* K, const void* V, int S, int T, const vo
 // r = 16 or 64 with A = 4); every other shape takes the runtime-general kernel with the
 // smallest register-resident fragment count that holds A * (rp / 2 / SLOT).
 template <class Tr, int D>
-static hipError_t correct_t(const void* K, const void* V, int S, int T, const void* U,
-                            const void* W, int A, int r, const float* w, const uint8_t* mask,
-                            const void* K_fb, const void* V_fb, void* K_out, void* V_out,
-                            float* next_partials, int* ctr, hipStream_t st) {
-  const int rp = (r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
-#define KVC_ARGS K, V, S, T, U, W, A, r, rp, w, mask, K_fb, V_fb, K_out, V_out, next_partials, ctr, st
+static hipError_t correct_t(CorrectLaunch L, hipStream_t st) {
+  L.rp = (L.r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
   if constexpr (Tr::SLOT == 8 && D == 128) {
-    if (r == 32) {
-      switch (A) {
-        case 1: return correct_v<Tr, D, 1, 2, 0>(KVC_ARGS);
-        case 2: return correct_v<Tr, D, 2, 2, 0>(KVC_ARGS);
-        case 4: return correct_v<Tr, D, 4, 2, 0>(KVC_ARGS);
-        case 6: return correct_v<Tr, D, 6, 2, 0>(KVC_ARGS);
-        case 8: return correct_v<Tr, D, 8, 2, 0>(KVC_ARGS);
+    if (L.r == 32) {
+      switch (L.A) {
+        case 1: return correct_v<Tr, D, 1, 2, 0>(L, st);
+        case 2: return correct_v<Tr, D, 2, 2, 0>(L, st);
+        case 4: return correct_v<Tr, D, 4, 2, 0>(L, st);
+        case 6: return correct_v<Tr, D, 6, 2, 0>(L, st);
+        case 8: return correct_v<Tr, D, 8, 2, 0>(L, st);
         default: break;
       }
     }
-    if (r == 16 && A == 4) return correct_v<Tr, D, 4, 1, 0>(KVC_ARGS);
-    if (r == 64 && A == 4) return correct_v<Tr, D, 4, 4, 0>(KVC_ARGS);
+    if (L.r == 16 && L.A == 4) return correct_v<Tr, D, 4, 1, 0>(L, st);
+    if (L.r == 64 && L.A == 4) return correct_v<Tr, D, 4, 4, 0>(L, st);
   }
-  const int nfrag = A * (rp / 2 / Tr::SLOT);
+  const int nfrag = L.A * (L.rp / 2 / Tr::SLOT);
   constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
-  if (nfrag <= F0) return correct_v<Tr, D, 0, 0, F0>(KVC_ARGS);
-  if (nfrag <= F1) return correct_v<Tr, D, 0, 0, F1>(KVC_ARGS);
-  return correct_v<Tr, D, 0, 0, F2>(KVC_ARGS);
-#undef KVC_ARGS
+  if (nfrag <= F0) return correct_v<Tr, D, 0, 0, F0>(L, st);
+  if (nfrag <= F1) return correct_v<Tr, D, 0, 0, F1>(L, st);
+  return correct_v<Tr, D, 0, 0, F2>(L, st);
 }
 
-hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
-                          const void* U, const void* W, int A, int r, const float* w,
-                          const uint8_t* mask, const void* K_fb, const void* V_fb, void* K_out,
-                          void* V_out, float* next_partials, int* ctr, hipStream_t st) {
-  if (S == 0) return hipSuccess;
-  if (dtype == KVC_BF16)
-    return d == 128 ? correct_t<TrBF16, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                             V_out, next_partials, ctr, st)
-                    : correct_t<TrBF16, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                            V_out, next_partials, ctr, st);
-  return d == 128 ? correct_t<TrF32, 128>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                          V_out, next_partials, ctr, st)
-                  : correct_t<TrF32, 64>(K, V, S, T, U, W, A, r, w, mask, K_fb, V_fb, K_out,
-                                         V_out, next_partials, ctr, st);
+hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st) {
+  if (L.S == 0) return hipSuccess;
+  if (L.dtype == KVC_BF16)
+    return L.d == 128 ? correct_t<TrBF16, 128>(L, st) : correct_t<TrBF16, 64>(L, st);
+  return L.d == 128 ? correct_t<TrF32, 128>(L, st) : correct_t<TrF32, 64>(L, st);
 }
 
 }  // namespace kvc

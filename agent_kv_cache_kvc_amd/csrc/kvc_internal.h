@@ -12,9 +12,9 @@ namespace kvc {
 // ---------------------------------------------------------------- launch geometry
 constexpr int kWave = 64;             // CDNA wavefront width
 constexpr int kBlock = 256;           // 4 waves per workgroup everywhere
-constexpr int kPoolRows = 256;        // tokens per pooling workgroup
 constexpr int kCorrRowsPerIter = 128; // tokens per correction workgroup iteration (4 waves x 32)
 constexpr int kCorrIters = 4;         // iterations per correction workgroup (512 tokens)
+constexpr int kChunk = kCorrRowsPerIter * kCorrIters;  // tokens per work item and chunk sum
 constexpr int kMaxA = 16;             // anchors per segment held in registers
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
@@ -23,17 +23,21 @@ constexpr int kJacobiMaxSweeps = 40;  // hard cap: every workgroup leaves the sw
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// chunk sums per segment and per K|V (one all-zero chunk when T = 0)
+inline int chunks_of(int T) { return T > 0 ? ceil_div(T, kChunk) : 1; }
+
+// segments per batch of the fused correction queue: about 256 work items per batch and kind
+inline int fused_batch(int n_chunks) { return n_chunks >= 128 ? 1 : 128 / n_chunks; }
+
 // ---------------------------------------------------------------- correction workspace
 struct CorrectLayout {
   int S, T, d, A;
-  int n_pool_tiles;   // pooling partials per segment and per K|V
-  int n_corr_tiles;   // correction workgroups per segment and per K|V
-  size_t off_pool;    // float [2][S][n_pool_tiles][d]
-  size_t off_next;    // float [2][S][n_corr_tiles][d]   (pooled output partials)
-  size_t off_q;       // float [S][2d]
+  int n_chunks;       // chunk sums per segment and per K|V
+  size_t off_pool;    // float [2][S][n_chunks][d]   chunk sums of the source
+  size_t off_next;    // float [2][S][n_chunks][d]   chunk sums of the output (pooled next)
   size_t off_w;       // float [S][A]
-  size_t off_score;   // float [S]
   size_t off_mask;    // uint8 [S]
+  size_t off_done;    // int [S]: finished pooling items per segment (fused pass)
   size_t off_ctr;     // int [1]: work counter of the correction pass
   size_t bytes;
 };
@@ -44,19 +48,44 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.T = T;
   c.d = d;
   c.A = A;
-  c.n_pool_tiles = T > 0 ? ceil_div(T, kPoolRows) : 1;
-  c.n_corr_tiles = T > 0 ? ceil_div(T, kCorrRowsPerIter * kCorrIters) : 1;
+  c.n_chunks = chunks_of(T);
+  const size_t sums = sizeof(float) * 2ull * c.S * c.n_chunks * d;
   size_t o = 0;
-  c.off_pool = o;  o = align_up(o + sizeof(float) * 2ull * c.S * c.n_pool_tiles * d, 256);
-  c.off_next = o;  o = align_up(o + sizeof(float) * 2ull * c.S * c.n_corr_tiles * d, 256);
-  c.off_q = o;     o = align_up(o + sizeof(float) * (size_t)c.S * 2 * d, 256);
+  c.off_pool = o;  o = align_up(o + sums, 256);
+  c.off_next = o;  o = align_up(o + sums, 256);
   c.off_w = o;     o = align_up(o + sizeof(float) * (size_t)c.S * A, 256);
-  c.off_score = o; o = align_up(o + sizeof(float) * (size_t)c.S, 256);
   c.off_mask = o;  o = align_up(o + (size_t)c.S, 256);
+  c.off_done = o;  o = align_up(o + sizeof(int) * (size_t)c.S, 256);
   c.off_ctr = o;   o = align_up(o + sizeof(int), 256);
   c.bytes = o;
   return c;
 }
+
+// Everything one correction launch needs (see launch_correct).
+struct CorrectLaunch {
+  const void* K;
+  const void* V;
+  int S, T, d, dtype;
+  const void* U;
+  const void* W;
+  int A, r, rp;
+  float* w_ws;              // weights (from launch_score, or published by the fused pass)
+  const uint8_t* mask_ws;   // fallback flags from launch_score (not fused)
+  const void* K_fb;
+  const void* V_fb;
+  void* K_out;
+  void* V_out;
+  float* next_partials;     // chunk sums of the output, or null
+  int* ctr;
+  bool fused;               // pooling + matching + correction in one queue
+  float* pool_partials;     // fused: chunk sums of the source
+  int* done;                // fused: per-segment counters
+  const float* desc;        // fused: anchor descriptors
+  float tau;
+  uint8_t* mask_out;        // fused: matching outputs
+  float* score_out;
+  float* w_out;
+};
 
 // ---------------------------------------------------------------- fit workspace
 struct FitLayout {
@@ -97,18 +126,16 @@ inline FitLayout fit_layout(int M, int T, int d, int r, int target_wgs = 2048) {
 
 // ---------------------------------------------------------------- launchers (.hip files)
 hipError_t launch_pool_partials(const void* K, const void* V, int S, int T, int d, int dtype,
-                                float* partials, int n_tiles, hipStream_t st);
-hipError_t launch_score(const float* partials, int n_tiles, int T, const float* q_in,
-                        const float* desc, int S, int d, int A, float tau, float* q_ws,
-                        float* w_ws, float* score_ws, uint8_t* mask_ws, float* q_out,
-                        float* score_out, float* w_out, uint8_t* mask_out, int* ctr,
-                        hipStream_t st);
-hipError_t launch_correct(const void* K, const void* V, int S, int T, int d, int dtype,
-                          const void* U, const void* W, int A, int r, const float* w,
-                          const uint8_t* mask, const void* K_fb, const void* V_fb, void* K_out,
-                          void* V_out, float* next_partials, int* ctr, hipStream_t st);
-hipError_t launch_reduce_pool(const float* partials, int n_tiles, int T, int S, int d,
+                                float* partials, int n_chunks, hipStream_t st);
+hipError_t launch_reduce_pool(const float* partials, int n_chunks, int T, int S, int d,
                               float* q_out, hipStream_t st);
+// Matching of every segment from chunk sums (or from q_in when not null); resets *ctr.
+hipError_t launch_score(const float* partials, int n_chunks, int T, const float* q_in,
+                        const float* desc, int S, int d, int A, float tau, float* w_ws,
+                        uint8_t* mask_ws, float* score_out, float* w_out, uint8_t* mask_out,
+                        int* ctr, hipStream_t st);
+// Correction (after launch_score), or the fused pass (resets its own counters).
+hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
                       float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                       hipStream_t st);

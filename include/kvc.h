@@ -85,11 +85,15 @@ kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T
  *   A, r        : 1 <= A, 1 <= r <= 64, A * ceil(r/16)*16 <= 256
  *   tau         : reliability threshold (+inf: every segment falls back; -inf: none)
  *   q_in        : [L,H,2d] float32 or NULL: a precomputed pooled descriptor of (K, V);
- *                 when NULL it is computed here (one extra read of K and V)
+ *                 when NULL it is computed in the same pass (pooling, matching and
+ *                 correction run as one launch; q is bit-identical to the one
+ *                 kvc_pool_descriptor returns)
  *   K_fb, V_fb  : [L,H,T,d] dtype or NULL (both or neither)
  *   K_out, V_out: [L,H,T,d] dtype, written; may equal K / V (in place); must not
  *                 otherwise overlap any input
- *   mask_out    : [L,H] uint8, 1 = fall back, written
+ *   mask_out    : [L,H] uint8, 1 = fall back, written (2 would flag an internal wait of
+ *                 the single-launch pass that gave up after 0.2 s; the segment is then
+ *                 copied through; not expected on a device that runs the whole grid)
  *   score_out   : [L,H] float32 or NULL;  w_out: [L,H,A] float32 or NULL
  *   q_next_out  : [L,H,2d] float32 or NULL: pooled descriptor of (K_out, V_out)
  *   ws          : at least kvc_correct_workspace_bytes(L,H,T,d,A,r) bytes

@@ -150,18 +150,23 @@ _S_BASE, _S_OUTLIER, _S_UO, _S_VO, _S_NOISE, _S_ANCHOR, _S_COS, _S_DIR, _S_QNOIS
 
 
 def _orthonormal(shape_batch, n, k, g, device) -> torch.Tensor:
-    """[..., n, k] float64 with orthonormal columns: QR of a Gaussian, diag(R) > 0.
+    """[..., n, k] float64 with orthonormal columns: the Q factor (diag(R) > 0) of a Gaussian,
+    formed by Gram-Schmidt with one re-orthogonalisation pass (plain tensor arithmetic, so the
+    generator needs no dense solver library on the device).
 
     When n < k only n columns can be orthonormal; the remaining k - n columns are zero.
     """
     x = torch.randn(*shape_batch, n, k, generator=g, device=device, dtype=torch.float64)
-    q, rr = torch.linalg.qr(x)
-    sgn = torch.sign(torch.diagonal(rr, dim1=-2, dim2=-1))
-    sgn = torch.where(sgn == 0, torch.ones_like(sgn), sgn)
-    q = q * sgn.unsqueeze(-2)
-    if q.shape[-1] < k:
-        pad = torch.zeros(*shape_batch, n, k - q.shape[-1], dtype=q.dtype, device=device)
-        q = torch.cat([q, pad], dim=-1)
+    m = min(n, k)
+    q = torch.zeros(*shape_batch, n, k, dtype=torch.float64, device=device)
+    for j in range(m):
+        v = x[..., :, j]
+        if j > 0:
+            prev = q[..., :, :j]
+            for _ in range(2):
+                c = (prev * v.unsqueeze(-1)).sum(-2)
+                v = v - (prev * c.unsqueeze(-2)).sum(-1)
+        q[..., :, j] = v / torch.linalg.vector_norm(v, dim=-1, keepdim=True)
     return q
 
 
