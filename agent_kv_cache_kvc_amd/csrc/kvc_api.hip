@@ -113,8 +113,9 @@ kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, 1);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_pool);
-  KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, part, c.n_chunks, st), "pool");
-  KVC_HIP(kvc::launch_reduce_pool(part, c.n_chunks, T, S, d, q_out, st), "pool reduce");
+  const int nc = kvc::chunks_of(T, d, dtype);
+  KVC_HIP(kvc::launch_pool_partials(K, V, S, T, d, dtype, part, nc, st), "pool");
+  KVC_HIP(kvc::launch_reduce_pool(part, nc, T, S, d, q_out, st), "pool reduce");
   return ok();
 }
 
@@ -157,8 +158,8 @@ static kvc_status validate_correct(const void* K, const void* V, int L, int H, i
 }
 
 // One correction pass.  Without q_in or earlier chunk sums, pooling, matching and correction
-// run as one fused launch; otherwise the matching kernel reads q_in (or the chunk sums that the
-// previous pass of a chain left in the workspace) and the correction kernel follows it.
+// run as one fused launch; with them the matching kernel reads q_in (or the chunk sums that
+// the previous pass of a chain left in the workspace) and the correction kernel follows.
 static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, int T, int d,
                                   int dtype, const float* desc, const void* U, const void* W,
                                   int A, int r, float tau, const float* q_in,
@@ -167,7 +168,9 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
                                   uint8_t* mask_out, float* score_out, float* w_out,
                                   bool want_next, void* ws, hipStream_t st) {
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  const int nc = kvc::chunks_of(T, d, dtype);
   char* base = static_cast<char*>(ws);
+  float* pool = reinterpret_cast<float*>(base + c.off_pool);
   kvc::CorrectLaunch cl{};
   cl.K = K;
   cl.V = V;
@@ -189,7 +192,7 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
   cl.ctr = reinterpret_cast<int*>(base + c.off_ctr);
   cl.fused = q_in == nullptr && next_partials_in == nullptr;
   if (cl.fused) {
-    cl.pool_partials = reinterpret_cast<float*>(base + c.off_pool);
+    cl.pool_partials = pool;
     cl.done = reinterpret_cast<int*>(base + c.off_done);
     cl.desc = desc;
     cl.tau = tau;
@@ -197,8 +200,7 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
     cl.score_out = score_out;
     cl.w_out = w_out;
   } else {
-    KVC_HIP(kvc::launch_score(next_partials_in, c.n_chunks, T, q_in, desc, c.S, d, A, tau,
-                              reinterpret_cast<float*>(base + c.off_w),
+    KVC_HIP(kvc::launch_score(next_partials_in, nc, T, q_in, desc, c.S, d, A, tau, cl.w_ws,
                               reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
                               mask_out, cl.ctr, st),
             "score");
@@ -226,7 +228,8 @@ kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d,
   if (q_next_out) {
     const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
     float* next = reinterpret_cast<float*>(static_cast<char*>(ws) + c.off_next);
-    KVC_HIP(kvc::launch_reduce_pool(next, c.n_chunks, T, c.S, d, q_next_out, st), "q_next");
+    KVC_HIP(kvc::launch_reduce_pool(next, kvc::chunks_of(T, d, dtype), T, c.S, d, q_next_out, st),
+            "q_next");
   }
   return ok();
 }

@@ -6,14 +6,16 @@
 // added to K and V; a segment whose best match is below tau falls back to dense prefill.
 //
 // Kernels (all deterministic: fixed-order reductions, no floating-point atomics)
-//   pool_partials_kernel  token sums of K and V per 512-token chunk          (HBM stream)
+//   pool_partials_kernel  token sums of K and V per chunk                    (HBM stream)
 //   reduce_pool_kernel    chunk sums -> q (the pooling entry point)
 //   score_kernel          chunk sums or q -> cosines, softmax, score, mask  (one wave/segment)
 //   correct_kernel        X' = X + sum_a w_a U_a W_a on MFMA, or copy-through (HBM stream);
-//                         its fused form also carries the pooling and the matching of every
-//                         segment in the same work queue (one launch for the whole step)
+//                         its fused form also pools and matches every segment in the same
+//                         work queue, so a whole correction step is one launch
 //   reset_kernel          zeroes the counters of the fused form
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -49,6 +51,23 @@ struct TrF32 {
   __device__ static floatx16 mma(const frag& a, const frag& b, const floatx16& c) {
     return mfma_f32(a, b, c);
   }
+};
+
+// Tiles of 32 tokens per wave in one work item; the item's X stays in registers, 64 VGPRs
+// per lane (bf16 d=128: 2 tiles, 256 tokens per item; f32 d=128: 1 tile, 128 tokens).
+template <class Tr, int D>
+constexpr int item_tiles() {
+  return item_tiles_for(D * (int)sizeof(typename Tr::elem));
+}
+
+// Coalesced layout of a 32-token wave tile: access j of lane l covers token TPI j + l / LPT
+// and channels 64 h + VEC (l % LPT) ... of half h (TPI = 64 / LPT tokens per access).
+template <class Tr, int D>
+struct Tile {
+  static constexpr int NH = D / 64;        // 64-channel halves
+  static constexpr int JN = Tr::LPT / 2;   // coalesced accesses per half per 32 tokens
+  static constexpr int TPI = kWave / Tr::LPT;
+  u32x4 v[NH][JN];
 };
 
 constexpr int kStageRow = 68;  // floats per staged token row (64 + 4: conflict-free rows)
@@ -91,12 +110,49 @@ __device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
   }
 }
 
+// One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).
+template <class Tr, int D>
+__device__ __forceinline__ void load_tile(const typename Tr::elem* __restrict__ X, int t0, int T,
+                                          int lrow, int lcol, Tile<Tr, D>& tile) {
+  using TL = Tile<Tr, D>;
+  if (t0 + 32 <= T) {
+#pragma unroll
+    for (int h = 0; h < TL::NH; ++h)
+#pragma unroll
+      for (int j = 0; j < TL::JN; ++j)
+        tile.v[h][j] = *reinterpret_cast<const u32x4*>(X + (size_t)(t0 + TL::TPI * j + lrow) * D +
+                                                       64 * h + lcol);
+  } else {
+#pragma unroll
+    for (int h = 0; h < TL::NH; ++h)
+#pragma unroll
+      for (int j = 0; j < TL::JN; ++j) {
+        const int tok = t0 + TL::TPI * j + lrow;
+        tile.v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
+                               : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
+}
+
+template <class Tr, int D>
+__device__ __forceinline__ void add_tile(const Tile<Tr, D>& tile, float (&qs)[D / 64][Tr::VEC]) {
+  using TL = Tile<Tr, D>;
+#pragma unroll
+  for (int h = 0; h < TL::NH; ++h)
+#pragma unroll
+    for (int j = 0; j < TL::JN; ++j) {
+      float fv[Tr::VEC];
+      unpack_in<Tr>(tile.v[h][j], fv);
+#pragma unroll
+      for (int e = 0; e < Tr::VEC; ++e) qs[h][e] += fv[e];
+    }
+}
+
 // ------------------------------------------------------------------------- chunk sums
-// Coalesced layout of a 32-token wave tile: access j of lane l covers token TPI j + l / LPT
-// and channels 64 h + VEC (l % LPT) ... of half h.  A lane adds its tokens in (tile, access)
-// order, then the lanes sharing a channel are added by a butterfly and the 4 waves in fixed
-// order.  Every pooled sum in this file (inputs, fused pooling items, outputs) takes this
-// order, so the pooled descriptor of a cache does not depend on which pass computed it.
+// A lane adds its tokens in (tile, access) order, then the lanes sharing a channel are added
+// by a butterfly and the 4 waves in fixed order.  Every pooled sum in this file (inputs,
+// fused pooling, outputs) takes this order over the same chunks, so the pooled
+// descriptor of a cache does not depend on which pass computed it.
 template <class Tr, int D>
 __device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
                                              int tid) {
@@ -118,70 +174,37 @@ __device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float
   return out;  // valid for tid < D; the caller synchronises before `red` is written again
 }
 
-// Token sums of the chunk [tb, min(T, tb + kChunk)) of one [T, D] segment.
-template <class Tr, int D>
-__device__ __forceinline__ float chunk_sums(const typename Tr::elem* __restrict__ X, int tb,
-                                            int T, float (*red)[D], int tid) {
-  constexpr int NH = D / 64, VEC = Tr::VEC, LPT = Tr::LPT, TPI = kWave / LPT;
-  constexpr int JN = LPT / 2;
-  const int lane = tid % kWave, wave = tid / kWave;
-  const int lrow = lane / LPT, lcol = VEC * (lane % LPT);
-  float qs[NH][VEC];
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
-#pragma unroll 2
-  for (int it = 0; it < kCorrIters; ++it) {
-    const int t0 = tb + it * kCorrRowsPerIter + wave * 32;
-    u32x4 v[NH][JN];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int j = 0; j < JN; ++j) {
-        const int tok = t0 + TPI * j + lrow;
-        v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
-                          : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int j = 0; j < JN; ++j) {
-        float fv[VEC];
-        unpack_in<Tr>(v[h][j], fv);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qs[h][e] += fv[e];
-      }
-  }
-  return finish_sums<Tr, D>(qs, red, tid);
-}
-
 // grid (n_chunks, S, 2): chunk sums of K (z = 0) and V (z = 1).
 template <class Tr, int D>
 __global__ __launch_bounds__(kBlock) void pool_partials_kernel(
     const typename Tr::elem* __restrict__ K, const typename Tr::elem* __restrict__ V, int T,
     float* __restrict__ partials, int n_chunks) {
+  constexpr int NT = item_tiles<Tr, D>();
   __shared__ float red[4][D];
   const int chunk = blockIdx.x, s = blockIdx.y, x = blockIdx.z, S = gridDim.y;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const typename Tr::elem* X = (x == 0 ? K : V) + (size_t)s * T * D;
-  const float v = chunk_sums<Tr, D>(X, chunk * kChunk, T, red, threadIdx.x);
-  if (threadIdx.x < D) partials[(((size_t)x * S + s) * n_chunks + chunk) * D + threadIdx.x] = v;
+  const int first = chunk * NT * kRowsPerPass + wave * 32;
+  Tile<Tr, D> xr[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl)
+    load_tile<Tr, D>(X, first + tl * kRowsPerPass, T, lane / Tr::LPT, Tr::VEC * (lane % Tr::LPT),
+                     xr[tl]);
+  float qs[D / 64][Tr::VEC];
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+    for (int e = 0; e < Tr::VEC; ++e) qs[h][e] = 0.f;
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) add_tile<Tr, D>(xr[tl], qs);
+  const float v = finish_sums<Tr, D>(qs, red, tid);
+  if (tid < D) partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
 }
 
 // ------------------------------------------------------------------------- matching
-// Chunk sums written by other workgroups of the running kernel are read through the
-// device-coherent path (agent-scope atomic loads); sums from earlier launches with plain loads.
-template <bool COHERENT>
-__device__ __forceinline__ float load_sum(const float* p) {
-  if constexpr (COHERENT)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-
 // Chunk sums -> pooled descriptor [mean K ; mean V]; one wave, lane holds channels
 // lane + 64 i.  The sums are added in chunk order; loads go out 8 chunks at a time.
-template <int D, bool COHERENT>
+template <int D>
 __device__ __forceinline__ void pooled_query(const float* __restrict__ partials, int n_chunks,
                                              int T, int s, int S, int lane,
                                              float (&q)[2 * D / kWave]) {
@@ -198,8 +221,7 @@ __device__ __forceinline__ void pooled_query(const float* __restrict__ partials,
         const int c = lane + kWave * i;
         const int x = c / D, ch = c % D;
         v[u][i] = (c0 + u < n_chunks)
-                      ? load_sum<COHERENT>(partials +
-                                           (((size_t)x * S + s) * n_chunks + c0 + u) * D + ch)
+                      ? partials[(((size_t)x * S + s) * n_chunks + c0 + u) * D + ch]
                       : 0.f;
       }
 #pragma unroll
@@ -275,7 +297,7 @@ __global__ __launch_bounds__(kWave) void reduce_pool_kernel(const float* __restr
   constexpr int PER = 2 * D / kWave;
   const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
   float q[PER];
-  pooled_query<D, false>(partials, n_chunks, T, s, S, lane, q);
+  pooled_query<D>(partials, n_chunks, T, s, S, lane, q);
 #pragma unroll
   for (int i = 0; i < PER; ++i) q_out[(size_t)s * 2 * D + lane + kWave * i] = q[i];
 }
@@ -295,7 +317,7 @@ __global__ __launch_bounds__(kWave) void score_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
   } else {
-    pooled_query<D, false>(partials, n_chunks, T, s, S, lane, q);
+    pooled_query<D>(partials, n_chunks, T, s, S, lane, q);
   }
   float score;
   uint8_t fall;
@@ -318,41 +340,34 @@ __global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
 }
 
 // ------------------------------------------------------------------------- correction
-// Persistent workgroups (4 waves) take work items from a counter.  A correction item is
-// (segment, K|V, 512-token chunk); a wave owns 32 tokens per tile and all d channels.
+// Persistent workgroups (4 waves) take work items from a counter.  A work item is
+// (segment, K|V, chunk of NT x 128 tokens); each wave owns NT tiles of 32 tokens, loads
+// them into registers at the start of the item and keeps them there until X' is stored.
 //
 // MFMA: (delta X)^T = W^T U^T per 32-channel block; A operand = W_a^T staged in LDS (rows in
 // operand order, see cinv32), B operand = U_a rows (8 consecutive k per lane, straight from
 // HBM); result register i of lane l = (token l % 32, channel 16 (l / 32) + i).  Each anchor's
 // product is finished in float32 and scaled by its weight, so w never passes through bf16.
 // k layout: r is padded to rp (multiple of 2*SLOT); lane half g covers k in
-// [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.
-//
-// Memory: X is loaded and X' stored with coalesced 16-byte accesses; the MFMA result goes
-// through a per-wave LDS tile [32][64 + 4] floats to meet that layout.  The next tile's U
-// (double-buffered) is requested before the current tile's MFMAs, and each half of the next
-// tile's X as soon as the epilogue has consumed that half.
+// [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.  The MFMA result
+// goes through a per-wave LDS tile [32][64 + 4] floats to meet the coalesced layout of X;
+// the next tile's U (double-buffered) is requested before the current tile's MFMAs.
 //
 // FUSED: the queue also holds pooling items (segment, K|V, chunk) that publish chunk sums and
-// count them per segment.  Items are ordered by batches of `batch` segments as
-//   P0, P1, C0, P2, C1, ..., P(nb-1), C(nb-2), C(nb-1)
-// (P = pooling items of a batch, C = its correction items), so a correction item only waits
-// for pooling items taken from the queue before it: each of those is held by a running
-// workgroup that does not wait, so every wait ends.  A batch's correction re-reads K and V
-// shortly after its pooling read them.  The last pooling item of a segment (the one whose
-// count increment completes the set) computes q, the weights and the fallback flag, publishes
-// them and moves the count past n_ci; correction items wait for that.  Published values are
-// written with device-coherent stores whose completion is awaited before the count moves, and
-// read with device-coherent loads (device-scope release/acquire fences would write back or
-// invalidate the whole L2 at every item on this target).  The step needs one launch.
-template <class Tr, int D, int NF>
-struct CorrTile {
-  static constexpr int NH = D / 64;        // 64-channel halves
-  static constexpr int JN = Tr::LPT / 2;   // coalesced accesses per half per 32 tokens
-  u32x4 x[NH][JN];                         // X of the tile in flight (coalesced layout)
-  typename Tr::frag u[NF];                 // U fragments of the tile in flight
-};
-
+// count them per segment.  Items are grouped in slots of `batch` segments and the pooling
+// slots run `lead` slots ahead of the correction slots:
+//   P0 .. P(lead-1), C0, P(lead), C1, P(lead+1), ..., C(nb-1)
+// so a correction item only waits for pooling items taken from the queue before it; each of
+// those is held by a running workgroup that does not wait, hence every wait ends, with no
+// condition on how many workgroups are resident.  The segment's last pooling item to count
+// computes q, the weights and the fallback flag, publishes them and moves the count past n_ci
+// (by 1, or by 2 for a fallback); correction items issue their loads of X first and then
+// wait for that.  Published values are written with device-coherent stores whose completion
+// is awaited before the count moves, and read with device-coherent loads (device-scope
+// release/acquire fences would write back or invalidate the whole L2 at every item on this
+// target).  K and V are read twice (pooling, then correction): keeping a chunk in registers
+// between the two was measured slower, since every signal is a memory round trip of several
+// microseconds under a saturated memory system and two workgroups per CU cannot hide it.
 struct CorrectArgs {
   const void* K;
   const void* V;
@@ -367,20 +382,31 @@ struct CorrectArgs {
   float* next_partials;    // chunk sums of the output, or null
   int* ctr;                // work counter
   float* pool_partials;    // fused: [2][S][n_chunks][D] chunk sums of the source
-  int* done;               // fused: [S] pooling items finished per segment, then n_ci + 1
-                           //        (matched) or n_ci + 2 (matched, fallback)
+  int* done;               // fused: [S] items pooled, then n_ci + 1 (matched) or
+                           //        n_ci + 2 (matched, fallback)
   const float* desc;       // fused: [S][A][2D] anchor descriptors
   uint8_t* mask_out;       // fused outputs
   float* score_out;
   float* w_out;
   float tau;
-  int T, S, A, r, rp, n_chunks, n_items, batch;
+  int T, S, A, r, rp, n_chunks, n_items;
+  int batch, lead;         // fused: segments per slot, pooling slots ahead of correction
 };
 
-// Bounded wait of a correction item: 0.2 s of the 100 MHz constant clock.  A safety net that
-// the queue order above never reaches; if it were reached the segment is flagged with
-// mask value 2 and its output is the copy-through.
+// Bounded wait of a correction item of the fused form: 0.2 s of the 100 MHz constant clock.
+// A safety net that the queue order above never reaches; if it were reached the segment is
+// flagged with mask value 2 and its output is the copy-through.
 constexpr long long kWaitTicks = 20000000ll;
+
+__device__ __forceinline__ void order_stores_before_signal() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0): stores acknowledged
+}
+
+__device__ __forceinline__ void order_loads_after_signal() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // NA > 0: compile-time anchor count NA and MFMA steps per anchor KSC (r = 2 KSC SLOT);
 // NA == 0: runtime A and r with up to NFG register-resident fragments.
@@ -388,14 +414,15 @@ template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
+  using TL = Tile<Tr, D>;
   constexpr bool FIX = NA > 0;
   constexpr int NF = FIX ? NA * KSC : NFG;
-  using Tile = CorrTile<Tr, D, NF>;
+  constexpr int NT = item_tiles<Tr, D>();
   constexpr int VEC = Tr::VEC;
   constexpr int SLOT = Tr::SLOT;
   constexpr int LPT = Tr::LPT;
-  constexpr int TPI = kWave / LPT;  // tokens per coalesced access
-  constexpr int NH = Tile::NH, JN = Tile::JN;
+  constexpr int TPI = TL::TPI;
+  constexpr int NH = TL::NH, JN = TL::JN;
   constexpr int PADK = 16 / sizeof(elem);
   constexpr int PER = 2 * D / kWave;
 
@@ -412,6 +439,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float wsh[kMaxA];
   __shared__ float red[4][D];
+  __shared__ float qsh[2 * D];
   __shared__ int s_item;
   __shared__ int s_mask;
   __shared__ int s_last;
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   const int KS = FIX ? KSC : half / SLOT;  // MFMA steps per anchor
   const int nfrag = A * KS;
   const bool uvec = FIX || (r % VEC) == 0;
-  const int n_ci = 2 * n_chunks;             // items per segment and kind
+  const int n_ci = 2 * n_chunks;             // items per segment
 
   for (;;) {
     // lane-derived values are recomputed per item (kept out of the loop-carried registers)
@@ -442,69 +470,105 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= args.n_items) break;
 
-    // ---- decode the item
     bool pool_item = false;
     int s, ci;
     if constexpr (FUSED) {
       const int per_slot = args.batch * n_ci;
       const int k = item / per_slot, o = item - k * per_slot;
       const int nb = (S + args.batch - 1) / args.batch;
+      const int ld = min(args.lead, nb);
       int b;
-      if (k == 0) {
+      if (k < ld) {
         pool_item = true;
-        b = 0;
-      } else if (k == 2 * nb - 1) {
-        b = nb - 1;
-      } else if (k & 1) {
-        pool_item = true;
-        b = (k + 1) / 2;
+        b = k;
       } else {
-        b = k / 2 - 1;
+        const int kk = k - ld, paired = nb - ld;  // C(j) then P(j + ld) while any P is left
+        if (kk < 2 * paired) {
+          b = kk >> 1;
+          if (kk & 1) {
+            pool_item = true;
+            b += ld;
+          }
+        } else {
+          b = paired + (kk - 2 * paired);
+        }
       }
       s = b * args.batch + o / n_ci;
-      ci = o % n_ci;
-      if (s >= S) {  // padding of the last batch
+      ci = o - (o / n_ci) * n_ci;
+      if (s >= S) {  // padding of the last slot
         __syncthreads();
         continue;
       }
     } else {
       s = item / n_ci;
-      ci = item % n_ci;
+      ci = item - s * n_ci;
     }
-    const int x = ci / n_chunks, chunk = ci % n_chunks;
+    const int x = ci / n_chunks, chunk = ci - x * n_chunks;
     const size_t seg = (size_t)s * T * D;
     const elem* X = (x == 0 ? K : V) + seg;
     elem* Y = (x == 0 ? K_out : V_out) + seg;
     const elem* Xfb = (x == 0 ? K_fb : V_fb);
-    const int tb = chunk * kChunk;
+    const int first = chunk * NT * kRowsPerPass + wave * 32;
+    const int n_my =
+        first < T ? min(NT, (T - first + kRowsPerPass - 1) / kRowsPerPass) : 0;
 
-    if constexpr (FUSED) {
-      if (pool_item) {
-        // fields used only here are read through an opaque pointer to the kernel arguments,
-        // so they are loaded per item instead of holding scalar registers for the whole kernel
-        const __attribute__((address_space(4))) CorrectArgs* pa =
-            (const __attribute__((address_space(4))) CorrectArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-        asm volatile("" : "+s"(pa));
-        // ---- pooling item: chunk sums of the source, published, then counted
-        const float v = chunk_sums<Tr, D>(X, tb, T, red, tid);
+    // ---- this wave's tiles of X, held in registers for the whole item
+    TL xr[NT];
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) load_tile<Tr, D>(X, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+
+    if (FUSED && pool_item) {
+      // fields used only here are read through an opaque pointer to the kernel arguments,
+      // so they are loaded when needed instead of holding scalar registers for the whole
+      // kernel
+      const __attribute__((address_space(4))) CorrectArgs* pa =
+          (const __attribute__((address_space(4))) CorrectArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(pa));
+      {
+        float qs[NH][VEC];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+#pragma unroll
+        for (int tl = 0; tl < NT; ++tl) add_tile<Tr, D>(xr[tl], qs);
+        const float v = finish_sums<Tr, D>(qs, red, tid);
         if (tid < D)
           __hip_atomic_store(pa->pool_partials + (((size_t)x * S + s) * n_chunks + chunk) * D + tid,
                              v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // order only: the stores are complete before the barrier, the count after it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+      }
+      order_stores_before_signal();
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == n_ci - 1;
+      __syncthreads();
+      if (s_last) {
+        // the segment's last item to count matches it: q (one thread per channel, chunk
+        // sums added in chunk order), then weights and flag
+        order_loads_after_signal();
+        if (tid < 2 * D) {
+          const float* p = pa->pool_partials + ((size_t)(tid / D) * S + s) * n_chunks * D + tid % D;
+          float sum = 0.f;
+          for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              v[u] = c0 + u < n_chunks
+                         ? __hip_atomic_load(p + (size_t)(c0 + u) * D, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (c0 + u < n_chunks) sum += v[u];
+          }
+          qsh[tid] = T > 0 ? sum / (float)T : 0.f;
+        }
         __syncthreads();
-        if (tid == 0)
-          s_last = __hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == n_ci - 1;
-        __syncthreads();
-        if (s_last && wave == 0) {
-          // the segment's last pooling item matches it: q from all chunk sums, weights and
-          // flag published, then the count moves past n_ci (by 1, or by 2 for a fallback)
-          __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (wave == 0) {
           float q[PER];
-          pooled_query<D, true>(pa->pool_partials, n_chunks, T, s, S, lane, q);
+#pragma unroll
+          for (int i = 0; i < PER; ++i) q[i] = qsh[lane + kWave * i];
           float score;
           uint8_t fall;
           const float wv = segment_weights<D>(q, pa->desc, s, A, pa->tau, lane, score, fall);
@@ -517,79 +581,19 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             pa->mask_out[s] = fall;
             if (pa->score_out) pa->score_out[s] = score;
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-          __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+          order_stores_before_signal();
           if (lane == 0)
             __hip_atomic_fetch_add(pa->done + s, 1 + (int)fall, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();  // `red`, s_last and the item id are free for the next item
-        continue;
       }
-      // ---- correction item: wait until the segment is matched
-      if (tid == 0) {
-        int v = __hip_atomic_load(args.done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v <= n_ci) {
-          const long long t_end = wall_clock64() + kWaitTicks;
-          do {
-            __builtin_amdgcn_s_sleep(2);
-            v = __hip_atomic_load(args.done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } while (v <= n_ci && wall_clock64() < t_end);
-          if (v <= n_ci) args.mask_out[s] = 2;
-        }
-        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        s_mask = v != n_ci + 1;
-      }
-    } else {
-      if (tid == 0) s_mask = args.mask[s];
-    }
-    __syncthreads();
-    const bool masked = s_mask != 0;
-
-    float qs[NH][VEC];
-    if constexpr (POOL_OUT) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+      __syncthreads();  // `red`, `qsh`, s_last and the item id are free for the next item
+      continue;
     }
 
-    if (masked) {
-      // dense-prefill stand-in: copy the fallback cache (or the source) bit for bit
-      const elem* src = Xfb ? Xfb + seg : X;
-      for (int it = 0; it < kCorrIters; ++it) {
-        const int t0 = tb + it * kCorrRowsPerIter + wave * 32;
-        if (t0 >= T) break;
-        u32x4 v[NH][JN];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            const int tok = t0 + TPI * j + lrow;
-            v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(src + tok * D + 64 * h + lcol)
-                              : u32x4{0u, 0u, 0u, 0u};
-          }
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            const int tok = t0 + TPI * j + lrow;
-            if (tok < T) {
-              *reinterpret_cast<u32x4*>(Y + tok * D + 64 * h + lcol) = v[h][j];
-              if constexpr (POOL_OUT) {
-                float fv[VEC];
-                unpack_in<Tr>(v[h][j], fv);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) qs[h][e] += fv[e];
-              }
-            }
-          }
-      }
-    } else {
-      if (tid < A) wsh[tid] = load_sum<FUSED>(args.w_ws + (size_t)s * A + tid);
-      // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for
-      //      k >= r)
+    // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
+    //      in the fused form this overlaps the wait for the segment's weights
+    {
       const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
       const int n_w = A * r * (D / VEC);
       for (int q = tid; q < n_w; q += kBlock) {
@@ -615,37 +619,81 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
           wt[ac * RS + k] = Tr::e(0.f);
         }
       }
-      __syncthreads();
+    }
 
-      const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
-      const int first = tb + wave * 32;
-      const int n_my =
-          first < T ? min(kCorrIters, (T - first + kCorrRowsPerIter - 1) / kCorrRowsPerIter) : 0;
-
-      Tile b;
-      frag u2[NF];
-      auto load_x = [&](int h, int t0) {
-        if (t0 + 32 <= T) {
-#pragma unroll
-          for (int j = 0; j < JN; ++j)
-            b.x[h][j] =
-                *reinterpret_cast<const u32x4*>(X + (t0 + TPI * j + lrow) * D + 64 * h + lcol);
-        } else {
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            const int tok = t0 + TPI * j + lrow;
-            b.x[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + tok * D + 64 * h + lcol)
-                                : u32x4{0u, 0u, 0u, 0u};
-          }
+    if constexpr (FUSED) {
+      if (tid == 0) {
+        int* done = args.done + s;
+        int v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v <= n_ci) {
+          const long long t_end = wall_clock64() + kWaitTicks;
+          do {
+            __builtin_amdgcn_s_sleep(2);
+            v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } while (v <= n_ci && wall_clock64() < t_end);
+          if (v <= n_ci) args.mask_out[s] = 2;
         }
-      };
+        order_loads_after_signal();
+        s_mask = v != n_ci + 1;
+        if (v == n_ci + 1)
+          for (int a = 0; a < A; ++a)
+            wsh[a] = __hip_atomic_load(args.w_ws + (size_t)s * A + a, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      if (tid == 0) s_mask = args.mask[s];
+      if (tid < A) wsh[tid] = args.w_ws[(size_t)s * A + tid];
+    }
+    __syncthreads();
+    const bool masked = s_mask != 0;
+
+    float qs[NH][VEC];
+    if constexpr (POOL_OUT) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+    }
+
+    if (masked) {
+      // dense-prefill stand-in: the fallback cache, or the source, bit for bit
+      if (Xfb != nullptr) {
+#pragma unroll
+        for (int tl = 0; tl < NT; ++tl)
+          load_tile<Tr, D>(Xfb + seg, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+      }
+      const bool store = Xfb != nullptr || Y != X;  // in place with no fallback: unchanged
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        const int t0 = first + tl * kRowsPerPass;
+        if (tl < n_my) {
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int j = 0; j < JN; ++j) {
+              const int tok = t0 + TPI * j + lrow;
+              if (tok < T) {
+                if (store)
+                  *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = xr[tl].v[h][j];
+                if constexpr (POOL_OUT) {
+                  float fv[VEC];
+                  unpack_in<Tr>(xr[tl].v[h][j], fv);
+#pragma unroll
+                  for (int e = 0; e < VEC; ++e) qs[h][e] += fv[e];
+                }
+              }
+            }
+        }
+      }
+    } else {
+      const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
       auto load_u = [&](frag (&dst)[NF], int t0) {
         const int t = t0 + ln;
         if (FIX && t0 + 32 <= T) {
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             const int a = f / KS, ks = f - a * KS;
-            const elem* up = Useg + (a * T + t) * r + g * half + ks * SLOT;
+            const elem* up = Useg + ((size_t)a * T + t) * r + g * half + ks * SLOT;
             if constexpr (SLOT == 8) dst[f] = *reinterpret_cast<const u32x4*>(up);
             else dst[f] = Tr::f(*up);
           }
@@ -657,7 +705,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
           if (f < nfrag) {
             const int a = f / KS, ks = f - a * KS;
             const int k0 = g * half + ks * SLOT;
-            const elem* up = Useg + (a * T + t) * r + k0;
+            const elem* up = Useg + ((size_t)a * T + t) * r + k0;
             if constexpr (SLOT == 8) {
               u32x4 v = {0u, 0u, 0u, 0u};
               if (valid && k0 < r) {
@@ -678,12 +726,11 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         }
       };
 
-      // one tile: MFMAs on `cu`; the next tile's U goes to `nu` before the MFMAs start
-      auto run_tile = [&](int it, frag (&cu)[NF], frag (&nu)[NF]) {
-        const int t0 = first + it * kCorrRowsPerIter;
-        const int tn = t0 + kCorrRowsPerIter;
-        const bool more = it + 1 < n_my;
-        if (more) load_u(nu, tn);
+      // one tile of this wave: MFMAs on `cu`; the next tile's U goes to `nu` first
+      auto run_tile = [&](auto tl_c, frag (&cu)[NF], frag (&nu)[NF]) {
+        constexpr int tl = decltype(tl_c)::value;
+        const int t0 = first + tl * kRowsPerPass;
+        if (tl + 1 < n_my) load_u(nu, t0 + kRowsPerPass);
         const bool full = t0 + 32 <= T;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
@@ -737,12 +784,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             for (int e = 0; e < VEC; e += 4)
               *reinterpret_cast<floatx4*>(&dv[e]) =
                   *reinterpret_cast<const floatx4*>(stage + row * kStageRow + lcol + e);
-            unpack_in<Tr>(b.x[h][j], xv);
+            unpack_in<Tr>(xr[tl].v[h][j], xv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
             const u32x4 o = pack_out<Tr>(dv);
             if (full || tok < T) {
-              *reinterpret_cast<u32x4*>(Y + tok * D + 64 * h + lcol) = o;
+              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = o;
               if constexpr (POOL_OUT) {
                 float fo[VEC];
                 unpack_in<Tr>(o, fo);
@@ -752,23 +799,25 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             }
           }
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-          if (more) load_x(h, tn);  // this half of X is consumed
         }
       };
 
+      frag ua[NF], ub[NF];
       if (n_my > 0) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) load_x(h, first);
-        load_u(b.u, first);
+        load_u(ua, first);
+        run_tile(std::integral_constant<int, 0>{}, ua, ub);
       }
-      for (int it = 0; it < n_my; it += 2) {
-        run_tile(it, b.u, u2);
-        if (it + 1 < n_my) run_tile(it + 1, u2, b.u);
+      if constexpr (NT >= 2) {
+        if (n_my > 1) run_tile(std::integral_constant<int, 1>{}, ub, ua);
+      }
+      if constexpr (NT >= 4) {
+        if (n_my > 2) run_tile(std::integral_constant<int, 2>{}, ua, ub);
+        if (n_my > 3) run_tile(std::integral_constant<int, 3>{}, ub, ua);
       }
     }
 
     if constexpr (POOL_OUT) {
-      // token sums of the stored output, in the order of chunk_sums
+      // token sums of the stored output, in the order of the input chunk sums
       const float v = finish_sums<Tr, D>(qs, red, tid);
       if (tid < D) args.next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
     }
@@ -839,10 +888,9 @@ hipError_t launch_score(const float* partials, int n_chunks, int T, const float*
 
 template <class Tr, int D, int NA, int KSC, int NFG>
 static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
-  using elem = typename Tr::elem;
-  const int PADK = 16 / (int)sizeof(elem);
+  const int PADK = 16 / (int)sizeof(typename Tr::elem);
   const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
-                     (size_t)L.A * D * (L.rp + PADK) * sizeof(elem);
+                     (size_t)L.A * D * (L.rp + PADK) * sizeof(typename Tr::elem);
   CorrectArgs a{};
   a.K = L.K;
   a.V = L.V;
@@ -868,17 +916,8 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.A = L.A;
   a.r = L.r;
   a.rp = L.rp;
-  a.n_chunks = chunks_of(L.T);
-  const int per_kind = L.S * 2 * a.n_chunks;  // correction (or pooling) items
-  if (L.fused) {
-    a.batch = fused_batch(a.n_chunks);
-    a.n_items = 2 * ceil_div(L.S, a.batch) * a.batch * 2 * a.n_chunks;
-  } else {
-    a.batch = 0;
-    a.n_items = per_kind;
-  }
-  const int want = L.fused ? 2 * per_kind : per_kind;
-  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
+  a.n_chunks = chunks_of(L.T, L.d, L.dtype);
+  a.n_items = L.S * 2 * a.n_chunks;
   const bool pool = L.next_partials != nullptr;
   auto k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
                            : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
@@ -887,11 +926,17 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   if (lds > 48 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int want = a.n_items;
   if (L.fused) {
+    a.batch = fused_batch(a.n_chunks);
+    a.lead = kFusedLead;
+    a.n_items = 2 * ceil_div(L.S, a.batch) * a.batch * 2 * a.n_chunks;
+    want = 2 * L.S * 2 * a.n_chunks;
     hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(kBlock), 0, st, L.ctr, L.done, L.S);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
   hipLaunchKernelGGL(k, dim3(grid), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }

@@ -461,16 +461,16 @@ __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
   constexpr int DR = D + 8;             // LDS row stride of the delta tile (bf16)
   constexpr int UR = 36;                // LDS row stride of the U staging tile (floats)
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  constexpr int LD = kCorrRowsPerIter * CPR / kBlock;  // chunks per thread per tile
-  __shared__ __align__(16) uint16_t dt[kCorrRowsPerIter * DR];
+  constexpr int LD = kRowsPerPass * CPR / kBlock;  // chunks per thread per tile
+  __shared__ __align__(16) uint16_t dt[kRowsPerPass * DR];
   __shared__ __align__(16) float us[4][32 * UR];
   const int tile = blockIdx.x, m = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, ln = lane & 31;
   const uint16_t* src = delta + (size_t)m * T * D;
   const bool uvec = (r % 4) == 0;
-  const int t_first = tile * kProjIters * kCorrRowsPerIter;
-  const int n_it = min(kProjIters, (T - t_first + kCorrRowsPerIter - 1) / kCorrRowsPerIter);
+  const int t_first = tile * kProjIters * kRowsPerPass;
+  const int n_it = min(kProjIters, (T - t_first + kRowsPerPass - 1) / kRowsPerPass);
   float* ust = us[wave];
   for (int mb = 0; mb < rpad / 32; ++mb) {
     const int jrow = mb * 32 + cmap32(ln);
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
     };
     if (n_it > 0) load_tile(t_first);
     for (int it = 0; it < n_it; ++it) {
-      const int t0 = t_first + it * kCorrRowsPerIter;
+      const int t0 = t_first + it * kRowsPerPass;
       __syncthreads();  // previous tile's fragments are consumed
 #pragma unroll
       for (int q = 0; q < LD; ++q) {
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
         *reinterpret_cast<u32x4*>(&dt[(c / CPR) * DR + 8 * (c % CPR)]) = ld[q];
       }
       __syncthreads();
-      if (it + 1 < n_it) load_tile(t0 + kCorrRowsPerIter);
+      if (it + 1 < n_it) load_tile(t0 + kRowsPerPass);
       floatx16 acc0, acc1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kBlock, 2) void project_f32_kernel(const float* __r
     for (int ks = 0; ks < KH; ++ks)
       a[ks] = (j < r) ? W[((size_t)m * r + j) * D + g * KH + ks] : 0.f;
     for (int it = 0; it < kProjIters; ++it) {
-      const int t0 = (tile * kProjIters + it) * kCorrRowsPerIter + wave * 32;
+      const int t0 = (tile * kProjIters + it) * kRowsPerPass + wave * 32;
       if (t0 >= T) break;
       const int t = t0 + ln;
       const bool valid = t < T;
@@ -620,7 +620,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
                      f.rpad, sweeps);
   e = hipGetLastError();
   if (e != hipSuccess || f.T == 0) return e;
-  const int n_tiles = ceil_div(f.T, kCorrRowsPerIter * kProjIters);
+  const int n_tiles = ceil_div(f.T, kRowsPerPass * kProjIters);
   const dim3 g3(n_tiles, f.M);
   if (dtype == KVC_BF16)
     hipLaunchKernelGGL((project_bf16_kernel<D>), g3, dim3(kBlock), 0, st,

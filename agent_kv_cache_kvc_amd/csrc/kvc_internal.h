@@ -12,9 +12,7 @@ namespace kvc {
 // ---------------------------------------------------------------- launch geometry
 constexpr int kWave = 64;             // CDNA wavefront width
 constexpr int kBlock = 256;           // 4 waves per workgroup everywhere
-constexpr int kCorrRowsPerIter = 128; // tokens per correction workgroup iteration (4 waves x 32)
-constexpr int kCorrIters = 4;         // iterations per correction workgroup (512 tokens)
-constexpr int kChunk = kCorrRowsPerIter * kCorrIters;  // tokens per work item and chunk sum
+constexpr int kRowsPerPass = 128;     // tokens of one 32-token tile per wave, 4 waves
 constexpr int kMaxA = 16;             // anchors per segment held in registers
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
@@ -23,21 +21,38 @@ constexpr int kJacobiMaxSweeps = 40;  // hard cap: every workgroup leaves the sw
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// chunk sums per segment and per K|V (one all-zero chunk when T = 0)
-inline int chunks_of(int T) { return T > 0 ? ceil_div(T, kChunk) : 1; }
+// Tiles of kRowsPerPass tokens per correction work item (and per pooled chunk): the item's
+// share of X held in registers is 64 VGPRs per lane, i.e. 16 KB per wave.
+constexpr int item_tiles_for(int row_bytes) {
+  return row_bytes <= 128 ? 4 : (row_bytes <= 256 ? 2 : 1);
+}
+inline int chunk_tokens(int d, int dtype) {
+  return kRowsPerPass * item_tiles_for(d * (dtype == KVC_BF16 ? 2 : 4));
+}
 
-// segments per batch of the fused correction queue: about 256 work items per batch and kind
-inline int fused_batch(int n_chunks) { return n_chunks >= 128 ? 1 : 128 / n_chunks; }
+// chunk sums per segment and per K|V (one all-zero chunk when T = 0)
+inline int chunks_of(int T, int d, int dtype) {
+  return T > 0 ? ceil_div(T, chunk_tokens(d, dtype)) : 1;
+}
+// the most chunks any dtype gives (workspace sizes do not depend on the dtype)
+inline int max_chunks_of(int T) { return T > 0 ? ceil_div(T, kRowsPerPass) : 1; }
+
+// Fused correction queue: about 128 work items per slot, pooling 4 slots ahead.
+inline int fused_batch(int n_chunks) {
+  const int n_ci = 2 * n_chunks;
+  return n_ci >= 128 ? 1 : 128 / n_ci;
+}
+constexpr int kFusedLead = 4;
 
 // ---------------------------------------------------------------- correction workspace
 struct CorrectLayout {
   int S, T, d, A;
-  int n_chunks;       // chunk sums per segment and per K|V
+  int max_chunks;     // chunk sums per segment and per K|V, most any dtype needs
   size_t off_pool;    // float [2][S][n_chunks][d]   chunk sums of the source
   size_t off_next;    // float [2][S][n_chunks][d]   chunk sums of the output (pooled next)
   size_t off_w;       // float [S][A]
   size_t off_mask;    // uint8 [S]
-  size_t off_done;    // int [S]: finished pooling items per segment (fused pass)
+  size_t off_done;    // int [S]: per-segment counters of the fused pass
   size_t off_ctr;     // int [1]: work counter of the correction pass
   size_t bytes;
 };
@@ -48,8 +63,8 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.T = T;
   c.d = d;
   c.A = A;
-  c.n_chunks = chunks_of(T);
-  const size_t sums = sizeof(float) * 2ull * c.S * c.n_chunks * d;
+  c.max_chunks = max_chunks_of(T);
+  const size_t sums = sizeof(float) * 2ull * c.S * c.max_chunks * d;
   size_t o = 0;
   c.off_pool = o;  o = align_up(o + sums, 256);
   c.off_next = o;  o = align_up(o + sums, 256);
@@ -77,7 +92,7 @@ struct CorrectLaunch {
   void* V_out;
   float* next_partials;     // chunk sums of the output, or null
   int* ctr;
-  bool fused;               // pooling + matching + correction in one queue
+  bool fused;               // pooling + matching + correction in one launch
   float* pool_partials;     // fused: chunk sums of the source
   int* done;                // fused: per-segment counters
   const float* desc;        // fused: anchor descriptors
