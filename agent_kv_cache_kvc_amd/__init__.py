@@ -31,6 +31,7 @@ __all__ = [
     "correct_chain",
     "fit_anchor",
     "correct_workspace_bytes",
+    "chain_workspace_bytes",
     "fit_workspace_bytes",
     "KVC_BF16",
     "KVC_F32",
@@ -127,6 +128,10 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def correct_workspace_bytes(L, H, T, d, A, r) -> int:
     return int(lib().kvc_correct_workspace_bytes(L, H, T, d, A, r))
+
+
+def chain_workspace_bytes(L, H, T, d, A, r) -> int:
+    return int(lib().kvc_chain_workspace_bytes(L, H, T, d, A, r))
 
 
 def fit_workspace_bytes(M, T, d, r) -> int:

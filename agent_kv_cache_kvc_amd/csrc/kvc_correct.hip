@@ -512,10 +512,14 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const int n_my =
         first < T ? min(NT, (T - first + kRowsPerPass - 1) / kRowsPerPass) : 0;
 
-    // ---- this wave's tiles of X, held in registers for the whole item
+    // ---- this wave's tiles of X, held in registers for the whole item (a segment already
+    //      known to fall back to a fallback cache loads that cache instead)
+    const bool fb_known = !FUSED && Xfb != nullptr && args.mask[s] != 0;
+    const elem* Xsrc = fb_known ? Xfb + seg : X;
     TL xr[NT];
 #pragma unroll
-    for (int tl = 0; tl < NT; ++tl) load_tile<Tr, D>(X, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+    for (int tl = 0; tl < NT; ++tl)
+      load_tile<Tr, D>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
 
     if (FUSED && pool_item) {
       // fields used only here are read through an opaque pointer to the kernel arguments,
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 
     if (masked) {
       // dense-prefill stand-in: the fallback cache, or the source, bit for bit
-      if (Xfb != nullptr) {
+      if (Xfb != nullptr && !fb_known) {
 #pragma unroll
         for (int tl = 0; tl < NT; ++tl)
           load_tile<Tr, D>(Xfb + seg, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);

@@ -47,6 +47,26 @@ def correct_bytes(cfg, mask: np.ndarray) -> int:
     return 2 * kv + factors + S * A * 2 * d * 4
 
 
+def chain_bytes(cfg, masks, with_fb: bool) -> int:
+    """Algorithmic HBM bytes of one kvc_correct_chain call.  Edge 0 reads every source
+    segment (its descriptor needs them); an edge >= 1 takes its descriptor from the previous
+    edge's output pass and reads only its reliable source segments; a fallback segment reads
+    the fallback cache when one is given."""
+    S, T, d, A, r = cfg.L * cfg.H, cfg.T, cfg.d, cfg.A, cfg.r
+    es = 2 if cfg.dtype == "bf16" else 4
+    seg = 2 * T * d * es  # K and V of one segment
+    total = 0
+    for e, m in enumerate(masks):
+        reliable = int((m == 0).sum())
+        masked = S - reliable
+        total += (S if e == 0 else reliable) * seg          # source reads
+        total += masked * seg if with_fb else 0              # fallback reads
+        total += reliable * 2 * A * (T * r + r * d) * es     # factors
+        total += S * A * 2 * d * 4                            # descriptors
+        total += S * seg                                      # outputs
+    return total
+
+
 def fit_bytes_flops(M, T, d, r):
     """Algorithmic bytes (delta read twice, U and W written) and flops of one fit."""
     by = 2 * M * T * d * 2 + M * T * r * 4 + M * r * d * 4
@@ -146,12 +166,87 @@ def cpu_baseline(cfg, case, desc, n_seg: int, budget_s: float = 12.0):
             "tokens_layers_per_s": round(n_seg * cfg.T / cfg.H / dt, 1)}
 
 
+def chain_leg(dev, stream, n):
+    """kvc_correct_chain over the 3-edge workflow A0 -> A1 -> A2 -> A3 at T = 32768."""
+    cfg = synth.CONFIGS["chain_t32768"]
+    log(f"[bench] chain leg: generating {cfg.name}")
+    case = synth.generate(cfg, dev)
+    edges = []
+    for e, ed in enumerate(case.edges):
+        srcK = case.K0 if e == 0 else case.edges[e - 1].exact_K
+        srcV = case.V0 if e == 0 else case.edges[e - 1].exact_V
+        q = kvc.pool_descriptor(srcK, srcV)
+        edges.append({"desc": synth.build_descriptors(case, e, q.double()), "U": ed.U, "W": ed.W,
+                      "K_fb": ed.exact_K, "V_fb": ed.exact_V})
+    outs = [(torch.empty_like(case.K0), torch.empty_like(case.V0)) for _ in edges]
+    ws = torch.empty(kvc.chain_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, cfg.A, cfg.r),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        return kvc.correct_chain(case.K0, case.V0, edges, cfg.tau, outputs=outs, workspace=ws)
+
+    res = run()
+    torch.cuda.synchronize()
+    masks = [x.mask.cpu().numpy() for x in res]
+    errs = []
+    for e, x in enumerate(res):
+        ex = case.edges[e].exact_K.double()
+        errs.append(float(torch.linalg.vector_norm(x.K.double() - ex) / torch.linalg.vector_norm(ex)))
+    for _ in range(3):
+        run()
+    ms = time_events(run, n, stream)
+    nbytes = chain_bytes(cfg, masks, True)
+    log(f"[bench] chain {ms:.3f} ms")
+    return {"workload": f"{cfg.name}: {cfg.n_edges} edges, {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, "
+                        f"A={cfg.A}, r={cfg.r}, tau={cfg.tau}, fallback from the next agent's "
+                        "exact cache",
+            "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes,
+            "tokens_layers_per_s": round(cfg.n_edges * cfg.T * cfg.L / (ms * 1e-3), 1),
+            "reuse_per_edge": [round(float(1 - m.mean()), 4) for m in masks],
+            "k_rel_err_vs_exact_per_edge": [round(x, 6) for x in errs]}
+
+
+def fit32k_leg(dev, stream, n):
+    """kvc_fit_anchor on the delta of the chain workload's first edge (M = 512, T = 32768)."""
+    cfg = synth.CONFIGS["chain_t32768"].replace(n_edges=1)
+    log(f"[bench] fit leg at T={cfg.T}: generating")
+    case = synth.generate(cfg, dev)
+    delta = synth.fit_input(case)
+    del case
+    torch.cuda.empty_cache()
+    M, T = delta.shape[0], delta.shape[1]
+    fws = torch.empty(kvc.fit_workspace_bytes(M, T, cfg.d, cfg.r), dtype=torch.uint8, device=dev)
+
+    def fit():
+        return kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
+
+    res = fit()
+    torch.cuda.synchronize()
+    k = res.k_eff.cpu().numpy()
+    ms = time_events(fit, n, stream)
+    by, syrk, gemm, proj = fit_bytes_flops(M, T, cfg.d, cfg.r)
+    log(f"[bench] fit at T={T}: {ms:.3f} ms")
+    return {"workload": f"delta of chain edge 0: M={M} matrices x T={T} x d={cfg.d} bf16, r={cfg.r}",
+            "ms": round(ms, 4),
+            "tflops_syrk_plus_proj": round((syrk + proj) / (ms * 1e-3) / 1e12, 3),
+            "tflops_gemm_count": round((gemm + proj) / (ms * 1e-3) / 1e12, 3),
+            "mfma_bf16_frac_gemm_count": round((gemm + proj) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+            "gbs": round(by / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "k_eff_min_max": [int(k.min()), int(k.max())]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-fit", action="store_true")
+    ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--only-fit32k", action="store_true",
+                    help="run only the T=32768 fit leg (for a profile of its kernels)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-segments", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
@@ -163,6 +258,10 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.only_fit32k:
+        print(json.dumps({"fit_t32768": fit32k_leg(dev, stream, max(3, args.steps // 10))}),
+              flush=True)
+        return
 
     cfg = synth.CONFIGS["llama8b_t2048"]
     log(f"[bench] generating {cfg.name} on {dev}")
@@ -273,6 +372,12 @@ def main():
         }
         log(f"[bench] fit {ms_f:.3f} ms")
         del delta, fws
+        torch.cuda.empty_cache()
+    if not args.no_chain:
+        out["chain"] = chain_leg(dev, stream, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
+    if not args.no_fit:
+        out["fit_t32768"] = fit32k_leg(dev, stream, max(3, args.steps // 10))
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle on a sample)")
