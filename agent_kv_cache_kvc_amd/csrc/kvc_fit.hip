@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
 
 // ------------------------------------------------------------------------- Jacobi
 // One 512-thread workgroup per matrix; LDS holds A (starts as G), column-major, column
-// stride d + 4 floats, 16-byte chunks of a column swizzled (bit 1 flipped in the upper half)
-// so that the 8 lanes of a pair read distinct banks.  Each step of a sweep rotates d/2
+// stride d + 4 floats, 16-byte chunks of a column swizzled (see jrow) so that the lanes of a
+// pair read distinct banks.  Each step of a sweep rotates d/2
 // disjoint column pairs (round-robin "circle" ordering, every pair once per sweep); a pair
 // is owned by 512/(d/2) adjacent lanes, each holding d/(that) rows.  For columns a_i, a_j:
 //   alpha = |a_i|^2, beta = |a_j|^2, gamma = a_i . a_j,
@@ -192,22 +192,41 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
 // columns orthogonal, so a_j = lambda_j v_j: lambda_j = |a_j| and v_j = a_j / |a_j| (no V is
 // kept).  A pair is left alone when |gamma| <= max(tol sqrt(alpha beta), eta |G|_F^2); the
 // loop ends after a sweep without rotations or after kJacobiMaxSweeps sweeps (the decision
-// is uniform across the workgroup).  The kept vectors are re-orthonormalised by two passes
+// is uniform across the workgroup).  Squared column norms are computed exactly at the start
+// of each sweep and carried through the sweep by the rotation's own identities
+// (alpha' = alpha - t gamma, beta' = beta + t gamma), so a step computes one dot product per
+// pair.  A pair whose columns have not changed since the same pair was checked one sweep
+// earlier and left alone is skipped (its check would repeat the same numbers, up to the
+// rounding of the refreshed norms).  The kept vectors are re-orthonormalised by two passes
 // of Gram-Schmidt in descending order, which also completes null directions (a zero or
 // noise-level column) with canonical basis vectors.
 constexpr int kJacobiBlock = 512;
 
-__device__ __forceinline__ void rr_pair(int p, int step, int n, int& i, int& j) {
-  const int a = (p == 0) ? 0 : ((p - 1 + step) % (n - 1)) + 1;
-  const int b = ((n - 2 - p + step) % (n - 1)) + 1;
-  i = min(a, b);
-  j = max(a, b);
-}
-
-// float index of element `row` inside a column (swizzled 16-byte chunks)
+// float index of element `row` inside a column: 16-byte chunk c is stored at c ^ ((c >> 3) & 3),
+// so the 8 lanes that read 8 chunks 4 apart (one 16-row slice each) hit 8 distinct 4-bank
+// groups in one LDS pass
 __device__ __forceinline__ int jrow(int row) {
   const int c = row >> 2;
-  return ((c ^ (((c >> 4) & 1) << 1)) << 2) | (row & 3);
+  return ((c ^ ((c >> 3) & 3)) << 2) | (row & 3);
+}
+
+// Sum over aligned groups of N = 8 or 16 lanes with DPP (no LDS traffic): xor 1 and xor 2
+// inside quads, then the half-row mirror (lane i <-> 7 - i) joins the two quads of 8 lanes,
+// and for 16 the row mirror (i <-> 15 - i) joins the halves.  Every lane of a group ends with
+// the same bits (each step adds the same two values in either order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xf, 0xf, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (N == 16) v += dpp_f<0x140>(v);  // row_mirror
+  return v;
 }
 
 template <int D>
@@ -243,7 +262,10 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   __shared__ float coef[D];
   __shared__ float xs[D];
   __shared__ float sgn[D];
+  __shared__ float nrm[D];     // squared column norms, carried through a sweep
+  __shared__ int lastrot[D];   // global step of the column's last rotation
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (tid < D) lastrot[tid] = -(1 << 30);
 
   // ---- G = sum of the partials (fixed order), mirrored to a full symmetric matrix
   const float* P = partials + (size_t)m * nsplit * NBLK * 1024;
@@ -266,53 +288,75 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   const float abs_floor = eta * f2;
 
   // ---- sweeps
+  constexpr int TPC = kJacobiBlock / D;  // threads per column for the exact norms
   const int p = tid / TPP, sub = tid % TPP;
   int sweep = 0;
   for (; sweep < kJacobiMaxSweeps; ++sweep) {
+    {
+      const float* a = Am + (tid / TPC) * CS;
+      float ss = 0.f;
+      for (int k = tid % TPC; k < D; k += TPC) ss += a[jrow(k)] * a[jrow(k)];
+#pragma unroll
+      for (int off = 1; off < TPC; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      if (tid % TPC == 0) nrm[tid / TPC] = ss;
+      __syncthreads();
+    }
     int rotated = 0;
+    // circle ordering, advanced incrementally: slot p pairs positions a and b of the circle
+    int ia = (p - 1 + D - 1) % (D - 1), ib = (D - 2 - p) % (D - 1);
     for (int step = 0; step < D - 1; ++step) {
-      int ci, cj;
-      rr_pair(p, step, D, ci, cj);
-      float* ai = Am + ci * CS;
-      float* aj = Am + cj * CS;
-      float xi[RPT], xj[RPT];
-#pragma unroll
-      for (int k = 0; k < RPT; k += 4) {
-        const int o = jrow(sub * RPT + k);
-        *reinterpret_cast<floatx4*>(&xi[k]) = *reinterpret_cast<const floatx4*>(ai + o);
-        *reinterpret_cast<floatx4*>(&xj[k]) = *reinterpret_cast<const floatx4*>(aj + o);
-      }
-      float al = 0.f, be = 0.f, ga = 0.f;
-#pragma unroll
-      for (int k = 0; k < RPT; ++k) {
-        al += xi[k] * xi[k];
-        be += xj[k] * xj[k];
-        ga += xi[k] * xj[k];
-      }
-#pragma unroll
-      for (int off = 1; off < TPP; off <<= 1) {
-        al += __shfl_xor(al, off, 64);
-        be += __shfl_xor(be, off, 64);
-        ga += __shfl_xor(ga, off, 64);
-      }
-      const float lim = fmaxf(tol * sqrtf(al) * sqrtf(be), abs_floor);
-      if (fabsf(ga) > lim) {
-        rotated = 1;
-        const float zeta = (be - al) / (2.f * ga);
-        const float t = copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
-        const float c = 1.f / sqrtf(1.f + t * t);
-        const float s = c * t;
-#pragma unroll
-        for (int k = 0; k < RPT; ++k) {
-          const float u = xi[k], v = xj[k];
-          xi[k] = c * u - s * v;
-          xj[k] = s * u + c * v;
-        }
+      const int gstep = sweep * (D - 1) + step;
+      const int pa = (p == 0) ? 0 : ia + 1, pb = ib + 1;
+      ia = (ia + 1 == D - 1) ? 0 : ia + 1;
+      ib = (ib + 1 == D - 1) ? 0 : ib + 1;
+      const int ci = min(pa, pb), cj = max(pa, pb);
+      const int lri = lastrot[ci], lrj = lastrot[cj];
+      const float nri = nrm[ci], nrj = nrm[cj];
+      const bool active = sweep == 0 || max(lri, lrj) >= gstep - (D - 1);
+      if (active) {
+        float* ai = Am + ci * CS;
+        float* aj = Am + cj * CS;
+        float xi[RPT], xj[RPT];
 #pragma unroll
         for (int k = 0; k < RPT; k += 4) {
           const int o = jrow(sub * RPT + k);
-          *reinterpret_cast<floatx4*>(ai + o) = *reinterpret_cast<floatx4*>(&xi[k]);
-          *reinterpret_cast<floatx4*>(aj + o) = *reinterpret_cast<floatx4*>(&xj[k]);
+          *reinterpret_cast<floatx4*>(&xi[k]) = *reinterpret_cast<const floatx4*>(ai + o);
+          *reinterpret_cast<floatx4*>(&xj[k]) = *reinterpret_cast<const floatx4*>(aj + o);
+        }
+        float ga = 0.f;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) ga += xi[k] * xj[k];
+        ga = group_sum<TPP>(ga);
+        const float al = fmaxf(nri, 0.f), be = fmaxf(nrj, 0.f);
+        const float lim =
+            fmaxf(tol * __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be), abs_floor);
+        if (fabsf(ga) > lim) {
+          rotated = 1;
+          // hardware reciprocal / square root / reciprocal square root (about 1 ulp): the
+          // angle only steers convergence, and c^2 + s^2 = 1 holds to a few ulp either way
+          const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
+          const float t = copysignf(1.f, zeta) *
+                          __builtin_amdgcn_rcpf(fabsf(zeta) + __builtin_amdgcn_sqrtf(1.f + zeta * zeta));
+          const float c = __builtin_amdgcn_rsqf(1.f + t * t);
+          const float s = c * t;
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) {
+            const float u = xi[k], v = xj[k];
+            xi[k] = c * u - s * v;
+            xj[k] = s * u + c * v;
+          }
+#pragma unroll
+          for (int k = 0; k < RPT; k += 4) {
+            const int o = jrow(sub * RPT + k);
+            *reinterpret_cast<floatx4*>(ai + o) = *reinterpret_cast<floatx4*>(&xi[k]);
+            *reinterpret_cast<floatx4*>(aj + o) = *reinterpret_cast<floatx4*>(&xj[k]);
+          }
+          if (sub == 0) {
+            nrm[ci] = al - t * ga;
+            nrm[cj] = be + t * ga;
+            lastrot[ci] = gstep;
+            lastrot[cj] = gstep;
+          }
         }
       }
       __syncthreads();
