@@ -455,20 +455,25 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   const bool uvec = FIX || (r % VEC) == 0;
   const int n_ci = 2 * n_chunks;             // items per segment
 
+  if (threadIdx.x == 0) s_item = atomicAdd(args.ctr, 1);
+  __syncthreads();
+  int item = __builtin_amdgcn_readfirstlane(s_item);
   for (;;) {
     // lane-derived values are recomputed per item (kept out of the loop-carried registers)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
+    if (item >= args.n_items) break;
+    // the next item is requested now and read at the end of this one (the counter's round
+    // trip overlaps the item)
+    int nxt = 0;
+    if (tid == 0) nxt = atomicAdd(args.ctr, 1);
+    {
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane >> 5, ln = lane & 31;
     float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
     const int lrow = lane / LPT;               // token within a coalesced access
     const int lcol = VEC * (lane % LPT);       // channel offset within a half row
-    if (tid == 0) s_item = atomicAdd(args.ctr, 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= args.n_items) break;
 
     bool pool_item = false;
     int s, ci;
@@ -495,10 +500,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       }
       s = b * args.batch + o / n_ci;
       ci = o - (o / n_ci) * n_ci;
-      if (s >= S) {  // padding of the last slot
-        __syncthreads();
-        continue;
-      }
+      if (s >= S) goto next_item;  // padding of the last slot
     } else {
       s = item / n_ci;
       ci = item - s * n_ci;
@@ -591,8 +593,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      __syncthreads();  // `red`, `qsh`, s_last and the item id are free for the next item
-      continue;
+      goto next_item;
     }
 
     // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
@@ -825,7 +826,11 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       const float v = finish_sums<Tr, D>(qs, red, tid);
       if (tid < D) args.next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
     }
-    __syncthreads();  // LDS (W^T, weights, staging, item id) is free for the next item
+    }
+  next_item:
+    if (tid == 0) s_item = nxt;
+    __syncthreads();  // LDS (W^T, weights, staging, chunk sums, item id) is free for the next item
+    item = __builtin_amdgcn_readfirstlane(s_item);
   }
 }
 
