@@ -484,6 +484,572 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   }
 }
 
+// ------------------------------------------------------------------------- eigensolver
+// Tridiagonal route for r <= kEigMaxR (one 512-thread workgroup per matrix, two per CU):
+//  1. G (sum of the Gram partials, float64) in LDS as a packed lower triangle; Householder
+//     reduction to tridiagonal form in float64.  For column k with x = G[k+1:, k] and the
+//     trailing block B: alpha = -sign(x_0) |x|, v = x - alpha e_1, t = 2 / v.v,
+//     p = t B v, w = p - (t/2)(p.v) v, B <- B - v w^T - w v^T.  B v and v.B v come from
+//     B x (B v = B x - alpha B e_1), so one pass over B and one reduction serve a column;
+//     v stays in column k, d_k = G[k][k], e_k = alpha.
+//  2. Every eigenvalue by 4-point multisection on Sturm counts of the tridiagonal matrix
+//     (float32, four lanes per eigenvalue, 13 steps shrink the Gershgorin interval by
+//     5^13 > 2^30); negatives from rounding are clamped to 0 (G is a Gram matrix).
+//  3. Eigenvectors of the r largest: inverse iteration in float64, two solves of
+//     (T - lambda I) y = b with one LU factorisation (partial pivoting); 16 lanes per vector,
+//     each holding D/16 consecutive rows of the factors in registers, the elimination chain
+//     handed from lane to lane.  Then the Householder reflectors are applied back.
+//  4. If the r vectors are orthonormal to 1e-7 they are kept; otherwise (clusters of equal
+//     eigenvalues, null directions) two passes of Gram-Schmidt in descending order, with
+//     null directions completed by canonical basis vectors.  Then the canonical sign.
+constexpr int kEigBlock = 512;
+constexpr int kEigMaxR = 32;
+constexpr int kEigSections = 13;
+constexpr double kEigOrthoTol = 1e-7;
+
+__device__ __forceinline__ int pk(int i, int j) { return i * (i + 1) / 2 + j; }  // j <= i
+
+// lanes whose DPP source lies outside the row read 0
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const int2 h = __builtin_bit_cast(int2, x);
+  int2 o;
+  o.x = __builtin_amdgcn_mov_dpp(h.x, CTRL, 0xf, 0xf, true);
+  o.y = __builtin_amdgcn_mov_dpp(h.y, CTRL, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, o);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+// sum over aligned groups of N lanes (4, 8 or 16); every lane of the group gets it
+template <int N>
+__device__ __forceinline__ double group_sum_d(double v) {
+  v += dpp_d<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += dpp_d<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v += dpp_d<0x141>(v);   // row_half_mirror
+  if constexpr (N >= 16) v += dpp_d<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const int2 h = __builtin_bit_cast(int2, v);
+  int2 o;
+  o.x = __builtin_amdgcn_readlane(h.x, lane);
+  o.y = __builtin_amdgcn_readlane(h.y, lane);
+  return __builtin_bit_cast(double, o);
+}
+
+// wavefront sum in a fixed order (rows of 16 lanes, then the four rows); uniform result
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = group_sum_d<16>(v);
+  return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
+}
+
+// deterministic workgroup sum (waves in fixed order); every thread gets it
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  constexpr int NW = kEigBlock / kWave;
+  v = wave_sum_d(v);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[w];
+  return s;
+}
+
+__device__ __forceinline__ double block_max_d(double v, double* red) {
+  constexpr int NW = kEigBlock / kWave;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) s = fmax(s, red[w]);
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
+    const float* __restrict__ partials, int nsplit, int r, double energy,
+    float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
+    uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad) {
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  constexpr int NW = kEigBlock / kWave;
+  constexpr int RPL = D / 16;  // rows per lane of an eigenvector
+  extern __shared__ __align__(16) double P[];  // packed lower triangle, then the vectors
+  __shared__ __align__(16) double xs[D], cs[D], bx[D], vv[D], ww[D], dd[D], ee[D], tau[D];
+  __shared__ double red[2 * NW + 2];
+  __shared__ float lamd[D];  // eigenvalues, descending
+  __shared__ float df[D], e2f[D];
+  __shared__ double coef[kEigMaxR];
+  const int m = blockIdx.x, tid = threadIdx.x;
+
+  // ---- G = sum of the partials (fixed split order, float64), lower triangle
+  {
+    const float* Pm = partials + (size_t)m * nsplit * NBLK * 1024;
+    constexpr int PER = NBLK * 1024 / kEigBlock;  // 20 (D = 128) or 6 (D = 64)
+    constexpr int U4 = 4;
+    for (int t0 = 0; t0 < PER; t0 += U4) {
+      double acc[U4];
+#pragma unroll
+      for (int u = 0; u < U4; ++u) acc[u] = 0.0;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float* src = Pm + (size_t)sp * NBLK * 1024;
+#pragma unroll
+        for (int u = 0; u < U4; ++u)
+          if (t0 + u < PER) acc[u] += (double)src[(t0 + u) * kEigBlock + tid];
+      }
+#pragma unroll
+      for (int u = 0; u < U4; ++u) {
+        if (t0 + u >= PER) continue;
+        const int e = (t0 + u) * kEigBlock + tid;
+        const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
+        int I = 0, rem = blk;
+        while (rem >= NB - I) { rem -= NB - I; ++I; }
+        const int J = I + rem;
+        const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
+        const int col = J * 32 + (l % 32);
+        if (row <= col) P[pk(col, row)] = acc[u];  // a diagonal block's upper half only
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- Householder tridiagonalisation, two barriers per column.  The matrix lives in
+  //      registers: thread (tid / 16, j = tid % 16) holds rows R0 .. R0 + TR - 1 and the
+  //      columns 32 h + 2 j + e (register column c = 2 h + e), so the 16 lanes of a DPP row
+  //      hold whole rows and read each vector of columns as one contiguous, conflict-free
+  //      16-byte access per lane.  Step k:
+  //      A. every wave applies the previous rank-2 update (v, w in vv / ww; zero at k = 0)
+  //         and in the same pass forms B x (x = column k below row k, in xs) and its
+  //         partial sums x.x and x.B x; the wave holding row k + 1 writes it (= column
+  //         k + 1 of the updated matrix) to cs;
+  //      B. wave 0 forms alpha, t, v and w (B v = B x - alpha B e_1 needs only column
+  //         k + 1), then the next x and d_{k+1} from column k + 1, v and w.
+  //      Waves whose rows all lie above the trailing block skip the arithmetic of A (v and
+  //      w vanish there).  P keeps the reflectors.
+  {
+    constexpr int TR = D / 32, TC = D / 16;
+    constexpr int WROWS = (kWave / 16) * TR;  // rows per wave
+    constexpr int RPW = D / kWave;            // rows per lane of wave 0
+    static_assert(TR == 4 || TR == 2, "row tiles of 4 or 2 rows");
+    const int R0i = (tid / 16) * TR, C0i = 2 * (tid % 16), tidi = tid;  // C0: column of c = 0
+    const int wave = tid / kWave;
+    double g[TR][TC];
+#pragma unroll
+    for (int a = 0; a < TR; ++a) {
+      int R = R0i + a, C0 = C0i;
+      asm volatile("" : "+v"(R), "+v"(C0));
+#pragma unroll
+      for (int c = 0; c < TC; ++c) {
+        const int C = C0 + 32 * (c >> 1) + (c & 1);
+        g[a][c] = P[R >= C ? pk(R, C) : pk(C, R)];
+      }
+    }
+    if (tid < D) {
+      xs[tid] = tid >= 1 ? P[pk(tid, 0)] : 0.0;  // column 0 below the diagonal
+      vv[tid] = 0.0;
+      ww[tid] = 0.0;
+      if (tid == 0) dd[0] = P[0];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int k = 0; k < D - 2; ++k) {
+      // per-step copies of the thread's indices: addresses are recomputed in every step
+      // rather than held in registers across the loop
+      int R0 = R0i, C0 = C0i, tid = tidi;
+      asm volatile("" : "+v"(R0), "+v"(C0), "+v"(tid));
+      double sa = 0.0, sb = 0.0;
+      if (wave * WROWS + WROWS - 1 >= k) {  // uniform per wave
+        double vr[TR], wr[TR], s[TR];
+#pragma unroll
+        for (int a = 0; a < TR; ++a) { vr[a] = vv[R0 + a]; wr[a] = ww[R0 + a]; s[a] = 0.0; }
+#pragma unroll
+        for (int c = 0; c < TC; ++c) {
+          const int C = C0 + 32 * (c >> 1) + (c & 1);
+          const double vc = vv[C], wc = ww[C], xc = xs[C];
+#pragma unroll
+          for (int a = 0; a < TR; ++a) {
+            g[a][c] = fma(-wr[a], vc, fma(-vr[a], wc, g[a][c]));
+            s[a] = fma(g[a][c], xc, s[a]);
+          }
+        }
+        // row k + 1 of the updated matrix is column k + 1: cs
+        if (wave * WROWS <= k + 1 && k + 1 < wave * WROWS + WROWS && R0 <= k + 1 &&
+            k + 1 < R0 + TR) {
+          // the tile row is the same on every active lane: a scalar branch picks it
+          const int as = __builtin_amdgcn_readfirstlane(k + 1 - R0);
+#pragma unroll
+          for (int a = 0; a < TR; ++a) {
+            if (as == a) {
+#pragma unroll
+              for (int c = 0; c < TC; ++c) {
+                const int C = C0 + 32 * (c >> 1) + (c & 1);
+                cs[C] = C >= k + 1 ? g[a][c] : 0.0;
+              }
+            }
+          }
+        }
+        // sum over the row block's 16 lanes, scattered: lane l ends with the row
+        // rsel(l) = 2 (l & 1) + ((l >> 1) & 1) (TR = 4) or l & 1 (TR = 2)
+        const int l = tid & 15;
+        const bool b0 = l & 1, b1 = (l >> 1) & 1;
+        double acc;
+        if constexpr (TR == 4) {
+          const double send0 = b0 ? s[0] : s[2], send1 = b0 ? s[1] : s[3];
+          double keep0 = b0 ? s[2] : s[0], keep1 = b0 ? s[3] : s[1];
+          keep0 += dpp_d<0xB1>(send0);  // lane l ^ 1
+          keep1 += dpp_d<0xB1>(send1);
+          const double send = b1 ? keep0 : keep1;
+          acc = (b1 ? keep1 : keep0) + dpp_d<0x4E>(send);  // lane l ^ 2
+        } else {
+          const double send = b0 ? s[0] : s[1];
+          acc = (b0 ? s[1] : s[0]) + dpp_d<0xB1>(send);
+          acc += dpp_d<0x4E>(acc);
+        }
+        acc += dpp_d<0x124>(acc);  // row_ror:4
+        acc += dpp_d<0x128>(acc);  // row_ror:8
+        // lanes 0 .. TR - 1 of the row block: row R, its B x and its share of the sums
+        const int R = R0 + (TR == 4 ? 2 * (l & 1) + ((l >> 1) & 1) : (l & 1));
+        if (l < TR) {
+          bx[R] = acc;
+          const double x = xs[R];  // zero above row k + 1
+          sa = x * x;
+          sb = x * acc;
+        }
+        // lanes 0 .. TR - 1 of the four row blocks: quad sums, then the four blocks
+        sa += dpp_d<0xB1>(sa);
+        sb += dpp_d<0xB1>(sb);
+        if constexpr (TR == 4) {
+          sa += dpp_d<0x4E>(sa);
+          sb += dpp_d<0x4E>(sb);
+        }
+        sa = ((readlane_d(sa, 0) + readlane_d(sa, 16)) + readlane_d(sa, 32)) + readlane_d(sa, 48);
+        sb = ((readlane_d(sb, 0) + readlane_d(sb, 16)) + readlane_d(sb, 32)) + readlane_d(sb, 48);
+      }
+      if (tid % kWave == 0) { red[2 * wave] = sa; red[2 * wave + 1] = sb; }
+      __syncthreads();
+      if (wave == 0) {
+        const double x0 = xs[k + 1], b00 = cs[k + 1], bx0 = bx[k + 1];
+        double nx2 = 0.0, xbx = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { nx2 += red[2 * w]; xbx += red[2 * w + 1]; }
+        // x = 0 (nothing to annihilate) gives alpha = t = 0, hence v = w = 0: no change
+        const double nx = sqrt(nx2);
+        const double alpha = nx2 == 0.0 ? 0.0 : (x0 >= 0.0 ? -nx : nx);
+        const double t = nx2 == 0.0 ? 0.0 : 1.0 / (nx2 - x0 * alpha);  // 2 / v.v
+        const double vbv = xbx - 2.0 * alpha * bx0 + alpha * alpha * b00;
+        const double K = 0.5 * t * t * vbv;  // (t/2) p.v
+        const double v1 = x0 - alpha, w1 = t * (bx0 - alpha * b00) - K * v1;  // row k + 1
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+          const int Ru = tid + kWave * u;
+          const double xr = xs[Ru], br = bx[Ru], cr = cs[Ru];
+          double v = 0.0, w = 0.0;
+          if (Ru >= k + 1) {
+            v = Ru == k + 1 ? v1 : xr;
+            w = t * (br - alpha * cr) - K * v;
+            P[pk(Ru, k)] = v;  // the reflector is kept in column k
+          }
+          vv[Ru] = v;
+          ww[Ru] = w;
+          // column k + 1 of the updated matrix below row k + 1: the next x
+          xs[Ru] = Ru >= k + 2 ? cr - v * w1 - w * v1 : 0.0;
+        }
+        if (tid == 0) {
+          ee[k] = alpha;
+          tau[k] = t;
+          dd[k + 1] = b00 - 2.0 * v1 * w1;
+        }
+      }
+      __syncthreads();
+    }
+    // the last update: e_{D-2} is the next x, d_{D-1} comes from the register tile
+    {
+      int R0 = R0i, C0 = C0i;
+      asm volatile("" : "+v"(R0), "+v"(C0));
+      const double vl = vv[D - 1], wl = ww[D - 1];
+      if (tid == 0) {
+        ee[D - 2] = xs[D - 1];
+        tau[D - 2] = 0.0;
+        ee[D - 1] = 0.0;
+      }
+      if (R0 == D - TR && C0 == 30) dd[D - 1] = g[TR - 1][TC - 1] - 2.0 * vl * wl;  // column D - 1
+    }
+  }
+  __syncthreads();
+  double ghi = 0.0, ge2 = 0.0;
+  if (tid < D) {
+    df[tid] = (float)dd[tid];
+    e2f[tid] = tid < D - 1 ? (float)(ee[tid] * ee[tid]) : 0.f;
+    ghi = dd[tid] + (tid > 0 ? fabs(ee[tid - 1]) : 0.0) + fabs(ee[tid]);
+    ge2 = ee[tid] * ee[tid];
+  }
+  const float hi0 = (float)block_max_d(ghi, red);
+  const float pivmin = 1e-30f * fmaxf(1.f, (float)block_max_d(ge2, red));
+
+  // ---- every eigenvalue by multisection (four lanes per eigenvalue, the ev-th smallest)
+  {
+    const int ev = tid / 4, q = tid % 4;
+    if (ev < D) {
+      float lo = -1e-6f * hi0 - pivmin, hi = hi0 * (1.f + 1e-6f) + pivmin;
+      for (int it = 0; it < kEigSections; ++it) {
+        const float w5 = (hi - lo) * 0.2f;
+        const float mid = lo + (float)(q + 1) * w5;
+        int cnt = 0;
+        float qv = 1.f;
+        for (int j = 0; j < D; ++j) {
+          const float e2 = j > 0 ? e2f[j - 1] : 0.f;
+          qv = (df[j] - mid) - e2 * __builtin_amdgcn_rcpf(qv);
+          const bool neg = qv <= pivmin;
+          cnt += neg;
+          qv = neg ? fminf(qv, -pivmin) : qv;
+        }
+        // counts and points of the quad, exactly as each lane evaluated them
+        const int c0 = dpp_i<0x00>(cnt), c1 = dpp_i<0x55>(cnt);
+        const int c2 = dpp_i<0xAA>(cnt), c3 = dpp_i<0xFF>(cnt);
+        const int mb = __builtin_bit_cast(int, mid);
+        const float m0 = __builtin_bit_cast(float, dpp_i<0x00>(mb));
+        const float m1 = __builtin_bit_cast(float, dpp_i<0x55>(mb));
+        const float m2 = __builtin_bit_cast(float, dpp_i<0xAA>(mb));
+        const float m3 = __builtin_bit_cast(float, dpp_i<0xFF>(mb));
+        float nlo = m3, nhi = hi;
+        if (c3 > ev) { nlo = m2; nhi = m3; }
+        if (c2 > ev) { nlo = m1; nhi = m2; }
+        if (c1 > ev) { nlo = m0; nhi = m1; }
+        if (c0 > ev) { nlo = lo; nhi = m0; }
+        lo = nlo;
+        hi = nhi;
+      }
+      if (q == 0) lamd[D - 1 - ev] = fmaxf(0.5f * (lo + hi), 0.f);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    for (int k = 0; k < D; ++k) total += (double)lamd[k];
+    int ke = 0;
+    if (total > 0.0) {
+      const double need = energy * total;
+      double run = 0.0;
+      ke = D;
+      for (int k = 0; k < D; ++k) {
+        run += (double)lamd[k];
+        if (run >= need) { ke = k + 1; break; }
+      }
+    }
+    k_eff_out[m] = ke;
+  }
+  if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = lamd[tid];
+
+  // ---- inverse iteration for the r largest: vector vec on lanes 16 vec .. 16 vec + 15,
+  //      lane L holding rows L RPL .. L RPL + RPL - 1 of the LU factors and of y
+  const int vec = tid / 16, L = tid % 16;
+  double z[RPL];
+  {
+    const double lam = (double)lamd[vec < D ? vec : 0];
+    const double tiny = 1e-300 + 1e-16 * fmax((double)lamd[0], 1e-300);
+    double Rrp[RPL], Rc1[RPL], Rml[RPL], Ry[RPL];  // 1/pivot, U's next entry, multiplier, y
+    unsigned sw = 0;                              // bit u: rows u and u + 1 were swapped
+    auto rhs0 = [&](int j) { return 1.0 + 0.1 * (double)((j * (2 * vec + 3)) % 7); };
+    // factorisation of T - lambda I and the first right-hand side: every lane of the group
+    // runs the same chain and keeps its own rows
+    {
+      double cb = dd[0] - lam, cc = ee[0], ry = rhs0(0);
+      for (int b = 0; b < 16; ++b) {
+        const bool own = L == b;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+          const int j = b * RPL + u;
+          if (j < D - 1) {
+            const double na = ee[j], nb = dd[j + 1] - lam;
+            const double nc = j + 1 < D - 1 ? ee[j + 1] : 0.0;
+            const double ny = rhs0(j + 1);
+            const bool swp = fabs(na) > fabs(cb);
+            const double piv = swp ? na : cb, oth = swp ? cb : na;
+            const double pg = fabs(piv) > tiny ? piv : (piv < 0.0 ? -tiny : tiny);
+            const double rp = 1.0 / pg;
+            const double mlt = oth * rp;
+            const double c1 = swp ? nb : cc, yj = swp ? ny : ry;
+            const double nry = swp ? ry - mlt * ny : ny - mlt * ry;
+            const double ncb = swp ? cc - mlt * nb : nb - mlt * cc;
+            const double ncc = swp ? -mlt * nc : nc;
+            if (own) {
+              Rrp[u] = rp; Rc1[u] = c1; Rml[u] = mlt; Ry[u] = yj;
+              sw |= (unsigned)swp << u;
+            }
+            cb = ncb; cc = ncc; ry = nry;
+          } else {
+            const double pg = fabs(cb) > tiny ? cb : (cb < 0.0 ? -tiny : tiny);
+            if (own) { Rrp[u] = 1.0 / pg; Rc1[u] = 0.0; Rml[u] = 0.0; Ry[u] = ry; }
+          }
+        }
+      }
+    }
+    // back substitution U x = y in place; (x_{j+1}, x_{j+2}) move from lane L + 1 to lane L
+    auto back_solve = [&]() {
+      double x1 = 0.0, x2 = 0.0, ssq = 0.0;
+      for (int b = 15; b >= 0; --b) {
+        const bool own = L == b;
+#pragma unroll
+        for (int u = RPL - 1; u >= 0; --u) {
+          const int j = b * RPL + u;
+          const double c2 = ((sw >> u) & 1u) && j + 1 < D - 1 ? ee[j + 1] : 0.0;
+          const double xj = (Ry[u] - Rc1[u] * x1 - c2 * x2) * Rrp[u];
+          if (own) { Ry[u] = xj; ssq += xj * xj; }
+          x2 = x1;
+          x1 = xj;
+        }
+        x1 = dpp_d<0x101>(x1);  // row_shl:1 — lane L takes lane L + 1
+        x2 = dpp_d<0x101>(x2);
+      }
+      ssq = group_sum_d<16>(ssq);
+      return ssq > 0.0 ? 1.0 / sqrt(ssq) : 0.0;
+    };
+    const double s1 = back_solve();
+    // second right-hand side s1 y: the same row operations; ry moves from lane L to L + 1
+    {
+      const double halo = dpp_d<0x101>(Ry[0]);  // y of the next lane's first row
+      double ry = s1 * Ry[0];
+      for (int b = 0; b < 16; ++b) {
+        const bool own = L == b;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+          const int j = b * RPL + u;
+          if (j < D - 1) {
+            const double ny = s1 * (u + 1 < RPL ? Ry[u + 1 < RPL ? u + 1 : 0] : halo);
+            const bool swp = (sw >> u) & 1u;
+            const double mlt = Rml[u];
+            const double out = swp ? ny : ry;
+            ry = swp ? ry - mlt * ny : ny - mlt * ry;
+            if (own) Ry[u] = out;
+          } else if (own) {
+            Ry[u] = ry;
+          }
+        }
+        ry = dpp_d<0x111>(ry);  // row_shr:1 — lane L takes lane L - 1
+      }
+    }
+    const double s2 = back_solve();
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) z[u] = s2 * Ry[u];
+  }
+
+  // ---- back-transformation z = H_0 H_1 ... H_{D-3} y on the same lanes
+  for (int k = D - 3; k >= 0; --k) {
+    const double tk = tau[k];
+    if (tk == 0.0) continue;  // uniform
+    double pv[RPL];
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int j = L * RPL + u;
+      pv[u] = j > k ? P[pk(j, k)] : 0.0;
+      s += pv[u] * z[u];
+    }
+    s = group_sum_d<16>(s) * tk;
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) z[u] -= s * pv[u];
+  }
+  __syncthreads();  // P (reflectors) is no longer read: it holds the vectors from here on
+  double* Z = P;    // [r][D]
+  if (vec < r) {
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) Z[vec * D + L * RPL + u] = z[u];
+  }
+  __syncthreads();
+
+  // ---- orthonormality of the r vectors: max |Z Z^T - I| over the lower triangle
+  double defect = 0.0;
+  for (int pidx = tid; pidx < r * (r + 1) / 2; pidx += kEigBlock) {
+    int a = 0;
+    while ((a + 1) * (a + 2) / 2 <= pidx) ++a;
+    const int b = pidx - a * (a + 1) / 2;
+    double c = 0.0;
+    for (int t2 = 0; t2 < D; ++t2) {
+      const int col = (t2 + tid) & (D - 1);  // skewed start: no bank conflicts
+      c += Z[a * D + col] * Z[b * D + col];
+    }
+    const double dv = fabs(c - (a == b ? 1.0 : 0.0));
+    defect = fmax(defect, dv == dv ? dv : 1e300);  // a NaN sends the matrix to Gram-Schmidt
+  }
+  defect = block_max_d(defect, red);
+
+  // ---- otherwise two passes of Gram-Schmidt in descending order with completion
+  if (!(defect <= kEigOrthoTol)) {
+    const int q16 = tid % 16;
+    for (int k = 0; k < r; ++k) {
+      int cand = -1;  // -1: the computed vector, else canonical basis vector e_cand
+      for (;;) {
+        if (tid < D) xs[tid] = (cand < 0) ? Z[k * D + tid] : (tid == cand ? 1.0 : 0.0);
+        __syncthreads();
+        const double n0 = block_sum_d(tid < D ? xs[tid] * xs[tid] : 0.0, red);
+        for (int pass = 0; pass < 2; ++pass) {
+          {  // coef_i = z_i . x for i < k (16 lanes per coefficient)
+            const int i = tid / 16;
+            double c = 0.0;
+            if (i < k) {
+#pragma unroll
+              for (int t2 = 0; t2 < RPL; ++t2) c += Z[i * D + q16 + 16 * t2] * xs[q16 + 16 * t2];
+            }
+            c = group_sum_d<16>(c);
+            if (i < k && q16 == 0) coef[i] = c;
+          }
+          __syncthreads();
+          if (tid < D) {
+            double v = xs[tid];
+            for (int i = 0; i < k; ++i) v -= coef[i] * Z[i * D + tid];
+            xs[tid] = v;
+          }
+          __syncthreads();
+        }
+        const double n1 = block_sum_d(tid < D ? xs[tid] * xs[tid] : 0.0, red);
+        const bool ok = (cand < 0) ? (n0 > 0.0 && n1 > 1e-4 * n0) : (n1 > 1.0 / (4.0 * D));
+        if (ok || cand == D - 1) {
+          const double inv = n1 > 0.0 ? 1.0 / sqrt(n1) : 0.0;
+          if (tid < D) Z[k * D + tid] = xs[tid] * inv;
+          __syncthreads();
+          break;
+        }
+        ++cand;
+        __syncthreads();
+      }
+    }
+  }
+  // ---- canonical sign: largest |entry| (first on ties) positive; outputs
+  __shared__ float sgn[kEigMaxR];
+  if (tid < r) {
+    double best = -1.0, bv = 0.0;
+    for (int j = 0; j < D; ++j) {
+      const double av = fabs(Z[tid * D + j]);
+      if (av > best) { best = av; bv = Z[tid * D + j]; }
+    }
+    sgn[tid] = bv < 0.0 ? -1.f : 1.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < rpad * D; e += kEigBlock) {
+    const int kk = e / D, c = e % D;
+    float wv = 0.f;
+    if (kk < r) {
+      wv = sgn[kk] * (float)Z[kk * D + c];
+      W_out[((size_t)m * r + kk) * D + c] = wv;
+    }
+    if (w_hi) {
+      const uint16_t hi = f32_to_bf16(wv);
+      const uint16_t lo = f32_to_bf16(wv - bf16_to_f32(hi));
+      w_hi[((size_t)m * rpad + kk) * D + c] = hi;
+      w_lo[((size_t)m * rpad + kk) * D + c] = lo;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------- projection
 // grid (n_tiles, M): U[t, j] = sum_c delta[t, c] W[j, c].  Orientation U^T = W delta^T:
 // A operand = W rows (row m of a 32-block = component 32 mb + cmap32(m)), B operand =
@@ -655,13 +1221,22 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
                        f.T, f.chunk, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)D * (D + 4) * sizeof(float);
-  allow_dynamic_lds(jacobi_kernel<D>, lds);
-  const float tol = 2e-6f, eta = 1e-12f;
-  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials, f.nsplit,
-                     f.r, energy, tol, eta, W_out, eig, k_eff,
-                     dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
-                     f.rpad, sweeps);
+  if (f.r <= kEigMaxR) {
+    const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
+    allow_dynamic_lds(eig_kernel<D>, lds);
+    hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
+                       f.nsplit, f.r, energy, W_out, eig, k_eff,
+                       dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
+                       f.rpad);
+  } else {
+    const size_t lds = (size_t)D * (D + 4) * sizeof(float);
+    allow_dynamic_lds(jacobi_kernel<D>, lds);
+    const float tol = 2e-6f, eta = 1e-12f;
+    hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials,
+                       f.nsplit, f.r, energy, tol, eta, W_out, eig, k_eff,
+                       dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
+                       f.rpad, sweeps);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || f.T == 0) return e;
   const int n_tiles = ceil_div(f.T, kRowsPerPass * kProjIters);
