@@ -160,7 +160,8 @@ def cpu_baseline(cfg, case, desc, n_seg: int, budget_s: float = 12.0):
     dt = (time.perf_counter() - t0) / reps
     sub = cfg.replace(L=n_seg, H=1)
     gbs = correct_bytes(sub, out["mask"]) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n_seg} of {cfg.L * cfg.H} segments of the same workload, fp64 numpy, "
                       f"{reps} rep(s) of {dt:.2f} s",
             "tokens_layers_per_s": round(n_seg * cfg.T / cfg.H / dt, 1)}
@@ -236,6 +237,39 @@ def fit32k_leg(dev, stream, n):
             "gbs": round(by / (ms * 1e-3) / 1e9, 2),
             "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "k_eff_min_max": [int(k.min()), int(k.max())]}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_fit(delta, r, n_mat: int = 16, budget_s: float = 8.0):
+    """The fp64 oracle's fit (truncated SVD) timed on a sample of the delta matrices."""
+    import oracle  # only this leg touches the oracle
+
+    M, T, d = delta.shape
+    sample = synth.to_f64(delta[: min(n_mat, M)])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.fit_anchor(sample, r)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    n = sample.shape[0]
+    by, syrk, gemm, proj = fit_bytes_flops(n, T, d, r)
+    return {"value": round((syrk + proj) / dt / 1e12, 5), "unit": "TFLOP/s (SYRK + projection count)",
+            "gbs": round(by / dt / 1e9, 4), "cores": threads, "cpu": cpu_model(), "kind": "oracle",
+            "sample": f"{n} of {M} matrices (T={T}, d={d}, r={r}), fp64 numpy SVD, "
+                      f"{reps} rep(s) of {dt:.2f} s"}
 
 
 def main():
@@ -371,6 +405,9 @@ def main():
             "hbm_frac": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
         log(f"[bench] fit {ms_f:.3f} ms")
+        if not args.no_cpu:
+            log("[bench] cpu baseline of the fit (oracle on a sample)")
+            out["cpu_baseline_fit"] = cpu_baseline_fit(delta, fcfg.r)
         del delta, fws
         torch.cuda.empty_cache()
     if not args.no_chain:
