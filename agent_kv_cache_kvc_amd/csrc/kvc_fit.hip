@@ -492,9 +492,11 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
 //     p = t B v, w = p - (t/2)(p.v) v, B <- B - v w^T - w v^T.  B v and v.B v come from
 //     B x (B v = B x - alpha B e_1), so one pass over B and one reduction serve a column;
 //     v stays in column k, d_k = G[k][k], e_k = alpha.
-//  2. Every eigenvalue by 4-point multisection on Sturm counts of the tridiagonal matrix
-//     (float32, four lanes per eigenvalue, 13 steps shrink the Gershgorin interval by
-//     5^13 > 2^30); negatives from rounding are clamped to 0 (G is a Gram matrix).
+//  2. The r largest eigenvalues by multisection on Sturm counts of the tridiagonal matrix
+//     (float32, eight lanes per eigenvalue); negatives from rounding are clamped to 0 (G is
+//     a Gram matrix).  The effective rank compares running sums with the trace of G; the
+//     other eigenvalues are found (four lanes each) only when they are output or when the
+//     r largest do not reach the energy threshold.
 //  3. Eigenvectors of the r largest: inverse iteration in float64, two solves of
 //     (T - lambda I) y = b with one LU factorisation (partial pivoting); 16 lanes per vector,
 //     each holding D/16 consecutive rows of the factors in registers, the elimination chain
@@ -504,7 +506,6 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
 //     null directions completed by canonical basis vectors.  Then the canonical sign.
 constexpr int kEigBlock = 512;
 constexpr int kEigMaxR = 32;
-constexpr int kEigSections = 13;
 constexpr double kEigOrthoTol = 1e-7;
 
 __device__ __forceinline__ int pk(int i, int j) { return i * (i + 1) / 2 + j; }  // j <= i
@@ -572,6 +573,46 @@ __device__ __forceinline__ double block_max_d(double v, double* red) {
 #pragma unroll
   for (int w = 1; w < NW; ++w) s = fmax(s, red[w]);
   return s;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_fl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf,
+                                                            0xf, true));
+}
+
+// The ev-th smallest eigenvalue of the symmetric tridiagonal matrix (diagonal df, squared
+// off-diagonals e2f > 0) by P-point multisection on Sturm counts, P aligned lanes per
+// eigenvalue (q = lane within the group).  Each step splits [lo, hi] into P + 1 parts; the
+// new interval ends at the lowest point with more than ev eigenvalues below it and starts
+// at the highest point under that one, so it always brackets the eigenvalue even where
+// rounding makes the counts non-monotone.  4 points x 13 steps or 8 points x 10 steps
+// shrink the start interval more than 2^30 times.
+template <int P, int D>
+__device__ float multisect(int ev, float lo, float hi, const float* df, const float* e2f, int q) {
+  static_assert(P == 4 || P == 8, "groups of 4 or 8 lanes");
+  constexpr int NIT = P == 4 ? 13 : 10;
+  for (int it = 0; it < NIT; ++it) {
+    const float mid = lo + (float)(q + 1) * ((hi - lo) * (1.f / (P + 1)));
+    // Sturm count: the number of negative pivots of T - mid I
+    float qv = df[0] - mid;
+    int cnt = qv < 0.f;
+    for (int j = 1; j < D; ++j) {
+      qv = (df[j] - mid) - e2f[j - 1] * __builtin_amdgcn_rcpf(qv);
+      cnt += qv < 0.f;
+    }
+    float h = cnt > ev ? mid : hi;
+    h = fminf(h, dpp_fl<0xB1>(h));
+    h = fminf(h, dpp_fl<0x4E>(h));
+    if constexpr (P == 8) h = fminf(h, dpp_fl<0x141>(h));
+    float l = mid < h ? mid : lo;
+    l = fmaxf(l, dpp_fl<0xB1>(l));
+    l = fmaxf(l, dpp_fl<0x4E>(l));
+    if constexpr (P == 8) l = fmaxf(l, dpp_fl<0x141>(l));
+    lo = l;
+    hi = h;
+  }
+  return 0.5f * (lo + hi);
 }
 
 template <int D>
@@ -672,13 +713,18 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
 #pragma unroll
         for (int a = 0; a < TR; ++a) { vr[a] = vv[R0 + a]; wr[a] = ww[R0 + a]; s[a] = 0.0; }
 #pragma unroll
-        for (int c = 0; c < TC; ++c) {
-          const int C = C0 + 32 * (c >> 1) + (c & 1);
-          const double vc = vv[C], wc = ww[C], xc = xs[C];
+        for (int h = 0; h < TC / 2; ++h) {
+          // columns 32 h .. 32 h + 31 all at or left of column k are never read again
+          if (32 * h + 31 <= k) continue;
 #pragma unroll
-          for (int a = 0; a < TR; ++a) {
-            g[a][c] = fma(-wr[a], vc, fma(-vr[a], wc, g[a][c]));
-            s[a] = fma(g[a][c], xc, s[a]);
+          for (int e = 0; e < 2; ++e) {
+            const int c = 2 * h + e, C = C0 + 32 * h + e;
+            const double vc = vv[C], wc = ww[C], xc = xs[C];
+#pragma unroll
+            for (int a = 0; a < TR; ++a) {
+              g[a][c] = fma(-wr[a], vc, fma(-vr[a], wc, g[a][c]));
+              s[a] = fma(g[a][c], xc, s[a]);
+            }
           }
         }
         // row k + 1 of the updated matrix is column k + 1: cs
@@ -738,13 +784,28 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
       __syncthreads();
       if (wave == 0) {
         const double x0 = xs[k + 1], b00 = cs[k + 1], bx0 = bx[k + 1];
-        double nx2 = 0.0, xbx = 0.0;
+        // the eight wave sums pairwise (a short dependence chain)
+        double pa[NW], pb[NW];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) { nx2 += red[2 * w]; xbx += red[2 * w + 1]; }
-        // x = 0 (nothing to annihilate) gives alpha = t = 0, hence v = w = 0: no change
-        const double nx = sqrt(nx2);
+        for (int w = 0; w < NW; ++w) { pa[w] = red[2 * w]; pb[w] = red[2 * w + 1]; }
+#pragma unroll
+        for (int span = 1; span < NW; span *= 2)
+#pragma unroll
+          for (int w = 0; w + span < NW; w += 2 * span) { pa[w] += pa[w + span]; pb[w] += pb[w + span]; }
+        const double nx2 = pa[0], xbx = pb[0];
+        // |x| and t = 2 / v.v = 1 / (|x| (|x| + |x_0|)) from the hardware reciprocal square
+        // root and reciprocal, each refined by two Newton steps (x = 0 gives alpha = t = 0,
+        // hence v = w = 0: no change)
+        double y = __builtin_amdgcn_rsq(nx2);
+        y = y * fma(-0.5 * nx2 * y, y, 1.5);
+        y = y * fma(-0.5 * nx2 * y, y, 1.5);
+        const double nx = nx2 * y;
+        const double den = nx + fabs(x0);
+        double rd = __builtin_amdgcn_rcp(den);
+        rd = rd * fma(-den, rd, 2.0);
+        rd = rd * fma(-den, rd, 2.0);
         const double alpha = nx2 == 0.0 ? 0.0 : (x0 >= 0.0 ? -nx : nx);
-        const double t = nx2 == 0.0 ? 0.0 : 1.0 / (nx2 - x0 * alpha);  // 2 / v.v
+        const double t = nx2 == 0.0 ? 0.0 : y * rd;
         const double vbv = xbx - 2.0 * alpha * bx0 + alpha * alpha * b00;
         const double K = 0.5 * t * t * vbv;  // (t/2) p.v
         const double v1 = x0 - alpha, w1 = t * (bx0 - alpha * b00) - K * v1;  // row k + 1
@@ -785,59 +846,55 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
     }
   }
   __syncthreads();
-  double ghi = 0.0, ge2 = 0.0;
+  double ghi = 0.0;
   if (tid < D) {
     df[tid] = (float)dd[tid];
-    e2f[tid] = tid < D - 1 ? (float)(ee[tid] * ee[tid]) : 0.f;
+    // a zero off-diagonal is replaced by a tiny one: the Sturm recurrence then never forms
+    // 0 * inf (the eigenvalues move by far less than float32 resolves)
+    e2f[tid] = tid < D - 1 ? fmaxf((float)(ee[tid] * ee[tid]), 1e-36f) : 0.f;
     ghi = dd[tid] + (tid > 0 ? fabs(ee[tid - 1]) : 0.0) + fabs(ee[tid]);
-    ge2 = ee[tid] * ee[tid];
   }
   const float hi0 = (float)block_max_d(ghi, red);
-  const float pivmin = 1e-30f * fmaxf(1.f, (float)block_max_d(ge2, red));
+  // the total energy: trace of G = sum of its eigenvalues (float64, fixed order)
+  const double trace = block_sum_d(tid < D ? dd[tid] : 0.0, red);
+  const float lo_start = -(1e-6f * hi0 + 1e-30f), hi_start = hi0 * (1.f + 1e-6f) + 1e-30f;
 
-  // ---- every eigenvalue by multisection (four lanes per eigenvalue, the ev-th smallest)
-  {
-    const int ev = tid / 4, q = tid % 4;
-    if (ev < D) {
-      float lo = -1e-6f * hi0 - pivmin, hi = hi0 * (1.f + 1e-6f) + pivmin;
-      for (int it = 0; it < kEigSections; ++it) {
-        const float w5 = (hi - lo) * 0.2f;
-        const float mid = lo + (float)(q + 1) * w5;
-        int cnt = 0;
-        float qv = 1.f;
-        for (int j = 0; j < D; ++j) {
-          const float e2 = j > 0 ? e2f[j - 1] : 0.f;
-          qv = (df[j] - mid) - e2 * __builtin_amdgcn_rcpf(qv);
-          const bool neg = qv <= pivmin;
-          cnt += neg;
-          qv = neg ? fminf(qv, -pivmin) : qv;
-        }
-        // counts and points of the quad, exactly as each lane evaluated them
-        const int c0 = dpp_i<0x00>(cnt), c1 = dpp_i<0x55>(cnt);
-        const int c2 = dpp_i<0xAA>(cnt), c3 = dpp_i<0xFF>(cnt);
-        const int mb = __builtin_bit_cast(int, mid);
-        const float m0 = __builtin_bit_cast(float, dpp_i<0x00>(mb));
-        const float m1 = __builtin_bit_cast(float, dpp_i<0x55>(mb));
-        const float m2 = __builtin_bit_cast(float, dpp_i<0xAA>(mb));
-        const float m3 = __builtin_bit_cast(float, dpp_i<0xFF>(mb));
-        float nlo = m3, nhi = hi;
-        if (c3 > ev) { nlo = m2; nhi = m3; }
-        if (c2 > ev) { nlo = m1; nhi = m2; }
-        if (c1 > ev) { nlo = m0; nhi = m1; }
-        if (c0 > ev) { nlo = lo; nhi = m0; }
-        lo = nlo;
-        hi = nhi;
-      }
-      if (q == 0) lamd[D - 1 - ev] = fmaxf(0.5f * (lo + hi), 0.f);
-    }
+  // ---- the r largest eigenvalues by 8-point multisection (eight lanes per eigenvalue),
+  //      then the effective rank if their energy reaches the threshold; the other
+  //      eigenvalues (4-point multisection) only when they are asked for or needed
+  __shared__ int s_ke, s_all;
+  if (tid < 8 * r) {
+    const float lam = multisect<8, D>(D - 1 - tid / 8, lo_start, hi_start, df, e2f, tid % 8);
+    if (tid % 8 == 0) lamd[tid / 8] = fmaxf(lam, 0.f);
   }
   __syncthreads();
   if (tid == 0) {
-    double total = 0.0;
-    for (int k = 0; k < D; ++k) total += (double)lamd[k];
-    int ke = 0;
-    if (total > 0.0) {
-      const double need = energy * total;
+    int ke = -1;
+    if (!(trace > 0.0)) {
+      ke = 0;
+    } else {
+      const double need = energy * trace;
+      double run = 0.0;
+      for (int k = 0; k < r; ++k) {
+        run += (double)lamd[k];
+        if (run >= need) { ke = k + 1; break; }
+      }
+    }
+    s_ke = ke;
+    s_all = eig_out != nullptr || ke < 0;
+  }
+  __syncthreads();
+  if (s_all) {  // uniform
+    if (tid < 4 * (D - r)) {
+      const float lam = multisect<4, D>(D - 1 - r - tid / 4, lo_start, hi_start, df, e2f, tid % 4);
+      if (tid % 4 == 0) lamd[r + tid / 4] = fmaxf(lam, 0.f);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int ke = s_ke;
+    if (ke < 0) {
+      const double need = energy * trace;
       double run = 0.0;
       ke = D;
       for (int k = 0; k < D; ++k) {
@@ -854,7 +911,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   const int vec = tid / 16, L = tid % 16;
   double z[RPL];
   {
-    const double lam = (double)lamd[vec < D ? vec : 0];
+    const double lam = vec < r ? (double)lamd[vec] : 0.0;  // lanes past r: unused
     const double tiny = 1e-300 + 1e-16 * fmax((double)lamd[0], 1e-300);
     double Rrp[RPL], Rc1[RPL], Rml[RPL], Ry[RPL];  // 1/pivot, U's next entry, multiplier, y
     unsigned sw = 0;                              // bit u: rows u and u + 1 were swapped
