@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kWave) void score_kernel(
 
 __global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
                                                        int* __restrict__ done, int S) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ctr = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) ctr[threadIdx.x] = 0;
   for (int i = blockIdx.x * kBlock + threadIdx.x; i < S; i += gridDim.x * kBlock) done[i] = 0;
 }
 
@@ -353,9 +353,11 @@ __global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
 // goes through a per-wave LDS tile [32][64 + 4] floats to meet the coalesced layout of X;
 // the next tile's U (double-buffered) is requested before the current tile's MFMAs.
 //
-// FUSED: the queue also holds pooling items (segment, K|V, chunk) that publish chunk sums and
-// count them per segment.  Items are grouped in slots of `batch` segments and the pooling
-// slots run `lead` slots ahead of the correction slots:
+// FUSED: the queues also hold pooling items (segment, K|V, chunk) that publish chunk sums and
+// count them per segment.  Workgroup b takes items from queue b mod nq, which holds the
+// segments q, q + nq, q + 2 nq, ... (one queue per XCD: a chunk is read twice on one XCD).
+// In each queue, items are grouped in slots of `batch` segments and the pooling slots run
+// `lead` slots ahead of the correction slots:
 //   P0 .. P(lead-1), C0, P(lead), C1, P(lead+1), ..., C(nb-1)
 // so a correction item only waits for pooling items taken from the queue before it; each of
 // those is held by a running workgroup that does not wait, hence every wait ends, with no
@@ -380,7 +382,7 @@ struct CorrectArgs {
   void* K_out;
   void* V_out;
   float* next_partials;    // chunk sums of the output, or null
-  int* ctr;                // work counter
+  int* ctr;                // work counters, one per queue
   float* pool_partials;    // fused: [2][S][n_chunks][D] chunk sums of the source
   int* done;               // fused: [S] items pooled, then n_ci + 1 (matched) or
                            //        n_ci + 2 (matched, fallback)
@@ -391,6 +393,7 @@ struct CorrectArgs {
   float tau;
   int T, S, A, r, rp, n_chunks, n_items;
   int batch, lead;         // fused: segments per slot, pooling slots ahead of correction
+  int nq;                  // fused: queues (workgroup b serves queue b mod nq)
 };
 
 // Bounded wait of a correction item of the fused form: 0.2 s of the 100 MHz constant clock.
@@ -455,18 +458,25 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   const bool uvec = FIX || (r % VEC) == 0;
   const int n_ci = 2 * n_chunks;             // items per segment
 
-  if (threadIdx.x == 0) s_item = atomicAdd(args.ctr, 1);
+  // this workgroup's queue, its segments (q, q + nq, ...) and its item count
+  const int nq = FUSED ? args.nq : 1;
+  const int q = FUSED ? (int)(blockIdx.x % nq) : 0;
+  int* const ctr = args.ctr + q;
+  const int Sq = FUSED ? (S - q + nq - 1) / nq : S;
+  const int nbq = FUSED ? (Sq + args.batch - 1) / args.batch : 0;
+  const int n_items = FUSED ? 2 * nbq * args.batch * n_ci : args.n_items;
+  if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
   __syncthreads();
   int item = __builtin_amdgcn_readfirstlane(s_item);
   for (;;) {
     // lane-derived values are recomputed per item (kept out of the loop-carried registers)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    if (item >= args.n_items) break;
+    if (item >= n_items) break;
     // the next item is requested now and read at the end of this one (the counter's round
     // trip overlaps the item)
     int nxt = 0;
-    if (tid == 0) nxt = atomicAdd(args.ctr, 1);
+    if (tid == 0) nxt = atomicAdd(ctr, 1);
     {
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     if constexpr (FUSED) {
       const int per_slot = args.batch * n_ci;
       const int k = item / per_slot, o = item - k * per_slot;
-      const int nb = (S + args.batch - 1) / args.batch;
+      const int nb = nbq;
       const int ld = min(args.lead, nb);
       int b;
       if (k < ld) {
@@ -498,9 +508,10 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
           b = paired + (kk - 2 * paired);
         }
       }
-      s = b * args.batch + o / n_ci;
+      const int sq = b * args.batch + o / n_ci;  // segment within the queue
       ci = o - (o / n_ci) * n_ci;
-      if (s >= S) goto next_item;  // padding of the last slot
+      if (sq >= Sq) goto next_item;  // padding of the last slot
+      s = q + nq * sq;
     } else {
       s = item / n_ci;
       ci = item - s * n_ci;
@@ -678,8 +689,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             for (int j = 0; j < JN; ++j) {
               const int tok = t0 + TPI * j + lrow;
               if (tok < T) {
-                if (store)
-                  *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = xr[tl].v[h][j];
+                if (store)  // non-temporal: the output is not read again by this kernel
+                  __builtin_nontemporal_store(
+                      xr[tl].v[h][j], reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol));
                 if constexpr (POOL_OUT) {
                   float fv[VEC];
                   unpack_in<Tr>(xr[tl].v[h][j], fv);
@@ -794,7 +806,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
             const u32x4 o = pack_out<Tr>(dv);
             if (full || tok < T) {
-              *reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol) = o;
+              __builtin_nontemporal_store(  // L2 keeps the source for the second read
+                  o, reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol));
               if constexpr (POOL_OUT) {
                 float fo[VEC];
                 unpack_in<Tr>(o, fo);
@@ -935,17 +948,17 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   if (lds > 48 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  int want = a.n_items;
+  const int want = L.fused ? 2 * L.S * 2 * a.n_chunks : a.n_items;
+  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
+  a.nq = 1;
   if (L.fused) {
     a.batch = fused_batch(a.n_chunks);
     a.lead = kFusedLead;
-    a.n_items = 2 * ceil_div(L.S, a.batch) * a.batch * 2 * a.n_chunks;
-    want = 2 * L.S * 2 * a.n_chunks;
+    a.nq = grid < kMaxQueues ? grid : kMaxQueues;  // every queue is served
     hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(kBlock), 0, st, L.ctr, L.done, L.S);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
   hipLaunchKernelGGL(k, dim3(grid), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }

@@ -37,12 +37,18 @@ inline int chunks_of(int T, int d, int dtype) {
 // the most chunks any dtype gives (workspace sizes do not depend on the dtype)
 inline int max_chunks_of(int T) { return T > 0 ? ceil_div(T, kRowsPerPass) : 1; }
 
-// Fused correction queue: about 128 work items per slot, pooling 4 slots ahead.
+// Fused correction: one queue per XCD (workgroup b serves queue b mod nq, the XCD that the
+// round-robin dispatch places it on) holding the segments s with s mod nq equal to it, so a
+// chunk's pooling and correction items run on one XCD and the second read of K and V can
+// hit that XCD's L2.  Each queue has slots of about kFusedSlotItems items (whole segments)
+// and pools kFusedLead slots ahead of its correction items.
+constexpr int kMaxQueues = 8;
+constexpr int kFusedSlotItems = 16;
+constexpr int kFusedLead = 6;
 inline int fused_batch(int n_chunks) {
   const int n_ci = 2 * n_chunks;
-  return n_ci >= 128 ? 1 : 128 / n_ci;
+  return n_ci >= kFusedSlotItems ? 1 : kFusedSlotItems / n_ci;
 }
-constexpr int kFusedLead = 4;
 
 // ---------------------------------------------------------------- correction workspace
 struct CorrectLayout {
@@ -53,7 +59,7 @@ struct CorrectLayout {
   size_t off_w;       // float [S][A]
   size_t off_mask;    // uint8 [S]
   size_t off_done;    // int [S]: per-segment counters of the fused pass
-  size_t off_ctr;     // int [1]: work counter of the correction pass
+  size_t off_ctr;     // int [kMaxQueues]: work counters of the correction pass
   size_t bytes;
 };
 
@@ -71,7 +77,7 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_w = o;     o = align_up(o + sizeof(float) * (size_t)c.S * A, 256);
   c.off_mask = o;  o = align_up(o + (size_t)c.S, 256);
   c.off_done = o;  o = align_up(o + sizeof(int) * (size_t)c.S, 256);
-  c.off_ctr = o;   o = align_up(o + sizeof(int), 256);
+  c.off_ctr = o;   o = align_up(o + sizeof(int) * kMaxQueues, 256);
   c.bytes = o;
   return c;
 }

@@ -88,10 +88,17 @@ def copy_probe(dev, nbytes: int = 1 << 30, reps: int = 3):
     counters (FETCH_SIZE, WRITE_SIZE) for the same profiler run."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
+    b.copy_(a)  # untimed first touch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         b.copy_(a)
+    e1.record()
     torch.cuda.synchronize()
-    log(f"[bench] copy probe: {reps} x {nbytes} bytes")
+    ms = e0.elapsed_time(e1) / reps
+    log(f"[bench] copy probe: {reps} x {nbytes} bytes, {ms * 1e3:.1f} us each, "
+        f"{2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s of read + write traffic")
     del a, b
 
 
@@ -275,8 +282,8 @@ def cpu_baseline_fit(delta, r, n_mat: int = 16, budget_s: float = 8.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-fit", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--only-fit32k", action="store_true",
