@@ -6,8 +6,10 @@
 // energy.  The anchor is the best rank-r approximation of delta = exact - reused, found
 // through the eigen-decomposition of its Gram matrix:
 //   gram_kernel     G partials = delta_chunk^T delta_chunk on MFMA (upper 32x32 blocks)
-//   jacobi_kernel   sum partials in fixed order, one-sided Jacobi on G in LDS, sort,
-//                   effective rank (float64 running sum), canonical signs, W, bf16 hi/lo W
+//   eig_kernel      (r <= 32) sum partials in fixed order (float64), Householder
+//                   tridiagonalisation, multisection, inverse iteration, back-transformation,
+//                   effective rank, canonical signs, W, bf16 hi/lo W
+//   jacobi_kernel   (r > 32) the same outputs from one-sided Jacobi on G in LDS
 //   project_kernel  U = delta W^T on MFMA (W split into bf16 hi + lo for bf16 deltas)
 #include <hip/hip_runtime.h>
 

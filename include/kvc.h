@@ -132,11 +132,14 @@ kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T
  * (K|V, layer, head)).  The anchor is the best rank-r approximation U W of delta (the
  * compact low-rank state of the abstract; r = r_delta of Fig. 13), computed as
  *   G = delta^T delta (float32 accumulation of exact bf16 products, fixed order),
- *   G = Q diag(lambda) Q^T by one-sided Jacobi (float32), lambda sorted descending,
+ *   G = Q diag(lambda) Q^T, lambda sorted descending: for r <= 32 by Householder
+ *     tridiagonalisation (float64), multisection for the eigenvalues (float32) and inverse
+ *     iteration for the r vectors (float64); for r > 32 by one-sided Jacobi (float32),
  *   W = first r columns of Q, as rows, each row's largest-|.| entry positive,
  *   U = delta W^T (float32 accumulation),
- * and the effective rank k = min{k >= 1 : sum_{i<k} lambda_i >= energy * sum lambda}
- * (0 for a zero delta), the running sum and compare in float64 (Figs. 2, 7(a)).
+ * and the effective rank k = min{k >= 1 : sum_{i<k} lambda_i >= energy * total} with
+ * total = sum lambda = trace G = ||delta||_F^2 (0 for a zero delta), the running sum and
+ * compare in float64 (Figs. 2, 7(a)).
  *   delta    : [M,T,d] dtype, read only
  *   r        : 1 <= r <= d
  *   energy   : in (0, 1], 0.9 in the pages

@@ -1,4 +1,4 @@
-"""GPU parity of the anchor fit (kvc_fit_anchor: Gram, Jacobi, effective rank, projection)
+"""GPU parity of the anchor fit (kvc_fit_anchor: Gram, eigensolver, effective rank, projection)
 against the fp64 oracle's truncated SVD, through the C ABI."""
 import numpy as np
 import pytest
@@ -129,3 +129,38 @@ def test_vl_t9216_fit_full_size():
 
 def test_chain_t32768_fit_full_size():
     _full_fit(synth.CONFIGS["chain_t32768"].replace(n_edges=1), 6)
+
+
+@pytest.mark.parametrize("d,T,r,M,flat", [
+    (128, 700, 32, 4, False),   # effective rank within the r largest
+    (128, 600, 4, 3, True),     # flat spectrum: effective rank far above r
+    (64, 900, 16, 3, False),
+    (64, 500, 2, 2, True),
+])
+def test_fit_without_eigenvalues_matches(d, T, r, M, flat):
+    """Without eigenvalue output only the r largest are bracketed unless the effective rank
+    needs more; U, W and k_eff must not depend on that."""
+    say(f"[fit] want_eig False vs True: d={d} T={T} r={r} M={M} flat={flat}")
+    g = torch.Generator().manual_seed(T + r)
+    if flat:
+        x = torch.randn(M, T, d, generator=g, dtype=torch.float64)
+    else:
+        k = min(T, d)
+        x = torch.empty(M, T, d, dtype=torch.float64)
+        for m in range(M):
+            P, _ = torch.linalg.qr(torch.randn(T, k, generator=g, dtype=torch.float64))
+            Q, _ = torch.linalg.qr(torch.randn(d, k, generator=g, dtype=torch.float64))
+            x[m] = (P * (4.0 * 0.8 ** torch.arange(k, dtype=torch.float64))) @ Q.T
+    delta = x.to(torch.bfloat16).to(dev())
+    a = kvc.fit_anchor(delta, r=r, want_eig=True)
+    b = kvc.fit_anchor(delta, r=r, want_eig=False)
+    torch.cuda.synchronize()
+    assert b.eig is None
+    assert torch.equal(a.U, b.U) and torch.equal(a.W, b.W) and torch.equal(a.k_eff, b.k_eff)
+    dh = synth.to_f64(delta.cpu())
+    ref = oracle.fit_anchor(dh, r)
+    ok = energy_margin(ref["eig"], 0.9) > 1e-4
+    assert ok.any()
+    np.testing.assert_array_equal(b.k_eff.cpu().numpy()[ok], ref["k_eff"][ok])
+    if flat:
+        assert np.all(ref["k_eff"] > r)
