@@ -79,6 +79,16 @@ def test_small_shapes(dtype, d, T, A, r):
     _run_full(cfg)
 
 
+@pytest.mark.parametrize("L,H,T", [(1, 13, 2048), (3, 3, 1500), (5, 7, 300)])
+def test_segment_counts_not_a_multiple_of_the_queues(L, H, T):
+    """The fused form spreads segments over up to eight queues (segment s to queue s mod 8);
+    segment counts that leave queues uneven or empty must not change any result."""
+    base = synth.CONFIGS["llama8b_t2048"]
+    cfg = base.replace(name=f"queues_{L}x{H}_{T}", L=L, H=H, T=T, seed=2000 + L * H + T,
+                       fallback_prob=0.3)
+    _run_full(cfg)
+
+
 def test_fallback_sources_are_copied_bit_exact():
     cfg = synth.CONFIGS["llama8b_t2048"].replace(L=3, H=2, T=700, seed=77, fallback_prob=0.5)
     case, out, ref = _run_full(cfg, K_fb=True)
