@@ -545,6 +545,15 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
   return __builtin_bit_cast(double, o);
 }
 
+// a value that is the same on every lane, moved to scalar registers
+__device__ __forceinline__ double uniform_d(double v) {
+  const int2 h = __builtin_bit_cast(int2, v);
+  int2 o;
+  o.x = __builtin_amdgcn_readfirstlane(h.x);
+  o.y = __builtin_amdgcn_readfirstlane(h.y);
+  return __builtin_bit_cast(double, o);
+}
+
 // wavefront sum in a fixed order (rows of 16 lanes, then the four rows); uniform result
 __device__ __forceinline__ double wave_sum_d(double v) {
   v = group_sum_d<16>(v);
@@ -632,6 +641,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   __shared__ float lamd[D];  // eigenvalues, descending
   __shared__ float df[D], e2f[D];
   __shared__ double coef[kEigMaxR];
+  __shared__ double wyT[D / 4][16];  // per block of four reflectors: T (10), then column dots
   const int m = blockIdx.x, tid = threadIdx.x;
 
   // ---- G = sum of the partials (fixed split order, float64), lower triangle
@@ -842,6 +852,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
       if (tid == 0) {
         ee[D - 2] = xs[D - 1];
         tau[D - 2] = 0.0;
+        tau[D - 1] = 0.0;
         ee[D - 1] = 0.0;
       }
       if (R0 == D - TR && C0 == 30) dd[D - 1] = g[TR - 1][TC - 1] - 2.0 * vl * wl;  // column D - 1
@@ -934,7 +945,9 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
             const bool swp = fabs(na) > fabs(cb);
             const double piv = swp ? na : cb, oth = swp ? cb : na;
             const double pg = fabs(piv) > tiny ? piv : (piv < 0.0 ? -tiny : tiny);
-            const double rp = 1.0 / pg;
+            double rp = __builtin_amdgcn_rcp(pg);  // 1 / pivot, two Newton steps
+            rp = rp * fma(-pg, rp, 2.0);
+            rp = rp * fma(-pg, rp, 2.0);
             const double mlt = oth * rp;
             const double c1 = swp ? nb : cc, yj = swp ? ny : ry;
             const double nry = swp ? ry - mlt * ny : ny - mlt * ry;
@@ -1001,21 +1014,64 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
     for (int u = 0; u < RPL; ++u) z[u] = s2 * Ry[u];
   }
 
-  // ---- back-transformation z = H_0 H_1 ... H_{D-3} y on the same lanes
-  for (int k = D - 3; k >= 0; --k) {
-    const double tk = tau[k];
-    if (tk == 0.0) continue;  // uniform
-    double pv[RPL];
-    double s = 0.0;
-#pragma unroll
-    for (int u = 0; u < RPL; ++u) {
-      const int j = L * RPL + u;
-      pv[u] = j > k ? P[pk(j, k)] : 0.0;
-      s += pv[u] * z[u];
+  // ---- back-transformation z = H_0 H_1 ... H_{D-3} y on the same lanes, four reflectors at a
+  //      time: Q_b = H_{4b} H_{4b+1} H_{4b+2} H_{4b+3} = I - V T V^T with T upper triangular
+  //      (forward accumulation: T_ii = t_i, T(0:i, i) = -t_i T(0:i, 0:i) V(:, 0:i)^T v_i), so
+  //      one 16-lane reduction serves four reflectors.  Column dots first (one per thread).
+  {
+    constexpr int NBK = D / 4;
+    for (int e = tid; e < 6 * NBK; e += kEigBlock) {
+      const int b = e / 6, p = e % 6;
+      const int i = p < 3 ? 0 : (p < 5 ? 1 : 2);
+      const int j = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+      const int ki = 4 * b + i, kj = 4 * b + j;
+      double c = 0.0;
+      for (int row = kj + 1; row < D; ++row) c += P[pk(row, ki)] * P[pk(row, kj)];
+      wyT[b][10 + p] = c;
     }
-    s = group_sum_d<16>(s) * tk;
+    __syncthreads();
+    if (tid < NBK) {
+      const int b = tid;
+      double* T = wyT[b];
+      const double t0 = tau[4 * b], t1 = tau[4 * b + 1], t2 = tau[4 * b + 2], t3 = tau[4 * b + 3];
+      const double c01 = T[10], c02 = T[11], c03 = T[12], c12 = T[13], c13 = T[14], c23 = T[15];
+      const double T01 = -t1 * (t0 * c01);
+      const double T02 = -t2 * (t0 * c02 + T01 * c12), T12 = -t2 * (t1 * c12);
+      const double T03 = -t3 * (t0 * c03 + T01 * c13 + T02 * c23);
+      const double T13 = -t3 * (t1 * c13 + T12 * c23), T23 = -t3 * (t2 * c23);
+      T[0] = t0; T[1] = T01; T[2] = T02; T[3] = T03;
+      T[4] = t1; T[5] = T12; T[6] = T13;
+      T[7] = t2; T[8] = T23;
+      T[9] = t3;
+    }
+    __syncthreads();
+    for (int b = NBK - 1; b >= 0; --b) {
+      const double* T = wyT[b];
+      double pv[4][RPL], sv[4];
 #pragma unroll
-    for (int u = 0; u < RPL; ++u) z[u] -= s * pv[u];
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * b + i;
+        sv[i] = 0.0;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+          const int j = L * RPL + u;
+          pv[i][u] = j > k ? P[pk(j, k)] : 0.0;
+          sv[i] = fma(pv[i][u], z[u], sv[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = group_sum_d<16>(sv[i]);
+      double Tq[10];  // uniform: scalar registers
+#pragma unroll
+      for (int q = 0; q < 10; ++q) Tq[q] = uniform_d(T[q]);
+      const double u0 = Tq[0] * sv[0] + Tq[1] * sv[1] + Tq[2] * sv[2] + Tq[3] * sv[3];
+      const double u1 = Tq[4] * sv[1] + Tq[5] * sv[2] + Tq[6] * sv[3];
+      const double u2 = Tq[7] * sv[2] + Tq[8] * sv[3];
+      const double u3 = Tq[9] * sv[3];
+#pragma unroll
+      for (int u = 0; u < RPL; ++u)
+        z[u] -= pv[0][u] * u0 + pv[1][u] * u1 + pv[2][u] * u2 + pv[3][u] * u3;
+    }
   }
   __syncthreads();  // P (reflectors) is no longer read: it holds the vectors from here on
   double* Z = P;    // [r][D]

@@ -123,7 +123,7 @@ struct FitLayout {
   size_t bytes;
 };
 
-inline FitLayout fit_layout(int M, int T, int d, int r, int target_wgs = 2048) {
+inline FitLayout fit_layout(int M, int T, int d, int r, int target_wgs = 1024) {
   FitLayout f{};
   f.M = M; f.T = T; f.d = d; f.r = r;
   f.rpad = (r + 31) / 32 * 32;
