@@ -33,6 +33,9 @@ __all__ = [
     "correct_workspace_bytes",
     "chain_workspace_bytes",
     "fit_workspace_bytes",
+    "gram_accumulate",
+    "fit_from_gram",
+    "project",
     "KVC_BF16",
     "KVC_F32",
 ]
@@ -70,6 +73,11 @@ _SIGS = {
     "kvc_fit_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_fit_anchor": (_i, [_vp, _i, _i, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                             _sz, _vp]),
+    "kvc_gram_workspace_bytes": (_sz, [_i, _i, _i]),
+    "kvc_gram_accumulate": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "kvc_fit_from_gram": (_i, [_vp, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp]),
+    "kvc_project_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "kvc_project": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _vp, _vp, _sz, _vp]),
 }
 
 _LIB = None
@@ -262,7 +270,7 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
 
 @dataclasses.dataclass
 class FitResult:
-    U: torch.Tensor  # float32 [M, T, r]
+    U: Optional[torch.Tensor]  # float32 [M, T, r] (None from fit_from_gram)
     W: torch.Tensor  # float32 [M, r, d]
     k_eff: torch.Tensor  # int32 [M]
     eig: Optional[torch.Tensor] = None  # float32 [M, d], descending
@@ -283,3 +291,53 @@ def fit_anchor(delta: torch.Tensor, r: int = 32, energy: float = 0.9, *, want_ei
     _check(lib().kvc_fit_anchor(_ptr(delta), M, T, d, dt, int(r), float(energy), _ptr(U),
                                 _ptr(W), _ptr(k), _ptr(eig), _ptr(ws), ws.numel(), _stream(dev)))
     return FitResult(U, W, k, eig)
+
+
+def gram_accumulate(delta: torch.Tensor, G: Optional[torch.Tensor] = None, *,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """G += delta^T delta for a block of rows delta [M, T, d]; G float64 [M, d, d] (a new zero
+    G when None).  See kvc_gram_accumulate in include/kvc.h."""
+    M, T, d = delta.shape
+    dev = delta.device
+    dt = _dtype_code(delta)
+    _need(delta, "delta", (M, T, d), delta.dtype, dev)
+    if G is None:
+        G = torch.zeros(M, d, d, dtype=torch.float64, device=dev)
+    _need(G, "G", (M, d, d), torch.float64, dev)
+    ws = workspace if workspace is not None else _workspace(
+        lib().kvc_gram_workspace_bytes(M, T, d), dev)
+    _check(lib().kvc_gram_accumulate(_ptr(delta), M, T, d, dt, _ptr(G), _ptr(ws), ws.numel(),
+                                     _stream(dev)))
+    return G
+
+
+def fit_from_gram(G: torch.Tensor, r: int = 32, energy: float = 0.9, *,
+                  want_eig: bool = True) -> FitResult:
+    """W, k_eff (and eigenvalues) from an accumulated Gram matrix G float64 [M, d, d]; U is
+    None (see project).  See kvc_fit_from_gram in include/kvc.h."""
+    M, d, _ = G.shape
+    dev = G.device
+    _need(G, "G", (M, d, d), torch.float64, dev)
+    W = torch.empty(M, r, d, dtype=torch.float32, device=dev)
+    k = torch.empty(M, dtype=torch.int32, device=dev)
+    eig = torch.empty(M, d, dtype=torch.float32, device=dev) if want_eig else None
+    _check(lib().kvc_fit_from_gram(_ptr(G), M, d, int(r), float(energy), _ptr(W), _ptr(k),
+                                   _ptr(eig), _stream(dev)))
+    return FitResult(None, W, k, eig)
+
+
+def project(delta: torch.Tensor, W: torch.Tensor, *,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """U = delta W^T for delta [M, T, d] and W float32 [M, r, d].  See kvc_project."""
+    M, T, d = delta.shape
+    r = W.shape[1]
+    dev = delta.device
+    dt = _dtype_code(delta)
+    _need(delta, "delta", (M, T, d), delta.dtype, dev)
+    _need(W, "W", (M, r, d), torch.float32, dev)
+    U = torch.empty(M, T, r, dtype=torch.float32, device=dev)
+    need = lib().kvc_project_workspace_bytes(M, d, r, dt)
+    ws = workspace if workspace is not None else (_workspace(need, dev) if need else None)
+    _check(lib().kvc_project(_ptr(delta), M, T, d, dt, _ptr(W), r, _ptr(U), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(dev)))
+    return U

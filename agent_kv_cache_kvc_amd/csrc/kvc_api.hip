@@ -320,4 +320,77 @@ kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int
   return ok();
 }
 
+// --------------------------------------------------------------------------- streaming fit
+static kvc_status validate_fit_shape(int M, int d, int dtype) {
+  if (M < 0) return fail(KVC_ERR_ARG, "negative size (M=%d)", M);
+  if (d <= 0) return fail(KVC_ERR_ARG, "d must be positive (d=%d)", d);
+  if (dtype != KVC_BF16 && dtype != KVC_F32) return fail(KVC_ERR_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(KVC_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", d);
+  if (M > 65535) return fail(KVC_ERR_UNSUPPORTED, "M=%d exceeds 65535 matrices", M);
+  return KVC_OK;
+}
+
+size_t kvc_gram_workspace_bytes(int M, int T, int d) {
+  if (M < 0 || T < 0 || d <= 0) return 0;
+  return kvc::gram_ws_bytes(kvc::fit_layout(M, T, d, 1));
+}
+
+kvc_status kvc_gram_accumulate(const void* delta, int M, int T, int d, int dtype,
+                               double* G_inout, void* ws, size_t ws_bytes, void* stream) {
+  KVC_TRY(validate_fit_shape(M, d, dtype));
+  if (T < 0) return fail(KVC_ERR_ARG, "negative size (T=%d)", T);
+  if ((long long)M * T > kMaxElems / (2ll * d)) return fail(KVC_ERR_ARG, "delta too large");
+  if (M == 0 || T == 0) return ok();
+  KVC_TRY(check_tensor(delta, "delta"));
+  KVC_TRY(check_tensor(G_inout, "G", 8));
+  const size_t need = kvc_gram_workspace_bytes(M, T, d);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  const kvc::FitLayout f = kvc::fit_layout(M, T, d, 1);
+  KVC_HIP(kvc::launch_gram_accumulate(delta, f, dtype, G_inout, static_cast<char*>(ws),
+                                      reinterpret_cast<hipStream_t>(stream)),
+          "gram_accumulate");
+  return ok();
+}
+
+kvc_status kvc_fit_from_gram(const double* G, int M, int d, int r, double energy, float* W_out,
+                             int32_t* k_eff_out, float* eig_out, void* stream) {
+  KVC_TRY(validate_fit_shape(M, d, KVC_F32));
+  if (r < 1 || r > d) return fail(KVC_ERR_ARG, "r=%d (need 1 <= r <= d)", r);
+  if (!(energy > 0.0 && energy <= 1.0)) return fail(KVC_ERR_ARG, "energy must be in (0, 1]");
+  if (M == 0) return ok();
+  KVC_TRY(check_tensor(G, "G", 8));
+  KVC_TRY(check_tensor(W_out, "W_out"));
+  KVC_TRY(check_tensor(k_eff_out, "k_eff_out", 4));
+  if (eig_out) KVC_TRY(check_tensor(eig_out, "eig_out", 4));
+  KVC_HIP(kvc::launch_fit_from_gram(G, M, d, r, energy, W_out, k_eff_out, eig_out,
+                                    reinterpret_cast<hipStream_t>(stream)),
+          "fit_from_gram");
+  return ok();
+}
+
+size_t kvc_project_workspace_bytes(int M, int d, int r, int dtype) {
+  if (M < 0 || d <= 0 || r < 1) return 0;
+  return kvc::project_ws_bytes(M, d, r, dtype);
+}
+
+kvc_status kvc_project(const void* delta, int M, int T, int d, int dtype, const float* W, int r,
+                       float* U_out, void* ws, size_t ws_bytes, void* stream) {
+  KVC_TRY(validate_fit_shape(M, d, dtype));
+  if (T < 0) return fail(KVC_ERR_ARG, "negative size (T=%d)", T);
+  if (r < 1 || r > d) return fail(KVC_ERR_ARG, "r=%d (need 1 <= r <= d)", r);
+  if ((long long)M * T > kMaxElems / (2ll * d)) return fail(KVC_ERR_ARG, "delta too large");
+  if (M == 0 || T == 0) return ok();
+  KVC_TRY(check_tensor(delta, "delta"));
+  KVC_TRY(check_tensor(W, "W"));
+  KVC_TRY(check_tensor(U_out, "U_out"));
+  const size_t need = kvc_project_workspace_bytes(M, d, r, dtype);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  KVC_HIP(kvc::launch_project(delta, M, T, d, dtype, W, r, U_out, static_cast<char*>(ws),
+                              reinterpret_cast<hipStream_t>(stream)),
+          "project");
+  return ok();
+}
+
 }  // extern "C"

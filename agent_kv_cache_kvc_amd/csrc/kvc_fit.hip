@@ -246,7 +246,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 template <int D>
 __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
-    const float* __restrict__ partials, int nsplit, int r, double energy, float tol, float eta,
+    const float* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
+    double energy, float tol, float eta,
     float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
     uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad,
     int* __restrict__ sweeps_out) {
@@ -272,7 +273,16 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   // ---- G = sum of the partials (fixed order), mirrored to a full symmetric matrix
   const float* P = partials + (size_t)m * nsplit * NBLK * 1024;
   float fro = 0.f;
-  for (int e = tid; e < NBLK * 1024; e += kJacobiBlock) {
+  if (G_in != nullptr) {  // G as given (float64, full symmetric)
+    const double* Gm = G_in + (size_t)m * D * D;
+    for (int e = tid; e < D * D; e += kJacobiBlock) {
+      const int row = e / D, col = e % D;
+      const float v = (float)Gm[e];
+      Am[col * CS + jrow(row)] = v;
+      fro += v * v;
+    }
+  }
+  for (int e = tid; G_in == nullptr && e < NBLK * 1024; e += kJacobiBlock) {
     const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
     int I = 0, rem = blk;
     while (rem >= NB - I) { rem -= NB - I; ++I; }
@@ -628,9 +638,10 @@ __device__ float multisect(int ev, float lo, float hi, const float* df, const fl
 
 template <int D>
 __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
-    const float* __restrict__ partials, int nsplit, int r, double energy,
-    float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
-    uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad) {
+    const float* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
+    double energy, float* __restrict__ W_out, float* __restrict__ eig_out,
+    int32_t* __restrict__ k_eff_out, uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
+    int rpad) {
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int NW = kEigBlock / kWave;
@@ -644,8 +655,14 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   __shared__ double wyT[D / 4][16];  // per block of four reflectors: T (10), then column dots
   const int m = blockIdx.x, tid = threadIdx.x;
 
-  // ---- G = sum of the partials (fixed split order, float64), lower triangle
-  {
+  // ---- G = sum of the partials (fixed split order, float64), lower triangle; or G as given
+  if (G_in != nullptr) {
+    const double* Gm = G_in + (size_t)m * D * D;
+    for (int e = tid; e < D * D; e += kEigBlock) {
+      const int row = e / D, col = e % D;
+      if (col <= row) P[pk(row, col)] = Gm[e];
+    }
+  } else {
     const float* Pm = partials + (size_t)m * nsplit * NBLK * 1024;
     constexpr int PER = NBLK * 1024 / kEigBlock;  // 20 (D = 128) or 6 (D = 64)
     constexpr int U4 = 4;
@@ -1340,7 +1357,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
     allow_dynamic_lds(eig_kernel<D>, lds);
     hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
-                       f.nsplit, f.r, energy, W_out, eig, k_eff,
+                       f.nsplit, (const double*)nullptr, f.r, energy, W_out, eig, k_eff,
                        dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
                        f.rpad);
   } else {
@@ -1348,7 +1365,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     allow_dynamic_lds(jacobi_kernel<D>, lds);
     const float tol = 2e-6f, eta = 1e-12f;
     hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials,
-                       f.nsplit, f.r, energy, tol, eta, W_out, eig, k_eff,
+                       f.nsplit, (const double*)nullptr, f.r, energy, tol, eta, W_out, eig, k_eff,
                        dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
                        f.rpad, sweeps);
   }
@@ -1363,6 +1380,131 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     hipLaunchKernelGGL((project_f32_kernel<D>), g3, dim3(kBlock), 0, st, (const float*)delta,
                        W_out, f.T, f.r, f.rpad, U_out);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- streaming fit
+// G += delta^T delta from the Gram partials of one block of rows: each element of the upper
+// blocks is summed over the splits in fixed order (float64, from 0) and added to both
+// triangles of G, so a block accumulated onto G = 0 gives exactly the G of the one-call fit.
+template <int D>
+__global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const float* __restrict__ partials,
+                                                               int nsplit,
+                                                               double* __restrict__ G) {
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  const int m = blockIdx.y, e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= NBLK * 1024) return;
+  const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
+  int I = 0, rem = blk;
+  while (rem >= NB - I) { rem -= NB - I; ++I; }
+  const int J = I + rem;
+  const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
+  const int col = J * 32 + (l % 32);
+  if (row > col) return;  // a diagonal block's lower half holds no new element
+  const float* Pm = partials + (size_t)m * nsplit * NBLK * 1024 + e;
+  double v = 0.0;
+  for (int sp = 0; sp < nsplit; ++sp) v += (double)Pm[(size_t)sp * NBLK * 1024];
+  double* Gm = G + (size_t)m * D * D;
+  Gm[row * D + col] += v;
+  if (row != col) Gm[col * D + row] += v;
+}
+
+// W (float32, [M][r][D]) -> bf16 hi + lo rows for the projection ([M][rpad][D], rows >= r zero)
+template <int D>
+__global__ __launch_bounds__(kBlock) void split_w_kernel(const float* __restrict__ W, int r,
+                                                       int rpad, uint16_t* __restrict__ w_hi,
+                                                       uint16_t* __restrict__ w_lo) {
+  const int m = blockIdx.y;
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= rpad * D) return;
+  const int k = e / D;
+  const float wv = k < r ? W[(size_t)m * r * D + e] : 0.f;
+  const uint16_t hi = f32_to_bf16(wv);
+  w_hi[(size_t)m * rpad * D + e] = hi;
+  w_lo[(size_t)m * rpad * D + e] = f32_to_bf16(wv - bf16_to_f32(hi));
+}
+
+template <int D>
+static hipError_t gram_t(const void* delta, const FitLayout& f, int dtype, double* G, char* ws,
+                         hipStream_t st) {
+  constexpr int NBLK = (D / 32) * (D / 32 + 1) / 2;
+  float* partials = reinterpret_cast<float*>(ws + f.off_gram);
+  const dim3 g1(f.nsplit, f.M);
+  if (dtype == KVC_BF16)
+    hipLaunchKernelGGL((gram_bf16_kernel<D>), g1, dim3(kBlock), 0, st,
+                       (const uint16_t*)delta, f.T, f.chunk, partials);
+  else
+    hipLaunchKernelGGL((gram_f32_kernel<D>), g1, dim3(kBlock), 0, st, (const float*)delta,
+                       f.T, f.chunk, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gram_accumulate_kernel<D>), dim3(NBLK * 1024 / kBlock, f.M), dim3(kBlock),
+                     0, st, partials, f.nsplit, G);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t eig_from_gram_t(const double* G, int M, int r, double energy, float* W_out,
+                                  int32_t* k_eff, float* eig, hipStream_t st) {
+  const int rpad = (r + 31) / 32 * 32;
+  if (r <= kEigMaxR) {
+    const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
+    allow_dynamic_lds(eig_kernel<D>, lds);
+    hipLaunchKernelGGL((eig_kernel<D>), dim3(M), dim3(kEigBlock), lds, st,
+                       (const float*)nullptr, 0, G, r, energy, W_out, eig, k_eff,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, rpad);
+  } else {
+    const size_t lds = (size_t)D * (D + 4) * sizeof(float);
+    allow_dynamic_lds(jacobi_kernel<D>, lds);
+    const float tol = 2e-6f, eta = 1e-12f;
+    hipLaunchKernelGGL((jacobi_kernel<D>), dim3(M), dim3(kJacobiBlock), lds, st,
+                       (const float*)nullptr, 0, G, r, energy, tol, eta, W_out, eig, k_eff,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, rpad, (int*)nullptr);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t project_t(const void* delta, int M, int T, int dtype, const float* W, int r,
+                            float* U_out, char* ws, hipStream_t st) {
+  const int rpad = (r + 31) / 32 * 32;
+  const int n_tiles = ceil_div(T, kRowsPerPass * kProjIters);
+  const dim3 g3(n_tiles, M);
+  if (dtype == KVC_BF16) {
+    uint16_t* whi = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* wlo = whi + (size_t)M * rpad * D;
+    hipLaunchKernelGGL((split_w_kernel<D>), dim3(ceil_div(rpad * D, kBlock), M), dim3(kBlock),
+                       0, st, W, r, rpad, whi, wlo);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((project_bf16_kernel<D>), g3, dim3(kBlock), 0, st,
+                       (const uint16_t*)delta, whi, wlo, T, r, rpad, U_out);
+  } else {
+    hipLaunchKernelGGL((project_f32_kernel<D>), g3, dim3(kBlock), 0, st, (const float*)delta, W,
+                       T, r, rpad, U_out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_accumulate(const void* delta, const FitLayout& f, int dtype, double* G,
+                                  char* ws, hipStream_t st) {
+  if (f.M == 0 || f.T == 0) return hipSuccess;
+  return f.d == 128 ? gram_t<128>(delta, f, dtype, G, ws, st)
+                    : gram_t<64>(delta, f, dtype, G, ws, st);
+}
+
+hipError_t launch_fit_from_gram(const double* G, int M, int d, int r, double energy,
+                                float* W_out, int32_t* k_eff, float* eig, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  return d == 128 ? eig_from_gram_t<128>(G, M, r, energy, W_out, k_eff, eig, st)
+                  : eig_from_gram_t<64>(G, M, r, energy, W_out, k_eff, eig, st);
+}
+
+hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
+                          int r, float* U_out, char* ws, hipStream_t st) {
+  if (M == 0 || T == 0) return hipSuccess;
+  return d == 128 ? project_t<128>(delta, M, T, dtype, W, r, U_out, ws, st)
+                  : project_t<64>(delta, M, T, dtype, W, r, U_out, ws, st);
 }
 
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,

@@ -160,5 +160,18 @@ hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
                       float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                       hipStream_t st);
+// Streaming fit: G += delta^T delta (float64, full symmetric) through the Gram partials of
+// the workspace (FitLayout off_gram); eigensolver from a given G; projection U = delta W^T
+// (bf16 deltas stage W as bf16 hi/lo in ws: 2 * M * rpad * d * 2 bytes).
+hipError_t launch_gram_accumulate(const void* delta, const FitLayout& f, int dtype, double* G,
+                                  char* ws, hipStream_t st);
+hipError_t launch_fit_from_gram(const double* G, int M, int d, int r, double energy,
+                                float* W_out, int32_t* k_eff, float* eig, hipStream_t st);
+hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
+                          int r, float* U_out, char* ws, hipStream_t st);
+inline size_t gram_ws_bytes(const FitLayout& f) { return f.off_whi; }  // partials lead
+inline size_t project_ws_bytes(int M, int d, int r, int dtype) {
+  return dtype == KVC_BF16 ? 2ull * 2ull * M * ((r + 31) / 32 * 32) * d : 0;
+}
 
 }  // namespace kvc

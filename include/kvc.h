@@ -152,6 +152,38 @@ kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int
                           double energy, float* U_out, float* W_out, int32_t* k_eff_out,
                           float* eig_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Streaming fit for a growing shared context (the dynamically changing context of the
+ * abstract; generated tokens accumulating over turns, listing Figs. 10-11): the Gram matrix
+ * of a delta is accumulated block by block as rows are appended, and the anchor is refit
+ * from it.  With G accumulated over all rows of delta, kvc_fit_from_gram + kvc_project give
+ * the same W, k_eff and U as kvc_fit_anchor (bit for bit for r <= 32 when delta was
+ * accumulated in one call onto G = 0).
+ *
+ * kvc_gram_accumulate: G += delta^T delta for a block of rows.
+ *   delta   : [M,T,d] dtype, read only (the appended rows; T = 0 leaves G unchanged)
+ *   G_inout : [M,d,d] float64, full symmetric, 8-byte aligned; the caller zeroes it first
+ *             (products of the inputs are exact, summed in float32 per split of T, the
+ *             splits in a fixed order in float64)
+ *   ws      : at least kvc_gram_workspace_bytes(M,T,d) bytes, 256-byte aligned
+ * kvc_fit_from_gram: eigen-decomposition of G and the factors of kvc_fit_anchor.
+ *   G       : [M,d,d] float64 as accumulated; r, energy, W_out, k_eff_out, eig_out as in
+ *             kvc_fit_anchor (no workspace)
+ * kvc_project: U = delta W^T for any block of rows (e.g. only the appended ones).
+ *   W       : [M,r,d] float32 (from kvc_fit_from_gram or kvc_fit_anchor)
+ *   U_out   : [M,T,r] float32
+ *   ws      : kvc_project_workspace_bytes(M,d,r,dtype) bytes (0 for float32 deltas: NULL ok)
+ * Errors as for kvc_fit_anchor; nothing is enqueued when validation fails.
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_gram_workspace_bytes(int M, int T, int d);
+kvc_status kvc_gram_accumulate(const void* delta, int M, int T, int d, int dtype,
+                               double* G_inout, void* ws, size_t ws_bytes, void* stream);
+kvc_status kvc_fit_from_gram(const double* G, int M, int d, int r, double energy, float* W_out,
+                             int32_t* k_eff_out, float* eig_out, void* stream);
+size_t kvc_project_workspace_bytes(int M, int d, int r, int dtype);
+kvc_status kvc_project(const void* delta, int M, int T, int d, int dtype, const float* W, int r,
+                       float* U_out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

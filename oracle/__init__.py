@@ -9,7 +9,10 @@ from .kvc_oracle import (  # noqa: F401
     cosine_scores,
     effective_rank,
     fit_anchor,
+    fit_from_gram,
+    gram,
     pool,
+    project,
     reliability,
     rel_frobenius,
     round_to_bf16,

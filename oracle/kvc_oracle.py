@@ -280,6 +280,41 @@ def fit_anchor(delta, r: int, energy: float = 0.9) -> dict:
     return {"U": U, "W": W, "k_eff": effective_rank(eig, energy), "eig": eig}
 
 
+def gram(delta) -> np.ndarray:
+    """G = delta^T delta per matrix, float64: the Gram matrix whose eigen-decomposition gives
+    the anchor (lambda_i = sigma_i^2).  Rows appended to delta add their own Gram matrix:
+    gram(concat(D1, D2)) = gram(D1) + gram(D2), which is what lets the fit follow a
+    growing shared context (abstract: dynamically changing context; Figs. 10-11).
+    delta: [M, T, d] -> [M, d, d]."""
+    delta = np.asarray(delta, dtype=np.float64)
+    return np.einsum("mti,mtj->mij", delta, delta)
+
+
+def fit_from_gram(G, r: int, energy: float = 0.9) -> dict:
+    """The anchor's W, effective rank and eigenvalues from an accumulated Gram matrix:
+    the symmetric eigen-decomposition of G written out (eigenvalues descending, negative
+    round-off clamped to 0; W = the top-r eigenvectors as rows, each row's
+    largest-magnitude entry positive; k_eff as in effective_rank).  G: [M, d, d]."""
+    G = np.asarray(G, dtype=np.float64)
+    M, d, _ = G.shape
+    W = np.zeros((M, r, d))
+    eig = np.zeros((M, d))
+    for m in range(M):
+        lam, vec = np.linalg.eigh(0.5 * (G[m] + G[m].T))
+        order = np.argsort(-lam, kind="stable")
+        eig[m] = np.clip(lam[order], 0.0, None)
+        W[m] = _canonical_rows(vec[:, order[:r]].T)
+    return {"W": W, "k_eff": effective_rank(eig, energy), "eig": eig}
+
+
+def project(delta, W) -> np.ndarray:
+    """U = delta W^T for any block of rows: the anchor's row factor.  delta [M, T, d],
+    W [M, r, d] -> [M, T, r]."""
+    delta = np.asarray(delta, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return np.einsum("mtd,mrd->mtr", delta, W)
+
+
 # --------------------------------------------------------------------------------------
 # metrics
 # --------------------------------------------------------------------------------------

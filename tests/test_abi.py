@@ -117,3 +117,33 @@ def test_workspace_sizes_are_monotone():
     assert 0 < a < b
     assert kvc.fit_workspace_bytes(512, 8192, 128, 32) >= kvc.fit_workspace_bytes(512, 2048, 128, 32) > 0
     assert kvc.fit_workspace_bytes(1, 8192, 128, 32) > kvc.fit_workspace_bytes(1, 128, 128, 32) > 0
+
+
+def test_streaming_fit_rejects_bad_arguments():
+    lib = kvc.lib()
+    # kvc_gram_accumulate(delta, M, T, d, dtype, G, ws, ws_bytes, stream)
+    base = dict(delta=FAKE, M=4, T=64, d=128, dtype=0, G=FAKE, ws=None, nb=0, st=None)
+    for kw, status in [(dict(d=32), 2), (dict(dtype=5), 1), (dict(M=-1), 1), (dict(T=-1), 1),
+                       (dict(delta=None), 1), (dict(G=FAKE + 4), 1), (dict(), 4)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_gram_accumulate(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_gram_accumulate(*dict(base, T=0, delta=None, G=None).values()) == 0
+    # kvc_fit_from_gram(G, M, d, r, energy, W, k, eig, stream)
+    base = dict(G=FAKE, M=4, d=128, r=32, energy=0.9, W=FAKE, k=FAKE, eig=None, st=None)
+    for kw, status in [(dict(r=0), 1), (dict(r=129), 1), (dict(energy=2.0), 1), (dict(d=96), 2),
+                       (dict(G=None), 1), (dict(W=None), 1), (dict(k=FAKE + 2), 1)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_fit_from_gram(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_fit_from_gram(*dict(base, M=0, G=None, W=None, k=None).values()) == 0
+    # kvc_project(delta, M, T, d, dtype, W, r, U, ws, ws_bytes, stream)
+    base = dict(delta=FAKE, M=4, T=64, d=128, dtype=0, W=FAKE, r=32, U=FAKE, ws=None, nb=0,
+                st=None)
+    for kw, status in [(dict(r=0), 1), (dict(d=64, r=65), 1), (dict(U=None), 1), (dict(), 4)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_project(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_project_workspace_bytes(4, 128, 32, 1) == 0  # float32 deltas need none
+    assert lib.kvc_project_workspace_bytes(4, 128, 32, 0) == 2 * 2 * 4 * 32 * 128
+    assert lib.kvc_gram_workspace_bytes(512, 8192, 128) > lib.kvc_gram_workspace_bytes(1, 128, 128) > 0

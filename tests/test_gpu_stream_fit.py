@@ -1,0 +1,117 @@
+"""GPU parity of the streaming fit (kvc_gram_accumulate, kvc_fit_from_gram, kvc_project)
+against the fp64 oracle and against the one-call fit, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import agent_kv_cache_kvc_amd as kvc
+import oracle
+import synth
+from gpu_helpers import check_fit, dev, energy_margin, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _planted_delta(M, T, d, dtype, seed, decay=0.85):
+    g = torch.Generator().manual_seed(seed)
+    k = min(T, d)
+    out = torch.empty(M, T, d, dtype=torch.float64)
+    for m in range(M):
+        P, _ = torch.linalg.qr(torch.randn(T, k, generator=g, dtype=torch.float64))
+        Q, _ = torch.linalg.qr(torch.randn(d, k, generator=g, dtype=torch.float64))
+        s = 5.0 * decay ** torch.arange(k, dtype=torch.float64)
+        out[m] = (P * s) @ Q.T + 1e-3 * torch.randn(T, d, generator=g, dtype=torch.float64)
+    return out.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("dtype,d,T,r,M", [
+    ("bf16", 128, 700, 32, 4),
+    ("f32", 64, 300, 8, 3),
+    ("bf16", 64, 1000, 16, 2),
+])
+def test_one_block_from_zero_equals_the_one_call_fit(dtype, d, T, r, M):
+    """G accumulated once onto zero is the G of kvc_fit_anchor, so W, k_eff, the eigenvalues
+    and U = delta W^T agree bit for bit."""
+    say(f"[stream] one block {dtype} d={d} T={T} r={r} M={M}")
+    delta = _planted_delta(M, T, d, dtype, 10 + T).to(dev())
+    G = kvc.gram_accumulate(delta)
+    a = kvc.fit_from_gram(G, r=r)
+    U = kvc.project(delta, a.W)
+    b = kvc.fit_anchor(delta, r=r)
+    torch.cuda.synchronize()
+    assert torch.equal(a.W, b.W) and torch.equal(a.k_eff, b.k_eff) and torch.equal(a.eig, b.eig)
+    assert torch.equal(U, b.U)
+
+
+def test_gram_matches_the_oracle():
+    delta = _planted_delta(3, 900, 128, "bf16", 7).to(dev())
+    G = kvc.gram_accumulate(delta)
+    G = kvc.gram_accumulate(delta[:, :5].contiguous(), G)  # a second block
+    torch.cuda.synchronize()
+    dh = synth.to_f64(delta.cpu())
+    ref = oracle.gram(dh) + oracle.gram(dh[:, :5])
+    got = G.cpu().numpy()
+    np.testing.assert_array_equal(got, np.swapaxes(got, 1, 2))
+    assert oracle.rel_frobenius(got, ref) < 1e-6
+
+
+@pytest.mark.parametrize("dtype,d,blocks,r,M", [
+    ("bf16", 128, (300, 1, 517, 64), 32, 3),
+    ("f32", 128, (100, 400), 40, 2),      # r > 32: the Jacobi route
+    ("bf16", 64, (16, 16, 600), 8, 2),
+])
+def test_streamed_blocks_match_the_oracle(dtype, d, blocks, r, M):
+    """Rows appended block by block: the refit from the accumulated G is the fit of all rows,
+    and U of the last block alone is its projection on the new W."""
+    say(f"[stream] blocks {blocks} {dtype} d={d} r={r} M={M}")
+    T = sum(blocks)
+    delta = _planted_delta(M, T, d, dtype, 100 + T + r)
+    dd = delta.to(dev())
+    G = None
+    t0 = 0
+    for b in blocks:
+        G = kvc.gram_accumulate(dd[:, t0:t0 + b].contiguous(), G)
+        t0 += b
+    fit = kvc.fit_from_gram(G, r=r)
+    U_all = kvc.project(dd, fit.W)
+    last = dd[:, T - blocks[-1]:].contiguous()
+    U_last = kvc.project(last, fit.W)
+    torch.cuda.synchronize()
+    dh = synth.to_f64(delta)
+    ref = oracle.fit_anchor(dh, r)
+    ok = energy_margin(ref["eig"], 0.9) > 1e-4
+    assert ok.any()
+    sel = np.nonzero(ok)[0]
+    sub = {k: v[sel] for k, v in ref.items()}
+    check_fit(f"stream-{dtype}-{d}-{r}", U_all.cpu().double().numpy()[sel],
+              fit.W.cpu().double().numpy()[sel], fit.k_eff.cpu().numpy()[sel],
+              fit.eig.cpu().double().numpy()[sel], sub, r, dh[sel])
+    # the last block's U is its own projection (same kernel, rows independent)
+    np.testing.assert_array_equal(U_last.cpu().numpy(), U_all[:, T - blocks[-1]:].cpu().numpy())
+    want = oracle.project(synth.to_f64(last.cpu()), fit.W.cpu().double().numpy())
+    assert oracle.rel_frobenius(U_last.cpu().double().numpy(), want) < 1e-5
+
+
+def test_llama8b_t8192_streamed_in_four_blocks():
+    cfg = synth.CONFIGS["llama8b_t8192_fit"]
+    say(f"[stream] {cfg.name} in 4 blocks of {cfg.T // 4}")
+    case = synth.generate(cfg, dev())
+    delta = synth.fit_input(case)
+    del case
+    torch.cuda.empty_cache()
+    M, T, d = delta.shape
+    ws = torch.empty(kvc.lib().kvc_gram_workspace_bytes(M, T // 4, d), dtype=torch.uint8,
+                     device=dev())
+    G = None
+    for i in range(4):
+        G = kvc.gram_accumulate(delta[:, i * T // 4:(i + 1) * T // 4].contiguous(), G,
+                                workspace=ws)
+    fit = kvc.fit_from_gram(G, r=cfg.r, want_eig=False)
+    one = kvc.fit_anchor(delta, r=cfg.r, want_eig=False)
+    torch.cuda.synchronize()
+    assert torch.all(fit.k_eff == 11)
+    # the same rank-32 subspace as the one-call fit: W W^T agree
+    P1 = fit.W.double().transpose(1, 2) @ fit.W.double()
+    P2 = one.W.double().transpose(1, 2) @ one.W.double()
+    err = ((P1 - P2).norm(dim=(1, 2)) / P2.norm(dim=(1, 2))).max().item()
+    assert err < 1e-3, err
