@@ -412,6 +412,28 @@ def main():
             "hbm_frac": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
         log(f"[bench] fit {ms_f:.3f} ms")
+        # streaming update: the first 6144 rows are already in G; append the last 2048
+        # (accumulate, refit from G, project only the appended rows)
+        t_old = T - 2048
+        G = kvc.gram_accumulate(delta[:, :t_old].contiguous())
+        new = delta[:, t_old:].contiguous()
+        gws = torch.empty(kvc.lib().kvc_gram_workspace_bytes(M, T - t_old, fcfg.d),
+                          dtype=torch.uint8, device=dev)
+
+        def update():
+            kvc.gram_accumulate(new, G, workspace=gws)
+            res = kvc.fit_from_gram(G, r=fcfg.r, want_eig=False)
+            return kvc.project(new, res.W)
+
+        update()
+        torch.cuda.synchronize()
+        ms_u = time_events(update, nfit, stream)
+        out["fit_stream_update"] = {
+            "workload": f"append {T - t_old} rows to the {t_old}-row Gram of {M} matrices, refit, "
+                        f"project the appended rows",
+            "ms": round(ms_u, 4), "full_refit_ms": round(ms_f, 4)}
+        log(f"[bench] streaming update {ms_u:.3f} ms (full fit {ms_f:.3f} ms)")
+        del G, new, gws
         if not args.no_cpu:
             log("[bench] cpu baseline of the fit (oracle on a sample)")
             out["cpu_baseline_fit"] = cpu_baseline_fit(delta, fcfg.r)
