@@ -334,6 +334,23 @@ def main():
     log(f"[bench] step {ms_ev:.4f} ms (wall {wall:.4f} ms), {gbs:.1f} GB/s, reuse "
         f"{1 - mask.mean():.3f}")
 
+    # the base cache's own rank-r representation and effective rank (the same fit kernels on
+    # K and V of every segment; listing Fig. 2 reports it for real model caches)
+    base = torch.stack([K, V]).reshape(2 * cfg.L * cfg.H, cfg.T, cfg.d)
+    bf = kvc.fit_anchor(base, r=cfg.r, want_eig=True)
+    torch.cuda.synchronize()
+    ms_b = time_events(lambda: kvc.fit_anchor(base, r=cfg.r, want_eig=True), 3, stream)
+    ke = bf.k_eff.cpu().numpy()
+    eigs = bf.eig.double()
+    kept = (eigs[:, :cfg.r].sum(1) / eigs.sum(1)).cpu().numpy()
+    base_rank = {"workload": f"{cfg.name} K and V caches as {base.shape[0]} matrices of "
+                             f"{cfg.T} x {cfg.d}, r={cfg.r}",
+                 "ms": round(ms_b, 4), "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)),
+                                                               int(ke.max())],
+                 "energy_kept_at_r_mean": round(float(kept.mean()), 4)}
+    log(f"[bench] base-cache fit {ms_b:.3f} ms, effective rank median {int(np.median(ke))}")
+    del base, bf, eigs
+
     # the unfused form, for reference: matching kernel from a precomputed q, then correction
     q = kvc.pool_descriptor(K, V)
     torch.cuda.synchronize()
@@ -378,6 +395,7 @@ def main():
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_detail": traffic,
                      "ms_per_launch": round(ms_ev, 5)},
+        "base_cache_rank": base_rank,
         "with_q_in": {"ms": round(ms_k, 5), "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
                       "note": "q precomputed: matching kernel + unfused correction kernel"},
     }

@@ -164,3 +164,13 @@ def test_fit_without_eigenvalues_matches(d, T, r, M, flat):
     np.testing.assert_array_equal(b.k_eff.cpu().numpy()[ok], ref["k_eff"][ok])
     if flat:
         assert np.all(ref["k_eff"] > r)
+
+
+def test_base_cache_rank_representation():
+    """The fit kernels applied to a cache itself (its rank-r representation and effective
+    rank, as the listing's Fig. 2 reports for model caches): K and V of every segment."""
+    base = synth.CONFIGS["llama8b_t2048"]
+    cfg = base.replace(name="base_rank", L=2, H=2, T=600, seed=77)
+    case = synth.generate(cfg)
+    x = torch.stack([case.K0, case.V0]).reshape(2 * cfg.L * cfg.H, cfg.T, cfg.d)
+    _fit_and_check("base-cache", x, cfg.r)
