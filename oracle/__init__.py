@@ -8,14 +8,18 @@ from .kvc_oracle import (  # noqa: F401
     correct,
     cosine_scores,
     effective_rank,
+    fanout,
     fit_anchor,
     fit_from_gram,
     gram,
+    layer_error,
     pool,
     project,
+    rank_error_curve,
     reliability,
     rel_frobenius,
     round_to_bf16,
     round_to_dtype,
+    segment_error,
     softmax_weights,
 )

@@ -204,6 +204,23 @@ def chain(K0, V0, edges, tau, dtype) -> list:
     return res
 
 
+def fanout(K, V, targets, tau, dtype) -> list:
+    """Non-chained correction: every agent corrects the same context-free reference cache.
+
+    Fig. 3 and Fig. 6 / Table 9 of the listing compare chained correction (the source is the
+    preceding agent's cache) with non-chained correction, whose source is a context-free
+    reference cache of the shared context.  Reading: agent j's cache is that reference
+    corrected with agent j's own anchors, exactly as in ``correct``; the reference itself
+    is never modified, and every agent matches the same pooled descriptor.  ``targets`` is
+    a list of dicts with keys desc, U, W and optionally K_fb, V_fb.  Returns the per-agent
+    outputs of ``correct``.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    return [correct(K, V, t["desc"], t["U"], t["W"], tau, dtype,
+                    K_fb=t.get("K_fb"), V_fb=t.get("V_fb")) for t in targets]
+
+
 # --------------------------------------------------------------------------------------
 # anchor fit
 # --------------------------------------------------------------------------------------
@@ -327,3 +344,48 @@ def rel_frobenius(x, ref) -> float:
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((x - ref).ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+def segment_error(X, ref):
+    """Per-segment sums of the Fig. 3 error: (sum (X - ref)^2, sum ref^2) over the tokens and
+    channels of every (layer, kv-head) segment, float64.  X, ref: [L, H, T, d] ->
+    two [L, H] arrays.  Fig. 3 normalises the reconstruction error by the Frobenius norm of
+    the target (the exact cache from full prefill); per-layer (Fig. 3(a)) and per-agent
+    (Fig. 3(b)) errors are square roots of ratios of sums of these."""
+    X = np.asarray(X, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = X - ref
+    return (diff * diff).sum(axis=(-2, -1)), (ref * ref).sum(axis=(-2, -1))
+
+
+def layer_error(err_sq, ref_sq) -> np.ndarray:
+    """Relative error of every layer, sqrt(sum_h err / sum_h ref) (Fig. 3(a)); inputs [L, H]."""
+    num = np.asarray(err_sq, dtype=np.float64).sum(axis=-1)
+    den = np.asarray(ref_sq, dtype=np.float64).sum(axis=-1)
+    return np.sqrt(num / np.where(den > 0, den, 1.0))
+
+
+def rank_error_curve(eig) -> np.ndarray:
+    """Relative reconstruction error of the best rank-k approximation for k = 0..n (Fig. 7(b):
+    the error as the retained rank grows).  By Eckart-Young the rank-k truncation of delta
+    leaves exactly the singular values past k, so the error normalised by ||delta||_F is
+    sqrt(sum_{i > k} lambda_i / sum_i lambda_i) with lambda = sigma^2 sorted descending and
+    negative round-off clamped to 0; a zero matrix gives 0 at every k.
+    eig: [..., n] -> [..., n + 1]."""
+    lam = np.asarray(eig, dtype=np.float64)
+    lam = np.clip(-np.sort(-lam, axis=-1), 0.0, None)
+    n = lam.shape[-1]
+    flat = lam.reshape(-1, n)
+    out = np.zeros((flat.shape[0], n + 1))
+    for i, row in enumerate(flat):
+        total = 0.0
+        for v in row:
+            total += v
+        if total == 0.0:
+            continue
+        tail = 0.0  # sum_{i >= k} lambda_i, added from the smallest eigenvalue up
+        for k in range(n, -1, -1):
+            if k < n:
+                tail += row[k]
+            out[i, k] = np.sqrt(tail / total)
+    return out.reshape(lam.shape[:-1] + (n + 1,))
