@@ -9,7 +9,11 @@ Entry points (same names as the C ABI in include/kvc.h):
     pool_descriptor(K, V)                               -> q
     correct(K, V, desc, U, W, tau, ...)                 -> CorrectResult
     correct_chain(K0, V0, edges, tau)                   -> list[CorrectResult]
+    correct_fanout(K, V, agents, tau)                   -> list[CorrectResult]
     fit_anchor(delta, r=32, energy=0.9)                 -> FitResult
+    gram_accumulate / fit_from_gram / project           (streaming fit)
+    segment_error(X, ref)                               -> float64 [L, H, 2]
+    rank_error_curve(eig)                               -> float32 [M, n + 1]
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ __all__ = [
     "pool_descriptor",
     "correct",
     "correct_chain",
+    "correct_fanout",
     "fit_anchor",
     "correct_workspace_bytes",
     "chain_workspace_bytes",
@@ -36,6 +41,8 @@ __all__ = [
     "gram_accumulate",
     "fit_from_gram",
     "project",
+    "segment_error",
+    "rank_error_curve",
     "KVC_BF16",
     "KVC_F32",
 ]
@@ -70,6 +77,12 @@ _SIGS = {
     "kvc_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kvc_correct_chain": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_fanout_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "kvc_correct_fanout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
+                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_segment_error_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "kvc_segment_error": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "kvc_rank_error_curve": (_i, [_vp, _i, _i, _vp, _vp]),
     "kvc_fit_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_fit_anchor": (_i, [_vp, _i, _i, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                             _sz, _vp]),
@@ -266,6 +279,80 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
         _ptr(ws), ws.numel(), _stream(dev)))
     return res
+
+
+def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau: float, *,
+                   outputs: Optional[Sequence[tuple]] = None,
+                   workspace: Optional[torch.Tensor] = None) -> list:
+    """Non-chained correction of one reference cache toward several agents (see
+    kvc_correct_fanout in include/kvc.h).  ``agents``: one dict per agent with desc, U, W
+    and optionally K_fb, V_fb.  Returns one CorrectResult per agent."""
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    n = len(agents)
+    if n < 1:
+        raise ValueError("need at least one agent")
+    A = agents[0]["desc"].shape[2]
+    r = agents[0]["U"].shape[-1]
+    _need(K, "K", K.shape, K.dtype, dev)
+    _need(V, "V", K.shape, K.dtype, dev)
+    res = []
+    for j, ag in enumerate(agents):
+        _need(ag["desc"], f"desc[{j}]", (L, H, A, 2 * d), torch.float32, dev)
+        _need(ag["U"], f"U[{j}]", (2, L, H, A, T, r), K.dtype, dev)
+        _need(ag["W"], f"W[{j}]", (2, L, H, A, r, d), K.dtype, dev)
+        for name in ("K_fb", "V_fb"):
+            if ag.get(name) is not None:
+                _need(ag[name], f"{name}[{j}]", K.shape, K.dtype, dev)
+        if outputs is not None:
+            Ko, Vo = outputs[j]
+        else:
+            Ko, Vo = torch.empty_like(K), torch.empty_like(V)
+        res.append(CorrectResult(Ko, Vo, torch.empty(L, H, dtype=torch.uint8, device=dev),
+                                 torch.empty(L, H, dtype=torch.float32, device=dev)))
+    has_fb = any(ag.get("K_fb") is not None for ag in agents)
+    ws = workspace if workspace is not None else _workspace(
+        int(lib().kvc_fanout_workspace_bytes(L, H, T, d, A, r)), dev)
+    _check(lib().kvc_correct_fanout(
+        _ptr(K), _ptr(V), L, H, T, d, dt, n,
+        _ptr_array([ag["desc"] for ag in agents]), _ptr_array([ag["U"] for ag in agents]),
+        _ptr_array([ag["W"] for ag in agents]), A, r, float(tau),
+        _ptr_array([ag.get("K_fb") for ag in agents]) if has_fb else None,
+        _ptr_array([ag.get("V_fb") for ag in agents]) if has_fb else None,
+        _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
+        _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return res
+
+
+def segment_error(X: torch.Tensor, ref: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per segment [sum (X - ref)^2, sum ref^2] (float64 [L, H, 2]) for caches [L, H, T, d]
+    (see kvc_segment_error in include/kvc.h)."""
+    L, H, T, d = X.shape
+    dev = X.device
+    dt = _dtype_code(X)
+    _need(X, "X", (L, H, T, d), X.dtype, dev)
+    _need(ref, "ref", (L, H, T, d), X.dtype, dev)
+    o = out if out is not None else torch.empty(L, H, 2, dtype=torch.float64, device=dev)
+    _need(o, "out", (L, H, 2), torch.float64, dev)
+    ws = workspace if workspace is not None else _workspace(
+        lib().kvc_segment_error_workspace_bytes(L, H, T, d), dev)
+    _check(lib().kvc_segment_error(_ptr(X), _ptr(ref), L, H, T, d, dt, _ptr(o), _ptr(ws),
+                                   ws.numel(), _stream(dev)))
+    return o
+
+
+def rank_error_curve(eig: torch.Tensor) -> torch.Tensor:
+    """Relative error of the best rank-k approximation, k = 0..n, from descending eigenvalues
+    eig float32 [M, n] -> float32 [M, n + 1] (see kvc_rank_error_curve in include/kvc.h)."""
+    M, n = eig.shape
+    dev = eig.device
+    _need(eig, "eig", (M, n), torch.float32, dev)
+    c = torch.empty(M, n + 1, dtype=torch.float32, device=dev)
+    _check(lib().kvc_rank_error_curve(_ptr(eig), M, n, _ptr(c), _stream(dev)))
+    return c
 
 
 @dataclasses.dataclass

@@ -285,6 +285,109 @@ kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T
   return ok();
 }
 
+// --------------------------------------------------------------------------- fanout
+size_t kvc_fanout_workspace_bytes(int L, int H, int T, int d, int A, int r) {
+  return kvc_correct_workspace_bytes(L, H, T, d, A, r);
+}
+
+static bool overlaps(const void* a, const void* b, size_t n) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + n && y < x + n;
+}
+
+kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T, int d,
+                              int dtype, int n_agents, const float* const* desc,
+                              const void* const* U, const void* const* W, int A, int r,
+                              float tau, const void* const* K_fb, const void* const* V_fb,
+                              void* const* K_out, void* const* V_out,
+                              uint8_t* const* mask_out, float* const* score_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (n_agents < 1) return fail(KVC_ERR_ARG, "n_agents=%d (need >= 1)", n_agents);
+  if (!desc || !U || !W || !K_out || !V_out || !mask_out)
+    return fail(KVC_ERR_ARG, "desc, U, W, K_out, V_out and mask_out arrays are required");
+  if ((K_fb == nullptr) != (V_fb == nullptr))
+    return fail(KVC_ERR_ARG, "K_fb and V_fb arrays must both be given or both be NULL");
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  const size_t cache_bytes = (size_t)L * H * T * d * elem_size(dtype);
+  for (int j = 0; j < n_agents; ++j) {
+    const void* kf = K_fb ? K_fb[j] : nullptr;
+    const void* vf = V_fb ? V_fb[j] : nullptr;
+    kvc_status s = validate_correct(K, V, L, H, T, d, dtype, desc[j], U[j], W[j], A, r, nullptr,
+                                    kf, vf, K_out[j], V_out[j], mask_out[j], ws, ws_bytes);
+    if (s != KVC_OK) {
+      char tmp[512];
+      snprintf(tmp, sizeof(tmp), "agent %d: %s", j, g_err);
+      return fail(s, "%s", tmp);
+    }
+    if (score_out && score_out[j]) KVC_TRY(check_tensor(score_out[j], "score_out[j]", 4));
+    if (cache_bytes == 0) continue;
+    const void* outs[2] = {K_out[j], V_out[j]};
+    for (const void* o : outs) {
+      if (overlaps(o, K, cache_bytes) || overlaps(o, V, cache_bytes))
+        return fail(KVC_ERR_ARG, "agent %d writes over the shared reference cache", j);
+      for (int i = 0; i < j; ++i)
+        if (overlaps(o, K_out[i], cache_bytes) || overlaps(o, V_out[i], cache_bytes))
+          return fail(KVC_ERR_ARG, "outputs of agents %d and %d overlap", i, j);
+    }
+    if (overlaps(K_out[j], V_out[j], cache_bytes))
+      return fail(KVC_ERR_ARG, "agent %d: K_out and V_out overlap", j);
+  }
+  if (L * H == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  // Agent 0 runs the fused pass, which leaves the reference's chunk sums in the workspace;
+  // every later agent is matched from those sums (the same pooled descriptor, bit for bit)
+  // and its correction reads the reference once.
+  const float* pool = reinterpret_cast<const float*>(static_cast<char*>(ws) + c.off_pool);
+  for (int j = 0; j < n_agents; ++j) {
+    const void* kf = K_fb ? K_fb[j] : nullptr;
+    const void* vf = V_fb ? V_fb[j] : nullptr;
+    KVC_TRY(enqueue_correct(K, V, L, H, T, d, dtype, desc[j], U[j], W[j], A, r, tau, nullptr,
+                            j == 0 ? nullptr : pool, kf, vf, K_out[j], V_out[j], mask_out[j],
+                            score_out ? score_out[j] : nullptr, nullptr, false, ws, st));
+  }
+  return ok();
+}
+
+// --------------------------------------------------------------------------- error measures
+size_t kvc_segment_error_workspace_bytes(int L, int H, int T, int d) {
+  (void)d;
+  if (L < 0 || H < 0 || T < 0) return 0;
+  const size_t n = 2ull * L * H * kvc::segment_error_chunks(T) * sizeof(double);
+  return n > 0 ? n : 256;
+}
+
+kvc_status kvc_segment_error(const void* X, const void* ref, int L, int H, int T, int d,
+                             int dtype, double* out, void* ws, size_t ws_bytes, void* stream) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  if (L * H == 0) return ok();
+  if (T > 0) {
+    KVC_TRY(check_tensor(X, "X"));
+    KVC_TRY(check_tensor(ref, "ref"));
+  }
+  KVC_TRY(check_tensor(out, "out", 8));
+  const size_t need = kvc_segment_error_workspace_bytes(L, H, T, d);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  KVC_HIP(kvc::launch_segment_error(X, ref, L * H, T, d, dtype, static_cast<double*>(ws), out,
+                                    reinterpret_cast<hipStream_t>(stream)),
+          "segment_error");
+  return ok();
+}
+
+kvc_status kvc_rank_error_curve(const float* eig, int M, int n, float* curve_out, void* stream) {
+  if (M < 0 || n < 1) return fail(KVC_ERR_ARG, "M=%d n=%d (need M >= 0, n >= 1)", M, n);
+  if ((long long)M * (n + 1) > kMaxElems) return fail(KVC_ERR_ARG, "too large");
+  if (M == 0) return ok();
+  KVC_TRY(check_tensor(eig, "eig", 4));
+  KVC_TRY(check_tensor(curve_out, "curve_out", 4));
+  KVC_HIP(kvc::launch_rank_error_curve(eig, M, n, curve_out,
+                                       reinterpret_cast<hipStream_t>(stream)),
+          "rank_error_curve");
+  return ok();
+}
+
 // --------------------------------------------------------------------------- fit
 size_t kvc_fit_workspace_bytes(int M, int T, int d, int r) {
   if (M < 0 || T < 0 || d <= 0 || r < 1) return 0;

@@ -169,6 +169,12 @@ hipError_t launch_fit_from_gram(const double* G, int M, int d, int r, double ene
                                 float* W_out, int32_t* k_eff, float* eig, hipStream_t st);
 hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
                           int r, float* U_out, char* ws, hipStream_t st);
+// Error measures (kvc_metrics.hip): per-segment float64 sums of (X - R)^2 and R^2 through
+// chunk partials (2 doubles per segment and 256-token chunk), and the rank-error curve.
+int segment_error_chunks(int T);
+hipError_t launch_segment_error(const void* X, const void* R, int S, int T, int d, int dtype,
+                                double* partials, double* out, hipStream_t st);
+hipError_t launch_rank_error_curve(const float* eig, int M, int n, float* curve, hipStream_t st);
 inline size_t gram_ws_bytes(const FitLayout& f) { return f.off_whi; }  // partials lead
 inline size_t project_ws_bytes(int M, int d, int r, int dtype) {
   return dtype == KVC_BF16 ? 2ull * 2ull * M * ((r + 31) / 32 * 32) * d : 0;

@@ -174,6 +174,19 @@ def cpu_baseline(cfg, case, desc, n_seg: int, budget_s: float = 12.0):
             "tokens_layers_per_s": round(n_seg * cfg.T / cfg.H / dt, 1)}
 
 
+def study_errors(results, targets):
+    """Fig. 3's errors of corrected caches against the exact ones, from kvc_segment_error's
+    per-segment sums (K and V together): per agent, and per layer for every agent."""
+    per_agent, per_layer = [], []
+    for x, (EK, EV) in zip(results, targets):
+        s = kvc.segment_error(x.K, EK) + kvc.segment_error(x.V, EV)
+        s = s.cpu().double()
+        per_agent.append(round(float((s[..., 0].sum() / s[..., 1].sum()).sqrt()), 6))
+        lay = (s[..., 0].sum(-1) / s[..., 1].sum(-1)).sqrt()
+        per_layer.append([round(float(v), 5) for v in lay])
+    return per_agent, per_layer
+
+
 def chain_leg(dev, stream, n):
     """kvc_correct_chain over the 3-edge workflow A0 -> A1 -> A2 -> A3 at T = 32768."""
     cfg = synth.CONFIGS["chain_t32768"]
@@ -196,10 +209,7 @@ def chain_leg(dev, stream, n):
     res = run()
     torch.cuda.synchronize()
     masks = [x.mask.cpu().numpy() for x in res]
-    errs = []
-    for e, x in enumerate(res):
-        ex = case.edges[e].exact_K.double()
-        errs.append(float(torch.linalg.vector_norm(x.K.double() - ex) / torch.linalg.vector_norm(ex)))
+    errs, layer_errs = study_errors(res, [(ed.exact_K, ed.exact_V) for ed in case.edges])
     for _ in range(3):
         run()
     ms = time_events(run, n, stream)
@@ -213,7 +223,45 @@ def chain_leg(dev, stream, n):
             "algorithmic_bytes": nbytes,
             "tokens_layers_per_s": round(cfg.n_edges * cfg.T * cfg.L / (ms * 1e-3), 1),
             "reuse_per_edge": [round(float(1 - m.mean()), 4) for m in masks],
-            "k_rel_err_vs_exact_per_edge": [round(x, 6) for x in errs]}
+            "rel_err_vs_exact_per_agent": errs,
+            "rel_err_vs_exact_per_layer_last_agent": layer_errs[-1]}
+
+
+def fanout_leg(dev, stream, n):
+    """kvc_correct_fanout: non-chained correction of a context-free reference cache toward
+    three agents at T = 32768 (the chained workload's shape and agent count)."""
+    cfg = synth.CONFIGS["chain_t32768"]
+    log(f"[bench] non-chained leg: generating {cfg.n_edges} agents on a reference, T={cfg.T}")
+    case = synth.generate_fanout(cfg, dev)
+    q = kvc.pool_descriptor(case.K0, case.V0)
+    agents = [{"desc": synth.build_descriptors(case, j, q.double()), "U": ed.U, "W": ed.W,
+               "K_fb": ed.exact_K, "V_fb": ed.exact_V} for j, ed in enumerate(case.edges)]
+    outs = [(torch.empty_like(case.K0), torch.empty_like(case.V0)) for _ in agents]
+    ws = torch.empty(kvc.lib().kvc_fanout_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, cfg.A,
+                                                          cfg.r), dtype=torch.uint8, device=dev)
+
+    def run():
+        return kvc.correct_fanout(case.K0, case.V0, agents, cfg.tau, outputs=outs, workspace=ws)
+
+    res = run()
+    torch.cuda.synchronize()
+    masks = [x.mask.cpu().numpy() for x in res]
+    errs, layer_errs = study_errors(res, [(ed.exact_K, ed.exact_V) for ed in case.edges])
+    for _ in range(3):
+        run()
+    ms = time_events(run, n, stream)
+    nbytes = chain_bytes(cfg, masks, True)  # same accounting: agents >= 1 read the reference once
+    log(f"[bench] non-chained {ms:.3f} ms")
+    return {"workload": f"{cfg.n_edges} agents corrected from one context-free reference, "
+                        f"{cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
+                        f"tau={cfg.tau}, fallback from each agent's exact cache",
+            "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes,
+            "tokens_layers_per_s": round(cfg.n_edges * cfg.T * cfg.L / (ms * 1e-3), 1),
+            "reuse_per_agent": [round(float(1 - m.mean()), 4) for m in masks],
+            "rel_err_vs_exact_per_agent": errs,
+            "rel_err_vs_exact_per_layer_last_agent": layer_errs[-1]}
 
 
 def fit32k_leg(dev, stream, n):
@@ -430,6 +478,18 @@ def main():
             "hbm_frac": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
         log(f"[bench] fit {ms_f:.3f} ms")
+        # listing Fig. 7: effective rank and the error against the retained rank
+        fe = kvc.fit_anchor(delta, r=fcfg.r, want_eig=True, workspace=fws)
+        curve = kvc.rank_error_curve(fe.eig)
+        ms_c = time_events(lambda: kvc.rank_error_curve(fe.eig), 5, stream)
+        ranks = [1, 2, 4, 8, 11, 16, 32, 64, 128]
+        cm = curve.double().mean(0).cpu().numpy()
+        ke = fe.k_eff.cpu().numpy()
+        out["fit"]["rank_study"] = {
+            "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)), int(ke.max())],
+            "mean_rel_err_at_rank": {str(k): round(float(cm[k]), 6) for k in ranks},
+            "curve_ms": round(ms_c, 4)}
+        del fe, curve
         # streaming update: the first 6144 rows are already in G; append the last 2048
         # (accumulate, refit from G, project only the appended rows)
         t_old = T - 2048
@@ -459,6 +519,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_chain:
         out["chain"] = chain_leg(dev, stream, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
+        out["non_chained"] = fanout_leg(dev, stream, max(5, args.steps // 2))
         torch.cuda.empty_cache()
     if not args.no_fit:
         out["fit_t32768"] = fit32k_leg(dev, stream, max(3, args.steps // 10))

@@ -128,6 +128,56 @@ kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T
                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Non-chained correction (Fig. 3 and Fig. 6 / Table 9 of the listing: each agent corrects a
+ * context-free reference cache of the shared context instead of the preceding agent's
+ * cache).  One reference (K, V), n_agents targets: agent j's output is exactly what
+ * kvc_correct(K, V, desc[j], U[j], W[j], ...) stores, and its mask, score and weights are
+ * the same.  The reference is pooled once (every agent is matched against the same pooled
+ * descriptor, bit for bit); agent 0's pass is the fused single launch, every later agent
+ * takes the matching kernel and one read of the reference.  The same call serves one agent
+ * whose cache feeds several successors on a workflow graph.
+ *   n_agents >= 1.  desc, U, W, K_out, V_out, mask_out: HOST arrays of n_agents DEVICE
+ *   pointers laid out as for kvc_correct; K_fb / V_fb (the array or an entry, both or
+ *   neither per agent) and score_out may be NULL.  No output may overlap the reference or
+ *   another output (KVC_ERR_ARG).  (K, V) are read only.
+ *   ws: at least kvc_fanout_workspace_bytes(L,H,T,d,A,r) bytes.
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_fanout_workspace_bytes(int L, int H, int T, int d, int A, int r);
+kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T, int d,
+                              int dtype, int n_agents, const float* const* desc,
+                              const void* const* U, const void* const* W, int A, int r,
+                              float tau, const void* const* K_fb, const void* const* V_fb,
+                              void* const* K_out, void* const* V_out,
+                              uint8_t* const* mask_out, float* const* score_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Error measures of the studies.
+ *
+ * kvc_segment_error: Fig. 3 of the listing reports the reconstruction error of a cache
+ * normalised by the Frobenius norm of the target (the exact cache from full prefill), per
+ * layer (a) and per agent (b).  This call returns, per segment, the two sums those ratios
+ * are made of:  out[l,h,0] = sum_{t,c} (X - ref)^2,  out[l,h,1] = sum_{t,c} ref^2,  summed
+ * in float64 (the differences of the widened inputs are exact) in a fixed order.
+ *   X, ref : [L,H,T,d] dtype, read only;  out: [L,H,2] float64 (8-byte aligned), written
+ *   ws     : at least kvc_segment_error_workspace_bytes(L,H,T,d) bytes, 256-byte aligned
+ *
+ * kvc_rank_error_curve: Fig. 7(b) reports the relative reconstruction error as the
+ * retained rank grows.  The best rank-k approximation of delta leaves the singular values
+ * past k (Eckart-Young), so from the eigenvalues lambda = sigma^2 of delta^T delta:
+ *   curve[m,k] = sqrt( sum_{i>=k} lambda[m,i] / sum_i lambda[m,i] ),  k = 0..n,
+ * float64 sums (the tail added from the smallest eigenvalue up); negative entries count as
+ * 0; a zero total gives 0 at every k.
+ *   eig      : [M,n] float32, sorted descending (as kvc_fit_anchor's eig_out); the order
+ *              is not checked
+ *   curve_out: [M,n+1] float32, written
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_segment_error_workspace_bytes(int L, int H, int T, int d);
+kvc_status kvc_segment_error(const void* X, const void* ref, int L, int H, int T, int d,
+                             int dtype, double* out, void* ws, size_t ws_bytes, void* stream);
+kvc_status kvc_rank_error_curve(const float* eig, int M, int n, float* curve_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Rank-r anchor fit of a cache delta (delta = exact - reused, one [T,d] matrix per
  * (K|V, layer, head)).  The anchor is the best rank-r approximation U W of delta (the
  * compact low-rank state of the abstract; r = r_delta of Fig. 13), computed as

@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     build_descriptors,
     fit_input,
     generate,
+    generate_fanout,
     planted_spectrum,
     to_f64,
 )

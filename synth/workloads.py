@@ -41,6 +41,7 @@ __all__ = [
     "Edge",
     "Case",
     "generate",
+    "generate_fanout",
     "build_descriptors",
     "fit_input",
     "planted_spectrum",
@@ -268,6 +269,20 @@ def generate(cfg: Config | str, device="cpu") -> Case:
         ed = _edge(cfg, e, srcK, srcV, device)
         edges.append(ed)
         srcK, srcV = ed.exact_K, ed.exact_V
+    return Case(cfg=cfg, K0=K0, V0=V0, edges=edges)
+
+
+def generate_fanout(cfg: Config | str, device="cpu") -> Case:
+    """Non-chained workload: (K0, V0) is a context-free reference cache of the shared context
+    and edge j belongs to agent j, whose exact cache is reference + agent j's own planted
+    delta; every edge's source is the reference.  Deterministic for a given config (agent 0's
+    delta is the one ``generate`` plants on its first edge)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    device = torch.device(device)
+    K0 = _base_cache(cfg, 0, device)
+    V0 = _base_cache(cfg, 1, device)
+    edges = [_edge(cfg, e, K0, V0, device) for e in range(cfg.n_edges)]
     return Case(cfg=cfg, K0=K0, V0=V0, edges=edges)
 
 

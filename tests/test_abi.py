@@ -147,3 +147,56 @@ def test_streaming_fit_rejects_bad_arguments():
     assert lib.kvc_project_workspace_bytes(4, 128, 32, 1) == 0  # float32 deltas need none
     assert lib.kvc_project_workspace_bytes(4, 128, 32, 0) == 2 * 2 * 4 * 32 * 128
     assert lib.kvc_gram_workspace_bytes(512, 8192, 128) > lib.kvc_gram_workspace_bytes(1, 128, 128) > 0
+
+
+def test_fanout_rejects_bad_arguments():
+    lib = kvc.lib()
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE + (1 << 24))
+    big = 1 << 30
+    # kvc_correct_fanout(K, V, L, H, T, d, dtype, n, desc, U, W, A, r, tau, K_fb, V_fb,
+    #                    K_out, V_out, mask, score, ws, ws_bytes, stream)
+    st = lib.kvc_correct_fanout(FAKE, FAKE, 1, 1, 64, 128, 0, 0, arr, arr, arr, 4, 32, 0.3,
+                                None, None, arr, arr, arr, None, None, 0, None)
+    assert st == 1 and b"n_agents" in lib.kvc_last_error()
+    st = lib.kvc_correct_fanout(FAKE, FAKE, 1, 1, 64, 128, 0, 2, arr, None, arr, 4, 32, 0.3,
+                                None, None, arr, arr, arr, None, None, 0, None)
+    assert st == 1 and b"arrays" in lib.kvc_last_error()
+    # an agent's output on top of the shared reference
+    K, V = 1 << 28, 1 << 29
+    outk = (ctypes.c_void_p * 2)(K + 4096, 1 << 30)
+    outv = (ctypes.c_void_p * 2)(1 << 31, 1 << 32)
+    st = lib.kvc_correct_fanout(K, V, 1, 1, 64, 128, 0, 2, arr, arr, arr, 4, 32, 0.3, None,
+                                None, outk, outv, arr, None, FAKE, big, None)
+    assert st == 1 and b"reference" in lib.kvc_last_error()
+    # two agents writing the same cache
+    outk = (ctypes.c_void_p * 2)(1 << 30, 1 << 30)
+    st = lib.kvc_correct_fanout(K, V, 1, 1, 64, 128, 0, 2, arr, arr, arr, 4, 32, 0.3, None,
+                                None, outk, outv, arr, None, FAKE, big, None)
+    assert st == 1 and b"overlap" in lib.kvc_last_error()
+    # the per-agent checks of kvc_correct apply, with the agent named
+    st = lib.kvc_correct_fanout(K, V, 1, 1, 64, 128, 0, 2, arr, arr, arr, 17, 32, 0.3, None,
+                                None, outv, outk, arr, None, FAKE, big, None)
+    assert st == 2 and b"agent 0" in lib.kvc_last_error()
+    assert lib.kvc_fanout_workspace_bytes(32, 8, 2048, 128, 4, 32) == \
+        kvc.correct_workspace_bytes(32, 8, 2048, 128, 4, 32)
+
+
+def test_error_measures_reject_bad_arguments():
+    lib = kvc.lib()
+    # kvc_segment_error(X, ref, L, H, T, d, dtype, out, ws, ws_bytes, stream)
+    base = dict(X=FAKE, R=FAKE, L=2, H=2, T=300, d=128, dtype=0, out=FAKE, ws=None, nb=0,
+                st=None)
+    for kw, status in [(dict(d=96), 2), (dict(dtype=3), 1), (dict(T=-2), 1), (dict(X=None), 1),
+                       (dict(R=FAKE + 2), 1), (dict(out=FAKE + 4), 1), (dict(), 4),
+                       (dict(ws=FAKE + 64, nb=1 << 20), 4)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_segment_error(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_segment_error(*dict(base, L=0, X=None, R=None, out=None).values()) == 0
+    # two partials per segment and 256-token chunk
+    assert lib.kvc_segment_error_workspace_bytes(2, 2, 300, 128) == 2 * 4 * 2 * 8
+    # kvc_rank_error_curve(eig, M, n, curve, stream)
+    assert lib.kvc_rank_error_curve(FAKE, 4, 0, FAKE, None) == 1
+    assert lib.kvc_rank_error_curve(None, 4, 8, FAKE, None) == 1
+    assert lib.kvc_rank_error_curve(FAKE, 4, 8, FAKE + 2, None) == 1
+    assert lib.kvc_rank_error_curve(None, 0, 8, None, None) == 0
