@@ -6,6 +6,7 @@ this package.  The product path (the HIP library and its Python binding) never d
 from .kvc_oracle import (  # noqa: F401
     chain,
     correct,
+    correct_pooled,
     cosine_scores,
     effective_rank,
     fanout,
@@ -14,12 +15,14 @@ from .kvc_oracle import (  # noqa: F401
     gram,
     layer_error,
     pool,
+    pool_insert,
     project,
     rank_error_curve,
     reliability,
     rel_frobenius,
     round_to_bf16,
     round_to_dtype,
+    select_anchors,
     segment_error,
     softmax_weights,
 )

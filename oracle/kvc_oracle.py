@@ -222,6 +222,115 @@ def fanout(K, V, targets, tau, dtype) -> list:
 
 
 # --------------------------------------------------------------------------------------
+# online anchor pool
+# --------------------------------------------------------------------------------------
+
+
+def select_anchors(s, count, A: int):
+    """Top-A anchors of a segment's pool by cosine, for pools holding ``count`` valid slots.
+
+    Table 13 of the listing varies the capacity V of the online anchor pool (V = 10 in the
+    main setting).  Reading: the segment's current representation is scored against every
+    valid slot (``cosine_scores``); the A best slots (ties to the lower slot; a NaN score
+    ranks below every number) are combined with softmax weights over their scores; the
+    reliability score is the best valid score.  With fewer than A valid slots the unused
+    positions carry weight 0 and repeat the best slot.  An empty pool has score -inf, so the
+    segment falls back.  s: [..., V]; count: [...] int.  Returns (slots int [..., A],
+    w [..., A], score [...]).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    count = np.asarray(count)
+    lead = s.shape[:-1]
+    flat = s.reshape(-1, s.shape[-1])
+    cnt = count.reshape(-1)
+    slots = np.zeros((flat.shape[0], A), dtype=np.int64)
+    w = np.zeros((flat.shape[0], A))
+    score = np.full(flat.shape[0], -np.inf)
+    for i, row in enumerate(flat):
+        n = int(cnt[i])
+        if n <= 0:
+            continue
+        # rank by score descending, NaN last, ties by slot index (a stable sort)
+        key = np.where(np.isnan(row[:n]), np.inf, -row[:n])
+        order = np.argsort(key, kind="stable")
+        take = order[: min(A, n)]
+        slots[i, : len(take)] = take
+        slots[i, len(take):] = take[0]
+        sel = row[take]
+        w[i, : len(take)] = softmax_weights(sel)
+        score[i] = np.nan if np.isnan(row[:n]).any() else np.max(row[:n])
+    return slots.reshape(lead + (A,)), w.reshape(lead + (A,)), score.reshape(lead)
+
+
+def correct_pooled(K, V, anchor_pool: dict, A: int, tau, dtype, K_fb=None, V_fb=None) -> dict:
+    """Correction of a reused cache from each segment's online anchor pool.
+
+    ``anchor_pool``: desc [L, H, V, 2d], U [2, L, H, V, T, r], W [2, L, H, V, r, d], count [L, H].
+    Every segment is matched against its valid slots (``select_anchors``) and corrected with
+    the weighted sum of its selected anchors' low-rank deltas, or falls back, as in
+    ``correct``; the result is stored once in ``dtype``.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    U = np.asarray(anchor_pool["U"], dtype=np.float64)
+    W = np.asarray(anchor_pool["W"], dtype=np.float64)
+    q = pool(K, V)
+    s = cosine_scores(q, anchor_pool["desc"])
+    slots, w, score = select_anchors(s, anchor_pool["count"], A)
+    s32 = score.astype(np.float32)
+    mask = (~(s32 >= np.float32(tau))).astype(np.uint8)
+    L, H = K.shape[:2]
+    outs = []
+    for x, (X, X_fb) in enumerate(((K, K_fb), (V, V_fb))):
+        out = np.array(X, copy=True)
+        for l in range(L):
+            for h in range(H):
+                if mask[l, h]:
+                    if X_fb is not None:
+                        out[l, h] = np.asarray(X_fb, dtype=np.float64)[l, h]
+                    continue
+                delta = np.zeros_like(X[l, h])
+                for a in range(A):
+                    j = slots[l, h, a]
+                    delta += w[l, h, a] * (U[x, l, h, j] @ W[x, l, h, j])
+                out[l, h] = X[l, h] + delta
+        outs.append(out)
+    return {"K_exact": outs[0], "V_exact": outs[1],
+            "K_out": round_to_dtype(outs[0], dtype), "V_out": round_to_dtype(outs[1], dtype),
+            "q": q, "s": s, "slots": slots, "w": w, "score": score, "mask": mask}
+
+
+def pool_insert(pool_state: dict, mask, U_new, W_new, q, dtype) -> dict:
+    """Insert a new online anchor into the pool of every segment where ``mask`` is set.
+
+    After a fallback the dense prefill yields the exact cache, so the deviation of the
+    reused cache is observed and becomes a new anchor of that shared segment.  Reading
+    (the pages give no insertion or eviction rule): the anchor's factors are the rank-r fit
+    of delta = exact - reused (``fit_anchor``), stored once in the cache ``dtype``; its
+    descriptor is the pooled descriptor q of the reused cache; it goes to the slot after the
+    last one written (first-in first-out), replacing the oldest anchor once the pool holds
+    V.  pool_state: desc [L,H,V,2d], U [2,L,H,V,T,r], W [2,L,H,V,r,d], count [L,H],
+    head [L,H] (next slot).  U_new [2,L,H,T,r], W_new [2,L,H,r,d], q [L,H,2d].
+    Returns a new state; the input is not modified.
+    """
+    st = {k: np.array(v, copy=True) for k, v in pool_state.items()}
+    Vc = st["desc"].shape[2]
+    mask = np.asarray(mask)
+    L, H = mask.shape
+    for l in range(L):
+        for h in range(H):
+            if not mask[l, h]:
+                continue
+            j = int(st["head"][l, h])
+            st["U"][:, l, h, j] = round_to_dtype(np.asarray(U_new)[:, l, h], dtype)
+            st["W"][:, l, h, j] = round_to_dtype(np.asarray(W_new)[:, l, h], dtype)
+            st["desc"][l, h, j] = np.asarray(q, dtype=np.float64)[l, h].astype(np.float32)
+            st["head"][l, h] = (j + 1) % Vc
+            st["count"][l, h] = min(int(st["count"][l, h]) + 1, Vc)
+    return st
+
+
+# --------------------------------------------------------------------------------------
 # anchor fit
 # --------------------------------------------------------------------------------------
 
