@@ -10,6 +10,7 @@ Entry points (same names as the C ABI in include/kvc.h):
     correct(K, V, desc, U, W, tau, ...)                 -> CorrectResult
     correct_chain(K0, V0, edges, tau)                   -> list[CorrectResult]
     correct_fanout(K, V, agents, tau)                   -> list[CorrectResult]
+    AnchorPool.empty(...) / correct_pooled / anchor_pool_insert   (online anchor pool)
     fit_anchor(delta, r=32, energy=0.9)                 -> FitResult
     gram_accumulate / fit_from_gram / project           (streaming fit)
     segment_error(X, ref)                               -> float64 [L, H, 2]
@@ -34,6 +35,9 @@ __all__ = [
     "correct",
     "correct_chain",
     "correct_fanout",
+    "AnchorPool",
+    "correct_pooled",
+    "anchor_pool_insert",
     "fit_anchor",
     "correct_workspace_bytes",
     "chain_workspace_bytes",
@@ -80,6 +84,12 @@ _SIGS = {
     "kvc_fanout_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kvc_correct_fanout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
                                 ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_correct_pooled_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "kvc_correct_pooled": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "kvc_anchor_pool_insert": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                    _vp, _vp, _vp, _vp]),
     "kvc_segment_error_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_segment_error": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "kvc_rank_error_curve": (_i, [_vp, _i, _i, _vp, _vp]),
@@ -324,6 +334,95 @@ def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
         _ptr(ws), ws.numel(), _stream(dev)))
     return res
+
+
+@dataclasses.dataclass
+class AnchorPool:
+    """Device storage of the online anchor pools of all segments (see kvc_correct_pooled and
+    kvc_anchor_pool_insert in include/kvc.h): Vc slots per segment."""
+    desc: torch.Tensor  # float32 [L, H, Vc, 2d]
+    U: torch.Tensor  # cache dtype [2, L, H, Vc, T, r]
+    W: torch.Tensor  # cache dtype [2, L, H, Vc, r, d]
+    count: torch.Tensor  # int32 [L, H], valid slots
+    head: torch.Tensor  # int32 [L, H], next slot to write
+
+    @staticmethod
+    def empty(L, H, T, d, Vc, r, dtype=torch.bfloat16, device="cuda") -> "AnchorPool":
+        z = dict(device=device)
+        return AnchorPool(torch.zeros(L, H, Vc, 2 * d, dtype=torch.float32, **z),
+                          torch.zeros(2, L, H, Vc, T, r, dtype=dtype, **z),
+                          torch.zeros(2, L, H, Vc, r, d, dtype=dtype, **z),
+                          torch.zeros(L, H, dtype=torch.int32, **z),
+                          torch.zeros(L, H, dtype=torch.int32, **z))
+
+    @property
+    def Vc(self) -> int:
+        return self.desc.shape[2]
+
+
+def correct_pooled(K: torch.Tensor, V: torch.Tensor, pool: AnchorPool, A: int, tau: float, *,
+                   q_in: Optional[torch.Tensor] = None, K_fb: Optional[torch.Tensor] = None,
+                   V_fb: Optional[torch.Tensor] = None, K_out: Optional[torch.Tensor] = None,
+                   V_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> CorrectResult:
+    """Correct a reused cache from each segment's online anchor pool (top-A slots by cosine;
+    see kvc_correct_pooled in include/kvc.h).  The result's ``w`` holds the selected
+    anchors' weights; ``slots`` (int32 [L, H, A]) their pool slots."""
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    Vc = pool.Vc
+    r = pool.U.shape[-1]
+    _need(K, "K", (L, H, T, d), K.dtype, dev)
+    _need(V, "V", (L, H, T, d), K.dtype, dev)
+    _need(pool.desc, "desc_pool", (L, H, Vc, 2 * d), torch.float32, dev)
+    _need(pool.U, "U_pool", (2, L, H, Vc, T, r), K.dtype, dev)
+    _need(pool.W, "W_pool", (2, L, H, Vc, r, d), K.dtype, dev)
+    _need(pool.count, "count", (L, H), torch.int32, dev)
+    if q_in is not None:
+        _need(q_in, "q_in", (L, H, 2 * d), torch.float32, dev)
+    for name, t in (("K_fb", K_fb), ("V_fb", V_fb)):
+        if t is not None:
+            _need(t, name, (L, H, T, d), K.dtype, dev)
+    Ko = K_out if K_out is not None else torch.empty_like(K)
+    Vo = V_out if V_out is not None else torch.empty_like(V)
+    mask = torch.empty(L, H, dtype=torch.uint8, device=dev)
+    score = torch.empty(L, H, dtype=torch.float32, device=dev)
+    w = torch.empty(L, H, A, dtype=torch.float32, device=dev)
+    slots = torch.empty(L, H, A, dtype=torch.int32, device=dev)
+    ws = workspace if workspace is not None else _workspace(
+        lib().kvc_correct_pooled_workspace_bytes(L, H, T, d, A, r), dev)
+    _check(lib().kvc_correct_pooled(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(pool.desc),
+                                    _ptr(pool.U), _ptr(pool.W), _ptr(pool.count), Vc, int(A), r,
+                                    float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
+                                    _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(slots),
+                                    _ptr(ws), ws.numel(), _stream(dev)))
+    res = CorrectResult(Ko, Vo, mask, score, w)
+    res.slots = slots
+    return res
+
+
+def anchor_pool_insert(pool: AnchorPool, mask: torch.Tensor, U_new: torch.Tensor,
+                       W_new: torch.Tensor, q: torch.Tensor) -> AnchorPool:
+    """Insert new anchors (fit factors U_new float32 [2, L, H, T, r] or [2LH, T, r], W_new
+    float32 [2, L, H, r, d] or [2LH, r, d]) with descriptors q [L, H, 2d] into the pools of
+    the segments whose mask is set, first in first out (see kvc_anchor_pool_insert)."""
+    _, L, H, Vc, T, r = pool.U.shape
+    d = pool.W.shape[-1]
+    dev = pool.U.device
+    dt = _dtype_code(pool.U)
+    U_new = U_new.reshape(2, L, H, T, r)
+    W_new = W_new.reshape(2, L, H, r, d)
+    _need(mask, "mask", (L, H), torch.uint8, dev)
+    _need(U_new, "U_new", (2, L, H, T, r), torch.float32, dev)
+    _need(W_new, "W_new", (2, L, H, r, d), torch.float32, dev)
+    _need(q, "q", (L, H, 2 * d), torch.float32, dev)
+    _need(pool.head, "head", (L, H), torch.int32, dev)
+    _check(lib().kvc_anchor_pool_insert(_ptr(mask), _ptr(U_new), _ptr(W_new), _ptr(q), L, H, T,
+                                        d, dt, Vc, r, _ptr(pool.U), _ptr(pool.W),
+                                        _ptr(pool.desc), _ptr(pool.count), _ptr(pool.head),
+                                        _stream(dev)))
+    return pool
 
 
 def segment_error(X: torch.Tensor, ref: torch.Tensor, *, out: Optional[torch.Tensor] = None,

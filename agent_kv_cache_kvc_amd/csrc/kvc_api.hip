@@ -350,6 +350,98 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
   return ok();
 }
 
+// --------------------------------------------------------------------------- anchor pool
+size_t kvc_correct_pooled_workspace_bytes(int L, int H, int T, int d, int A, int r) {
+  return kvc_correct_workspace_bytes(L, H, T, d, A, r);
+}
+
+static kvc_status check_pool(int Vc, int A) {
+  if (Vc < 1) return fail(KVC_ERR_ARG, "Vc=%d (need >= 1)", Vc);
+  if (Vc > kvc::kMaxPool)
+    return fail(KVC_ERR_UNSUPPORTED, "Vc=%d exceeds %d pool slots", Vc, kvc::kMaxPool);
+  if (A > Vc) return fail(KVC_ERR_ARG, "A=%d exceeds the pool capacity Vc=%d", A, Vc);
+  return KVC_OK;
+}
+
+kvc_status kvc_correct_pooled(const void* K, const void* V, int L, int H, int T, int d,
+                              int dtype, const float* desc_pool, const void* U_pool,
+                              const void* W_pool, const int32_t* count, int Vc, int A, int r,
+                              float tau, const float* q_in, const void* K_fb, const void* V_fb,
+                              void* K_out, void* V_out, uint8_t* mask_out, float* score_out,
+                              float* w_out, int32_t* slot_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  KVC_TRY(validate_correct(K, V, L, H, T, d, dtype, desc_pool, U_pool, W_pool, A, r, q_in,
+                           K_fb, V_fb, K_out, V_out, mask_out, ws, ws_bytes));
+  KVC_TRY(check_pool(Vc, A));
+  if (score_out) KVC_TRY(check_tensor(score_out, "score_out", 4));
+  if (w_out) KVC_TRY(check_tensor(w_out, "w_out", 4));
+  if (slot_out) KVC_TRY(check_tensor(slot_out, "slot_out", 4));
+  if (L * H == 0) return ok();
+  KVC_TRY(check_tensor(count, "count", 4));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  const int nc = kvc::chunks_of(T, d, dtype);
+  char* base = static_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(base + c.off_pool);
+  if (q_in == nullptr)
+    KVC_HIP(kvc::launch_pool_partials(K, V, c.S, T, d, dtype, part, nc, st), "pool");
+  kvc::CorrectLaunch cl{};
+  cl.K = K;
+  cl.V = V;
+  cl.S = c.S;
+  cl.T = T;
+  cl.d = d;
+  cl.dtype = dtype;
+  cl.U = U_pool;
+  cl.W = W_pool;
+  cl.A = A;
+  cl.r = r;
+  cl.w_ws = reinterpret_cast<float*>(base + c.off_w);
+  cl.mask_ws = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  cl.K_fb = K_fb;
+  cl.V_fb = V_fb;
+  cl.K_out = K_out;
+  cl.V_out = V_out;
+  cl.ctr = reinterpret_cast<int*>(base + c.off_ctr);
+  cl.slot_ws = reinterpret_cast<int*>(base + c.off_slot);
+  cl.Vc = Vc;
+  KVC_HIP(kvc::launch_select(part, nc, T, q_in, desc_pool, count, Vc, c.S, d, A, tau, cl.w_ws,
+                             reinterpret_cast<int*>(base + c.off_slot),
+                             reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
+                             slot_out, mask_out, cl.ctr, st),
+          "select");
+  KVC_HIP(kvc::launch_correct(cl, st), "correct");
+  return ok();
+}
+
+kvc_status kvc_anchor_pool_insert(const uint8_t* mask, const float* U_new, const float* W_new,
+                                  const float* q, int L, int H, int T, int d, int dtype, int Vc,
+                                  int r, void* U_pool, void* W_pool, float* desc_pool,
+                                  int32_t* count, int32_t* head, void* stream) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  if (Vc < 1) return fail(KVC_ERR_ARG, "Vc=%d (need >= 1)", Vc);
+  if (Vc > kvc::kMaxPool)
+    return fail(KVC_ERR_UNSUPPORTED, "Vc=%d exceeds %d pool slots", Vc, kvc::kMaxPool);
+  if (r < 1 || r > d) return fail(KVC_ERR_ARG, "r=%d (need 1 <= r <= d)", r);
+  if (L * H == 0) return ok();
+  KVC_TRY(check_tensor(mask, "mask", 1));
+  KVC_TRY(check_tensor(W_new, "W_new", 4));
+  KVC_TRY(check_tensor(q, "q", 4));
+  KVC_TRY(check_tensor(W_pool, "W_pool", 4));
+  KVC_TRY(check_tensor(desc_pool, "desc_pool", 4));
+  KVC_TRY(check_tensor(count, "count", 4));
+  KVC_TRY(check_tensor(head, "head", 4));
+  if (T > 0) {
+    KVC_TRY(check_tensor(U_new, "U_new", 4));
+    KVC_TRY(check_tensor(U_pool, "U_pool", 4));
+  }
+  KVC_HIP(kvc::launch_pool_insert(mask, U_new, W_new, q, L * H, T, d, dtype, Vc, r, U_pool,
+                                  W_pool, desc_pool, count, head,
+                                  reinterpret_cast<hipStream_t>(stream)),
+          "pool insert");
+  return ok();
+}
+
 // --------------------------------------------------------------------------- error measures
 size_t kvc_segment_error_workspace_bytes(int L, int H, int T, int d) {
   (void)d;

@@ -333,6 +333,115 @@ __global__ __launch_bounds__(kWave) void score_kernel(
   }
 }
 
+// Online anchor pool: one wave per segment.  The pool's valid slots (the first count[s] of
+// Vc) are scored like segment_weights; the A best are selected (a NaN ranks last, ties go to
+// the lower slot), their softmax weights (temperature 1) and slots published; positions past
+// the valid count repeat the best slot with weight 0.  score = best valid score (NaN if any
+// valid score is NaN, -inf for an empty pool); fallback = !(score >= tau).  Resets *ctr.
+template <int D>
+__global__ __launch_bounds__(kWave) void select_kernel(
+    const float* __restrict__ partials, int n_chunks, int T, const float* __restrict__ q_in,
+    const float* __restrict__ desc, const int* __restrict__ count, int Vc, int A, float tau,
+    float* __restrict__ w_ws, int* __restrict__ slot_ws, uint8_t* __restrict__ mask_ws,
+    float* __restrict__ score_out, float* __restrict__ w_out, int* __restrict__ slot_out,
+    uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
+  constexpr int PER = 2 * D / kWave;
+  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
+  if (s == 0 && lane == 0) *ctr = 0;
+  float q[PER];
+  if (q_in != nullptr) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
+  } else {
+    pooled_query<D>(partials, n_chunks, T, s, S, lane, q);
+  }
+  float qq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
+  const float nq = sqrtf(wave_sum(qq));
+  int n = count[s];
+  n = n < 0 ? 0 : (n > Vc ? Vc : n);
+  float sc[kMaxPool];
+  bool nan = false;
+#pragma unroll
+  for (int v = 0; v < kMaxPool; ++v) {
+    sc[v] = 0.f;
+    if (v < n) {
+      const float* dv = desc + ((size_t)s * Vc + v) * 2 * D;
+      float dd = 0.f, dq = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const float x = dv[lane + kWave * i];
+        dd += x * x;
+        dq += x * q[i];
+      }
+      dd = wave_sum(dd);
+      dq = wave_sum(dq);
+      const float den = nq * sqrtf(dd);
+      const float c = (den == 0.f) ? 0.f : dq / den;
+      sc[v] = c;
+      nan |= (c != c);
+    }
+  }
+  const int nsel = A < n ? A : n;
+  uint32_t taken = 0u;
+  int sel[kMaxA];
+  float ss[kMaxA];
+#pragma unroll
+  for (int i = 0; i < kMaxA; ++i) {
+    sel[i] = 0;
+    ss[i] = 0.f;
+    if (i < nsel) {
+      int best = -1;
+      float bv = 0.f;
+#pragma unroll
+      for (int v = 0; v < kMaxPool; ++v) {
+        if (v < n && !((taken >> v) & 1u)) {
+          const float c = sc[v];
+          if (best < 0 || (!(c != c) && ((bv != bv) || c > bv))) {
+            best = v;
+            bv = c;
+          }
+        }
+      }
+      sel[i] = best;
+      ss[i] = bv;
+      taken |= 1u << best;
+    }
+  }
+  const float score = n == 0 ? -INFINITY : (nan ? __uint_as_float(0x7fc00000u) : ss[0]);
+  float ex[kMaxA];
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxA; ++i) {
+    ex[i] = 0.f;
+    if (i < nsel) {
+      ex[i] = expf(ss[i] - ss[0]);
+      z += ex[i];
+    }
+  }
+  float wv = 0.f;
+  int sv = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxA; ++i)
+    if (i == lane) {
+      wv = i < nsel ? ex[i] / z : 0.f;
+      sv = i < nsel ? sel[i] : sel[0];
+    }
+  const uint8_t fall = !(score >= tau);
+  if (lane < A) {
+    w_ws[(size_t)s * A + lane] = wv;
+    slot_ws[(size_t)s * A + lane] = sv;
+    if (w_out) w_out[(size_t)s * A + lane] = wv;
+    if (slot_out) slot_out[(size_t)s * A + lane] = sv;
+  }
+  if (lane == 0) {
+    mask_ws[s] = fall;
+    mask_out[s] = fall;
+    if (score_out) score_out[s] = score;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
                                                        int* __restrict__ done, int S) {
   if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) ctr[threadIdx.x] = 0;
@@ -387,6 +496,8 @@ struct CorrectArgs {
   int* done;               // fused: [S] items pooled, then n_ci + 1 (matched) or
                            //        n_ci + 2 (matched, fallback)
   const float* desc;       // fused: [S][A][2D] anchor descriptors
+  const int* slot_ws;      // SEL: [S][A] pool slot of each selected anchor
+  int Vc;                  // SEL: pool slots per segment (U, W hold Vc anchors per segment)
   uint8_t* mask_out;       // fused outputs
   float* score_out;
   float* w_out;
@@ -413,8 +524,11 @@ __device__ __forceinline__ void order_loads_after_signal() {
 
 // NA > 0: compile-time anchor count NA and MFMA steps per anchor KSC (r = 2 KSC SLOT);
 // NA == 0: runtime A and r with up to NFG register-resident fragments.
-template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED>
+// SEL (not fused): anchor a of segment s is pool slot slot_ws[s][a] of Vc slots per segment
+// (the online anchor pool); otherwise anchor a is slot a of A.
+template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED, bool SEL = false>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
+  static_assert(!(SEL && FUSED), "pool slot selection runs in the matching kernel");
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
   using TL = Tile<Tr, D>;
@@ -441,6 +555,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ float wsh[kMaxA];
+  __shared__ int ssl[kMaxA];
   __shared__ float red[4][D];
   __shared__ float qsh[2 * D];
   __shared__ int s_item;
@@ -457,6 +572,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   const int nfrag = A * KS;
   const bool uvec = FIX || (r % VEC) == 0;
   const int n_ci = 2 * n_chunks;             // items per segment
+  const int nslot = SEL ? args.Vc : A;       // anchors stored per segment
 
   // this workgroup's queue, its segments (q, q + nq, ...) and its item count
   const int nq = FUSED ? args.nq : 1;
@@ -607,10 +723,15 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       goto next_item;
     }
 
+    if constexpr (SEL) {
+      if (tid < A) ssl[tid] = args.slot_ws[(size_t)s * A + tid];
+      __syncthreads();
+    }
+
     // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
     //      in the fused form this overlaps the wait for the segment's weights
     {
-      const elem* Wseg = W + ((size_t)x * S + s) * A * r * D;
+      const elem* Wseg = W + ((size_t)x * S + s) * nslot * r * D;
       const int n_w = A * r * (D / VEC);
       for (int q = tid; q < n_w; q += kBlock) {
         // k varies fastest across lanes, so the transposed LDS writes are contiguous
@@ -620,7 +741,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         const int a = rest / (D / VEC);
         elem v[VEC];
         *reinterpret_cast<u32x4*>(v) =
-            *reinterpret_cast<const u32x4*>(Wseg + ((size_t)a * r + k) * D + c0);
+            *reinterpret_cast<const u32x4*>(Wseg + ((size_t)(SEL ? ssl[a] : a) * r + k) * D + c0);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const int c = c0 + j;
@@ -703,14 +824,15 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         }
       }
     } else {
-      const elem* Useg = U + ((size_t)x * S + s) * A * (size_t)T * r;
+      const elem* Useg = U + ((size_t)x * S + s) * nslot * (size_t)T * r;
       auto load_u = [&](frag (&dst)[NF], int t0) {
         const int t = t0 + ln;
         if (FIX && t0 + 32 <= T) {
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             const int a = f / KS, ks = f - a * KS;
-            const elem* up = Useg + ((size_t)a * T + t) * r + g * half + ks * SLOT;
+            const elem* up =
+                Useg + ((size_t)(SEL ? ssl[a] : a) * T + t) * r + g * half + ks * SLOT;
             if constexpr (SLOT == 8) dst[f] = *reinterpret_cast<const u32x4*>(up);
             else dst[f] = Tr::f(*up);
           }
@@ -722,7 +844,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
           if (f < nfrag) {
             const int a = f / KS, ks = f - a * KS;
             const int k0 = g * half + ks * SLOT;
-            const elem* up = Useg + ((size_t)a * T + t) * r + k0;
+            const elem* up = Useg + ((size_t)(SEL ? ssl[a] : a) * T + t) * r + k0;
             if constexpr (SLOT == 8) {
               u32x4 v = {0u, 0u, 0u, 0u};
               if (valid && k0 < r) {
@@ -908,7 +1030,24 @@ hipError_t launch_score(const float* partials, int n_chunks, int T, const float*
   return hipGetLastError();
 }
 
-template <class Tr, int D, int NA, int KSC, int NFG>
+hipError_t launch_select(const float* partials, int n_chunks, int T, const float* q_in,
+                         const float* desc, const int* count, int Vc, int S, int d, int A,
+                         float tau, float* w_ws, int* slot_ws, uint8_t* mask_ws,
+                         float* score_out, float* w_out, int* slot_out, uint8_t* mask_out,
+                         int* ctr, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL((select_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_chunks, T,
+                       q_in, desc, count, Vc, A, tau, w_ws, slot_ws, mask_ws, score_out, w_out,
+                       slot_out, mask_out, ctr);
+  else
+    hipLaunchKernelGGL((select_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_chunks, T,
+                       q_in, desc, count, Vc, A, tau, w_ws, slot_ws, mask_ws, score_out, w_out,
+                       slot_out, mask_out, ctr);
+  return hipGetLastError();
+}
+
+template <class Tr, int D, int NA, int KSC, int NFG, bool SEL = false>
 static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   const int PADK = 16 / (int)sizeof(typename Tr::elem);
   const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
@@ -929,6 +1068,8 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.pool_partials = L.pool_partials;
   a.done = L.done;
   a.desc = L.desc;
+  a.slot_ws = L.slot_ws;
+  a.Vc = L.Vc;
   a.mask_out = L.mask_out;
   a.score_out = L.score_out;
   a.w_out = L.w_out;
@@ -941,10 +1082,15 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.n_chunks = chunks_of(L.T, L.d, L.dtype);
   a.n_items = L.S * 2 * a.n_chunks;
   const bool pool = L.next_partials != nullptr;
-  auto k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
-                           : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
-                : (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, false, true>
-                           : correct_kernel<Tr, D, NA, KSC, NFG, false, false>);
+  void (*k)(CorrectArgs);
+  if constexpr (SEL) {
+    k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, true>;
+  } else {
+    k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
+                        : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
+             : (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, false, true>
+                        : correct_kernel<Tr, D, NA, KSC, NFG, false, false>);
+  }
   if (lds > 48 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -990,8 +1136,28 @@ static hipError_t correct_t(CorrectLaunch L, hipStream_t st) {
   return correct_v<Tr, D, 0, 0, F2>(L, st);
 }
 
+// The pooled correction (slot indirection): the 8B-shaped anchors (bf16, d = 128, A = 4,
+// r = 32) take their compile-time variant, every other shape the runtime-general kernel.
+template <class Tr, int D>
+static hipError_t correct_sel_t(CorrectLaunch L, hipStream_t st) {
+  L.rp = (L.r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
+  if constexpr (Tr::SLOT == 8 && D == 128) {
+    if (L.r == 32 && L.A == 4) return correct_v<Tr, D, 4, 2, 0, true>(L, st);
+  }
+  const int nfrag = L.A * (L.rp / 2 / Tr::SLOT);
+  constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
+  if (nfrag <= F0) return correct_v<Tr, D, 0, 0, F0, true>(L, st);
+  if (nfrag <= F1) return correct_v<Tr, D, 0, 0, F1, true>(L, st);
+  return correct_v<Tr, D, 0, 0, F2, true>(L, st);
+}
+
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st) {
   if (L.S == 0) return hipSuccess;
+  if (L.slot_ws != nullptr) {
+    if (L.dtype == KVC_BF16)
+      return L.d == 128 ? correct_sel_t<TrBF16, 128>(L, st) : correct_sel_t<TrBF16, 64>(L, st);
+    return L.d == 128 ? correct_sel_t<TrF32, 128>(L, st) : correct_sel_t<TrF32, 64>(L, st);
+  }
   if (L.dtype == KVC_BF16)
     return L.d == 128 ? correct_t<TrBF16, 128>(L, st) : correct_t<TrBF16, 64>(L, st);
   return L.d == 128 ? correct_t<TrF32, 128>(L, st) : correct_t<TrF32, 64>(L, st);

@@ -16,6 +16,7 @@ constexpr int kRowsPerPass = 128;     // tokens of one 32-token tile per wave, 4
 constexpr int kMaxA = 16;             // anchors per segment held in registers
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
+constexpr int kMaxPool = 32;          // slots of an online anchor pool per segment
 constexpr int kJacobiMaxSweeps = 40;  // hard cap: every workgroup leaves the sweep loop
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -60,6 +61,7 @@ struct CorrectLayout {
   size_t off_mask;    // uint8 [S]
   size_t off_done;    // int [S]: per-segment counters of the fused pass
   size_t off_ctr;     // int [kMaxQueues]: work counters of the correction pass
+  size_t off_slot;    // int [S][A]: pool slots of the selected anchors (pooled correction)
   size_t bytes;
 };
 
@@ -78,6 +80,7 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_mask = o;  o = align_up(o + (size_t)c.S, 256);
   c.off_done = o;  o = align_up(o + sizeof(int) * (size_t)c.S, 256);
   c.off_ctr = o;   o = align_up(o + sizeof(int) * kMaxQueues, 256);
+  c.off_slot = o;  o = align_up(o + sizeof(int) * (size_t)c.S * A, 256);
   c.bytes = o;
   return c;
 }
@@ -102,6 +105,8 @@ struct CorrectLaunch {
   float* pool_partials;     // fused: chunk sums of the source
   int* done;                // fused: per-segment counters
   const float* desc;        // fused: anchor descriptors
+  const int* slot_ws;       // pooled correction: [S][A] slots of Vc per segment, or null
+  int Vc;
   float tau;
   uint8_t* mask_out;        // fused: matching outputs
   float* score_out;
@@ -155,6 +160,19 @@ hipError_t launch_score(const float* partials, int n_chunks, int T, const float*
                         const float* desc, int S, int d, int A, float tau, float* w_ws,
                         uint8_t* mask_ws, float* score_out, float* w_out, uint8_t* mask_out,
                         int* ctr, hipStream_t st);
+// Online anchor pool: matching of every segment against its pool's valid slots, top-A
+// selection (weights and slots into the workspace); resets *ctr.
+hipError_t launch_select(const float* partials, int n_chunks, int T, const float* q_in,
+                         const float* desc, const int* count, int Vc, int S, int d, int A,
+                         float tau, float* w_ws, int* slot_ws, uint8_t* mask_ws,
+                         float* score_out, float* w_out, int* slot_out, uint8_t* mask_out,
+                         int* ctr, hipStream_t st);
+// Pool insertion: the slot after the last one written takes the new anchor (factors stored in
+// the cache dtype) of every segment whose mask is set; then head and count advance.
+hipError_t launch_pool_insert(const uint8_t* mask, const float* U_new, const float* W_new,
+                              const float* q, int S, int T, int d, int dtype, int Vc, int r,
+                              void* U_pool, void* W_pool, float* desc_pool, int* count,
+                              int* head, hipStream_t st);
 // Correction (after launch_score), or the fused pass (resets its own counters).
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,

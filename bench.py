@@ -264,6 +264,57 @@ def fanout_leg(dev, stream, n):
             "rel_err_vs_exact_per_layer_last_agent": layer_errs[-1]}
 
 
+def pool_leg(dev, stream, n, cfg, case):
+    """Online anchor pool on the 8B shape at T = 2048: kvc_correct_pooled with full pools of
+    V = 1, 5, 10, 20 slots (listing Table 13) and A = min(V, 4) selected anchors, and one
+    insertion (kvc_anchor_pool_insert) of fitted anchors for the segments that fell back."""
+    K, V = case.K0, case.V0
+    q = kvc.pool_descriptor(K, V)
+    torch.cuda.synchronize()
+    Ko, Vo = torch.empty_like(K), torch.empty_like(V)
+    es = 2
+    S = cfg.L * cfg.H
+    out = {"workload": f"{cfg.name}: pools of V slots per segment, A = min(V, {cfg.A}) selected, "
+                       "full pools", "per_capacity": {}}
+    for Vc in (1, 5, 10, 20):
+        A = min(Vc, cfg.A)
+        p = synth.generate_pool(cfg, Vc, dev, full=True)
+        desc = synth.pool_descriptors(p, q.double())
+        pool = kvc.AnchorPool(desc, p["U"], p["W"], p["count"], torch.zeros_like(p["count"]))
+        ws = torch.empty(kvc.lib().kvc_correct_pooled_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d,
+                                                                       A, cfg.r),
+                         dtype=torch.uint8, device=dev)
+
+        def run():
+            return kvc.correct_pooled(K, V, pool, A, cfg.tau, K_out=Ko, V_out=Vo, workspace=ws)
+
+        res = run()
+        torch.cuda.synchronize()
+        mask = res.mask.cpu().numpy()
+        reliable = int((mask == 0).sum())
+        nbytes = (2 * 2 * S * cfg.T * cfg.d * es + reliable * 2 * A * (cfg.T * cfg.r + cfg.r * cfg.d) * es
+                  + S * Vc * 2 * cfg.d * 4)
+        for _ in range(3):
+            run()
+        ms = time_events(run, n, stream)
+        out["per_capacity"][str(Vc)] = {"A": A, "ms": round(ms, 4),
+                                        "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                                        "reuse": round(reliable / S, 4)}
+        log(f"[bench] pooled correction V={Vc} A={A}: {ms:.4f} ms")
+        del p, desc, pool, res, ws
+    # insertion: the fallback segments of the V = 10 pass take the fit of the planted delta
+    Vc = 10
+    pool = kvc.AnchorPool.empty(cfg.L, cfg.H, cfg.T, cfg.d, Vc, cfg.r, torch.bfloat16, dev)
+    fit = kvc.fit_anchor(synth.fit_input(case), r=cfg.r, want_eig=False)
+    mask = (torch.rand(cfg.L, cfg.H, device=dev) < 0.2).to(torch.uint8)
+    torch.cuda.synchronize()
+    ms_i = time_events(lambda: kvc.anchor_pool_insert(pool, mask, fit.U, fit.W, q), n, stream)
+    out["insert"] = {"ms": round(ms_i, 4), "segments": int(mask.sum()),
+                     "note": "one insertion of rank-32 anchors into pools of 10 slots"}
+    log(f"[bench] pool insertion {ms_i:.4f} ms")
+    return out
+
+
 def fit32k_leg(dev, stream, n):
     """kvc_fit_anchor on the delta of the chain workload's first edge (M = 512, T = 32768)."""
     cfg = synth.CONFIGS["chain_t32768"].replace(n_edges=1)
@@ -399,6 +450,8 @@ def main():
     log(f"[bench] base-cache fit {ms_b:.3f} ms, effective rank median {int(np.median(ke))}")
     del base, bf, eigs
 
+    out_pool = pool_leg(dev, stream, max(10, args.steps // 2), cfg, case)
+
     # the unfused form, for reference: matching kernel from a precomputed q, then correction
     q = kvc.pool_descriptor(K, V)
     torch.cuda.synchronize()
@@ -444,6 +497,7 @@ def main():
                      "traffic_detail": traffic,
                      "ms_per_launch": round(ms_ev, 5)},
         "base_cache_rank": base_rank,
+        "anchor_pool": out_pool,
         "with_q_in": {"ms": round(ms_k, 5), "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
                       "note": "q precomputed: matching kernel + unfused correction kernel"},
     }

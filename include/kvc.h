@@ -152,6 +152,55 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
                               size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Online anchor pool (Table 13 of the listing varies the capacity V of each shared segment's
+ * pool of online anchors; V = 10 in the main setting).  The pages give no insertion,
+ * eviction or selection rule; this library reads them as follows.
+ *
+ * kvc_correct_pooled: kvc_correct against each segment's pool.  Per segment the first
+ * count[l,h] of the Vc slots are valid; each valid slot v is scored s_v = cos(q, desc[v]);
+ * the A best valid slots are selected (a NaN ranks last, ties go to the lower slot) and
+ * combined with softmax weights over their scores; score = the best valid score (NaN if any
+ * valid score is NaN, -inf for an empty pool, which therefore falls back); fallback =
+ * !(score >= tau).  With fewer than A valid slots the unused positions repeat the best slot
+ * with weight 0 (valid slots must hold finite factors).  Corrected output, fallback and
+ * rounding as in kvc_correct.  Pooling, matching and correction run as three launches (the
+ * pool is read after the query is known).
+ *   desc_pool : [L,H,Vc,2d] float32;  U_pool: [2,L,H,Vc,T,r] dtype;  W_pool: [2,L,H,Vc,r,d]
+ *   count     : [L,H] int32, valid slots per segment (clamped to [0, Vc] on the device)
+ *   Vc, A     : 1 <= A <= Vc <= 32; A and r as for kvc_correct
+ *   q_in      : as for kvc_correct (NULL: pooled here)
+ *   w_out     : [L,H,A] float32 or NULL;  slot_out: [L,H,A] int32 or NULL (selected slots)
+ *   other arguments as for kvc_correct (no q_next_out)
+ *   ws        : at least kvc_correct_pooled_workspace_bytes(L,H,T,d,A,r) bytes
+ *
+ * kvc_anchor_pool_insert: after a fallback, the dense prefill gives the exact cache, so the
+ * deviation delta = exact - reused of that segment is observed; its rank-r fit
+ * (kvc_fit_anchor on the [2*L*H, T, d] delta: K matrices, then V) becomes a new anchor.  For
+ * every segment with mask[l,h] != 0 the slot head[l,h] receives U_new and W_new (stored in
+ * the cache dtype, round to nearest even) and the descriptor q[l,h] (the pooled descriptor
+ * of the reused cache, as matched); then head advances by one slot modulo Vc (first in,
+ * first out: the oldest anchor is replaced once the pool is full) and count grows up to Vc.
+ *   mask  : [L,H] uint8;  U_new: [2,L,H,T,r] float32;  W_new: [2,L,H,r,d] float32
+ *   q     : [L,H,2d] float32
+ *   U_pool, W_pool, desc_pool: as above, updated in place
+ *   count, head: [L,H] int32, updated in place (start both at 0; a head outside [0, Vc)
+ *           is treated as 0)
+ *   1 <= Vc <= 32, 1 <= r <= d.  No workspace.
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_correct_pooled_workspace_bytes(int L, int H, int T, int d, int A, int r);
+kvc_status kvc_correct_pooled(const void* K, const void* V, int L, int H, int T, int d,
+                              int dtype, const float* desc_pool, const void* U_pool,
+                              const void* W_pool, const int32_t* count, int Vc, int A, int r,
+                              float tau, const float* q_in, const void* K_fb, const void* V_fb,
+                              void* K_out, void* V_out, uint8_t* mask_out, float* score_out,
+                              float* w_out, int32_t* slot_out, void* ws, size_t ws_bytes,
+                              void* stream);
+kvc_status kvc_anchor_pool_insert(const uint8_t* mask, const float* U_new, const float* W_new,
+                                  const float* q, int L, int H, int T, int d, int dtype, int Vc,
+                                  int r, void* U_pool, void* W_pool, float* desc_pool,
+                                  int32_t* count, int32_t* head, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Error measures of the studies.
  *
  * kvc_segment_error: Fig. 3 of the listing reports the reconstruction error of a cache

@@ -14,6 +14,8 @@ from .workloads import (  # noqa: F401
     fit_input,
     generate,
     generate_fanout,
+    generate_pool,
     planted_spectrum,
+    pool_descriptors,
     to_f64,
 )

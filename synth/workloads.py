@@ -42,6 +42,8 @@ __all__ = [
     "Case",
     "generate",
     "generate_fanout",
+    "generate_pool",
+    "pool_descriptors",
     "build_descriptors",
     "fit_input",
     "planted_spectrum",
@@ -284,6 +286,62 @@ def generate_fanout(cfg: Config | str, device="cpu") -> Case:
     V0 = _base_cache(cfg, 1, device)
     edges = [_edge(cfg, e, K0, V0, device) for e in range(cfg.n_edges)]
     return Case(cfg=cfg, K0=K0, V0=V0, edges=edges)
+
+
+_S_POOL_U, _S_POOL_W, _S_POOL_COUNT, _S_POOL_COS, _S_POOL_DIR, _S_POOL_ALLLOW = range(20, 26)
+
+
+def generate_pool(cfg: Config, Vc: int, device="cpu", full: bool = False) -> dict:
+    """Contents of an online anchor pool with ``Vc`` slots per segment (listing Table 13):
+    factors U [2, L, H, Vc, T, r] (Gaussian, standard deviation ``scale0``) and W [2, L, H, Vc, r, d] (orthonormal rows), both in the cache dtype;
+    count [L, H] int32 valid slots (uniform in 0..Vc, or Vc when ``full``); per-slot target
+    cosines [L, H, Vc] drawn without repetition from a grid of step 0.04 on [-0.2, 1) that
+    skips +-0.02 around tau (with probability ``fallback_prob`` a segment's valid slots all
+    lie below tau), so selections and decisions stay away from rounding ties; random
+    directions [L, H, Vc, 2d] for ``pool_descriptors``."""
+    L, H, T, d, r = cfg.L, cfg.H, cfg.T, cfg.d, cfg.r
+    dt = cfg.torch_dtype
+    g = _gen(device, cfg.seed, _S_POOL_U)
+    U = (cfg.scale0 * torch.randn(2, L, H, Vc, T, r, generator=g, device=device)).to(dt)
+    vo = _orthonormal((2, L, H, Vc), d, r, _gen(device, cfg.seed, _S_POOL_W), device)
+    W = vo.transpose(-1, -2).to(dt).contiguous()
+    if full:
+        count = torch.full((L, H), Vc, dtype=torch.int32, device=device)
+    else:
+        count = torch.randint(0, Vc + 1, (L, H), generator=_gen(device, cfg.seed, _S_POOL_COUNT),
+                              device=device, dtype=torch.int32)
+    grid = torch.arange(-0.2, 1.0, 0.04, dtype=torch.float64)
+    grid = grid[(grid - cfg.tau).abs() > 0.02]
+    low = grid[grid < cfg.tau]
+    gc = _gen("cpu", cfg.seed, _S_POOL_COS)
+    all_low = torch.rand(L, H, generator=_gen("cpu", cfg.seed, _S_POOL_ALLLOW),
+                         dtype=torch.float64) < cfg.fallback_prob
+    cos = torch.empty(L, H, Vc, dtype=torch.float64)
+    for l in range(L):
+        for h in range(H):
+            src = low if (all_low[l, h] and Vc <= low.numel()) else grid
+            cos[l, h] = src[torch.randperm(src.numel(), generator=gc)[:Vc]]
+    direction = torch.randn(L, H, Vc, 2 * d, generator=_gen(device, cfg.seed, _S_POOL_DIR),
+                            device=device, dtype=torch.float64)
+    return {"U": U, "W": W, "count": count, "cos": cos.to(device), "direction": direction}
+
+
+def pool_descriptors(pool: dict, q) -> torch.Tensor:
+    """Descriptors [L, H, Vc, 2d] float32 with cos(q, desc_v) = the pool's target cosines, built
+    as in ``build_descriptors`` for a pooled query ``q`` [L, H, 2d] supplied by the consumer."""
+    e = pool["direction"]
+    dev = e.device
+    q = torch.as_tensor(np.asarray(q) if not isinstance(q, torch.Tensor) else q)
+    q = q.to(device=dev, dtype=torch.float64)
+    qn = torch.linalg.vector_norm(q, dim=-1, keepdim=True)
+    safe = torch.where(qn > 0, qn, torch.ones_like(qn))
+    qh = (q / safe).unsqueeze(2)
+    e = e - (e * qh).sum(-1, keepdim=True) * qh
+    e = e / torch.linalg.vector_norm(e, dim=-1, keepdim=True)
+    c = pool["cos"].unsqueeze(-1)
+    desc = qn.unsqueeze(2) * (c * qh + torch.sqrt(torch.clamp(1.0 - c * c, min=0.0)) * e)
+    desc = torch.where(qn.unsqueeze(2) > 0, desc, pool["direction"])
+    return desc.to(torch.float32)
 
 
 def build_descriptors(case: Case, edge: int, q) -> torch.Tensor:

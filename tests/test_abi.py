@@ -200,3 +200,34 @@ def test_error_measures_reject_bad_arguments():
     assert lib.kvc_rank_error_curve(None, 4, 8, FAKE, None) == 1
     assert lib.kvc_rank_error_curve(FAKE, 4, 8, FAKE + 2, None) == 1
     assert lib.kvc_rank_error_curve(None, 0, 8, None, None) == 0
+
+
+def test_anchor_pool_rejects_bad_arguments():
+    lib = kvc.lib()
+    big = 1 << 30
+    # kvc_correct_pooled(K, V, L, H, T, d, dtype, desc, U, W, count, Vc, A, r, tau, q_in,
+    #                    K_fb, V_fb, K_out, V_out, mask, score, w, slot, ws, ws_bytes, stream)
+    base = dict(K=FAKE, V=FAKE, L=2, H=2, T=64, d=128, dtype=0, desc=FAKE, U=FAKE, W=FAKE,
+                count=FAKE, Vc=10, A=4, r=32, tau=0.3, q_in=None, K_fb=None, V_fb=None,
+                K_out=FAKE, V_out=FAKE, mask=FAKE, score=None, w=None, slot=None, ws=FAKE,
+                nb=big, st=None)
+    for kw, status, msg in [(dict(Vc=0), 1, "Vc=0"), (dict(Vc=33), 2, "Vc=33"),
+                            (dict(A=5, Vc=4), 1, "capacity"), (dict(count=None), 1, "count"),
+                            (dict(count=FAKE + 2), 1, "count"), (dict(A=17, Vc=20), 2, "A=17"),
+                            (dict(slot=FAKE + 1), 1, "slot_out"), (dict(ws=None), 4, "work")]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_correct_pooled(*a.values()) == status, (kw, lib.kvc_last_error())
+        assert msg in lib.kvc_last_error().decode()
+    assert lib.kvc_correct_pooled(*dict(base, L=0).values()) == 0
+    # kvc_anchor_pool_insert(mask, U_new, W_new, q, L, H, T, d, dtype, Vc, r, U_pool, W_pool,
+    #                        desc_pool, count, head, stream)
+    base = dict(mask=FAKE, U=FAKE, W=FAKE, q=FAKE, L=2, H=2, T=64, d=128, dtype=0, Vc=4, r=32,
+                Up=FAKE, Wp=FAKE, dp=FAKE, count=FAKE, head=FAKE, st=None)
+    for kw, status in [(dict(Vc=0), 1), (dict(Vc=40), 2), (dict(r=0), 1), (dict(r=129), 1),
+                       (dict(d=48), 2), (dict(mask=None), 1), (dict(head=None), 1),
+                       (dict(q=FAKE + 2), 1), (dict(U=None), 1)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_anchor_pool_insert(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_anchor_pool_insert(*dict(base, L=0).values()) == 0  # no segment: no-op
