@@ -470,7 +470,9 @@ kvc_status kvc_segment_error(const void* X, const void* ref, int L, int H, int T
 
 kvc_status kvc_rank_error_curve(const float* eig, int M, int n, float* curve_out, void* stream) {
   if (M < 0 || n < 1) return fail(KVC_ERR_ARG, "M=%d n=%d (need M >= 0, n >= 1)", M, n);
-  if ((long long)M * (n + 1) > kMaxElems) return fail(KVC_ERR_ARG, "too large");
+  if (n > kvc::rank_error_curve_max_n())
+    return fail(KVC_ERR_UNSUPPORTED, "n=%d exceeds %d eigenvalues", n,
+                kvc::rank_error_curve_max_n());
   if (M == 0) return ok();
   KVC_TRY(check_tensor(eig, "eig", 4));
   KVC_TRY(check_tensor(curve_out, "curve_out", 4));

@@ -333,40 +333,41 @@ __global__ __launch_bounds__(kWave) void score_kernel(
   }
 }
 
-// Online anchor pool: one wave per segment.  The pool's valid slots (the first count[s] of
-// Vc) are scored like segment_weights; the A best are selected (a NaN ranks last, ties go to
-// the lower slot), their softmax weights (temperature 1) and slots published; positions past
-// the valid count repeat the best slot with weight 0.  score = best valid score (NaN if any
-// valid score is NaN, -inf for an empty pool); fallback = !(score >= tau).  Resets *ctr.
+// Online anchor pool: one workgroup (4 waves) per segment.  The pool's valid slots (the
+// first count[s] of Vc) are scored like segment_weights, wave w taking slots w, w + 4, ... (the
+// same per-wave arithmetic, so a score is bit-identical to kvc_correct's for the same
+// descriptor); wave 0 then selects the A best (a NaN ranks last, ties go to the lower slot)
+// and publishes their softmax weights (temperature 1) and slots; positions past the valid
+// count repeat the best slot with weight 0.  score = best valid score (NaN if any valid score
+// is NaN, -inf for an empty pool); fallback = !(score >= tau).  Resets *ctr.
 template <int D>
-__global__ __launch_bounds__(kWave) void select_kernel(
+__global__ __launch_bounds__(kBlock) void select_kernel(
     const float* __restrict__ partials, int n_chunks, int T, const float* __restrict__ q_in,
     const float* __restrict__ desc, const int* __restrict__ count, int Vc, int A, float tau,
     float* __restrict__ w_ws, int* __restrict__ slot_ws, uint8_t* __restrict__ mask_ws,
     float* __restrict__ score_out, float* __restrict__ w_out, int* __restrict__ slot_out,
     uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
   constexpr int PER = 2 * D / kWave;
-  const int s = blockIdx.x, S = gridDim.x, lane = threadIdx.x;
-  if (s == 0 && lane == 0) *ctr = 0;
-  float q[PER];
-  if (q_in != nullptr) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
-  } else {
-    pooled_query<D>(partials, n_chunks, T, s, S, lane, q);
-  }
-  float qq = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
-  const float nq = sqrtf(wave_sum(qq));
+  constexpr int NW = kBlock / kWave;
+  __shared__ float sc_lds[kMaxPool];
+  const int s = blockIdx.x, S = gridDim.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (s == 0 && threadIdx.x == 0) *ctr = 0;
   int n = count[s];
   n = n < 0 ? 0 : (n > Vc ? Vc : n);
-  float sc[kMaxPool];
-  bool nan = false;
+  if (wave < n) {
+    float q[PER];
+    if (q_in != nullptr) {
 #pragma unroll
-  for (int v = 0; v < kMaxPool; ++v) {
-    sc[v] = 0.f;
-    if (v < n) {
+      for (int i = 0; i < PER; ++i) q[i] = q_in[(size_t)s * 2 * D + lane + kWave * i];
+    } else {
+      pooled_query<D>(partials, n_chunks, T, s, S, lane, q);
+    }
+    float qq = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) qq += q[i] * q[i];
+    const float nq = sqrtf(wave_sum(qq));
+    for (int v = wave; v < n; v += NW) {
       const float* dv = desc + ((size_t)s * Vc + v) * 2 * D;
       float dd = 0.f, dq = 0.f;
 #pragma unroll
@@ -378,10 +379,17 @@ __global__ __launch_bounds__(kWave) void select_kernel(
       dd = wave_sum(dd);
       dq = wave_sum(dq);
       const float den = nq * sqrtf(dd);
-      const float c = (den == 0.f) ? 0.f : dq / den;
-      sc[v] = c;
-      nan |= (c != c);
+      if (lane == 0) sc_lds[v] = (den == 0.f) ? 0.f : dq / den;
     }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float sc[kMaxPool];
+  bool nan = false;
+#pragma unroll
+  for (int v = 0; v < kMaxPool; ++v) {
+    sc[v] = v < n ? sc_lds[v] : 0.f;
+    nan |= v < n && (sc[v] != sc[v]);
   }
   const int nsel = A < n ? A : n;
   uint32_t taken = 0u;
@@ -1037,11 +1045,11 @@ hipError_t launch_select(const float* partials, int n_chunks, int T, const float
                          int* ctr, hipStream_t st) {
   if (S == 0) return hipSuccess;
   if (d == 128)
-    hipLaunchKernelGGL((select_kernel<128>), dim3(S), dim3(kWave), 0, st, partials, n_chunks, T,
+    hipLaunchKernelGGL((select_kernel<128>), dim3(S), dim3(kBlock), 0, st, partials, n_chunks, T,
                        q_in, desc, count, Vc, A, tau, w_ws, slot_ws, mask_ws, score_out, w_out,
                        slot_out, mask_out, ctr);
   else
-    hipLaunchKernelGGL((select_kernel<64>), dim3(S), dim3(kWave), 0, st, partials, n_chunks, T,
+    hipLaunchKernelGGL((select_kernel<64>), dim3(S), dim3(kBlock), 0, st, partials, n_chunks, T,
                        q_in, desc, count, Vc, A, tau, w_ws, slot_ws, mask_ws, score_out, w_out,
                        slot_out, mask_out, ctr);
   return hipGetLastError();

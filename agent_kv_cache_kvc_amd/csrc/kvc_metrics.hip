@@ -113,28 +113,35 @@ __global__ __launch_bounds__(kBlock) void segment_error_sum_kernel(
   out[(size_t)s * 2 + 1] = rr;
 }
 
-// One thread per matrix.  eig: [M, n] descending (negative round-off counts as 0);
+// One wave per matrix.  eig: [M, n] descending (negative round-off counts as 0);
 // curve[k] = sqrt(sum_{i >= k} lambda_i / sum_i lambda_i), the tail added from the smallest
-// eigenvalue up and the total from the largest down (float64); a zero total gives 0.
-__global__ __launch_bounds__(kBlock) void rank_error_curve_kernel(const float* __restrict__ eig,
-                                                                  int M, int n,
-                                                                  float* __restrict__ curve) {
-  const int m = blockIdx.x * kBlock + threadIdx.x;
-  if (m >= M) return;
+// eigenvalue up and the total from the largest down (float64, in that fixed order: the sums
+// are a dependent chain that lane 0 runs out of LDS); a zero total gives 0.  The eigenvalues
+// are staged and the curve written with coalesced accesses.
+constexpr int kCurveMax = 256;  // eigenvalues per matrix staged in LDS
+
+__global__ __launch_bounds__(kWave) void rank_error_curve_kernel(const float* __restrict__ eig,
+                                                                 int n,
+                                                                 float* __restrict__ curve) {
+  __shared__ double lam[kCurveMax];
+  __shared__ float out[kCurveMax + 1];
+  const int m = blockIdx.x, lane = threadIdx.x;
   const float* e = eig + (size_t)m * n;
   float* o = curve + (size_t)m * (n + 1);
-  double total = 0.0;
-  for (int i = 0; i < n; ++i) total += (double)fmaxf(e[i], 0.f);
-  if (!(total > 0.0)) {
-    for (int k = 0; k <= n; ++k) o[k] = 0.f;
-    return;
+  for (int i = lane; i < n; i += kWave) lam[i] = (double)fmaxf(e[i], 0.f);
+  __syncthreads();
+  if (lane == 0) {
+    double total = 0.0;
+    for (int i = 0; i < n; ++i) total += lam[i];
+    double tail = 0.0;
+    out[n] = 0.f;
+    for (int k = n - 1; k >= 0; --k) {
+      tail += lam[k];
+      out[k] = total > 0.0 ? (float)sqrt(tail / total) : 0.f;
+    }
   }
-  double tail = 0.0;
-  o[n] = 0.f;
-  for (int k = n - 1; k >= 0; --k) {
-    tail += (double)fmaxf(e[k], 0.f);
-    o[k] = (float)sqrt(tail / total);
-  }
+  __syncthreads();
+  for (int k = lane; k <= n; k += kWave) o[k] = out[k];
 }
 
 int segment_error_chunks(int T) { return T > 0 ? ceil_div(T, kErrChunk) : 0; }
@@ -166,10 +173,11 @@ hipError_t launch_segment_error(const void* X, const void* R, int S, int T, int 
   return hipGetLastError();
 }
 
+int rank_error_curve_max_n() { return kCurveMax; }
+
 hipError_t launch_rank_error_curve(const float* eig, int M, int n, float* curve, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(rank_error_curve_kernel, dim3(ceil_div(M, kBlock)), dim3(kBlock), 0, st,
-                     eig, M, n, curve);
+  hipLaunchKernelGGL(rank_error_curve_kernel, dim3(M), dim3(kWave), 0, st, eig, n, curve);
   return hipGetLastError();
 }
 

@@ -315,6 +315,55 @@ def pool_leg(dev, stream, n, cfg, case):
     return out
 
 
+def vl_leg(dev, stream, n):
+    """The vision-language-shaped cache (28 layers x 4 kv-heads x 9216 tokens x 128, 7000
+    high-variance visual tokens, A = 6, r = 32, tau = 0.6): kvc_correct (fused) and the fit."""
+    cfg = synth.CONFIGS["vl_t9216"]
+    log(f"[bench] vl leg: generating {cfg.name}")
+    case = synth.generate(cfg, dev)
+    desc = descriptors_on_device(case)
+    ed = case.edges[0]
+    Ko, Vo = torch.empty_like(case.K0), torch.empty_like(case.V0)
+    ws = torch.empty(kvc.correct_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, cfg.A, cfg.r),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return kvc.correct(case.K0, case.V0, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo,
+                           want_w=False, want_score=False, workspace=ws)
+
+    res = step()
+    torch.cuda.synchronize()
+    mask = res.mask.cpu().numpy()
+    nbytes = correct_bytes(cfg, mask)
+    for _ in range(5):
+        step()
+    ms = time_events(step, n, stream)
+    delta = synth.fit_input(case)
+    del case, Ko, Vo, res
+    M, T = delta.shape[0], delta.shape[1]
+    fws = torch.empty(kvc.fit_workspace_bytes(M, T, cfg.d, cfg.r), dtype=torch.uint8, device=dev)
+
+    def fit():
+        return kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
+
+    fr = fit()
+    torch.cuda.synchronize()
+    ke = fr.k_eff.cpu().numpy()
+    ms_f = time_events(fit, max(3, n // 5), stream)
+    by, syrk, gemm, proj = fit_bytes_flops(M, T, cfg.d, cfg.r)
+    log(f"[bench] vl correct {ms:.4f} ms, fit {ms_f:.3f} ms")
+    return {"workload": f"{cfg.name}: {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
+                        f"tau={cfg.tau}",
+            "correct_ms": round(ms, 4), "correct_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "correct_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_layers_per_s": round(cfg.T * cfg.L / (ms * 1e-3), 1),
+            "reuse_ratio": round(float(1 - mask.mean()), 4),
+            "fit_ms": round(ms_f, 4),
+            "fit_tflops_syrk_plus_proj": round((syrk + proj) / (ms_f * 1e-3) / 1e12, 3),
+            "fit_gbs": round(by / (ms_f * 1e-3) / 1e9, 2),
+            "k_eff_min_max": [int(ke.min()), int(ke.max())]}
+
+
 def fit32k_leg(dev, stream, n):
     """kvc_fit_anchor on the delta of the chain workload's first edge (M = 512, T = 32768)."""
     cfg = synth.CONFIGS["chain_t32768"].replace(n_edges=1)
@@ -388,6 +437,7 @@ def main():
     ap.add_argument("--only-fit32k", action="store_true",
                     help="run only the T=32768 fit leg (for a profile of its kernels)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-vl", action="store_true")
     ap.add_argument("--cpu-segments", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -578,6 +628,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_fit:
         out["fit_t32768"] = fit32k_leg(dev, stream, max(3, args.steps // 10))
+        torch.cuda.empty_cache()
+    if not args.no_vl:
+        out["vl"] = vl_leg(dev, stream, max(10, args.steps // 2))
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle on a sample)")

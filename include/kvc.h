@@ -218,7 +218,7 @@ kvc_status kvc_anchor_pool_insert(const uint8_t* mask, const float* U_new, const
  * float64 sums (the tail added from the smallest eigenvalue up); negative entries count as
  * 0; a zero total gives 0 at every k.
  *   eig      : [M,n] float32, sorted descending (as kvc_fit_anchor's eig_out); the order
- *              is not checked
+ *              is not checked;  1 <= n <= 256
  *   curve_out: [M,n+1] float32, written
  * ------------------------------------------------------------------------------------- */
 size_t kvc_segment_error_workspace_bytes(int L, int H, int T, int d);

@@ -197,6 +197,7 @@ def test_error_measures_reject_bad_arguments():
     assert lib.kvc_segment_error_workspace_bytes(2, 2, 300, 128) == 2 * 4 * 2 * 8
     # kvc_rank_error_curve(eig, M, n, curve, stream)
     assert lib.kvc_rank_error_curve(FAKE, 4, 0, FAKE, None) == 1
+    assert lib.kvc_rank_error_curve(FAKE, 4, 257, FAKE, None) == 2
     assert lib.kvc_rank_error_curve(None, 4, 8, FAKE, None) == 1
     assert lib.kvc_rank_error_curve(FAKE, 4, 8, FAKE + 2, None) == 1
     assert lib.kvc_rank_error_curve(None, 0, 8, None, None) == 0
