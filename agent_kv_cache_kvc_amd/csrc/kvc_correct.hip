@@ -550,6 +550,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   constexpr int NH = TL::NH, JN = TL::JN;
   constexpr int PADK = 16 / sizeof(elem);
   constexpr int PER = 2 * D / kWave;
+  // CMP (compact LDS, bf16 anchor counts of 6 and more at r = 32): W^T rows are stored
+  // unpadded with their 16-byte chunks XOR-swizzled by bits 2-3 of the row (the 16 rows that
+  // one quarter-wave reads then fall into 16 distinct bank groups), and the MFMA results are
+  // staged one 32-channel block at a time, so two workgroups still fit in a CU's LDS.
+  constexpr bool CMP = NA >= 6 && SLOT == 8 && KSC == 2;
+  constexpr int SROW = CMP ? 36 : kStageRow;  // floats per staged token row
 
   const elem* __restrict__ K = static_cast<const elem*>(args.K);
   const elem* __restrict__ V = static_cast<const elem*>(args.V);
@@ -570,12 +576,17 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   __shared__ int s_mask;
   __shared__ int s_last;
 
-  elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * kStageRow * sizeof(float));
+  elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * SROW * sizeof(float));
   const int A = FIX ? NA : args.A;
   const int r = FIX ? 2 * KSC * SLOT : args.r;
   const int rp = FIX ? 2 * KSC * SLOT : args.rp;
   const int RS = rp + PADK;
   const int half = rp / 2;
+  // LDS element of W^T row `row` (operand order), rank index k
+  auto widx = [&](int row, int k) -> int {
+    if constexpr (CMP) return row * rp + ((((k >> 3) ^ (row >> 2)) & 3) << 3) + (k & 7);
+    else return row * RS + k;
+  };
   const int KS = FIX ? KSC : half / SLOT;  // MFMA steps per anchor
   const int nfrag = A * KS;
   const bool uvec = FIX || (r % VEC) == 0;
@@ -605,7 +616,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane >> 5, ln = lane & 31;
-    float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * kStageRow;
+    float* stage = reinterpret_cast<float*>(smem_raw) + wave * 32 * SROW;
     const int lrow = lane / LPT;               // token within a coalesced access
     const int lcol = VEC * (lane % LPT);       // channel offset within a half row
 
@@ -753,7 +764,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const int c = c0 + j;
-          wt[(a * D + (c & ~31) + cinv32(c & 31)) * RS + k] = v[j];
+          wt[widx(a * D + (c & ~31) + cinv32(c & 31), k)] = v[j];
         }
       }
       if (!FIX && rp > r) {
@@ -877,7 +888,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       auto run_tile = [&](auto tl_c, frag (&cu)[NF], frag (&nu)[NF]) {
         constexpr int tl = decltype(tl_c)::value;
         const int t0 = first + tl * kRowsPerPass;
-        if (tl + 1 < n_my) load_u(nu, t0 + kRowsPerPass);
+        if constexpr (CMP) {
+          // one U buffer live at a time (registers): this tile's U is loaded here
+          if (tl > 0) load_u(cu, t0);
+        } else {
+          if (tl + 1 < n_my) load_u(nu, t0 + kRowsPerPass);
+        }
         const bool full = t0 + 32 <= T;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
@@ -885,7 +901,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 #pragma unroll 1
           for (int cbl = 0; cbl < 2; ++cbl) {
             const int cb = 2 * h + cbl;
-            const elem* ap = wt + (cb * 32 + ln) * RS + g * half;
+            const elem* ap = wt + (cb * 32 + ln) * RS + g * half;  // padded layout only
             floatx16 acc, tmp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -894,7 +910,10 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
               if (FIX || f < nfrag) {
                 const int a = f / KS, ks = f - a * KS;
                 frag af;
-                if constexpr (SLOT == 8) {
+                if constexpr (CMP) {
+                  af = *reinterpret_cast<const u32x4*>(
+                      wt + widx(a * D + cb * 32 + ln, g * half + ks * SLOT));
+                } else if constexpr (SLOT == 8) {
                   af = *reinterpret_cast<const u32x4*>(ap + a * D * RS + ks * SLOT);
                 } else {
                   af = ap[a * D * RS + ks];
@@ -914,12 +933,44 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                 }
               }
             }
-            float* sp = stage + ln * kStageRow + cbl * 32 + 16 * g;
+            float* sp = stage + ln * SROW + (CMP ? 0 : cbl * 32) + 16 * g;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               *reinterpret_cast<floatx4*>(sp + 4 * q) =
                   floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            if constexpr (CMP) {
+              // this block's 32 channels: the lanes that hold them add X, round and store
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+              for (int j = 0; j < JN; ++j) {
+                const int row = TPI * j + lrow;
+                const int tok = t0 + row;
+                if ((lcol >> 5) == cbl) {
+                  float dv[VEC], xv[VEC];
+#pragma unroll
+                  for (int e = 0; e < VEC; e += 4)
+                    *reinterpret_cast<floatx4*>(&dv[e]) = *reinterpret_cast<const floatx4*>(
+                        stage + row * SROW + (lcol & 31) + e);
+                  unpack_in<Tr>(xr[tl].v[h][j], xv);
+#pragma unroll
+                  for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
+                  const u32x4 o = pack_out<Tr>(dv);
+                  if (full || tok < T) {
+                    __builtin_nontemporal_store(
+                        o, reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol));
+                    if constexpr (POOL_OUT) {
+                      float fo[VEC];
+                      unpack_in<Tr>(o, fo);
+#pragma unroll
+                      for (int e = 0; e < VEC; ++e) qs[h][e] += fo[e];
+                    }
+                  }
+                }
+              }
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
           }
+          if constexpr (CMP) continue;
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
           // ---- add X, round once, coalesced store
 #pragma unroll
@@ -1058,8 +1109,9 @@ hipError_t launch_select(const float* partials, int n_chunks, int T, const float
 template <class Tr, int D, int NA, int KSC, int NFG, bool SEL = false>
 static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   const int PADK = 16 / (int)sizeof(typename Tr::elem);
-  const size_t lds = 4ull * 32 * kStageRow * sizeof(float) +
-                     (size_t)L.A * D * (L.rp + PADK) * sizeof(typename Tr::elem);
+  constexpr bool CMP = NA >= 6 && Tr::SLOT == 8 && KSC == 2;  // as in correct_kernel
+  const size_t lds = 4ull * 32 * (CMP ? 36 : kStageRow) * sizeof(float) +
+                     (size_t)L.A * D * (L.rp + (CMP ? 0 : PADK)) * sizeof(typename Tr::elem);
   CorrectArgs a{};
   a.K = L.K;
   a.V = L.V;

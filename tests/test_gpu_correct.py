@@ -64,6 +64,8 @@ SMALL = [
     ("bf16", 64, 129, 2, 64),
     ("bf16", 128, 260, 16, 16),
     ("bf16", 128, 96, 2, 7),
+    ("bf16", 128, 700, 6, 32),   # compact LDS layout (6 and 8 anchors of rank 32)
+    ("bf16", 128, 333, 8, 32),
     ("f32", 64, 256, 2, 8),
     ("f32", 128, 777, 3, 12),
     ("f32", 128, 64, 1, 64),
@@ -126,8 +128,9 @@ def test_threshold_extremes_and_zero_factors():
     assert math.isnan(out.score[0, 1].item())
 
 
-def test_in_place_and_precomputed_query():
-    cfg = synth.CONFIGS["llama8b_t2048"].replace(L=2, H=4, T=1000, seed=9)
+@pytest.mark.parametrize("A", [4, 6])
+def test_in_place_and_precomputed_query(A):
+    cfg = synth.CONFIGS["llama8b_t2048"].replace(L=2, H=4, T=1000, seed=9 + A, A=A)
     case = synth.generate(cfg)
     d = dev()
     desc, q = correct_inputs(case, "cpu")
