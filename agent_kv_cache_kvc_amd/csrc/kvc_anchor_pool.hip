@@ -13,10 +13,40 @@
 
 namespace kvc {
 
-constexpr int kInsRows = 64;  // token rows of U per workgroup
+constexpr int kInsRows = 128;  // token rows of U per workgroup
 
 __device__ __forceinline__ void put(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 __device__ __forceinline__ void put(float* p, float v) { *p = v; }
+
+// n consecutive values src -> dst in the cache dtype: 8 per thread with 16-byte accesses when
+// both ends are 16-byte aligned, element by element otherwise.
+template <class E>
+__device__ __forceinline__ void convert(E* __restrict__ dst, const float* __restrict__ src, int n,
+                                        int tid) {
+  const bool vec = (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(src) % 16 == 0);
+  int done = 0;
+  if (vec) {
+    const int n8 = n / 8;
+    for (int i = tid; i < n8; i += kBlock) {
+      const floatx4 a = reinterpret_cast<const floatx4*>(src)[2 * i];
+      const floatx4 b = reinterpret_cast<const floatx4*>(src)[2 * i + 1];
+      if constexpr (sizeof(E) == 2) {
+        u32x4 o;
+        o[0] = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+        o[1] = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+        o[2] = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
+        o[3] = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
+        reinterpret_cast<u32x4*>(dst)[i] = o;
+      } else {
+        reinterpret_cast<floatx4*>(dst)[2 * i] = a;
+        reinterpret_cast<floatx4*>(dst)[2 * i + 1] = b;
+      }
+    }
+    done = n8 * 8;
+  }
+  for (int i = done + tid; i < n; i += kBlock) put(dst + i, src[i]);
+}
 
 __device__ __forceinline__ int pool_slot(const int* head, int s, int Vc) {
   const int j = head[s];
@@ -38,14 +68,10 @@ __global__ __launch_bounds__(kBlock) void pool_insert_kernel(
     const int t0 = blk * kInsRows;
     const int rows = T - t0 < kInsRows ? T - t0 : kInsRows;
     const int n = rows * r;
-    const float* src = U_new + (m * T + t0) * r;
-    E* dst = U_pool + ((m * Vc + j) * T + t0) * r;
-    for (int i = tid; i < n; i += kBlock) put(dst + i, src[i]);
+    convert(U_pool + ((m * Vc + j) * T + t0) * r, U_new + (m * T + t0) * r, n, tid);
   } else {
     const int n = r * d;
-    const float* src = W_new + m * n;
-    E* dst = W_pool + (m * Vc + j) * n;
-    for (int i = tid; i < n; i += kBlock) put(dst + i, src[i]);
+    convert(W_pool + (m * Vc + j) * n, W_new + m * n, n, tid);
     if (x == 0)
       for (int i = tid; i < 2 * d; i += kBlock)
         desc_pool[((size_t)s * Vc + j) * 2 * d + i] = q[(size_t)s * 2 * d + i];

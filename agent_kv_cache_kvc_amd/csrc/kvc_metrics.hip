@@ -123,25 +123,28 @@ constexpr int kCurveMax = 256;  // eigenvalues per matrix staged in LDS
 __global__ __launch_bounds__(kWave) void rank_error_curve_kernel(const float* __restrict__ eig,
                                                                  int n,
                                                                  float* __restrict__ curve) {
-  __shared__ double lam[kCurveMax];
-  __shared__ float out[kCurveMax + 1];
+  __shared__ double lam[kCurveMax + 1];  // eigenvalues, then the tails
+  __shared__ double tot;
   const int m = blockIdx.x, lane = threadIdx.x;
   const float* e = eig + (size_t)m * n;
   float* o = curve + (size_t)m * (n + 1);
   for (int i = lane; i < n; i += kWave) lam[i] = (double)fmaxf(e[i], 0.f);
   __syncthreads();
-  if (lane == 0) {
+  if (lane == 0) {  // the two dependent chains of additions, in the fixed order
     double total = 0.0;
     for (int i = 0; i < n; ++i) total += lam[i];
     double tail = 0.0;
-    out[n] = 0.f;
+    lam[n] = 0.0;
     for (int k = n - 1; k >= 0; --k) {
       tail += lam[k];
-      out[k] = total > 0.0 ? (float)sqrt(tail / total) : 0.f;
+      lam[k] = tail;
     }
+    tot = total;
   }
   __syncthreads();
-  for (int k = lane; k <= n; k += kWave) o[k] = out[k];
+  const double total = tot;
+  for (int k = lane; k <= n; k += kWave)
+    o[k] = total > 0.0 ? (float)sqrt(lam[k] / total) : 0.f;
 }
 
 int segment_error_chunks(int T) { return T > 0 ? ceil_div(T, kErrChunk) : 0; }
