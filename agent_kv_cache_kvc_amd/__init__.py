@@ -194,6 +194,7 @@ class CorrectResult:
     score: Optional[torch.Tensor] = None  # float32 [L, H]
     w: Optional[torch.Tensor] = None  # float32 [L, H, A]
     q_next: Optional[torch.Tensor] = None  # float32 [L, H, 2d]
+    slots: Optional[torch.Tensor] = None  # int32 [L, H, A], pool slots (correct_pooled)
 
 
 def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tensor,
@@ -397,9 +398,7 @@ def correct_pooled(K: torch.Tensor, V: torch.Tensor, pool: AnchorPool, A: int, t
                                     float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
                                     _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(slots),
                                     _ptr(ws), ws.numel(), _stream(dev)))
-    res = CorrectResult(Ko, Vo, mask, score, w)
-    res.slots = slots
-    return res
+    return CorrectResult(Ko, Vo, mask, score, w, slots=slots)
 
 
 def anchor_pool_insert(pool: AnchorPool, mask: torch.Tensor, U_new: torch.Tensor,
