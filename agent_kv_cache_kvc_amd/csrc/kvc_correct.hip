@@ -110,26 +110,30 @@ __device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
   }
 }
 
-// One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).
-template <class Tr, int D>
+// One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).  LAST: the
+// last read of these bytes in this launch, issued non-temporal so the lines leave L2 first (the
+// fused pass keeps its pooling reads in L2 for the correction's second read).
+template <class Tr, int D, bool LAST = false>
 __device__ __forceinline__ void load_tile(const typename Tr::elem* __restrict__ X, int t0, int T,
                                           int lrow, int lcol, Tile<Tr, D>& tile) {
   using TL = Tile<Tr, D>;
+  auto ld = [](const typename Tr::elem* p) -> u32x4 {
+    if constexpr (LAST) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+  };
   if (t0 + 32 <= T) {
 #pragma unroll
     for (int h = 0; h < TL::NH; ++h)
 #pragma unroll
       for (int j = 0; j < TL::JN; ++j)
-        tile.v[h][j] = *reinterpret_cast<const u32x4*>(X + (size_t)(t0 + TL::TPI * j + lrow) * D +
-                                                       64 * h + lcol);
+        tile.v[h][j] = ld(X + (size_t)(t0 + TL::TPI * j + lrow) * D + 64 * h + lcol);
   } else {
 #pragma unroll
     for (int h = 0; h < TL::NH; ++h)
 #pragma unroll
       for (int j = 0; j < TL::JN; ++j) {
         const int tok = t0 + TL::TPI * j + lrow;
-        tile.v[h][j] = tok < T ? *reinterpret_cast<const u32x4*>(X + (size_t)tok * D + 64 * h + lcol)
-                               : u32x4{0u, 0u, 0u, 0u};
+        tile.v[h][j] = tok < T ? ld(X + (size_t)tok * D + 64 * h + lcol) : u32x4{0u, 0u, 0u, 0u};
       }
   }
 }
@@ -665,9 +669,15 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const bool fb_known = !FUSED && Xfb != nullptr && args.mask[s] != 0;
     const elem* Xsrc = fb_known ? Xfb + seg : X;
     TL xr[NT];
+    if (FUSED && pool_item) {
 #pragma unroll
-    for (int tl = 0; tl < NT; ++tl)
-      load_tile<Tr, D>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+      for (int tl = 0; tl < NT; ++tl)
+        load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+    } else {
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl)
+        load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+    }
 
     if (FUSED && pool_item) {
       // fields used only here are read through an opaque pointer to the kernel arguments,
