@@ -1169,7 +1169,7 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.nq = 1;
   if (L.fused) {
     a.batch = fused_batch(a.n_chunks);
-    a.lead = kFusedLead;
+    a.lead = fused_lead(a.batch * 2 * a.n_chunks);
     a.nq = grid < kMaxQueues ? grid : kMaxQueues;  // every queue is served
     hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(kBlock), 0, st, L.ctr, L.done, L.S);
     const hipError_t e = hipGetLastError();

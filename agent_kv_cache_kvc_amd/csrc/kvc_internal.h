@@ -42,10 +42,14 @@ inline int max_chunks_of(int T) { return T > 0 ? ceil_div(T, kRowsPerPass) : 1; 
 // round-robin dispatch places it on) holding the segments s with s mod nq equal to it, so a
 // chunk's pooling and correction items run on one XCD and the second read of K and V can
 // hit that XCD's L2.  Each queue has slots of about kFusedSlotItems items (whole segments)
-// and pools kFusedLead slots ahead of its correction items.
+// and pools about kFusedLeadItems items (at least four slots) ahead of its correction items.
 constexpr int kMaxQueues = 8;
 constexpr int kFusedSlotItems = 16;
-constexpr int kFusedLead = 6;
+constexpr int kFusedLeadItems = 96;  // pooling items a queue runs ahead of its corrections
+inline int fused_lead(int slot_items) {
+  const int l = (kFusedLeadItems + slot_items - 1) / slot_items;
+  return l < 4 ? 4 : l;
+}
 inline int fused_batch(int n_chunks) {
   const int n_ci = 2 * n_chunks;
   return n_ci >= kFusedSlotItems ? 1 : kFusedSlotItems / n_ci;
