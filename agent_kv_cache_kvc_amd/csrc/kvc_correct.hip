@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void pool_partials_kernel(
   Tile<Tr, D> xr[NT];
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl)
-    load_tile<Tr, D>(X, first + tl * kRowsPerPass, T, lane / Tr::LPT, Tr::VEC * (lane % Tr::LPT),
+    load_tile<Tr, D, true>(X, first + tl * kRowsPerPass, T, lane / Tr::LPT, Tr::VEC * (lane % Tr::LPT),
                      xr[tl]);
   float qs[D / 64][Tr::VEC];
 #pragma unroll

@@ -75,8 +75,9 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = ts + 8 * rg + i;
-      in[i] = (t < t_end) ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * cg)
-                          : u32x4{0u, 0u, 0u, 0u};
+      in[i] = (t < t_end)  // delta is read once here: non-temporal
+                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * cg))
+                  : u32x4{0u, 0u, 0u, 0u};
     }
   };
   if (t_begin < t_end) load_block(t_begin);
@@ -1229,7 +1230,8 @@ __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
       for (int q = 0; q < LD; ++q) {
         const int c = tid + q * kBlock;
         const int t = t0 + c / CPR;
-        ld[q] = t < T ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * (c % CPR))
+        ld[q] = t < T ? __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4*>(src + (size_t)t * D + 8 * (c % CPR)))
                       : u32x4{0u, 0u, 0u, 0u};
       }
     };
