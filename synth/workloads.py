@@ -295,8 +295,8 @@ def generate_pool(cfg: Config, Vc: int, device="cpu", full: bool = False) -> dic
     """Contents of an online anchor pool with ``Vc`` slots per segment (listing Table 13):
     factors U [2, L, H, Vc, T, r] (Gaussian, standard deviation ``scale0``) and W [2, L, H, Vc, r, d] (orthonormal rows), both in the cache dtype;
     count [L, H] int32 valid slots (uniform in 0..Vc, or Vc when ``full``); per-slot target
-    cosines [L, H, Vc] drawn without repetition from a grid of step 0.04 on [-0.2, 1) that
-    skips +-0.02 around tau (with probability ``fallback_prob`` a segment's valid slots all
+    cosines [L, H, Vc] drawn without repetition from a grid of step 0.04 (0.02 for pools of more
+    than 26 slots) on [-0.2, 1) that skips +-0.02 around tau (with probability ``fallback_prob`` a segment's valid slots all
     lie below tau), so selections and decisions stay away from rounding ties; random
     directions [L, H, Vc, 2d] for ``pool_descriptors``."""
     L, H, T, d, r = cfg.L, cfg.H, cfg.T, cfg.d, cfg.r
@@ -310,7 +310,8 @@ def generate_pool(cfg: Config, Vc: int, device="cpu", full: bool = False) -> dic
     else:
         count = torch.randint(0, Vc + 1, (L, H), generator=_gen(device, cfg.seed, _S_POOL_COUNT),
                               device=device, dtype=torch.int32)
-    grid = torch.arange(-0.2, 1.0, 0.04, dtype=torch.float64)
+    step = 0.04 if Vc <= 26 else 0.02  # enough distinct cosines for every slot
+    grid = torch.arange(-0.2, 1.0, step, dtype=torch.float64)
     grid = grid[(grid - cfg.tau).abs() > 0.02]
     low = grid[grid < cfg.tau]
     gc = _gen("cpu", cfg.seed, _S_POOL_COS)

@@ -25,7 +25,9 @@ def _host_pool(p, desc):
 @pytest.mark.parametrize("dtype,dd,T,Vc,A,r", [("bf16", 128, 600, 6, 4, 32),
                                                ("bf16", 64, 333, 10, 3, 16),
                                                ("f32", 128, 257, 5, 2, 8),
-                                               ("bf16", 128, 300, 20, 4, 32)])
+                                               ("bf16", 128, 300, 20, 4, 32),
+                                               ("bf16", 128, 200, 32, 16, 16),
+                                               ("bf16", 64, 100, 1, 1, 8)])
 def test_pooled_correction_matches_the_oracle(dtype, dd, T, Vc, A, r):
     cfg = synth.CONFIGS["llama8b_t2048"].replace(L=2, H=4, T=T, d=dd, dtype=dtype, A=A, r=r,
                                                  seed=51 + Vc, fallback_prob=0.25)
@@ -33,7 +35,8 @@ def test_pooled_correction_matches_the_oracle(dtype, dd, T, Vc, A, r):
     case = synth.generate(cfg)
     p = synth.generate_pool(cfg, Vc)
     p["count"][0, 0] = 0  # an empty pool
-    p["count"][1, 1] = min(A - 1, Vc) if A > 1 else 1  # fewer valid slots than A
+    p["count"][1, 1] = A - 1 if A > 1 else 1  # fewer valid slots than A
+    p["count"][1, 2] = Vc  # a full pool
     q = oracle.pool(synth.to_f64(case.K0), synth.to_f64(case.V0))
     desc = synth.pool_descriptors(p, q)
     ed = case.edges[0]
