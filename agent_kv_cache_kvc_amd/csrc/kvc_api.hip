@@ -335,17 +335,58 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
   }
   if (L * H == 0) return ok();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (n_agents == 1) {  // one agent: the fused single launch
+    KVC_TRY(enqueue_correct(K, V, L, H, T, d, dtype, desc[0], U[0], W[0], A, r, tau, nullptr,
+                            nullptr, K_fb ? K_fb[0] : nullptr, V_fb ? V_fb[0] : nullptr,
+                            K_out[0], V_out[0], mask_out[0], score_out ? score_out[0] : nullptr,
+                            nullptr, false, ws, st));
+    return ok();
+  }
+  // Several agents: the reference is pooled once; each agent is matched from those chunk sums
+  // (the same pooled descriptor, bit for bit); then one launch per group of up to kMaxTargets
+  // agents reads each tile of the reference once and corrects it for every agent of the group.
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
-  // Agent 0 runs the fused pass, which leaves the reference's chunk sums in the workspace;
-  // every later agent is matched from those sums (the same pooled descriptor, bit for bit)
-  // and its correction reads the reference once.
-  const float* pool = reinterpret_cast<const float*>(static_cast<char*>(ws) + c.off_pool);
-  for (int j = 0; j < n_agents; ++j) {
-    const void* kf = K_fb ? K_fb[j] : nullptr;
-    const void* vf = V_fb ? V_fb[j] : nullptr;
-    KVC_TRY(enqueue_correct(K, V, L, H, T, d, dtype, desc[j], U[j], W[j], A, r, tau, nullptr,
-                            j == 0 ? nullptr : pool, kf, vf, K_out[j], V_out[j], mask_out[j],
-                            score_out ? score_out[j] : nullptr, nullptr, false, ws, st));
+  const int nc = kvc::chunks_of(T, d, dtype);
+  char* base = static_cast<char*>(ws);
+  float* pool = reinterpret_cast<float*>(base + c.off_pool);
+  float* wmt = reinterpret_cast<float*>(base + c.off_wmt);
+  uint8_t* mmt = reinterpret_cast<uint8_t*>(base + c.off_mmt);
+  int* ctr = reinterpret_cast<int*>(base + c.off_ctr);
+  KVC_HIP(kvc::launch_pool_partials(K, V, c.S, T, d, dtype, pool, nc, st), "pool");
+  for (int j0 = 0; j0 < n_agents; j0 += kvc::kMaxTargets) {
+    const int n = n_agents - j0 < kvc::kMaxTargets ? n_agents - j0 : kvc::kMaxTargets;
+    kvc::CorrectLaunch cl{};
+    cl.K = K;
+    cl.V = V;
+    cl.S = c.S;
+    cl.T = T;
+    cl.d = d;
+    cl.dtype = dtype;
+    cl.U = U[j0];
+    cl.W = W[j0];
+    cl.A = A;
+    cl.r = r;
+    cl.w_ws = wmt;
+    cl.mask_ws = mmt;
+    cl.K_out = K_out[j0];
+    cl.V_out = V_out[j0];
+    cl.ctr = ctr;
+    cl.n_t = n;
+    for (int j = 0; j < n; ++j) {
+      const int g = j0 + j;
+      KVC_HIP(kvc::launch_score(pool, nc, T, nullptr, desc[g], c.S, d, A, tau,
+                                wmt + (size_t)j * c.S * A, mmt + (size_t)j * c.S,
+                                score_out ? score_out[g] : nullptr, nullptr, mask_out[g], ctr,
+                                st),
+              "score");
+      cl.tU[j] = U[g];
+      cl.tW[j] = W[g];
+      cl.tK[j] = K_out[g];
+      cl.tV[j] = V_out[g];
+      cl.tKfb[j] = K_fb ? K_fb[g] : nullptr;
+      cl.tVfb[j] = V_fb ? V_fb[g] : nullptr;
+    }
+    KVC_HIP(kvc::launch_correct(cl, st), "correct");
   }
   return ok();
 }

@@ -510,6 +510,13 @@ struct CorrectArgs {
   const float* desc;       // fused: [S][A][2D] anchor descriptors
   const int* slot_ws;      // SEL: [S][A] pool slot of each selected anchor
   int Vc;                  // SEL: pool slots per segment (U, W hold Vc anchors per segment)
+  int n_t;                 // MT: targets corrected from one read of the source
+  const void* tU[kMaxTargets];   // MT: per-target factors, outputs and fallback caches; the
+  const void* tW[kMaxTargets];   //     weights and flags of target j are w_ws + j S A and
+  void* tK[kMaxTargets];         //     mask + j S
+  void* tV[kMaxTargets];
+  const void* tKfb[kMaxTargets];
+  const void* tVfb[kMaxTargets];
   uint8_t* mask_out;       // fused outputs
   float* score_out;
   float* w_out;
@@ -538,9 +545,14 @@ __device__ __forceinline__ void order_loads_after_signal() {
 // NA == 0: runtime A and r with up to NFG register-resident fragments.
 // SEL (not fused): anchor a of segment s is pool slot slot_ws[s][a] of Vc slots per segment
 // (the online anchor pool); otherwise anchor a is slot a of A.
-template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED, bool SEL = false>
+// MT (not fused): each item's tiles of the source are read once and corrected for n_t
+// targets in turn (one source, several agents), each with its own factors, weights, flag,
+// output and fallback cache.
+template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED, bool SEL = false,
+          bool MT = false>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   static_assert(!(SEL && FUSED), "pool slot selection runs in the matching kernel");
+  static_assert(!(MT && (FUSED || SEL || POOL_OUT)), "several targets: plain correction only");
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
   using TL = Tile<Tr, D>;
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 
     // ---- this wave's tiles of X, held in registers for the whole item (a segment already
     //      known to fall back to a fallback cache loads that cache instead)
-    const bool fb_known = !FUSED && Xfb != nullptr && args.mask[s] != 0;
+    const bool fb_known = !FUSED && !MT && Xfb != nullptr && args.mask[s] != 0;
     const elem* Xsrc = fb_known ? Xfb + seg : X;
     TL xr[NT];
     if (FUSED && pool_item) {
@@ -752,6 +764,31 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       goto next_item;
     }
 
+    float qs[NH][VEC];
+    if constexpr (POOL_OUT) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
+    }
+
+    // one target, or (MT) each target in turn on the same source tiles
+    for (int tj = 0; tj < (MT ? args.n_t : 1); ++tj) {
+    const elem* Ut = U;
+    const elem* Wt = W;
+    elem* Yt = Y;
+    const elem* Xfbt = Xfb;
+    const float* w_src = args.w_ws;
+    const uint8_t* m_src = args.mask;
+    if constexpr (MT) {
+      Ut = static_cast<const elem*>(args.tU[tj]);
+      Wt = static_cast<const elem*>(args.tW[tj]);
+      Yt = static_cast<elem*>(x == 0 ? args.tK[tj] : args.tV[tj]) + seg;
+      Xfbt = static_cast<const elem*>(x == 0 ? args.tKfb[tj] : args.tVfb[tj]);
+      w_src += (size_t)tj * S * A;
+      m_src += (size_t)tj * S;
+    }
+
     if constexpr (SEL) {
       if (tid < A) ssl[tid] = args.slot_ws[(size_t)s * A + tid];
       __syncthreads();
@@ -760,7 +797,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
     //      in the fused form this overlaps the wait for the segment's weights
     {
-      const elem* Wseg = W + ((size_t)x * S + s) * nslot * r * D;
+      const elem* Wseg = Wt + ((size_t)x * S + s) * nslot * r * D;
       const int n_w = A * r * (D / VEC);
       for (int q = tid; q < n_w; q += kBlock) {
         // k varies fastest across lanes, so the transposed LDS writes are contiguous
@@ -807,21 +844,34 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                                        __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
-      if (tid == 0) s_mask = args.mask[s];
-      if (tid < A) wsh[tid] = args.w_ws[(size_t)s * A + tid];
+      if (tid == 0) s_mask = m_src[s];
+      if (tid < A) wsh[tid] = w_src[(size_t)s * A + tid];
     }
     __syncthreads();
     const bool masked = s_mask != 0;
 
-    float qs[NH][VEC];
-    if constexpr (POOL_OUT) {
+    if (MT && masked) {
+      // dense-prefill stand-in of this target: its fallback cache (copied tile by tile, the
+      // source tiles stay in registers for the next target) or the source
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int tl = 0; tl < NT; ++tl) {
+        const int t0 = first + tl * kRowsPerPass;
+        if (tl < n_my) {
+          TL fb;
+          if (Xfbt != nullptr) load_tile<Tr, D, true>(Xfbt + seg, t0, T, lrow, lcol, fb);
+          const TL& src = Xfbt != nullptr ? fb : xr[tl];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
-    }
-
-    if (masked) {
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int j = 0; j < JN; ++j) {
+              const int tok = t0 + TPI * j + lrow;
+              if (tok < T)
+                __builtin_nontemporal_store(
+                    src.v[h][j], reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol));
+            }
+        }
+      }
+    } else if (masked) {
       // dense-prefill stand-in: the fallback cache, or the source, bit for bit
       if (Xfb != nullptr && !fb_known) {
 #pragma unroll
@@ -853,7 +903,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         }
       }
     } else {
-      const elem* Useg = U + ((size_t)x * S + s) * nslot * (size_t)T * r;
+      const elem* Useg = Ut + ((size_t)x * S + s) * nslot * (size_t)T * r;
       auto load_u = [&](frag (&dst)[NF], int t0) {
         const int t = t0 + ln;
         if (FIX && t0 + 32 <= T) {
@@ -967,7 +1017,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                   const u32x4 o = pack_out<Tr>(dv);
                   if (full || tok < T) {
                     __builtin_nontemporal_store(
-                        o, reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol));
+                        o, reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol));
                     if constexpr (POOL_OUT) {
                       float fo[VEC];
                       unpack_in<Tr>(o, fo);
@@ -998,7 +1048,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             const u32x4 o = pack_out<Tr>(dv);
             if (full || tok < T) {
               __builtin_nontemporal_store(  // L2 keeps the source for the second read
-                  o, reinterpret_cast<u32x4*>(Y + (size_t)tok * D + 64 * h + lcol));
+                  o, reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol));
               if constexpr (POOL_OUT) {
                 float fo[VEC];
                 unpack_in<Tr>(o, fo);
@@ -1023,6 +1073,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         if (n_my > 2) run_tile(std::integral_constant<int, 2>{}, ua, ub);
         if (n_my > 3) run_tile(std::integral_constant<int, 3>{}, ub, ua);
       }
+    }
+
+    if constexpr (MT) __syncthreads();  // LDS (W^T, weights) is free for the next target
     }
 
     if constexpr (POOL_OUT) {
@@ -1116,7 +1169,7 @@ hipError_t launch_select(const float* partials, int n_chunks, int T, const float
   return hipGetLastError();
 }
 
-template <class Tr, int D, int NA, int KSC, int NFG, bool SEL = false>
+template <class Tr, int D, int NA, int KSC, int NFG, bool SEL = false, bool MT = false>
 static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   const int PADK = 16 / (int)sizeof(typename Tr::elem);
   constexpr bool CMP = NA >= 6 && Tr::SLOT == 8 && KSC == 2;  // as in correct_kernel
@@ -1140,6 +1193,15 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.desc = L.desc;
   a.slot_ws = L.slot_ws;
   a.Vc = L.Vc;
+  a.n_t = L.n_t;
+  for (int j = 0; j < kMaxTargets; ++j) {
+    a.tU[j] = L.tU[j];
+    a.tW[j] = L.tW[j];
+    a.tK[j] = L.tK[j];
+    a.tV[j] = L.tV[j];
+    a.tKfb[j] = L.tKfb[j];
+    a.tVfb[j] = L.tVfb[j];
+  }
   a.mask_out = L.mask_out;
   a.score_out = L.score_out;
   a.w_out = L.w_out;
@@ -1155,6 +1217,8 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   void (*k)(CorrectArgs);
   if constexpr (SEL) {
     k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, true>;
+  } else if constexpr (MT) {
+    k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, false, true>;
   } else {
     k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
                         : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
@@ -1221,8 +1285,28 @@ static hipError_t correct_sel_t(CorrectLaunch L, hipStream_t st) {
   return correct_v<Tr, D, 0, 0, F2, true>(L, st);
 }
 
+// The multi-target correction: the 8B-shaped anchors (bf16, d = 128, A = 4, r = 32) take
+// their compile-time variant, every other shape the runtime-general kernel.
+template <class Tr, int D>
+static hipError_t correct_mt_t(CorrectLaunch L, hipStream_t st) {
+  L.rp = (L.r + Tr::RPAD - 1) / Tr::RPAD * Tr::RPAD;
+  if constexpr (Tr::SLOT == 8 && D == 128) {
+    if (L.r == 32 && L.A == 4) return correct_v<Tr, D, 4, 2, 0, false, true>(L, st);
+  }
+  const int nfrag = L.A * (L.rp / 2 / Tr::SLOT);
+  constexpr int F0 = Tr::MAXF / 4, F1 = Tr::MAXF / 2, F2 = Tr::MAXF;
+  if (nfrag <= F0) return correct_v<Tr, D, 0, 0, F0, false, true>(L, st);
+  if (nfrag <= F1) return correct_v<Tr, D, 0, 0, F1, false, true>(L, st);
+  return correct_v<Tr, D, 0, 0, F2, false, true>(L, st);
+}
+
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st) {
   if (L.S == 0) return hipSuccess;
+  if (L.n_t > 0) {
+    if (L.dtype == KVC_BF16)
+      return L.d == 128 ? correct_mt_t<TrBF16, 128>(L, st) : correct_mt_t<TrBF16, 64>(L, st);
+    return L.d == 128 ? correct_mt_t<TrF32, 128>(L, st) : correct_mt_t<TrF32, 64>(L, st);
+  }
   if (L.slot_ws != nullptr) {
     if (L.dtype == KVC_BF16)
       return L.d == 128 ? correct_sel_t<TrBF16, 128>(L, st) : correct_sel_t<TrBF16, 64>(L, st);

@@ -17,6 +17,7 @@ constexpr int kMaxA = 16;             // anchors per segment held in registers
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
 constexpr int kMaxPool = 32;          // slots of an online anchor pool per segment
+constexpr int kMaxTargets = 8;        // targets of one multi-target correction launch
 constexpr int kJacobiMaxSweeps = 40;  // hard cap: every workgroup leaves the sweep loop
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -66,6 +67,8 @@ struct CorrectLayout {
   size_t off_done;    // int [S]: per-segment counters of the fused pass
   size_t off_ctr;     // int [kMaxQueues]: work counters of the correction pass
   size_t off_slot;    // int [S][A]: pool slots of the selected anchors (pooled correction)
+  size_t off_wmt;     // float [kMaxTargets][S][A]: weights of a multi-target launch
+  size_t off_mmt;     // uint8 [kMaxTargets][S]: flags of a multi-target launch
   size_t bytes;
 };
 
@@ -85,6 +88,8 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_done = o;  o = align_up(o + sizeof(int) * (size_t)c.S, 256);
   c.off_ctr = o;   o = align_up(o + sizeof(int) * kMaxQueues, 256);
   c.off_slot = o;  o = align_up(o + sizeof(int) * (size_t)c.S * A, 256);
+  c.off_wmt = o;   o = align_up(o + sizeof(float) * (size_t)kMaxTargets * c.S * A, 256);
+  c.off_mmt = o;   o = align_up(o + (size_t)kMaxTargets * c.S, 256);
   c.bytes = o;
   return c;
 }
@@ -111,6 +116,13 @@ struct CorrectLaunch {
   const float* desc;        // fused: anchor descriptors
   const int* slot_ws;       // pooled correction: [S][A] slots of Vc per segment, or null
   int Vc;
+  int n_t;                  // multi-target correction: 0 (off) or the targets below (w_ws and
+  const void* tU[kMaxTargets];  // mask_ws then hold n_t blocks of [S][A] weights / [S] flags)
+  const void* tW[kMaxTargets];
+  void* tK[kMaxTargets];
+  void* tV[kMaxTargets];
+  const void* tKfb[kMaxTargets];
+  const void* tVfb[kMaxTargets];
   float tau;
   uint8_t* mask_out;        // fused: matching outputs
   float* score_out;

@@ -133,9 +133,10 @@ kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T
  * cache).  One reference (K, V), n_agents targets: agent j's output is exactly what
  * kvc_correct(K, V, desc[j], U[j], W[j], ...) stores, and its mask, score and weights are
  * the same.  The reference is pooled once (every agent is matched against the same pooled
- * descriptor, bit for bit); agent 0's pass is the fused single launch, every later agent
- * takes the matching kernel and one read of the reference.  The same call serves one agent
- * whose cache feeds several successors on a workflow graph.
+ * descriptor, bit for bit); then one correction launch per group of up to 8 agents reads
+ * each tile of the reference once and corrects it for every agent of the group (a single
+ * agent takes kvc_correct's fused launch).  The same call serves one agent whose cache feeds
+ * several successors on a workflow graph.
  *   n_agents >= 1.  desc, U, W, K_out, V_out, mask_out: HOST arrays of n_agents DEVICE
  *   pointers laid out as for kvc_correct; K_fb / V_fb (the array or an entry, both or
  *   neither per agent) and score_out may be NULL.  No output may overlap the reference or
