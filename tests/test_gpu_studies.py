@@ -58,11 +58,16 @@ def test_fanout_matches_the_oracle(dtype, d, T, A, r):
     assert n_fall > 0
 
 
-def test_fanout_equals_one_correction_per_agent_bit_for_bit():
-    """Each agent's output, mask and score equal a kvc_correct call on the same inputs: agents
-    after the first are matched from the reference's chunk sums left by the first pass."""
-    cfg = synth.CONFIGS["llama8b_t2048"].replace(L=4, H=4, T=1300, seed=42, n_edges=4,
-                                                 fallback_prob=0.3)
+@pytest.mark.parametrize("n_agents,A,r,dtype", [(4, 4, 32, "bf16"), (9, 3, 16, "bf16"),
+                                                (2, 2, 8, "f32")])
+def test_fanout_equals_one_correction_per_agent_bit_for_bit(n_agents, A, r, dtype):
+    """Each agent's output, mask and score equal a kvc_correct call on the same inputs: every
+    agent is matched from the reference's chunk sums, and the multi-target correction (up to
+    8 agents per launch; 9 agents take two launches) does each agent's arithmetic exactly as
+    the single-target kernel."""
+    cfg = synth.CONFIGS["llama8b_t2048"].replace(L=4, H=4, T=1300, seed=42 + n_agents,
+                                                 n_edges=n_agents, fallback_prob=0.3, A=A, r=r,
+                                                 dtype=dtype)
     say(f"[fanout-vs-correct] L={cfg.L} H={cfg.H} T={cfg.T} agents={cfg.n_edges}")
     case, _, ag_g = _fanout_inputs(cfg, with_fb=True)
     K, V = case.K0.to(dev()), case.V0.to(dev())
