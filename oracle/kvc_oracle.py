@@ -93,9 +93,11 @@ def cosine_scores(q, desc) -> np.ndarray:
     q = np.asarray(q, dtype=np.float64)
     desc = np.asarray(desc, dtype=np.float64)
     dots = np.einsum("...k,...ak->...a", q, desc)
-    nq = np.sqrt(np.einsum("...k,...k->...", q, q))[..., None]
-    nd = np.sqrt(np.einsum("...ak,...ak->...a", desc, desc))
-    den = nq * nd
+    qq = np.einsum("...k,...k->...", q, q)[..., None]
+    dd = np.einsum("...ak,...ak->...a", desc, desc)
+    # ||q|| ||d|| as one square root of the product of the squared norms (one rounding fewer
+    # than a product of two roots: parallel vectors with exact squared norms give exactly 1)
+    den = np.sqrt(qq * dd)
     with np.errstate(invalid="ignore", divide="ignore"):
         s = np.where(den == 0, 0.0, dots / np.where(den == 0, 1.0, den))
     return s
@@ -119,15 +121,12 @@ def reliability(s, tau):
     Fig. 1(a): a shared segment's cache is reused when its correction is reliable and
     falls back to dense prefill otherwise; Table 3 gives one threshold tau per workload.
     Reading: the reliability score is the best anchor cosine and the comparison is
-    strict (score == tau reuses).  The decision is taken in float32, the precision in
-    which the GPU kernel holds the score and tau: the float64 score is rounded to float32
-    and compared with float32(tau).
+    strict (score == tau reuses, score < tau falls back); a NaN score compares false
+    and falls back.  Score and tau are compared as float64 values, tau as passed.
     """
     s = np.asarray(s, dtype=np.float64)
     score = np.max(s, axis=-1)  # NaN propagates
-    s32 = score.astype(np.float32)
-    t32 = np.float32(tau)
-    mask = ~(s32 >= t32)
+    mask = ~(score >= np.float64(tau))
     return score, mask.astype(np.uint8)
 
 
@@ -277,8 +276,7 @@ def correct_pooled(K, V, anchor_pool: dict, A: int, tau, dtype, K_fb=None, V_fb=
     q = pool(K, V)
     s = cosine_scores(q, anchor_pool["desc"])
     slots, w, score = select_anchors(s, anchor_pool["count"], A)
-    s32 = score.astype(np.float32)
-    mask = (~(s32 >= np.float32(tau))).astype(np.uint8)
+    mask = (~(score >= np.float64(tau))).astype(np.uint8)
     L, H = K.shape[:2]
     outs = []
     for x, (X, X_fb) in enumerate(((K, K_fb), (V, V_fb))):
@@ -324,7 +322,7 @@ def pool_insert(pool_state: dict, mask, U_new, W_new, q, dtype) -> dict:
             j = int(st["head"][l, h])
             st["U"][:, l, h, j] = round_to_dtype(np.asarray(U_new)[:, l, h], dtype)
             st["W"][:, l, h, j] = round_to_dtype(np.asarray(W_new)[:, l, h], dtype)
-            st["desc"][l, h, j] = np.asarray(q, dtype=np.float64)[l, h].astype(np.float32)
+            st["desc"][l, h, j] = round_to_dtype(np.asarray(q)[l, h], "f32")  # float32 pool
             st["head"][l, h] = (j + 1) % Vc
             st["count"][l, h] = min(int(st["count"][l, h]) + 1, Vc)
     return st

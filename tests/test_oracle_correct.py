@@ -34,7 +34,7 @@ def _brute_correct(K, V, desc, U, W, tau, K_fb=None, V_fb=None):
             m = max(s)
             ex = [math.exp(v - m) for v in s]
             w = [v / sum(ex) for v in ex]
-            fall = not (np.float32(m) >= np.float32(tau))
+            fall = not (m >= tau)  # NaN compares false: falls back
             masks[l, h] = fall
             for x, (X, Xfb, out) in enumerate(((K, K_fb, outK), (V, V_fb, outV))):
                 for t in range(T):

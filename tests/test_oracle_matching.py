@@ -149,9 +149,19 @@ def test_reliability_threshold_edges():
     assert list(mask) == [0, 1, 1]
     assert list(oracle.reliability(s, np.inf)[1]) == [1, 1, 1]
     assert list(oracle.reliability(s, -np.inf)[1]) == [0, 0, 1]
-    # the decision is taken in float32: a float64 score one float64-ulp below
-    # float32(tau) that rounds up to it reuses
+    # strict "<" on the float64 values: one float64 ulp below tau falls back, tau itself and
+    # one ulp above reuse (no rounding of either side)
+    for tau in (0.32, 0.6, 0.3, -0.2, 1.0):
+        below, above = np.nextafter(tau, -np.inf), np.nextafter(tau, np.inf)
+        assert oracle.reliability(np.array([below]), tau)[1] == 1
+        assert oracle.reliability(np.array([tau]), tau)[1] == 0
+        assert oracle.reliability(np.array([above]), tau)[1] == 0
+    # a score between float32(tau) and tau falls back, although score and tau would round
+    # to the same float32 value
     t32 = float(np.float32(0.32))
-    just_below = np.nextafter(t32, 0.0)
-    assert oracle.reliability(np.array([just_below]), 0.32)[1] == 0
-    assert oracle.reliability(np.array([float(np.nextafter(np.float32(t32), np.float32(0)))]), 0.32)[1] == 1
+    mid = 0.5 * (0.32 + t32)
+    assert t32 < mid < 0.32 and float(np.float32(mid)) == t32
+    assert oracle.reliability(np.array([mid]), 0.32)[1] == 1
+    # the score is the best cosine, whatever the other anchors hold; -inf never reuses
+    assert oracle.reliability(np.array([[-np.inf, 0.5]]), 0.5)[1][0] == 0
+    assert oracle.reliability(np.array([[-np.inf]]), -1e300)[1][0] == 1
