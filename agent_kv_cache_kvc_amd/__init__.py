@@ -27,6 +27,8 @@ import torch
 
 __all__ = [
     "KvcError",
+    "KvcWaitError",
+    "check_mask",
     "CorrectResult",
     "FitResult",
     "lib",
@@ -73,6 +75,7 @@ _sz = ctypes.c_size_t
 _SIGS = {
     "kvc_version": (ctypes.c_char_p, []),
     "kvc_last_error": (ctypes.c_char_p, []),
+    "kvc_test_fused_wait": (None, [ctypes.c_longlong, _i]),
     "kvc_pool_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_pool_descriptor": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "kvc_correct_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -126,6 +129,21 @@ def _check(status: int) -> None:
         raise KvcError(status, lib().kvc_last_error().decode())
 
 
+class KvcWaitError(RuntimeError):
+    """A segment of the single-launch correction pass gave up waiting for its matching result
+    (mask value 2): the segment was copied through as for a fallback."""
+
+
+def check_mask(mask: torch.Tensor) -> torch.Tensor:
+    """Raise KvcWaitError if any segment of a correction's fallback mask carries the value 2
+    (see mask_out of kvc_correct in include/kvc.h).  Synchronises with the mask's stream."""
+    bad = (mask == 2).nonzero()
+    if bad.numel():
+        raise KvcWaitError(f"{bad.shape[0]} segment(s) gave up waiting in the single-launch "
+                           f"pass and were copied through, first (l, h) = {tuple(bad[0].tolist())}")
+    return mask
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
@@ -157,6 +175,22 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _ws(workspace: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    """The caller's workspace after checking it (device, contiguity; the library checks its
+    size and alignment), or a new one of ``nbytes``."""
+    if workspace is None:
+        return _workspace(nbytes, device)
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace
+
+
+def _ws_bytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
 def correct_workspace_bytes(L, H, T, d, A, r) -> int:
     return int(lib().kvc_correct_workspace_bytes(L, H, T, d, A, r))
 
@@ -180,9 +214,9 @@ def pool_descriptor(K: torch.Tensor, V: torch.Tensor, *, out: Optional[torch.Ten
     q = out if out is not None else torch.empty(L, H, 2 * d, dtype=torch.float32, device=dev)
     _need(q, "q_out", (L, H, 2 * d), torch.float32, dev)
     nb = int(lib().kvc_pool_workspace_bytes(L, H, T, d))
-    ws = workspace if workspace is not None else _workspace(nb, dev)
+    ws = _ws(workspace, nb, dev)
     _check(lib().kvc_pool_descriptor(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(q), _ptr(ws),
-                                     ws.numel(), _stream(dev)))
+                                     _ws_bytes(ws), _stream(dev)))
     return q
 
 
@@ -202,11 +236,14 @@ def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tenso
             K_fb: Optional[torch.Tensor] = None, V_fb: Optional[torch.Tensor] = None,
             K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
             want_score: bool = True, want_w: bool = True, want_q_next: bool = False,
-            workspace: Optional[torch.Tensor] = None) -> CorrectResult:
+            workspace: Optional[torch.Tensor] = None, check: bool = True) -> CorrectResult:
     """Correct a reused cache with its segments' anchors (see kvc_correct in include/kvc.h).
 
     K, V: [L, H, T, d]; desc: [L, H, A, 2d] float32; U: [2, L, H, A, T, r];
     W: [2, L, H, A, r, d] (cache dtype).  Pass K_out=K, V_out=V to correct in place.
+    check: raise KvcWaitError if a segment of the single-launch pass gave up waiting
+    (mask 2).  That check synchronises with the stream; pass False in a timed loop and call
+    check_mask(result.mask) afterwards.
     """
     L, H, T, d = K.shape
     dev = K.device
@@ -231,11 +268,13 @@ def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tenso
     score = torch.empty(L, H, dtype=torch.float32, device=dev) if want_score else None
     w = torch.empty(L, H, A, dtype=torch.float32, device=dev) if want_w else None
     qn = torch.empty(L, H, 2 * d, dtype=torch.float32, device=dev) if want_q_next else None
-    ws = workspace if workspace is not None else _workspace(correct_workspace_bytes(L, H, T, d, A, r), dev)
+    ws = _ws(workspace, correct_workspace_bytes(L, H, T, d, A, r), dev)
     _check(lib().kvc_correct(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(desc), _ptr(U), _ptr(W), A,
                              r, float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
                              _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(qn), _ptr(ws),
-                             ws.numel(), _stream(dev)))
+                             _ws_bytes(ws), _stream(dev)))
+    if check and q_in is None:
+        check_mask(mask)
     return CorrectResult(Ko, Vo, mask, score, w, qn)
 
 
@@ -248,11 +287,13 @@ def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
 
 def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau: float, *,
                   outputs: Optional[Sequence[tuple]] = None,
-                  workspace: Optional[torch.Tensor] = None) -> list:
+                  workspace: Optional[torch.Tensor] = None, check: bool = True) -> list:
     """Chained correction A0 -> A1 -> ... (see kvc_correct_chain in include/kvc.h).
 
     ``edges``: one dict per edge with desc, U, W and optionally K_fb, V_fb.  ``outputs``:
     optional preallocated (K_out, V_out) per edge.  Returns one CorrectResult per edge.
+    check: raise KvcWaitError if a segment of edge 0's single-launch pass gave up waiting
+    (synchronises; see correct).
     """
     L, H, T, d = K0.shape
     dev = K0.device
@@ -262,7 +303,10 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
         raise ValueError("need at least one edge")
     A = edges[0]["desc"].shape[2]
     r = edges[0]["U"].shape[-1]
-    _need(V0, "V0", K0.shape, K0.dtype, dev)
+    _need(K0, "K0", (L, H, T, d), K0.dtype, dev)
+    _need(V0, "V0", (L, H, T, d), K0.dtype, dev)
+    if outputs is not None and len(outputs) != n:
+        raise ValueError(f"outputs holds {len(outputs)} pairs for {n} edges")
     res = []
     for e, ed in enumerate(edges):
         _need(ed["desc"], f"desc[{e}]", (L, H, A, 2 * d), torch.float32, dev)
@@ -273,13 +317,14 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
                 _need(ed[name], f"{name}[{e}]", K0.shape, K0.dtype, dev)
         if outputs is not None:
             Ko, Vo = outputs[e]
+            _need(Ko, f"K_out[{e}]", (L, H, T, d), K0.dtype, dev)
+            _need(Vo, f"V_out[{e}]", (L, H, T, d), K0.dtype, dev)
         else:
             Ko, Vo = torch.empty_like(K0), torch.empty_like(V0)
         res.append(CorrectResult(Ko, Vo, torch.empty(L, H, dtype=torch.uint8, device=dev),
                                  torch.empty(L, H, dtype=torch.float32, device=dev)))
     has_fb = [ed.get("K_fb") is not None for ed in edges]
-    ws = workspace if workspace is not None else _workspace(
-        int(lib().kvc_chain_workspace_bytes(L, H, T, d, A, r)), dev)
+    ws = _ws(workspace, int(lib().kvc_chain_workspace_bytes(L, H, T, d, A, r)), dev)
     _check(lib().kvc_correct_chain(
         _ptr(K0), _ptr(V0), L, H, T, d, dt, n,
         _ptr_array([ed["desc"] for ed in edges]), _ptr_array([ed["U"] for ed in edges]),
@@ -288,16 +333,19 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
         _ptr_array([ed.get("V_fb") for ed in edges]) if any(has_fb) else None,
         _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
-        _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(ws), _ws_bytes(ws), _stream(dev)))
+    if check:
+        check_mask(res[0].mask)
     return res
 
 
 def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau: float, *,
                    outputs: Optional[Sequence[tuple]] = None,
-                   workspace: Optional[torch.Tensor] = None) -> list:
+                   workspace: Optional[torch.Tensor] = None, check: bool = True) -> list:
     """Non-chained correction of one reference cache toward several agents (see
     kvc_correct_fanout in include/kvc.h).  ``agents``: one dict per agent with desc, U, W
-    and optionally K_fb, V_fb.  Returns one CorrectResult per agent."""
+    and optionally K_fb, V_fb.  Returns one CorrectResult per agent.  check: as for
+    correct (a single agent takes the single-launch pass)."""
     L, H, T, d = K.shape
     dev = K.device
     dt = _dtype_code(K)
@@ -306,8 +354,10 @@ def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau
         raise ValueError("need at least one agent")
     A = agents[0]["desc"].shape[2]
     r = agents[0]["U"].shape[-1]
-    _need(K, "K", K.shape, K.dtype, dev)
-    _need(V, "V", K.shape, K.dtype, dev)
+    _need(K, "K", (L, H, T, d), K.dtype, dev)
+    _need(V, "V", (L, H, T, d), K.dtype, dev)
+    if outputs is not None and len(outputs) != n:
+        raise ValueError(f"outputs holds {len(outputs)} pairs for {n} agents")
     res = []
     for j, ag in enumerate(agents):
         _need(ag["desc"], f"desc[{j}]", (L, H, A, 2 * d), torch.float32, dev)
@@ -318,13 +368,14 @@ def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau
                 _need(ag[name], f"{name}[{j}]", K.shape, K.dtype, dev)
         if outputs is not None:
             Ko, Vo = outputs[j]
+            _need(Ko, f"K_out[{j}]", (L, H, T, d), K.dtype, dev)
+            _need(Vo, f"V_out[{j}]", (L, H, T, d), K.dtype, dev)
         else:
             Ko, Vo = torch.empty_like(K), torch.empty_like(V)
         res.append(CorrectResult(Ko, Vo, torch.empty(L, H, dtype=torch.uint8, device=dev),
                                  torch.empty(L, H, dtype=torch.float32, device=dev)))
     has_fb = any(ag.get("K_fb") is not None for ag in agents)
-    ws = workspace if workspace is not None else _workspace(
-        int(lib().kvc_fanout_workspace_bytes(L, H, T, d, A, r)), dev)
+    ws = _ws(workspace, int(lib().kvc_fanout_workspace_bytes(L, H, T, d, A, r)), dev)
     _check(lib().kvc_correct_fanout(
         _ptr(K), _ptr(V), L, H, T, d, dt, n,
         _ptr_array([ag["desc"] for ag in agents]), _ptr_array([ag["U"] for ag in agents]),
@@ -333,7 +384,9 @@ def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau
         _ptr_array([ag.get("V_fb") for ag in agents]) if has_fb else None,
         _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
-        _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(ws), _ws_bytes(ws), _stream(dev)))
+    if check and n == 1:
+        check_mask(res[0].mask)
     return res
 
 
@@ -387,17 +440,18 @@ def correct_pooled(K: torch.Tensor, V: torch.Tensor, pool: AnchorPool, A: int, t
             _need(t, name, (L, H, T, d), K.dtype, dev)
     Ko = K_out if K_out is not None else torch.empty_like(K)
     Vo = V_out if V_out is not None else torch.empty_like(V)
+    _need(Ko, "K_out", (L, H, T, d), K.dtype, dev)
+    _need(Vo, "V_out", (L, H, T, d), K.dtype, dev)
     mask = torch.empty(L, H, dtype=torch.uint8, device=dev)
     score = torch.empty(L, H, dtype=torch.float32, device=dev)
     w = torch.empty(L, H, A, dtype=torch.float32, device=dev)
     slots = torch.empty(L, H, A, dtype=torch.int32, device=dev)
-    ws = workspace if workspace is not None else _workspace(
-        lib().kvc_correct_pooled_workspace_bytes(L, H, T, d, A, r), dev)
+    ws = _ws(workspace, lib().kvc_correct_pooled_workspace_bytes(L, H, T, d, A, r), dev)
     _check(lib().kvc_correct_pooled(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(pool.desc),
                                     _ptr(pool.U), _ptr(pool.W), _ptr(pool.count), Vc, int(A), r,
                                     float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
                                     _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(slots),
-                                    _ptr(ws), ws.numel(), _stream(dev)))
+                                    _ptr(ws), _ws_bytes(ws), _stream(dev)))
     return CorrectResult(Ko, Vo, mask, score, w, slots=slots)
 
 
@@ -435,10 +489,9 @@ def segment_error(X: torch.Tensor, ref: torch.Tensor, *, out: Optional[torch.Ten
     _need(ref, "ref", (L, H, T, d), X.dtype, dev)
     o = out if out is not None else torch.empty(L, H, 2, dtype=torch.float64, device=dev)
     _need(o, "out", (L, H, 2), torch.float64, dev)
-    ws = workspace if workspace is not None else _workspace(
-        lib().kvc_segment_error_workspace_bytes(L, H, T, d), dev)
+    ws = _ws(workspace, lib().kvc_segment_error_workspace_bytes(L, H, T, d), dev)
     _check(lib().kvc_segment_error(_ptr(X), _ptr(ref), L, H, T, d, dt, _ptr(o), _ptr(ws),
-                                   ws.numel(), _stream(dev)))
+                                   _ws_bytes(ws), _stream(dev)))
     return o
 
 
@@ -472,9 +525,9 @@ def fit_anchor(delta: torch.Tensor, r: int = 32, energy: float = 0.9, *, want_ei
     W = torch.empty(M, r, d, dtype=torch.float32, device=dev)
     k = torch.empty(M, dtype=torch.int32, device=dev)
     eig = torch.empty(M, d, dtype=torch.float32, device=dev) if want_eig else None
-    ws = workspace if workspace is not None else _workspace(fit_workspace_bytes(M, T, d, r), dev)
+    ws = _ws(workspace, fit_workspace_bytes(M, T, d, r), dev)
     _check(lib().kvc_fit_anchor(_ptr(delta), M, T, d, dt, int(r), float(energy), _ptr(U),
-                                _ptr(W), _ptr(k), _ptr(eig), _ptr(ws), ws.numel(), _stream(dev)))
+                                _ptr(W), _ptr(k), _ptr(eig), _ptr(ws), _ws_bytes(ws), _stream(dev)))
     return FitResult(U, W, k, eig)
 
 
@@ -489,9 +542,8 @@ def gram_accumulate(delta: torch.Tensor, G: Optional[torch.Tensor] = None, *,
     if G is None:
         G = torch.zeros(M, d, d, dtype=torch.float64, device=dev)
     _need(G, "G", (M, d, d), torch.float64, dev)
-    ws = workspace if workspace is not None else _workspace(
-        lib().kvc_gram_workspace_bytes(M, T, d), dev)
-    _check(lib().kvc_gram_accumulate(_ptr(delta), M, T, d, dt, _ptr(G), _ptr(ws), ws.numel(),
+    ws = _ws(workspace, lib().kvc_gram_workspace_bytes(M, T, d), dev)
+    _check(lib().kvc_gram_accumulate(_ptr(delta), M, T, d, dt, _ptr(G), _ptr(ws), _ws_bytes(ws),
                                      _stream(dev)))
     return G
 
@@ -522,7 +574,7 @@ def project(delta: torch.Tensor, W: torch.Tensor, *,
     _need(W, "W", (M, r, d), torch.float32, dev)
     U = torch.empty(M, T, r, dtype=torch.float32, device=dev)
     need = lib().kvc_project_workspace_bytes(M, d, r, dt)
-    ws = workspace if workspace is not None else (_workspace(need, dev) if need else None)
+    ws = _ws(workspace, need, dev) if (need or workspace is not None) else None
     _check(lib().kvc_project(_ptr(delta), M, T, d, dt, _ptr(W), r, _ptr(U), _ptr(ws),
-                             0 if ws is None else ws.numel(), _stream(dev)))
+                             0 if ws is None else _ws_bytes(ws), _stream(dev)))
     return U

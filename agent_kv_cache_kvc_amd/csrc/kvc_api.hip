@@ -90,6 +90,10 @@ const char* kvc_version(void) { return "kvc 0.1.0 gfx950"; }
 
 const char* kvc_last_error(void) { return g_err; }
 
+void kvc_test_fused_wait(long long wait_ticks, int withhold_segment) {
+  kvc::set_fused_wait_for_tests(wait_ticks, withhold_segment);
+}
+
 // --------------------------------------------------------------------------- pooling
 size_t kvc_pool_workspace_bytes(int L, int H, int T, int d) {
   if (L < 0 || H < 0 || T < 0 || d <= 0) return 0;

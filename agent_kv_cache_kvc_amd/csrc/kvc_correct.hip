@@ -110,9 +110,10 @@ __device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
   }
 }
 
-// One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).  LAST: the
-// last read of these bytes in this launch, issued non-temporal so the lines leave L2 first (the
-// fused pass keeps its pooling reads in L2 for the correction's second read).
+// One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).  LAST: issued
+// as non-temporal loads, so single-use lines leave L2 first.  Every read of K, V and the fallback
+// caches in this file takes it, both reads of the fused pass included (temporal pooling reads,
+// meant to keep a chunk in L2 for the correction's second read, measured slower).
 template <class Tr, int D, bool LAST = false>
 __device__ __forceinline__ void load_tile(const typename Tr::elem* __restrict__ X, int t0, int T,
                                           int lrow, int lcol, Tile<Tr, D>& tile) {
@@ -520,16 +521,33 @@ struct CorrectArgs {
   uint8_t* mask_out;       // fused outputs
   float* score_out;
   float* w_out;
+  long long wait_ticks;    // fused: limit of a correction item's wait (constant-clock ticks)
+  int withhold;            // fused: segment whose matching is not published (tests), or -1
   float tau;
   int T, S, A, r, rp, n_chunks, n_items;
   int batch, lead;         // fused: segments per slot, pooling slots ahead of correction
   int nq;                  // fused: queues (workgroup b serves queue b mod nq)
 };
 
-// Bounded wait of a correction item of the fused form: 0.2 s of the 100 MHz constant clock.
-// A safety net that the queue order above never reaches; if it were reached the segment is
-// flagged with mask value 2 and its output is the copy-through.
+// Bounded wait of a correction item of the fused form: 0.2 s of the 100 MHz constant clock by
+// default.  A safety net that the queue order above never reaches.  An item that reaches it
+// sets kGaveUp in the segment's counter (only while the segment is still unmatched, by
+// compare-and-swap), writes mask value 2 and copies its tiles through; every later item of the
+// segment sees the flag and copies through too, and the matching item, whose publishing add
+// returns the flag, writes mask value 2 as well.  So a segment is either corrected (or falls
+// back) as a whole, or is copied through as a whole with mask 2.
 constexpr long long kWaitTicks = 20000000ll;
+constexpr int kGaveUp = 1 << 30;  // above any item count: the counters stay below 2^30
+
+// Test hook (kvc_test_fused_wait): the wait limit of later fused launches, and one segment
+// whose matching result is withheld so that its correction items reach that limit.
+static long long g_wait_ticks = kWaitTicks;
+static int g_withhold_segment = -1;
+
+void set_fused_wait_for_tests(long long ticks, int withhold_segment) {
+  g_wait_ticks = ticks > 0 ? ticks : kWaitTicks;
+  g_withhold_segment = withhold_segment;
+}
 
 __device__ __forceinline__ void order_stores_before_signal() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -569,7 +587,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   // CMP (compact LDS, bf16 anchor counts of 6 and more at r = 32): W^T rows are stored
   // unpadded with their 16-byte chunks XOR-swizzled by bits 2-3 of the row (the 16 rows that
   // one quarter-wave reads then fall into 16 distinct bank groups), and the MFMA results are
-  // staged one 32-channel block at a time, so two workgroups still fit in a CU's LDS.
+  // staged one 32-channel block at a time.  Two workgroups then fit in a CU's 160 KB of LDS at
+  // A = 6 (about 70 KB each); at A = 8 one does (about 87 KB), and the launcher sizes the
+  // persistent grid from the occupancy it gets.
   constexpr bool CMP = NA >= 6 && SLOT == 8 && KSC == 2;
   constexpr int SROW = CMP ? 36 : kStageRow;  // floats per staged token row
 
@@ -681,15 +701,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const bool fb_known = !FUSED && !MT && Xfb != nullptr && args.mask[s] != 0;
     const elem* Xsrc = fb_known ? Xfb + seg : X;
     TL xr[NT];
-    if (FUSED && pool_item) {
 #pragma unroll
-      for (int tl = 0; tl < NT; ++tl)
-        load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
-    } else {
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl)
-        load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
-    }
+    for (int tl = 0; tl < NT; ++tl)
+      load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
 
     if (FUSED && pool_item) {
       // fields used only here are read through an opaque pointer to the kernel arguments,
@@ -714,8 +728,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       order_stores_before_signal();
       __syncthreads();
       if (tid == 0)
-        s_last = __hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == n_ci - 1;
+        s_last = (__hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) & ~kGaveUp) == n_ci - 1;
       __syncthreads();
       if (s_last) {
         // the segment's last item to count matches it: q (one thread per channel, chunk
@@ -751,14 +765,14 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                                __HIP_MEMORY_SCOPE_AGENT);
             if (pa->w_out) pa->w_out[(size_t)s * A + lane] = wv;
           }
-          if (lane == 0) {
-            pa->mask_out[s] = fall;
-            if (pa->score_out) pa->score_out[s] = score;
-          }
+          if (lane == 0 && pa->score_out) pa->score_out[s] = score;
           order_stores_before_signal();
-          if (lane == 0)
-            __hip_atomic_fetch_add(pa->done + s, 1 + (int)fall, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0 && s != pa->withhold) {
+            // publish; a correction item that gave up before this shows in the old value
+            const int old = __hip_atomic_fetch_add(pa->done + s, 1 + (int)fall, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            pa->mask_out[s] = (old & kGaveUp) ? 2 : fall;
+          }
         }
       }
       goto next_item;
@@ -795,8 +809,11 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     }
 
     // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
-    //      in the fused form this overlaps the wait for the segment's weights
-    {
+    //      in the fused form this overlaps the wait for the segment's weights.  Without the
+    //      fused pass the flag is known before the launch and a falling-back segment stages
+    //      nothing (its factors are not read).
+    const bool pre_masked = !FUSED && m_src[s] != 0;  // same address in every lane
+    if (!pre_masked) {
       const elem* Wseg = Wt + ((size_t)x * S + s) * nslot * r * D;
       const int n_w = A * r * (D / VEC);
       for (int q = tid; q < n_w; q += kBlock) {
@@ -829,15 +846,23 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
         int* done = args.done + s;
         int v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (v <= n_ci) {
-          const long long t_end = wall_clock64() + kWaitTicks;
+          const long long t_end = wall_clock64() + args.wait_ticks;
           do {
             __builtin_amdgcn_s_sleep(2);
             v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           } while (v <= n_ci && wall_clock64() < t_end);
-          if (v <= n_ci) args.mask_out[s] = 2;
+          // give up only while the segment is unmatched: each failed swap saw the count move,
+          // so the loop ends (the count is at most n_ci + 2)
+          while (v <= n_ci) {
+            if (__hip_atomic_compare_exchange_strong(done, &v, v | kGaveUp, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+              args.mask_out[s] = 2;
+              v |= kGaveUp;
+            }
+          }
         }
         order_loads_after_signal();
-        s_mask = v != n_ci + 1;
+        s_mask = v != n_ci + 1;  // fallback, or given up (flag set)
         if (v == n_ci + 1)
           for (int a = 0; a < A; ++a)
             wsh[a] = __hip_atomic_load(args.w_ws + (size_t)s * A + a, __ATOMIC_RELAXED,
@@ -876,7 +901,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       if (Xfb != nullptr && !fb_known) {
 #pragma unroll
         for (int tl = 0; tl < NT; ++tl)
-          load_tile<Tr, D>(Xfb + seg, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
+          load_tile<Tr, D, true>(Xfb + seg, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
       }
       const bool store = Xfb != nullptr || Y != X;  // in place with no fallback: unchanged
 #pragma unroll
@@ -1105,6 +1130,25 @@ static int device_cus() {
   return cache[dev];
 }
 
+// Workgroups of `k` (kBlock threads, `lds` bytes of dynamic LDS) resident per CU, from the
+// runtime's occupancy calculator (at least 1; at most 2, the persistent grid's target).  Cached
+// per kernel and LDS size.
+static int resident_per_cu(const void* k, size_t lds) {
+  struct Entry { const void* k; size_t lds; int dev; int n; };
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == k && cache[i].lds == lds && cache[i].dev == dev) return cache[i].n;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kBlock, lds) != hipSuccess || n < 1)
+    n = 1;
+  if (n > 2) n = 2;
+  if (used < 64) cache[used++] = Entry{k, lds, dev, n};
+  return n;
+}
+
 // ------------------------------------------------------------------------- launchers
 template <class Tr, int D>
 static hipError_t pool_partials_t(const void* K, const void* V, int S, int T, float* partials,
@@ -1205,6 +1249,8 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.mask_out = L.mask_out;
   a.score_out = L.score_out;
   a.w_out = L.w_out;
+  a.wait_ticks = g_wait_ticks;
+  a.withhold = g_withhold_segment;
   a.tau = L.tau;
   a.T = L.T;
   a.S = L.S;
@@ -1229,7 +1275,8 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int want = L.fused ? 2 * L.S * 2 * a.n_chunks : a.n_items;
-  const int grid = want < 2 * device_cus() ? want : 2 * device_cus();
+  const int cap = resident_per_cu(reinterpret_cast<const void*>(k), lds) * device_cus();
+  const int grid = want < cap ? want : cap;
   a.nq = 1;
   if (L.fused) {
     a.batch = fused_batch(a.n_chunks);

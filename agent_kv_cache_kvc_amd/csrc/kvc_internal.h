@@ -189,6 +189,8 @@ hipError_t launch_pool_insert(const uint8_t* mask, const float* U_new, const flo
                               const float* q, int S, int T, int d, int dtype, int Vc, int r,
                               void* U_pool, void* W_pool, float* desc_pool, int* count,
                               int* head, hipStream_t st);
+// Test hook of the fused pass's bounded wait (see kvc_test_fused_wait).
+void set_fused_wait_for_tests(long long ticks, int withhold_segment);
 // Correction (after launch_score), or the fused pass (resets its own counters).
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,

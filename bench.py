@@ -1,15 +1,25 @@
-"""Benchmark of the KV-cache correction hot path on one MI355X.
+"""Benchmark of the KVCMAS hot path on one MI355X.
 
-Step = one kvc_correct over the Llama-3.1-8B-shaped shared-context cache (32 layers x 8
-kv-heads x 2048 tokens x 128 channels, bf16, A = 4 anchors of rank 32, tau = 0.32): pool the
-descriptor, score the anchors, softmax, reliability mask, low-rank correction of K and V.
-Inputs are synthetic (seeded), resident in HBM before the timed region.
+Step (the headline) = one pass of the whole hot path over the largest single-GPU workload,
+the chained workflow A0 -> A1 -> A2 -> A3 on the Llama-3.1-8B KV shape at 32768 shared
+tokens (32 layers x 8 kv-heads x 128 channels, bf16, A = 4 anchors of rank 32, tau = 0.32):
+  * kvc_correct_chain over the three edges (pool, cosine match, softmax, reliability mask,
+    low-rank correction of K and V, fallback from the next agent's exact cache; edge e's
+    output is edge e+1's source), and
+  * kvc_fit_anchor of edge 0's delta (exact - reused, 512 matrices of 32768 x 128): Gram,
+    eigen-decomposition, effective rank at 90% energy, rank-32 factors, projection.
+Inputs are synthetic (seeded), resident in HBM before the timed region.  Each step is
+bracketed by HIP events on the launch stream (chain and fit separately); the reported step
+time is the median over the timed steps.
 
-value = algorithmic bytes of the step / step time, where the algorithmic bytes are
-K and V read once, K' and V' written once, U and W of the reliable segments read once and
-the descriptors read once.  The step is one fused launch (after a one-workgroup counter
-reset), so the roofline figure of its kernel is the step figure.  The fit (kvc_fit_anchor) is measured as its own leg on the
-8192-token delta.  The oracle is timed on the host on a bounded sample (cpu_baseline).
+value = algorithmic bytes of the step / step time (GB/s).  Algorithmic bytes of the chain:
+every source segment of edge 0 read once (its descriptor needs them), the reliable source
+segments of later edges (their descriptor comes from the previous edge's output pass), the
+fallback cache of every falling-back segment, U and W of the reliable segments, the
+descriptors, and every output written once.  Of the fit: delta read twice (Gram and
+projection), U and W written.  The other legs (8B T = 2048 step, anchor pool, fit at 8192,
+streaming update, non-chained, vision-language shape, tiny latency) are reported alongside;
+the oracle is timed on the host on a bounded sample of the headline workload (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -76,6 +86,37 @@ def fit_bytes_flops(M, T, d, r):
     return by, syrk, gemm, proj
 
 
+def fanout_bytes(cfg, masks, with_fb: bool) -> int:
+    """Algorithmic HBM bytes of one kvc_correct_fanout call: the shared reference read once
+    (its descriptor needs every segment; the correction of all agents of a launch takes its
+    tiles from one read), then per agent the fallback cache of its falling-back segments, U
+    and W of its reliable segments, its descriptors and its outputs."""
+    S, T, d, A, r = cfg.L * cfg.H, cfg.T, cfg.d, cfg.A, cfg.r
+    es = 2 if cfg.dtype == "bf16" else 4
+    seg = 2 * T * d * es
+    total = S * seg
+    for m in masks:
+        reliable = int((m == 0).sum())
+        total += (S - reliable) * seg if with_fb else 0
+        total += reliable * 2 * A * (T * r + r * d) * es
+        total += S * A * 2 * d * 4
+        total += S * seg
+    return total
+
+
+def per_call_ms(fn, n, stream):
+    """Median and mean of n calls, each bracketed by its own pair of HIP events on ``stream``."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    evs[-1][1].synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), float(t.mean())
+
+
 def descriptors_on_device(case):
     """Anchor descriptors from the library's own pooled query of the source cache."""
     q = kvc.pool_descriptor(case.K0, case.V0)
@@ -83,7 +124,7 @@ def descriptors_on_device(case):
     return synth.build_descriptors(case, 0, q.double())
 
 
-def copy_probe(dev, nbytes: int = 1 << 30, reps: int = 3):
+def copy_probe(dev, nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size: the reference reading of the HBM byte
     counters (FETCH_SIZE, WRITE_SIZE) for the same profiler run."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -97,22 +138,27 @@ def copy_probe(dev, nbytes: int = 1 << 30, reps: int = 3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] copy probe: {reps} x {nbytes} bytes, {ms * 1e3:.1f} us each, "
-        f"{2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s of read + write traffic")
+        f"{gbs:.0f} GB/s of read + write traffic")
     del a, b
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": f"torch device-to-device copy of {nbytes >> 20} MiB ({reps} reps, mean), "
+                    "read + write bytes / time"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_correct_llama8b.md")
+TRAFFIC_CHAIN_FILE = os.path.join(ROOT, "profiles", "traffic_chain_t32768.md")
 KERNEL_SOURCE = os.path.join(ROOT, "agent_kv_cache_kvc_amd", "csrc", "kvc_correct.hip")
 
 
-def traffic_record(nbytes: int):
-    """HBM bytes per launch of the correction kernel from the committed counter summary, or
-    None when the summary is missing or the kernel source changed since it was taken."""
+def traffic_record(nbytes: int, path: str = TRAFFIC_FILE):
+    """HBM bytes of the measured kernel launches from a committed counter summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
     import hashlib
 
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
         src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
@@ -130,7 +176,7 @@ def traffic_record(nbytes: int):
         return None
     return {"bytes": total, "fetch_bytes": int(rec["fetch_bytes"]),
             "write_bytes": int(rec["write_bytes"]),
-            "vs_algorithmic": round(total / nbytes, 4), "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+            "vs_algorithmic": round(total / nbytes, 4), "source": os.path.relpath(path, ROOT)}
 
 
 def time_events(fn, n, stream):
@@ -187,10 +233,11 @@ def study_errors(results, targets):
     return per_agent, per_layer
 
 
-def chain_leg(dev, stream, n):
-    """kvc_correct_chain over the 3-edge workflow A0 -> A1 -> A2 -> A3 at T = 32768."""
+def headline_leg(dev, stream, steps: int, warmup: int):
+    """The step: kvc_correct_chain over A0 -> A1 -> A2 -> A3 at T = 32768, then kvc_fit_anchor
+    of edge 0's delta.  Returns (result dict, case, edges, delta) for the CPU-baseline leg."""
     cfg = synth.CONFIGS["chain_t32768"]
-    log(f"[bench] chain leg: generating {cfg.name}")
+    log(f"[bench] generating {cfg.name} on {dev}")
     case = synth.generate(cfg, dev)
     edges = []
     for e, ed in enumerate(case.edges):
@@ -199,32 +246,157 @@ def chain_leg(dev, stream, n):
         q = kvc.pool_descriptor(srcK, srcV)
         edges.append({"desc": synth.build_descriptors(case, e, q.double()), "U": ed.U, "W": ed.W,
                       "K_fb": ed.exact_K, "V_fb": ed.exact_V})
+    delta = synth.fit_input(case, 0)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     outs = [(torch.empty_like(case.K0), torch.empty_like(case.V0)) for _ in edges]
     ws = torch.empty(kvc.chain_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, cfg.A, cfg.r),
                      dtype=torch.uint8, device=dev)
+    M, T = delta.shape[0], delta.shape[1]
+    fws = torch.empty(kvc.fit_workspace_bytes(M, T, cfg.d, cfg.r), dtype=torch.uint8, device=dev)
+    state = {}
 
-    def run():
-        return kvc.correct_chain(case.K0, case.V0, edges, cfg.tau, outputs=outs, workspace=ws)
+    def chain():
+        state["res"] = kvc.correct_chain(case.K0, case.V0, edges, cfg.tau, outputs=outs,
+                                         workspace=ws, check=False)
 
-    res = run()
+    def fit():
+        state["fit"] = kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
+
+    chain()
+    fit()
     torch.cuda.synchronize()
-    masks = [x.mask.cpu().numpy() for x in res]
-    errs, layer_errs = study_errors(res, [(ed.exact_K, ed.exact_V) for ed in case.edges])
-    for _ in range(3):
-        run()
-    ms = time_events(run, n, stream)
-    nbytes = chain_bytes(cfg, masks, True)
-    log(f"[bench] chain {ms:.3f} ms")
-    return {"workload": f"{cfg.name}: {cfg.n_edges} edges, {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, "
-                        f"A={cfg.A}, r={cfg.r}, tau={cfg.tau}, fallback from the next agent's "
-                        "exact cache",
-            "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
-            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": nbytes,
-            "tokens_layers_per_s": round(cfg.n_edges * cfg.T * cfg.L / (ms * 1e-3), 1),
-            "reuse_per_edge": [round(float(1 - m.mean()), 4) for m in masks],
-            "rel_err_vs_exact_per_agent": errs,
-            "rel_err_vs_exact_per_layer_last_agent": layer_errs[-1]}
+    kvc.check_mask(state["res"][0].mask)
+    masks = [x.mask.cpu().numpy() for x in state["res"]]
+    errs, layer_errs = study_errors(state["res"], [(ed.exact_K, ed.exact_V) for ed in case.edges])
+    k_eff = state["fit"].k_eff.cpu().numpy()
+    for _ in range(warmup):
+        chain()
+        fit()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1, e2 in evs:
+        e0.record(stream)
+        chain()
+        e1.record(stream)
+        fit()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    kvc.check_mask(state["res"][0].mask)
+    t_chain = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    t_fit = np.array([b.elapsed_time(c) for _, b, c in evs])
+    t_step = np.array([a.elapsed_time(c) for a, _, c in evs])
+    ms, ms_c, ms_f = float(np.median(t_step)), float(np.median(t_chain)), float(np.median(t_fit))
+    cbytes = chain_bytes(cfg, masks, True)
+    fby, syrk, gemm, proj = fit_bytes_flops(M, T, cfg.d, cfg.r)
+    nbytes = cbytes + fby
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cgbs = cbytes / (ms_c * 1e-3) / 1e9
+    log(f"[bench] step {ms:.4f} ms (chain {ms_c:.4f} ms, fit {ms_f:.4f} ms; mean "
+        f"{t_step.mean():.4f} ms, wall {wall:.4f} ms), {gbs:.1f} GB/s")
+    res = {
+        "ms": ms, "ms_mean": float(t_step.mean()), "wall_ms": wall, "gbs": gbs,
+        "bytes": nbytes,
+        "chain": {"workload": f"{cfg.name}: {cfg.n_edges} edges, {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} "
+                              f"bf16, A={cfg.A}, r={cfg.r}, tau={cfg.tau}, fallback from the next "
+                              "agent's exact cache",
+                  "ms": round(ms_c, 4), "gbs": round(cgbs, 2),
+                  "hbm_frac": round(cgbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": cbytes,
+                  "tokens_layers_per_s": round(cfg.n_edges * cfg.T * cfg.L / (ms_c * 1e-3), 1),
+                  "reuse_per_edge": [round(float(1 - m.mean()), 4) for m in masks],
+                  "rel_err_vs_exact_per_agent": errs,
+                  "rel_err_vs_exact_per_layer_last_agent": layer_errs[-1]},
+        "fit": {"workload": f"delta of edge 0: M={M} matrices x T={T} x d={cfg.d} bf16, r={cfg.r}",
+                "ms": round(ms_f, 4),
+                "tflops_syrk_plus_proj": round((syrk + proj) / (ms_f * 1e-3) / 1e12, 3),
+                "tflops_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12, 3),
+                "mfma_bf16_frac_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12
+                                                   / BF16_PEAK_TFLOPS, 5),
+                "gbs": round(fby / (ms_f * 1e-3) / 1e9, 2),
+                "hbm_frac": round(fby / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": fby,
+                "k_eff_min_max": [int(k_eff.min()), int(k_eff.max())]},
+    }
+    del outs, ws, fws, state
+    return res, case, edges, delta
+
+
+def cpu_baseline_headline(case, edges, delta, n_seg: int = 6, n_mat: int = 12,
+                          budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the headline workload: the three-edge chain on
+    n_seg segments and the fit of n_mat delta matrices, scaled by the same byte formulas."""
+    import oracle  # only this leg touches the oracle
+
+    cfg = case.cfg
+    idx = [((7 * i) % cfg.L, (3 * i + 1) % cfg.H) for i in range(n_seg)]
+    ls = torch.tensor([i[0] for i in idx], device=case.device)
+    hs = torch.tensor([i[1] for i in idx], device=case.device)
+
+    def seg(x):  # [L, H, ...] -> [n_seg, 1, ...] float64 on the host
+        return synth.to_f64(x[ls, hs])[:, None]
+
+    K0, V0 = seg(case.K0), seg(case.V0)
+    oedges = [{"desc": seg(ed["desc"]),
+               "U": synth.to_f64(ed["U"][:, ls, hs])[:, :, None],
+               "W": synth.to_f64(ed["W"][:, ls, hs])[:, :, None],
+               "K_fb": seg(ed["K_fb"]), "V_fb": seg(ed["V_fb"])} for ed in edges]
+    mats = synth.to_f64(delta[: n_mat])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        res = oracle.chain(K0, V0, oedges, cfg.tau, cfg.dtype)
+        oracle.fit_anchor(mats, cfg.r)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    sub = cfg.replace(L=n_seg, H=1)
+    nbytes = chain_bytes(sub, [r["mask"] for r in res], True) + \
+        fit_bytes_flops(n_mat, cfg.T, cfg.d, cfg.r)[0]
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "cpu": cpu_model(), "kind": "oracle",
+            "sample": f"the 3-edge chain on {n_seg} of {cfg.L * cfg.H} segments and the fit of "
+                      f"{n_mat} of {delta.shape[0]} delta matrices of {cfg.name}, fp64 numpy, "
+                      f"{reps} rep(s) of {dt:.2f} s",
+            "tokens_layers_per_s": round(cfg.n_edges * n_seg * cfg.T / cfg.H / dt, 1)}
+
+
+def tiny_leg(dev, n: int = 200):
+    """Latency of the tiny configuration (1 x 1 x 256 x 64 fp32, A = 2, r = 8): one kvc_correct
+    (single-launch pass) and one kvc_fit_anchor, each a median over n calls of per-call events."""
+    cfg = synth.CONFIGS["tiny"]
+    case = synth.generate(cfg, dev)
+    desc = descriptors_on_device(case)
+    ed = case.edges[0]
+    Ko, Vo = torch.empty_like(case.K0), torch.empty_like(case.V0)
+    ws = torch.empty(kvc.correct_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, cfg.A, cfg.r),
+                     dtype=torch.uint8, device=dev)
+    delta = synth.fit_input(case)
+    fws = torch.empty(kvc.fit_workspace_bytes(delta.shape[0], cfg.T, cfg.d, cfg.r),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def corr():
+        kvc.correct(case.K0, case.V0, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo,
+                    want_w=False, want_score=False, workspace=ws, check=False)
+
+    def fit():
+        kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
+
+    for _ in range(20):
+        corr()
+        fit()
+    torch.cuda.synchronize()
+    c_med, c_mean = per_call_ms(corr, n, stream)
+    f_med, f_mean = per_call_ms(fit, n, stream)
+    log(f"[bench] tiny: correct {c_med * 1e3:.1f} us, fit {f_med * 1e3:.1f} us (medians)")
+    return {"workload": "tiny: 1x1x256x64 fp32, A=2, r=8, tau=0.3 (latency-bound)",
+            "correct_us_median": round(c_med * 1e3, 2), "correct_us_mean": round(c_mean * 1e3, 2),
+            "fit_us_median": round(f_med * 1e3, 2), "fit_us_mean": round(f_mean * 1e3, 2),
+            "calls": n}
 
 
 def fanout_leg(dev, stream, n):
@@ -241,7 +413,8 @@ def fanout_leg(dev, stream, n):
                                                           cfg.r), dtype=torch.uint8, device=dev)
 
     def run():
-        return kvc.correct_fanout(case.K0, case.V0, agents, cfg.tau, outputs=outs, workspace=ws)
+        return kvc.correct_fanout(case.K0, case.V0, agents, cfg.tau, outputs=outs, workspace=ws,
+                                  check=False)
 
     res = run()
     torch.cuda.synchronize()
@@ -249,8 +422,8 @@ def fanout_leg(dev, stream, n):
     errs, layer_errs = study_errors(res, [(ed.exact_K, ed.exact_V) for ed in case.edges])
     for _ in range(3):
         run()
-    ms = time_events(run, n, stream)
-    nbytes = chain_bytes(cfg, masks, True)  # same accounting: agents >= 1 read the reference once
+    ms, _ = per_call_ms(run, n, stream)
+    nbytes = fanout_bytes(cfg, masks, True)
     log(f"[bench] non-chained {ms:.3f} ms")
     return {"workload": f"{cfg.n_edges} agents corrected from one context-free reference, "
                         f"{cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
@@ -296,7 +469,7 @@ def pool_leg(dev, stream, n, cfg, case):
                   + S * Vc * 2 * cfg.d * 4)
         for _ in range(3):
             run()
-        ms = time_events(run, n, stream)
+        ms, _ = per_call_ms(run, n, stream)
         out["per_capacity"][str(Vc)] = {"A": A, "ms": round(ms, 4),
                                         "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
                                         "reuse": round(reliable / S, 4)}
@@ -329,15 +502,16 @@ def vl_leg(dev, stream, n):
 
     def step():
         return kvc.correct(case.K0, case.V0, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo,
-                           want_w=False, want_score=False, workspace=ws)
+                           want_w=False, want_score=False, workspace=ws, check=False)
 
     res = step()
     torch.cuda.synchronize()
-    mask = res.mask.cpu().numpy()
+    mask = kvc.check_mask(res.mask).cpu().numpy()
     nbytes = correct_bytes(cfg, mask)
     for _ in range(5):
         step()
-    ms = time_events(step, n, stream)
+    ms, _ = per_call_ms(step, n, stream)
+    kvc.check_mask(res.mask)
     delta = synth.fit_input(case)
     del case, Ko, Vo, res
     M, T = delta.shape[0], delta.shape[1]
@@ -349,7 +523,7 @@ def vl_leg(dev, stream, n):
     fr = fit()
     torch.cuda.synchronize()
     ke = fr.k_eff.cpu().numpy()
-    ms_f = time_events(fit, max(3, n // 5), stream)
+    ms_f, _ = per_call_ms(fit, max(3, n // 5), stream)
     by, syrk, gemm, proj = fit_bytes_flops(M, T, cfg.d, cfg.r)
     log(f"[bench] vl correct {ms:.4f} ms, fit {ms_f:.3f} ms")
     return {"workload": f"{cfg.name}: {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
@@ -362,36 +536,6 @@ def vl_leg(dev, stream, n):
             "fit_tflops_syrk_plus_proj": round((syrk + proj) / (ms_f * 1e-3) / 1e12, 3),
             "fit_gbs": round(by / (ms_f * 1e-3) / 1e9, 2),
             "k_eff_min_max": [int(ke.min()), int(ke.max())]}
-
-
-def fit32k_leg(dev, stream, n):
-    """kvc_fit_anchor on the delta of the chain workload's first edge (M = 512, T = 32768)."""
-    cfg = synth.CONFIGS["chain_t32768"].replace(n_edges=1)
-    log(f"[bench] fit leg at T={cfg.T}: generating")
-    case = synth.generate(cfg, dev)
-    delta = synth.fit_input(case)
-    del case
-    torch.cuda.empty_cache()
-    M, T = delta.shape[0], delta.shape[1]
-    fws = torch.empty(kvc.fit_workspace_bytes(M, T, cfg.d, cfg.r), dtype=torch.uint8, device=dev)
-
-    def fit():
-        return kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
-
-    res = fit()
-    torch.cuda.synchronize()
-    k = res.k_eff.cpu().numpy()
-    ms = time_events(fit, n, stream)
-    by, syrk, gemm, proj = fit_bytes_flops(M, T, cfg.d, cfg.r)
-    log(f"[bench] fit at T={T}: {ms:.3f} ms")
-    return {"workload": f"delta of chain edge 0: M={M} matrices x T={T} x d={cfg.d} bf16, r={cfg.r}",
-            "ms": round(ms, 4),
-            "tflops_syrk_plus_proj": round((syrk + proj) / (ms * 1e-3) / 1e12, 3),
-            "tflops_gemm_count": round((gemm + proj) / (ms * 1e-3) / 1e12, 3),
-            "mfma_bf16_frac_gemm_count": round((gemm + proj) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
-            "gbs": round(by / (ms * 1e-3) / 1e9, 2),
-            "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "k_eff_min_max": [int(k.min()), int(k.max())]}
 
 
 def cpu_model() -> str:
@@ -427,32 +571,9 @@ def cpu_baseline_fit(delta, r, n_mat: int = 16, budget_s: float = 8.0):
                       f"{reps} rep(s) of {dt:.2f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--no-fit", action="store_true")
-    ap.add_argument("--no-chain", action="store_true")
-    ap.add_argument("--only-fit32k", action="store_true",
-                    help="run only the T=32768 fit leg (for a profile of its kernels)")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-vl", action="store_true")
-    ap.add_argument("--cpu-segments", type=int, default=64)
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              f"sharding is a design note, not a measured path.", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    if args.only_fit32k:
-        print(json.dumps({"fit_t32768": fit32k_leg(dev, stream, max(3, args.steps // 10))}),
-              flush=True)
-        return
-
+def llama8b_leg(dev, stream, steps: int, warmup: int):
+    """kvc_correct over the 8B shape at T = 2048 (single-launch pass), its base-cache rank,
+    the anchor pool and the q-given form."""
     cfg = synth.CONFIGS["llama8b_t2048"]
     log(f"[bench] generating {cfg.name} on {dev}")
     case = synth.generate(cfg, dev)
@@ -465,23 +586,33 @@ def main():
 
     def step():
         return kvc.correct(K, V, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo, want_w=False,
-                           want_score=False, workspace=ws)
+                           want_score=False, workspace=ws, check=False)
 
     res = step()
     torch.cuda.synchronize()
-    mask = res.mask.cpu().numpy()
+    mask = kvc.check_mask(res.mask).cpu().numpy()
     nbytes = correct_bytes(cfg, mask)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms_ev = time_events(step, args.steps, stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps * 1e3
-    gbs = nbytes / (ms_ev * 1e-3) / 1e9
-    tlps = cfg.T * cfg.L / (ms_ev * 1e-3)
-    log(f"[bench] step {ms_ev:.4f} ms (wall {wall:.4f} ms), {gbs:.1f} GB/s, reuse "
-        f"{1 - mask.mean():.3f}")
+    ms, ms_mean = per_call_ms(step, steps, stream)
+    kvc.check_mask(res.mask)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] llama8b_t2048 step {ms:.4f} ms, {gbs:.1f} GB/s, reuse {1 - mask.mean():.3f}")
+    traffic = traffic_record(nbytes)
+    out = {"workload": f"{cfg.name}: {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
+                       f"tau={cfg.tau}, one kvc_correct (single-launch pass)",
+           "ms": round(ms, 5), "ms_mean": round(ms_mean, 5), "gbs": round(gbs, 2),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+           "tokens_layers_per_s": round(cfg.T * cfg.L / (ms * 1e-3), 1),
+           "reuse_ratio": round(float(1 - mask.mean()), 4),
+           "roofline": {"bound": "hbm",
+                        "kernel": "correct_kernel, fused form (pooling, matching and correction "
+                                  "in one launch; a one-workgroup counter reset precedes it)",
+                        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": traffic["bytes"] if traffic else None,
+                        "traffic_detail": traffic}}
 
     # the base cache's own rank-r representation and effective rank (the same fit kernels on
     # K and V of every segment; listing Fig. 2 reports it for real model caches)
@@ -492,15 +623,16 @@ def main():
     ke = bf.k_eff.cpu().numpy()
     eigs = bf.eig.double()
     kept = (eigs[:, :cfg.r].sum(1) / eigs.sum(1)).cpu().numpy()
-    base_rank = {"workload": f"{cfg.name} K and V caches as {base.shape[0]} matrices of "
-                             f"{cfg.T} x {cfg.d}, r={cfg.r}",
-                 "ms": round(ms_b, 4), "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)),
-                                                               int(ke.max())],
-                 "energy_kept_at_r_mean": round(float(kept.mean()), 4)}
+    out["base_cache_rank"] = {
+        "workload": f"{cfg.name} K and V caches as {base.shape[0]} matrices of {cfg.T} x {cfg.d}, "
+                    f"r={cfg.r}",
+        "ms": round(ms_b, 4), "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)),
+                                                       int(ke.max())],
+        "energy_kept_at_r_mean": round(float(kept.mean()), 4)}
     log(f"[bench] base-cache fit {ms_b:.3f} ms, effective rank median {int(np.median(ke))}")
     del base, bf, eigs
 
-    out_pool = pool_leg(dev, stream, max(10, args.steps // 2), cfg, case)
+    out["anchor_pool"] = pool_leg(dev, stream, max(10, steps // 2), cfg, case)
 
     # the unfused form, for reference: matching kernel from a precomputed q, then correction
     q = kvc.pool_descriptor(K, V)
@@ -512,129 +644,166 @@ def main():
 
     for _ in range(3):
         corr_q_in()
-    ms_k = time_events(corr_q_in, args.steps, stream)
+    ms_k, _ = per_call_ms(corr_q_in, steps, stream)
     log(f"[bench] with q_in (score + correct kernels) {ms_k:.4f} ms")
-    if args.copy_probe:
-        copy_probe(dev)
+    out["with_q_in"] = {"ms": round(ms_k, 5), "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
+                        "note": "q precomputed: matching kernel + unfused correction kernel"}
+    return out
 
-    traffic = traffic_record(nbytes)
+
+def fit8k_leg(dev, stream, steps: int, no_cpu: bool):
+    """kvc_fit_anchor on the 8192-token delta (M = 512), the Fig. 7 rank study and the
+    streaming update (append 2048 rows to a 6144-row Gram, refit, project the new rows)."""
+    fcfg = synth.CONFIGS["llama8b_t8192_fit"]
+    log(f"[bench] fit leg: generating {fcfg.name}")
+    fcase = synth.generate(fcfg, dev)
+    delta = synth.fit_input(fcase)
+    del fcase
+    torch.cuda.empty_cache()
+    M, T = delta.shape[0], delta.shape[1]
+    fws = torch.empty(kvc.fit_workspace_bytes(M, T, fcfg.d, fcfg.r), dtype=torch.uint8,
+                      device=dev)
+
+    def fit():
+        return kvc.fit_anchor(delta, r=fcfg.r, want_eig=False, workspace=fws)
+
+    fit()
+    torch.cuda.synchronize()
+    ms_f, _ = per_call_ms(fit, steps, stream)
+    by, syrk, gemm, proj = fit_bytes_flops(M, T, fcfg.d, fcfg.r)
+    out = {"workload": f"{fcfg.name}: delta of M={M} matrices x T={T} x d={fcfg.d}, r={fcfg.r}",
+           "ms": round(ms_f, 4),
+           "tflops_syrk_plus_proj": round((syrk + proj) / (ms_f * 1e-3) / 1e12, 3),
+           "tflops_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12, 3),
+           "mfma_bf16_frac_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12
+                                              / BF16_PEAK_TFLOPS, 5),
+           "gbs": round(by / (ms_f * 1e-3) / 1e9, 2),
+           "hbm_frac": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] fit {ms_f:.3f} ms")
+    # listing Fig. 7: effective rank and the error against the retained rank
+    fe = kvc.fit_anchor(delta, r=fcfg.r, want_eig=True, workspace=fws)
+    curve = kvc.rank_error_curve(fe.eig)
+    ms_c = time_events(lambda: kvc.rank_error_curve(fe.eig), 5, stream)
+    ranks = [1, 2, 4, 8, 11, 16, 32, 64, 128]
+    cm = curve.double().mean(0).cpu().numpy()
+    ke = fe.k_eff.cpu().numpy()
+    out["rank_study"] = {
+        "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)), int(ke.max())],
+        "mean_rel_err_at_rank": {str(k): round(float(cm[k]), 6) for k in ranks},
+        "curve_ms": round(ms_c, 4)}
+    del fe, curve
+    t_old = T - 2048
+    G = kvc.gram_accumulate(delta[:, :t_old].contiguous())
+    new = delta[:, t_old:].contiguous()
+    gws = torch.empty(kvc.lib().kvc_gram_workspace_bytes(M, T - t_old, fcfg.d),
+                      dtype=torch.uint8, device=dev)
+
+    def update():
+        kvc.gram_accumulate(new, G, workspace=gws)
+        res = kvc.fit_from_gram(G, r=fcfg.r, want_eig=False)
+        return kvc.project(new, res.W)
+
+    update()
+    torch.cuda.synchronize()
+    ms_u, _ = per_call_ms(update, steps, stream)
+    stream_upd = {"workload": f"append {T - t_old} rows to the {t_old}-row Gram of {M} matrices, "
+                              "refit, project the appended rows",
+                  "ms": round(ms_u, 4), "full_refit_ms": round(ms_f, 4)}
+    log(f"[bench] streaming update {ms_u:.3f} ms (full fit {ms_f:.3f} ms)")
+    del G, new, gws
+    cpu = None
+    if not no_cpu:
+        log("[bench] cpu baseline of the fit (oracle on a sample)")
+        cpu = cpu_baseline_fit(delta, fcfg.r)
+    return out, stream_upd, cpu
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run only the headline step (for profiles of its kernels)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the secondary legs")
+    ap.add_argument("--no-vl", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              f"sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    copy = copy_probe(dev)
+    torch.cuda.empty_cache()
+
+    head, case, edges, delta = headline_leg(dev, stream, args.steps, args.warmup)
+    cfg = case.cfg
+    traffic = traffic_record(head["chain"]["algorithmic_bytes"], TRAFFIC_CHAIN_FILE)
+    cgbs = head["chain"]["gbs"]
     out = {
         "metric": "corrected-KV GB/s and tokens*layers/s (% of HBM peak); anchor-fit TFLOP/s",
-        "value": round(gbs, 2),
+        "value": round(head["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_ev, 5),
+        "ms_per_step": round(head["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama8b_t2048", "layers": cfg.L, "kv_heads": cfg.H,
-                   "tokens": cfg.T, "head_dim": cfg.d, "anchors": cfg.A, "rank": cfg.r,
-                   "tau": cfg.tau, "cache_dtype": cfg.dtype,
-                   "reuse_ratio": round(float(1 - mask.mean()), 4)},
-        "tokens_layers_per_s": round(tlps, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_step": nbytes,
+        "config": {"workload": cfg.name, "layers": cfg.L, "kv_heads": cfg.H, "tokens": cfg.T,
+                   "head_dim": cfg.d, "anchors": cfg.A, "rank": cfg.r, "tau": cfg.tau,
+                   "edges": cfg.n_edges, "cache_dtype": cfg.dtype,
+                   "step": "kvc_correct_chain over the 3 edges + kvc_fit_anchor of edge 0's "
+                           "delta (512 x 32768 x 128)"},
+        "timing": {"statistic": "median of per-step HIP-event times", "ms_mean": round(head["ms_mean"], 5),
+                   "wall_ms_per_step": round(head["wall_ms"], 5)},
+        "tokens_layers_per_s": head["chain"]["tokens_layers_per_s"],
+        "hbm_frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
+        "frac_of_copy_ceiling": round(head["gbs"] / copy["gbs"], 4),
+        "algorithmic_bytes_per_step": head["bytes"],
         "roofline": {"bound": "hbm",
-                     "kernel": "correct_kernel, fused form (pooling, matching and correction "
-                               "in one launch; a one-workgroup counter reset precedes it)",
-                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "kernel": "correct_kernel, the chain's correction passes (one launch per "
+                               "edge, 3 per step: single-launch pass with output pooling on edge "
+                               "0, matched from the previous output's chunk sums on edges 1-2); "
+                               "achieved = the chain's algorithmic bytes / its median time",
+                     "achieved": cgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(cgbs / HBM_PEAK_GBS, 4),
+                     "frac_of_copy_ceiling": round(cgbs / copy["gbs"], 4),
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_detail": traffic,
-                     "ms_per_launch": round(ms_ev, 5)},
-        "base_cache_rank": base_rank,
-        "anchor_pool": out_pool,
-        "with_q_in": {"ms": round(ms_k, 5), "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
-                      "note": "q precomputed: matching kernel + unfused correction kernel"},
+                     "ms_per_launch": round(head["chain"]["ms"] / cfg.n_edges, 5),
+                     "launches": cfg.n_edges},
+        "chain": head["chain"],
+        "fit_t32768": head["fit"],
+        "copy_ceiling": copy,
     }
-    del res
-    if not args.no_fit:
-        fcfg = synth.CONFIGS["llama8b_t8192_fit"]
-        log(f"[bench] fit leg: generating {fcfg.name}")
-        del Ko, Vo
-        fcase = synth.generate(fcfg, dev)
-        delta = synth.fit_input(fcase)
-        del fcase
-        torch.cuda.empty_cache()
-        M, T = delta.shape[0], delta.shape[1]
-        fws = torch.empty(kvc.fit_workspace_bytes(M, T, fcfg.d, fcfg.r), dtype=torch.uint8,
-                          device=dev)
-
-        def fit():
-            return kvc.fit_anchor(delta, r=fcfg.r, want_eig=False, workspace=fws)
-
-        fit()
-        torch.cuda.synchronize()
-        nfit = max(3, args.steps // 10)
-        ms_f = time_events(fit, nfit, stream)
-        by, syrk, gemm, proj = fit_bytes_flops(M, T, fcfg.d, fcfg.r)
-        out["fit"] = {
-            "workload": f"{fcfg.name}: delta of M={M} matrices x T={T} x d={fcfg.d}, r={fcfg.r}",
-            "ms": round(ms_f, 4),
-            "tflops_syrk_plus_proj": round((syrk + proj) / (ms_f * 1e-3) / 1e12, 3),
-            "tflops_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12, 3),
-            "mfma_bf16_frac_gemm_count": round((gemm + proj) / (ms_f * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
-            "gbs": round(by / (ms_f * 1e-3) / 1e9, 2),
-            "hbm_frac": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        }
-        log(f"[bench] fit {ms_f:.3f} ms")
-        # listing Fig. 7: effective rank and the error against the retained rank
-        fe = kvc.fit_anchor(delta, r=fcfg.r, want_eig=True, workspace=fws)
-        curve = kvc.rank_error_curve(fe.eig)
-        ms_c = time_events(lambda: kvc.rank_error_curve(fe.eig), 5, stream)
-        ranks = [1, 2, 4, 8, 11, 16, 32, 64, 128]
-        cm = curve.double().mean(0).cpu().numpy()
-        ke = fe.k_eff.cpu().numpy()
-        out["fit"]["rank_study"] = {
-            "k_eff_min_median_max": [int(ke.min()), int(np.median(ke)), int(ke.max())],
-            "mean_rel_err_at_rank": {str(k): round(float(cm[k]), 6) for k in ranks},
-            "curve_ms": round(ms_c, 4)}
-        del fe, curve
-        # streaming update: the first 6144 rows are already in G; append the last 2048
-        # (accumulate, refit from G, project only the appended rows)
-        t_old = T - 2048
-        G = kvc.gram_accumulate(delta[:, :t_old].contiguous())
-        new = delta[:, t_old:].contiguous()
-        gws = torch.empty(kvc.lib().kvc_gram_workspace_bytes(M, T - t_old, fcfg.d),
-                          dtype=torch.uint8, device=dev)
-
-        def update():
-            kvc.gram_accumulate(new, G, workspace=gws)
-            res = kvc.fit_from_gram(G, r=fcfg.r, want_eig=False)
-            return kvc.project(new, res.W)
-
-        update()
-        torch.cuda.synchronize()
-        ms_u = time_events(update, nfit, stream)
-        out["fit_stream_update"] = {
-            "workload": f"append {T - t_old} rows to the {t_old}-row Gram of {M} matrices, refit, "
-                        f"project the appended rows",
-            "ms": round(ms_u, 4), "full_refit_ms": round(ms_f, 4)}
-        log(f"[bench] streaming update {ms_u:.3f} ms (full fit {ms_f:.3f} ms)")
-        del G, new, gws
-        if not args.no_cpu:
-            log("[bench] cpu baseline of the fit (oracle on a sample)")
-            out["cpu_baseline_fit"] = cpu_baseline_fit(delta, fcfg.r)
-        del delta, fws
-        torch.cuda.empty_cache()
-    if not args.no_chain:
-        out["chain"] = chain_leg(dev, stream, max(5, args.steps // 2))
-        torch.cuda.empty_cache()
-        out["non_chained"] = fanout_leg(dev, stream, max(5, args.steps // 2))
-        torch.cuda.empty_cache()
-    if not args.no_fit:
-        out["fit_t32768"] = fit32k_leg(dev, stream, max(3, args.steps // 10))
-        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle on a sample of the headline workload)")
+        out["cpu_baseline"] = cpu_baseline_headline(case, edges, delta)
+    del case, edges, delta
+    torch.cuda.empty_cache()
+    if args.headline_only or args.no_legs:
+        print(json.dumps(out), flush=True)
+        return
+    out["llama8b_t2048"] = llama8b_leg(dev, stream, max(20, args.steps), max(5, args.warmup))
+    torch.cuda.empty_cache()
+    fit8k, upd, cpu_fit = fit8k_leg(dev, stream, max(5, args.steps // 2), args.no_cpu)
+    out["fit"] = fit8k
+    out["fit_stream_update"] = upd
+    if cpu_fit:
+        out["cpu_baseline_fit"] = cpu_fit
+    torch.cuda.empty_cache()
+    out["non_chained"] = fanout_leg(dev, stream, max(5, args.steps // 2))
+    torch.cuda.empty_cache()
     if not args.no_vl:
         out["vl"] = vl_leg(dev, stream, max(10, args.steps // 2))
         torch.cuda.empty_cache()
-    if not args.no_cpu:
-        log("[bench] cpu baseline (oracle on a sample)")
-        out["cpu_baseline"] = cpu_baseline(cfg, case, desc, args.cpu_segments)
+    out["tiny"] = tiny_leg(dev)
     print(json.dumps(out), flush=True)
 
 

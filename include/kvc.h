@@ -53,6 +53,15 @@ const char* kvc_version(void);
  * valid until that thread's next call); "" if none. */
 const char* kvc_last_error(void);
 
+/* Test hook of the single-launch correction pass's bounded wait (see mask_out of
+ * kvc_correct).  For every later single-launch pass in this process: wait_ticks is the
+ * wait limit in ticks of the 100 MHz constant clock (<= 0 restores the default of
+ * 20,000,000 = 0.2 s), and the matching result of segment withhold_segment (l * H + h) is
+ * never published (-1, the default: none), so that its correction items reach the limit,
+ * give up and copy the segment through with mask 2.  Every kernel still runs to its end.
+ * Process-wide, not thread-safe; meant for tests of the give-up path only. */
+void kvc_test_fused_wait(long long wait_ticks, int withhold_segment);
+
 /* ---------------------------------------------------------------------------------------
  * Pooled descriptor (Fig. 1(b): the current cache representation that is matched
  * against the online anchors).  Read here as the token mean of K followed by the token
@@ -91,9 +100,11 @@ kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T
  *   K_fb, V_fb  : [L,H,T,d] dtype or NULL (both or neither)
  *   K_out, V_out: [L,H,T,d] dtype, written; may equal K / V (in place); must not
  *                 otherwise overlap any input
- *   mask_out    : [L,H] uint8, 1 = fall back, written (2 would flag an internal wait of
- *                 the single-launch pass that gave up after 0.2 s; the segment is then
- *                 copied through; not expected on a device that runs the whole grid)
+ *   mask_out    : [L,H] uint8, 1 = fall back, written.  2 flags a segment whose
+ *                 correction gave up waiting for its matching result in the single-launch
+ *                 pass (a 0.2 s safety net that the pass's work order never reaches); the
+ *                 whole segment is then written as for a fallback (X_fb if given, else X),
+ *                 and its score and weights are undefined.  The Python binding raises on it.
  *   score_out   : [L,H] float32 or NULL;  w_out: [L,H,A] float32 or NULL
  *   q_next_out  : [L,H,2d] float32 or NULL: pooled descriptor of (K_out, V_out)
  *   ws          : at least kvc_correct_workspace_bytes(L,H,T,d,A,r) bytes

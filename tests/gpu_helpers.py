@@ -41,6 +41,8 @@ def check_close(name: str, got: np.ndarray, ref: np.ndarray, rel=REL_FROB, mabs=
     err = oracle.rel_frobenius(got, ref)
     m = float(np.max(np.abs(ref))) if ref.size else 0.0
     worst = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    say(f"  {name}: rel-Frobenius {err:.3e} (bar {rel:.0e}), max-abs {worst:.3e} "
+        f"= {worst / m if m > 0 else 0.0:.3e} x max|ref| (bar {mabs:.0e})")
     assert err <= rel, f"{name}: relative Frobenius error {err:.3e} > {rel:.0e}"
     assert worst <= mabs * m + 1e-30, f"{name}: max-abs error {worst:.3e} > {mabs:.0e} * {m:.3e}"
     return err
