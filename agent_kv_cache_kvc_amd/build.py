@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvc.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["kvc_api.hip", "kvc_correct.hip", "kvc_fit.hip", "kvc_metrics.hip",
+SOURCES = ["kvc_api.hip", "kvc_correct.hip", "kvc_correct_general.hip", "kvc_fit.hip",
+           "kvc_metrics.hip",
            "kvc_anchor_pool.hip"]
 
 HIPCC_FLAGS = [

@@ -54,19 +54,15 @@ kvc_status check_tensor(const void* p, const char* name, size_t align = 16) {
   return KVC_OK;
 }
 
-kvc_status check_anchors(int A, int r, int dtype) {
+// Anchor shape: 1 <= A, 1 <= r <= d, A * r <= 256 (both dtypes).  Shapes outside the
+// specialised kernel's budget take the general correction (kvc::correct_specialised).
+kvc_status check_anchors(int A, int r, int d) {
   if (A < 1) return fail(KVC_ERR_ARG, "A=%d (need >= 1)", A);
   if (r < 1) return fail(KVC_ERR_ARG, "r=%d (need >= 1)", r);
-  if (A > kvc::kMaxA) return fail(KVC_ERR_UNSUPPORTED, "A=%d exceeds %d anchors", A, kvc::kMaxA);
-  if (r > kvc::kMaxR) return fail(KVC_ERR_UNSUPPORTED, "r=%d exceeds %d", r, kvc::kMaxR);
-  if (dtype == KVC_BF16) {
-    const int rp = (r + 15) / 16 * 16;
-    if (A * rp > kvc::kMaxKSlots)
-      return fail(KVC_ERR_UNSUPPORTED, "A*ceil16(r)=%d exceeds %d", A * rp, kvc::kMaxKSlots);
-  } else {
-    const int rp = (r + 7) / 8 * 8;
-    if (A * rp > 64) return fail(KVC_ERR_UNSUPPORTED, "fp32: A*ceil8(r)=%d exceeds 64", A * rp);
-  }
+  if (r > d) return fail(KVC_ERR_ARG, "r=%d exceeds d=%d", r, d);
+  if ((long long)A * r > kvc::kMaxAnchorsGeneral)
+    return fail(KVC_ERR_UNSUPPORTED, "A*r=%lld exceeds %d", (long long)A * r,
+                kvc::kMaxAnchorsGeneral);
   return KVC_OK;
 }
 
@@ -136,7 +132,7 @@ static kvc_status validate_correct(const void* K, const void* V, int L, int H, i
                                    const void* V_fb, void* K_out, void* V_out,
                                    uint8_t* mask_out, void* ws, size_t ws_bytes) {
   KVC_TRY(check_cache_shape(L, H, T, d, dtype));
-  KVC_TRY(check_anchors(A, r, dtype));
+  KVC_TRY(check_anchors(A, r, d));
   if (L * H == 0) return KVC_OK;
   if (T > 0) {
     KVC_TRY(check_tensor(K, "K"));
@@ -164,6 +160,61 @@ static kvc_status validate_correct(const void* K, const void* V, int L, int H, i
 // One correction pass.  Without q_in or earlier chunk sums, pooling, matching and correction
 // run as one fused launch; with them the matching kernel reads q_in (or the chunk sums that
 // the previous pass of a chain left in the workspace) and the correction kernel follows.
+// The general correction (anchor shapes outside the specialised kernel): q from q_in, from the
+// previous pass's output chunk sums, or from a pooling pass; matching of any number of
+// anchors; the correction; then, if asked, the output's chunk sums by a pooling pass.
+static kvc_status enqueue_correct_general(const void* K, const void* V, int L, int H, int T,
+                                          int d, int dtype, const float* desc, const void* U,
+                                          const void* W, int A, int r, float tau,
+                                          const float* q_in, const float* next_partials_in,
+                                          const void* K_fb, const void* V_fb, void* K_out,
+                                          void* V_out, uint8_t* mask_out, float* score_out,
+                                          float* w_out, bool want_next, void* ws,
+                                          hipStream_t st) {
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  const int nc = kvc::chunks_of(T, d, dtype);
+  char* base = static_cast<char*>(ws);
+  float* pool = reinterpret_cast<float*>(base + c.off_pool);
+  float* qws = reinterpret_cast<float*>(base + c.off_q);
+  const float* q = q_in;
+  if (q == nullptr) {
+    const float* part = next_partials_in;
+    if (part == nullptr) {
+      KVC_HIP(kvc::launch_pool_partials(K, V, c.S, T, d, dtype, pool, nc, st), "pool");
+      part = pool;
+    }
+    KVC_HIP(kvc::launch_reduce_pool(part, nc, T, c.S, d, qws, st), "pool reduce");
+    q = qws;
+  }
+  kvc::CorrectLaunch cl{};
+  cl.K = K;
+  cl.V = V;
+  cl.S = c.S;
+  cl.T = T;
+  cl.d = d;
+  cl.dtype = dtype;
+  cl.U = U;
+  cl.W = W;
+  cl.A = A;
+  cl.r = r;
+  cl.w_ws = reinterpret_cast<float*>(base + c.off_w);
+  cl.mask_ws = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  cl.K_fb = K_fb;
+  cl.V_fb = V_fb;
+  cl.K_out = K_out;
+  cl.V_out = V_out;
+  KVC_HIP(kvc::launch_score_general(q, desc, c.S, d, A, tau, cl.w_ws,
+                                    reinterpret_cast<uint8_t*>(base + c.off_mask), score_out,
+                                    w_out, mask_out, st),
+          "score");
+  KVC_HIP(kvc::launch_correct_general(cl, st), "correct");
+  if (want_next)
+    KVC_HIP(kvc::launch_pool_partials(K_out, V_out, c.S, T, d, dtype,
+                                      reinterpret_cast<float*>(base + c.off_next), nc, st),
+            "pool of the output");
+  return KVC_OK;
+}
+
 static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, int T, int d,
                                   int dtype, const float* desc, const void* U, const void* W,
                                   int A, int r, float tau, const float* q_in,
@@ -171,6 +222,10 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
                                   const void* V_fb, void* K_out, void* V_out,
                                   uint8_t* mask_out, float* score_out, float* w_out,
                                   bool want_next, void* ws, hipStream_t st) {
+  if (!kvc::correct_specialised(A, r, dtype))
+    return enqueue_correct_general(K, V, L, H, T, d, dtype, desc, U, W, A, r, tau, q_in,
+                                   next_partials_in, K_fb, V_fb, K_out, V_out, mask_out,
+                                   score_out, w_out, want_next, ws, st);
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
   const int nc = kvc::chunks_of(T, d, dtype);
   char* base = static_cast<char*>(ws);
@@ -349,10 +404,24 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
   // Several agents: the reference is pooled once; each agent is matched from those chunk sums
   // (the same pooled descriptor, bit for bit); then one launch per group of up to kMaxTargets
   // agents reads each tile of the reference once and corrects it for every agent of the group.
+  // Anchor shapes outside the specialised kernel: the general correction, agent by agent, all
+  // matched against the reference's one pooled descriptor.
   const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
   const int nc = kvc::chunks_of(T, d, dtype);
   char* base = static_cast<char*>(ws);
   float* pool = reinterpret_cast<float*>(base + c.off_pool);
+  if (!kvc::correct_specialised(A, r, dtype)) {
+    float* qws = reinterpret_cast<float*>(base + c.off_q);
+    KVC_HIP(kvc::launch_pool_partials(K, V, c.S, T, d, dtype, pool, nc, st), "pool");
+    KVC_HIP(kvc::launch_reduce_pool(pool, nc, T, c.S, d, qws, st), "pool reduce");
+    for (int j = 0; j < n_agents; ++j)
+      KVC_TRY(enqueue_correct_general(K, V, L, H, T, d, dtype, desc[j], U[j], W[j], A, r, tau,
+                                      qws, nullptr, K_fb ? K_fb[j] : nullptr,
+                                      V_fb ? V_fb[j] : nullptr, K_out[j], V_out[j],
+                                      mask_out[j], score_out ? score_out[j] : nullptr, nullptr,
+                                      false, ws, st));
+    return ok();
+  }
   float* wmt = reinterpret_cast<float*>(base + c.off_wmt);
   uint8_t* mmt = reinterpret_cast<uint8_t*>(base + c.off_mmt);
   int* ctr = reinterpret_cast<int*>(base + c.off_ctr);
@@ -455,7 +524,10 @@ kvc_status kvc_correct_pooled(const void* K, const void* V, int L, int H, int T,
                              reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
                              slot_out, mask_out, cl.ctr, st),
           "select");
-  KVC_HIP(kvc::launch_correct(cl, st), "correct");
+  if (kvc::correct_specialised(A, r, dtype))
+    KVC_HIP(kvc::launch_correct(cl, st), "correct");
+  else
+    KVC_HIP(kvc::launch_correct_general(cl, st), "correct");
   return ok();
 }
 

@@ -398,10 +398,10 @@ __global__ __launch_bounds__(kBlock) void select_kernel(
   }
   const int nsel = A < n ? A : n;
   uint32_t taken = 0u;
-  int sel[kMaxA];
-  float ss[kMaxA];
+  int sel[kMaxPool];
+  float ss[kMaxPool];
 #pragma unroll
-  for (int i = 0; i < kMaxA; ++i) {
+  for (int i = 0; i < kMaxPool; ++i) {
     sel[i] = 0;
     ss[i] = 0.f;
     if (i < nsel) {
@@ -423,10 +423,10 @@ __global__ __launch_bounds__(kBlock) void select_kernel(
     }
   }
   const float score = n == 0 ? -INFINITY : (nan ? __uint_as_float(0x7fc00000u) : ss[0]);
-  float ex[kMaxA];
+  float ex[kMaxPool];
   float z = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxA; ++i) {
+  for (int i = 0; i < kMaxPool; ++i) {
     ex[i] = 0.f;
     if (i < nsel) {
       ex[i] = expf(ss[i] - ss[0]);
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kBlock) void select_kernel(
   float wv = 0.f;
   int sv = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxA; ++i)
+  for (int i = 0; i < kMaxPool; ++i)
     if (i == lane) {
       wv = i < nsel ? ex[i] / z : 0.f;
       sv = i < nsel ? sel[i] : sel[0];

@@ -37,11 +37,13 @@ __constant__ int c_blk64[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
 // grid (nsplit, M).  Each slab of SLAB = 16384/D tokens is loaded as 8x8 bf16 blocks
 // (one per thread, 8 rows x 16 bytes, coalesced), transposed in registers and stored
 // channel-major in LDS, so an MFMA fragment (8 consecutive tokens of one channel) is a
-// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator.
+// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator;
+// the accumulator holds one slab (SLAB / 16 MFMA steps) and is then added to a float64 sum,
+// so rounding only ever affects the sum of one slab's products.  The partials are float64.
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __restrict__ delta,
                                                               int T, int chunk,
-                                                              float* __restrict__ partials) {
+                                                              double* __restrict__ partials) {
   constexpr int SLAB = 16384 / D;
   constexpr int SR = SLAB + 8;  // LDS row stride (bf16 elements), 16-byte pad
   constexpr int NB = D / 32;
@@ -63,10 +65,14 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
     J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
   }
   floatx16 acc[3];
+  double sum[3][16];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      acc[b][i] = 0.f;
+      sum[b][i] = 0.0;
+    }
 
   // ---- 8x8 block of this thread: rows ts + 8 rg + i, channels 8 cg .. 8 cg + 7; the next
   //      slab's block is requested before the current slab's MFMAs
@@ -110,24 +116,33 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
         }
       }
     }
+    // ---- the slab's float32 sums into the float64 sums
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sum[b][i] += (double)acc[b][i];
+        acc[b][i] = 0.f;
+      }
   }
   // ---- write this workgroup's blocks: [m][split][blk][reg][lane]
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (I[b] >= 0) {
-      float* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+      double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = acc[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = sum[b][i];
     }
   }
 }
 
 // ------------------------------------------------------------------------- Gram, fp32
-// Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2.
+// Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2; each
+// slab's float32 sums are added to float64 sums as in the bf16 kernel.
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __restrict__ delta,
                                                              int T, int chunk,
-                                                             float* __restrict__ partials) {
+                                                             double* __restrict__ partials) {
   constexpr int SLAB = 8192 / D;
   constexpr int SR = D + 4;
   constexpr int NB = D / 32;
@@ -147,10 +162,14 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
     J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
   }
   floatx16 acc[3];
+  double sum[3][16];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      acc[b][i] = 0.f;
+      sum[b][i] = 0.0;
+    }
   for (int ts = t_begin; ts < t_end; ts += SLAB) {
     __syncthreads();
     for (int q = tid; q < SLAB * C4; q += kBlock) {
@@ -171,15 +190,51 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
         }
       }
     }
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sum[b][i] += (double)acc[b][i];
+        acc[b][i] = 0.f;
+      }
   }
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (I[b] >= 0) {
-      float* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+      double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = acc[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = sum[b][i];
     }
   }
+}
+
+// ------------------------------------------------------------------------- k_eff certificate
+// Is the effective rank k of a fast path certain?  lam: the path's eigenvalues, descending,
+// valid up to k; trace: its total energy (float64).  The decision compares running sums
+// C_j = sum_{i<=j} lambda_i with need = energy * trace at j = k - 1 (below) and j = k (at or
+// above).  The path's C_j differs from that of the exact delta^T delta by at most
+//   j * eig_err                       eigenvalues found to eig_err each (absolute), plus
+//   (sqrt(j) + 1) * gamma * trace     Gram error E with ||E||_F <= gamma * trace (the sum of
+//                                     the j largest eigenvalues moves by at most
+//                                     sqrt(j) ||E||_F (Ky Fan), the trace by ||E||_F), plus
+//   4e-13 * sqrt(j + 1) * trace       float64 reduction to tridiagonal form and summation.
+// Both sides must clear their bound; otherwise the exact path decides (keff_exact_kernel).
+template <int D, typename F>
+__device__ bool keff_certain(const F* lam, int k, double energy, double trace, double eig_err,
+                             double gamma) {
+  if (!(trace > 0.0) || k <= 0) return true;  // zero delta: k = 0 is exact
+  const double need = energy * trace;
+  double run = 0.0;
+  for (int j = 0; j < k - 1; ++j) run += (double)lam[j];
+  auto bound = [&](int j) {
+    return (double)j * eig_err + (sqrt((double)j) + 1.0) * gamma * trace +
+           4e-13 * sqrt((double)j + 1.0) * trace;
+  };
+  const double below = run;                      // C_{k-1}
+  const double above = run + (double)lam[k - 1]; // C_k
+  if (!(need - below > bound(k - 1))) return false;
+  if (k < D && !(above - need >= bound(k))) return false;
+  return true;
 }
 
 // ------------------------------------------------------------------------- Jacobi
@@ -247,8 +302,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 template <int D>
 __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
-    const float* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
-    double energy, float tol, float eta,
+    const double* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
+    double energy, double gamma, float tol, float eta,
     float* __restrict__ W_out, float* __restrict__ eig_out, int32_t* __restrict__ k_eff_out,
     uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo, int rpad,
     int* __restrict__ sweeps_out) {
@@ -268,11 +323,12 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   __shared__ float sgn[D];
   __shared__ float nrm[D];     // squared column norms, carried through a sweep
   __shared__ int lastrot[D];   // global step of the column's last rotation
+  __shared__ double diag[D];   // G's diagonal (float64): the trace is the total energy
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   if (tid < D) lastrot[tid] = -(1 << 30);
 
-  // ---- G = sum of the partials (fixed order), mirrored to a full symmetric matrix
-  const float* P = partials + (size_t)m * nsplit * NBLK * 1024;
+  // ---- G = sum of the partials (fixed order, float64), mirrored to a full symmetric matrix
+  const double* P = partials + (size_t)m * nsplit * NBLK * 1024;
   float fro = 0.f;
   if (G_in != nullptr) {  // G as given (float64, full symmetric)
     const double* Gm = G_in + (size_t)m * D * D;
@@ -281,6 +337,7 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
       const float v = (float)Gm[e];
       Am[col * CS + jrow(row)] = v;
       fro += v * v;
+      if (row == col) diag[row] = Gm[e];
     }
   }
   for (int e = tid; G_in == nullptr && e < NBLK * 1024; e += kJacobiBlock) {
@@ -291,11 +348,13 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
     const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
     const int col = J * 32 + (l % 32);
     if (row > col) continue;  // a diagonal block's lower half: its mirror writes it
-    float v = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) v += P[(size_t)sp * NBLK * 1024 + e];
+    double vd = 0.0;
+    for (int sp = 0; sp < nsplit; ++sp) vd += P[(size_t)sp * NBLK * 1024 + e];
+    const float v = (float)vd;
     Am[col * CS + jrow(row)] = v;
     Am[row * CS + jrow(col)] = v;
     fro += (row == col) ? v * v : 2.f * v * v;
+    if (row == col) diag[row] = vd;
   }
   const float f2 = block_sum<D>(fro, redf);
   const float abs_floor = eta * f2;
@@ -403,8 +462,9 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
   }
   __syncthreads();
   if (tid == 0) {
+    // total energy = trace of G (float64, fixed order), as in the tridiagonal route
     double total = 0.0;
-    for (int k = 0; k < D; ++k) total += (double)lam[order[k]];
+    for (int k = 0; k < D; ++k) total += diag[k];
     int ke = 0;
     if (total > 0.0) {
       const double need = energy * total;
@@ -415,9 +475,14 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
         if (run >= need) { ke = k + 1; break; }
       }
     }
-    k_eff_out[m] = ke;
+    // eigenvalues from float32 rotations stopped at tol: each within (64 eps + 4 tol) ||G||_F;
+    // a decision inside the bound is flagged (-1 - k) for keff_exact_kernel
+    for (int k = 0; k < D; ++k) xs[k] = lam[order[k]];
+    const double eig_err = (64.0 * 0x1p-24 + 4.0 * (double)tol) * sqrt((double)f2);
+    k_eff_out[m] = keff_certain<D>(xs, ke, energy, total, eig_err, gamma) ? ke : -1 - ke;
     if (sweeps_out) sweeps_out[m] = sweep;
   }
+  __syncthreads();  // xs is reused below
   if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = lam[order[tid]];
 
   // ---- kept vectors: two-pass classical Gram-Schmidt in descending order, written back
@@ -639,8 +704,8 @@ __device__ float multisect(int ev, float lo, float hi, const float* df, const fl
 
 template <int D>
 __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
-    const float* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
-    double energy, float* __restrict__ W_out, float* __restrict__ eig_out,
+    const double* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
+    double energy, double gamma, float* __restrict__ W_out, float* __restrict__ eig_out,
     int32_t* __restrict__ k_eff_out, uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
     int rpad) {
   constexpr int NB = D / 32;
@@ -664,7 +729,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
       if (col <= row) P[pk(row, col)] = Gm[e];
     }
   } else {
-    const float* Pm = partials + (size_t)m * nsplit * NBLK * 1024;
+    const double* Pm = partials + (size_t)m * nsplit * NBLK * 1024;
     constexpr int PER = NBLK * 1024 / kEigBlock;  // 20 (D = 128) or 6 (D = 64)
     constexpr int U4 = 4;
     for (int t0 = 0; t0 < PER; t0 += U4) {
@@ -672,10 +737,10 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
 #pragma unroll
       for (int u = 0; u < U4; ++u) acc[u] = 0.0;
       for (int sp = 0; sp < nsplit; ++sp) {
-        const float* src = Pm + (size_t)sp * NBLK * 1024;
+        const double* src = Pm + (size_t)sp * NBLK * 1024;
 #pragma unroll
         for (int u = 0; u < U4; ++u)
-          if (t0 + u < PER) acc[u] += (double)src[(t0 + u) * kEigBlock + tid];
+          if (t0 + u < PER) acc[u] += src[(t0 + u) * kEigBlock + tid];
       }
 #pragma unroll
       for (int u = 0; u < U4; ++u) {
@@ -933,7 +998,9 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
         if (run >= need) { ke = k + 1; break; }
       }
     }
-    k_eff_out[m] = ke;
+    // a decision inside the error bound of this path is flagged (-1 - k) for keff_exact_kernel
+    const double eig_err = 16.0 * 0x1p-24 * (double)hi0;  // float32 Sturm counts (see keff_certain)
+    k_eff_out[m] = keff_certain<D>(lamd, ke, energy, trace, eig_err, gamma) ? ke : -1 - ke;
   }
   if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = lamd[tid];
 
@@ -1183,6 +1250,181 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   }
 }
 
+// ------------------------------------------------------------------------- exact effective rank
+// For the matrices a fast path flagged (k_eff_out[m] < 0, see keff_certain) the effective
+// rank is decided again from float64 arithmetic throughout, so that it is exact up to float64
+// rounding:
+//   G      from delta: every product and sum in float64 (SRC 0: bf16 delta, 1: fp32 delta);
+//          or the given G, symmetrised as (G + G^T) / 2 (SRC 2)
+//   T      Householder reduction of G to tridiagonal form (float64, IEEE division and sqrt)
+//   lambda every eigenvalue of T by 4-point multisection on float64 Sturm counts: 24 steps
+//          shrink the Gershgorin interval 5^24 > 2^55 times
+//   k_eff  the definition: eigenvalues clamped at 0, sorted descending, the first k whose
+//          running sum reaches energy * (their total)
+// The flag is replaced by k_eff, and eig_out (if given) by these eigenvalues.  One 512-thread
+// workgroup per matrix; unflagged matrices leave at once.  Deterministic (fixed orders).
+constexpr int kExactBlock = 512;
+constexpr int kExactSlab = 64;  // rows of delta staged per step of the Gram
+
+template <int D, int SRC>
+__global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __restrict__ src,
+                                                                int T, double energy,
+                                                                int32_t* __restrict__ k_eff,
+                                                                float* __restrict__ eig_out) {
+  constexpr int GS = D + 1;            // row stride of G in LDS (doubles)
+  constexpr int TR = D / 32, TC = D / 16;  // Gram tile of a thread: TR rows x TC columns
+  constexpr int NW = kExactBlock / kWave;
+  constexpr int RT = kExactBlock / D;  // threads per row of a matrix-vector product
+  extern __shared__ __align__(16) double Gs[];  // [D][GS]; the Gram stages delta here first
+  __shared__ double vv[D], ww[D], dd[D], ee[D], red[NW];
+  __shared__ double lam[D];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  if (k_eff[m] >= 0) return;  // uniform: only flagged matrices
+
+  // ---- G in float64
+  if constexpr (SRC == 2) {
+    const double* Gm = static_cast<const double*>(src) + (size_t)m * D * D;
+    for (int e = tid; e < D * D; e += kExactBlock) {
+      const int i = e / D, j = e % D;
+      Gs[i * GS + j] = 0.5 * (Gm[(size_t)i * D + j] + Gm[(size_t)j * D + i]);
+    }
+  } else {
+    float* stage = reinterpret_cast<float*>(Gs);  // [kExactSlab][D], exact copies of delta
+    const int i0 = TR * (tid / 16), j0 = TC * (tid % 16);
+    double acc[TR][TC];
+#pragma unroll
+    for (int a = 0; a < TR; ++a)
+#pragma unroll
+      for (int b = 0; b < TC; ++b) acc[a][b] = 0.0;
+    for (int t0 = 0; t0 < T; t0 += kExactSlab) {
+      const int n = min(kExactSlab, T - t0);
+      for (int e = tid; e < n * D; e += kExactBlock) {
+        const size_t g = ((size_t)m * T + t0) * D + e;
+        if constexpr (SRC == 0)
+          stage[e] = bf16_to_f32(static_cast<const uint16_t*>(src)[g]);
+        else
+          stage[e] = static_cast<const float*>(src)[g];
+      }
+      __syncthreads();
+      for (int t = 0; t < n; ++t) {
+        double xa[TR], xb[TC];
+#pragma unroll
+        for (int a = 0; a < TR; ++a) xa[a] = (double)stage[t * D + i0 + a];
+#pragma unroll
+        for (int b = 0; b < TC; ++b) xb[b] = (double)stage[t * D + j0 + b];
+#pragma unroll
+        for (int a = 0; a < TR; ++a)
+#pragma unroll
+          for (int b = 0; b < TC; ++b) acc[a][b] = fma(xa[a], xb[b], acc[a][b]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < TR; ++a)
+#pragma unroll
+      for (int b = 0; b < TC; ++b) Gs[(i0 + a) * GS + j0 + b] = acc[a][b];
+  }
+  __syncthreads();
+
+  // ---- Householder reduction to tridiagonal form: column k, x = G[k+1:, k],
+  //      alpha = -sign(x_0) |x|, v = x - alpha e_1, t = 2 / v.v = 1 / (|x|^2 - alpha x_0),
+  //      p = t B v, w = p - (t/2)(p.v) v, B <- B - v w^T - w v^T on the trailing block B
+  for (int k = 0; k < D - 2; ++k) {
+    const double xk = tid > k && tid < D ? Gs[tid * GS + k] : 0.0;
+    const double nx2 = block_sum_d(xk * xk, red);
+    const double x0 = Gs[(k + 1) * GS + k];
+    const double nx = sqrt(nx2);
+    const double alpha = nx2 == 0.0 ? 0.0 : (x0 >= 0.0 ? -nx : nx);
+    const double t = nx2 == 0.0 ? 0.0 : 1.0 / (nx2 - alpha * x0);
+    if (tid < D) vv[tid] = tid > k + 1 ? xk : (tid == k + 1 ? x0 - alpha : 0.0);
+    if (tid == 0) {
+      dd[k] = Gs[k * GS + k];
+      ee[k] = alpha;
+    }
+    __syncthreads();
+    // p_i = t sum_j B_ij v_j: RT threads per row, partial sums joined in a fixed order
+    {
+      const int i = tid / RT, part = tid % RT;
+      double pv = 0.0;
+      if (i > k)
+        for (int j = k + 1 + part; j < D; j += RT) pv = fma(Gs[i * GS + j], vv[j], pv);
+#pragma unroll
+      for (int off = 1; off < RT; off <<= 1) pv += __shfl_xor(pv, off, 64);
+      if (part == 0) ww[i] = i > k ? t * pv : 0.0;
+    }
+    __syncthreads();
+    const double pdotv = block_sum_d(tid < D ? ww[tid] * vv[tid] : 0.0, red);
+    const double K = 0.5 * t * pdotv;
+    if (tid < D) ww[tid] -= K * vv[tid];
+    __syncthreads();
+    for (int e = tid; e < D * D; e += kExactBlock) {
+      const int i = e / D, j = e % D;
+      if (i > k && j > k) Gs[i * GS + j] -= vv[i] * ww[j] + ww[i] * vv[j];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dd[D - 2] = Gs[(D - 2) * GS + D - 2];
+    dd[D - 1] = Gs[(D - 1) * GS + D - 1];
+    ee[D - 2] = Gs[(D - 1) * GS + D - 2];
+    ee[D - 1] = 0.0;
+  }
+  __syncthreads();
+
+  // ---- every eigenvalue: 4 lanes per eigenvalue, Gershgorin start interval
+  double lo0 = 0.0, hi0 = 0.0, max_e2 = 0.0;
+  for (int i = 0; i < D; ++i) {  // the same on every thread
+    const double r0 = (i > 0 ? fabs(ee[i - 1]) : 0.0) + fabs(ee[i]);
+    lo0 = i == 0 ? dd[i] - r0 : fmin(lo0, dd[i] - r0);
+    hi0 = i == 0 ? dd[i] + r0 : fmax(hi0, dd[i] + r0);
+    max_e2 = fmax(max_e2, ee[i] * ee[i]);
+  }
+  const double pivmin = 1e-290 * fmax(1.0, max_e2);
+  const double pad = 1e-12 * fmax(fabs(lo0), fabs(hi0)) + 1e-290;
+  if (tid < 4 * D) {
+    const int ev = tid / 4, q = tid % 4;
+    double lo = lo0 - pad, hi = hi0 + pad;
+    for (int it = 0; it < 24; ++it) {
+      const double x = lo + (double)(q + 1) * ((hi - lo) / 5.0);
+      // Sturm count: negative pivots of T - x I
+      double pv = dd[0] - x;
+      if (fabs(pv) < pivmin) pv = -pivmin;
+      int cnt = pv < 0.0;
+      for (int j = 1; j < D; ++j) {
+        pv = (dd[j] - x) - (ee[j - 1] * ee[j - 1]) / pv;
+        if (fabs(pv) < pivmin) pv = -pivmin;
+        cnt += pv < 0.0;
+      }
+      double h = cnt > ev ? x : hi;
+      h = fmin(h, __shfl_xor(h, 1, 64));
+      h = fmin(h, __shfl_xor(h, 2, 64));
+      double l = x < h ? x : lo;
+      l = fmax(l, __shfl_xor(l, 1, 64));
+      l = fmax(l, __shfl_xor(l, 2, 64));
+      lo = l;
+      hi = h;
+    }
+    if (q == 0) lam[D - 1 - ev] = fmax(0.5 * (lo + hi), 0.0);  // descending order
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    for (int i = 0; i < D; ++i) total += lam[i];
+    int ke = 0;
+    if (total != 0.0) {
+      const double need = energy * total;
+      double run = 0.0;
+      ke = D;
+      for (int i = 0; i < D; ++i) {
+        run += lam[i];
+        if (run >= need) { ke = i + 1; break; }
+      }
+    }
+    k_eff[m] = ke;
+  }
+  if (eig_out && tid < D) eig_out[(size_t)m * D + tid] = (float)lam[tid];
+}
+
 // ------------------------------------------------------------------------- projection
 // grid (n_tiles, M): U[t, j] = sum_c delta[t, c] W[j, c].  Orientation U^T = W delta^T:
 // A operand = W rows (row m of a 32-block = component 32 mb + cmap32(m)), B operand =
@@ -1338,11 +1580,35 @@ static void allow_dynamic_lds(K kernel, size_t bytes) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Bound on the Gram error of the fast path per unit of trace (see keff_certain): each float32
+// accumulator holds one slab of products before it joins the float64 sum, so an element's
+// error is at most (steps + 2) roundings of the sum of the slab's |products| (steps = MFMA
+// steps per slab: SLAB / 16 for bf16, 2 products per step for fp32), doubled for safety.
+template <int D>
+static double gram_gamma(int dtype) {
+  const double steps = dtype == KVC_BF16 ? (16384.0 / D) / 16.0 : 2.0 * (8192.0 / D) / 2.0;
+  return 2.0 * (steps + 2.0) * 0x1p-24;
+}
+
+// Flagged effective ranks (k_eff_out < 0) decided again in float64 (keff_exact_kernel).
+template <int D>
+static hipError_t launch_keff_exact(const void* src, int src_kind, int M, int T, double energy,
+                                    int32_t* k_eff, float* eig, hipStream_t st) {
+  const size_t lds = (size_t)D * (D + 1) * sizeof(double);
+  void (*k)(const void*, int, double, int32_t*, float*) =
+      src_kind == 0 ? keff_exact_kernel<D, 0>
+                    : (src_kind == 1 ? keff_exact_kernel<D, 1> : keff_exact_kernel<D, 2>);
+  allow_dynamic_lds(k, lds);
+  hipLaunchKernelGGL(k, dim3(M), dim3(kExactBlock), lds, st, src, T, energy, k_eff, eig);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double energy,
                         float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                         hipStream_t st) {
-  float* partials = reinterpret_cast<float*>(ws + f.off_gram);
+  double* partials = reinterpret_cast<double*>(ws + f.off_gram);
+  const double gamma = gram_gamma<D>(dtype);
   uint16_t* whi = reinterpret_cast<uint16_t*>(ws + f.off_whi);
   uint16_t* wlo = reinterpret_cast<uint16_t*>(ws + f.off_wlo);
   int* sweeps = reinterpret_cast<int*>(ws + f.off_sweeps);
@@ -1359,7 +1625,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
     allow_dynamic_lds(eig_kernel<D>, lds);
     hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
-                       f.nsplit, (const double*)nullptr, f.r, energy, W_out, eig, k_eff,
+                       f.nsplit, (const double*)nullptr, f.r, energy, gamma, W_out, eig, k_eff,
                        dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
                        f.rpad);
   } else {
@@ -1367,11 +1633,13 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     allow_dynamic_lds(jacobi_kernel<D>, lds);
     const float tol = 2e-6f, eta = 1e-12f;
     hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials,
-                       f.nsplit, (const double*)nullptr, f.r, energy, tol, eta, W_out, eig, k_eff,
-                       dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
+                       f.nsplit, (const double*)nullptr, f.r, energy, gamma, tol, eta, W_out, eig,
+                       k_eff, dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
                        f.rpad, sweeps);
   }
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_keff_exact<D>(delta, dtype == KVC_BF16 ? 0 : 1, f.M, f.T, energy, k_eff, eig, st);
   if (e != hipSuccess || f.T == 0) return e;
   const int n_tiles = ceil_div(f.T, kRowsPerPass * kProjIters);
   const dim3 g3(n_tiles, f.M);
@@ -1389,7 +1657,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
 // blocks is summed over the splits in fixed order (float64, from 0) and added to both
 // triangles of G, so a block accumulated onto G = 0 gives exactly the G of the one-call fit.
 template <int D>
-__global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const float* __restrict__ partials,
+__global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const double* __restrict__ partials,
                                                                int nsplit,
                                                                double* __restrict__ G) {
   constexpr int NB = D / 32;
@@ -1403,9 +1671,9 @@ __global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const float* __
   const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
   const int col = J * 32 + (l % 32);
   if (row > col) return;  // a diagonal block's lower half holds no new element
-  const float* Pm = partials + (size_t)m * nsplit * NBLK * 1024 + e;
+  const double* Pm = partials + (size_t)m * nsplit * NBLK * 1024 + e;
   double v = 0.0;
-  for (int sp = 0; sp < nsplit; ++sp) v += (double)Pm[(size_t)sp * NBLK * 1024];
+  for (int sp = 0; sp < nsplit; ++sp) v += Pm[(size_t)sp * NBLK * 1024];
   double* Gm = G + (size_t)m * D * D;
   Gm[row * D + col] += v;
   if (row != col) Gm[col * D + row] += v;
@@ -1430,7 +1698,7 @@ template <int D>
 static hipError_t gram_t(const void* delta, const FitLayout& f, int dtype, double* G, char* ws,
                          hipStream_t st) {
   constexpr int NBLK = (D / 32) * (D / 32 + 1) / 2;
-  float* partials = reinterpret_cast<float*>(ws + f.off_gram);
+  double* partials = reinterpret_cast<double*>(ws + f.off_gram);
   const dim3 g1(f.nsplit, f.M);
   if (dtype == KVC_BF16)
     hipLaunchKernelGGL((gram_bf16_kernel<D>), g1, dim3(kBlock), 0, st,
@@ -1453,17 +1721,19 @@ static hipError_t eig_from_gram_t(const double* G, int M, int r, double energy, 
     const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
     allow_dynamic_lds(eig_kernel<D>, lds);
     hipLaunchKernelGGL((eig_kernel<D>), dim3(M), dim3(kEigBlock), lds, st,
-                       (const float*)nullptr, 0, G, r, energy, W_out, eig, k_eff,
+                       (const double*)nullptr, 0, G, r, energy, 0.0, W_out, eig, k_eff,
                        (uint16_t*)nullptr, (uint16_t*)nullptr, rpad);
   } else {
     const size_t lds = (size_t)D * (D + 4) * sizeof(float);
     allow_dynamic_lds(jacobi_kernel<D>, lds);
     const float tol = 2e-6f, eta = 1e-12f;
     hipLaunchKernelGGL((jacobi_kernel<D>), dim3(M), dim3(kJacobiBlock), lds, st,
-                       (const float*)nullptr, 0, G, r, energy, tol, eta, W_out, eig, k_eff,
+                       (const double*)nullptr, 0, G, r, energy, 0.0, tol, eta, W_out, eig, k_eff,
                        (uint16_t*)nullptr, (uint16_t*)nullptr, rpad, (int*)nullptr);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_keff_exact<D>(G, 2, M, 0, energy, k_eff, eig, st);
 }
 
 template <int D>

@@ -14,6 +14,7 @@ constexpr int kWave = 64;             // CDNA wavefront width
 constexpr int kBlock = 256;           // 4 waves per workgroup everywhere
 constexpr int kRowsPerPass = 128;     // tokens of one 32-token tile per wave, 4 waves
 constexpr int kMaxA = 16;             // anchors per segment held in registers
+constexpr int kMaxAnchorsGeneral = 256;  // A * r <= 256: the general correction's bound
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
 constexpr int kMaxPool = 32;          // slots of an online anchor pool per segment
@@ -69,6 +70,7 @@ struct CorrectLayout {
   size_t off_slot;    // int [S][A]: pool slots of the selected anchors (pooled correction)
   size_t off_wmt;     // float [kMaxTargets][S][A]: weights of a multi-target launch
   size_t off_mmt;     // uint8 [kMaxTargets][S]: flags of a multi-target launch
+  size_t off_q;       // float [S][2d]: pooled descriptors (general correction)
   size_t bytes;
 };
 
@@ -90,6 +92,7 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_slot = o;  o = align_up(o + sizeof(int) * (size_t)c.S * A, 256);
   c.off_wmt = o;   o = align_up(o + sizeof(float) * (size_t)kMaxTargets * c.S * A, 256);
   c.off_mmt = o;   o = align_up(o + (size_t)kMaxTargets * c.S, 256);
+  c.off_q = o;     o = align_up(o + sizeof(float) * 2ull * c.S * d, 256);
   c.bytes = o;
   return c;
 }
@@ -137,7 +140,7 @@ struct FitLayout {
   int nsplit;       // Gram partials per matrix
   int chunk;        // rows per Gram workgroup (multiple of slab)
   int nblk;         // upper-triangular 32x32 blocks of G
-  size_t off_gram;  // float [M][nsplit][nblk][16][64]
+  size_t off_gram;  // double [M][nsplit][nblk][16][64]
   size_t off_whi;   // bf16 [M][rpad][d]
   size_t off_wlo;   // bf16 [M][rpad][d]
   size_t off_sweeps;// int [M]
@@ -158,7 +161,7 @@ inline FitLayout fit_layout(int M, int T, int d, int r, int target_wgs = 1024) {
   f.chunk = slabs_per * f.slab;
   f.nsplit = T > 0 ? ceil_div(T, f.chunk) : 1;
   size_t o = 0;
-  f.off_gram = o;   o = align_up(o + sizeof(float) * (size_t)M * f.nsplit * f.nblk * 1024, 256);
+  f.off_gram = o;   o = align_up(o + sizeof(double) * (size_t)M * f.nsplit * f.nblk * 1024, 256);
   f.off_whi = o;    o = align_up(o + 2ull * M * f.rpad * d, 256);
   f.off_wlo = o;    o = align_up(o + 2ull * M * f.rpad * d, 256);
   f.off_sweeps = o; o = align_up(o + sizeof(int) * (size_t)M, 256);
@@ -193,6 +196,18 @@ hipError_t launch_pool_insert(const uint8_t* mask, const float* U_new, const flo
 void set_fused_wait_for_tests(long long ticks, int withhold_segment);
 // Correction (after launch_score), or the fused pass (resets its own counters).
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
+// Anchor shapes the specialised correction kernel holds in registers and LDS.
+inline bool correct_specialised(int A, int r, int dtype) {
+  if (A > kMaxA || r > kMaxR) return false;
+  return dtype == KVC_BF16 ? A * ((r + 15) / 16 * 16) <= kMaxKSlots : A * ((r + 7) / 8 * 8) <= 64;
+}
+// General correction (kvc_correct_general.hip): matching of any number of anchors from q
+// [S][2d], then the correction as one contraction over the anchors' concatenated rank index
+// (uses K, V, U, W, w_ws, mask_ws, slot_ws / Vc, K_fb, V_fb, K_out, V_out, S, T, d, dtype, A, r).
+hipError_t launch_score_general(const float* q, const float* desc, int S, int d, int A,
+                                float tau, float* w_ws, uint8_t* mask_ws, float* score_out,
+                                float* w_out, uint8_t* mask_out, hipStream_t st);
+hipError_t launch_correct_general(const CorrectLaunch& L, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
                       float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                       hipStream_t st);

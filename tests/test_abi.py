@@ -54,11 +54,13 @@ def _correct(**kw):
     (dict(d=0), 1, "positive"),
     (dict(dtype=7), 1, "dtype"),
     (dict(A=0), 1, "A=0"),
-    (dict(A=17), 2, "A=17"),
+    (dict(A=17), 2, "A*r=544"),
     (dict(r=0), 1, "r=0"),
-    (dict(r=65), 2, "r=65"),
-    (dict(A=8, r=48), 2, "A*ceil16"),
-    (dict(dtype=1, A=2, r=40), 2, "fp32"),
+    (dict(r=65), 2, "A*r=260"),
+    (dict(A=8, r=48), 2, "A*r=384"),
+    (dict(A=257, r=1), 2, "A*r=257"),
+    (dict(d=64, A=1, r=65), 1, "exceeds d=64"),
+    (dict(A=1, r=129), 1, "exceeds d=128"),
     (dict(K_fb=FAKE), 1, "both"),
     (dict(mask=None), 1, "mask_out"),
     (dict(ws=None), 4, "workspace"),
@@ -214,7 +216,7 @@ def test_anchor_pool_rejects_bad_arguments():
                 nb=big, st=None)
     for kw, status, msg in [(dict(Vc=0), 1, "Vc=0"), (dict(Vc=33), 2, "Vc=33"),
                             (dict(A=5, Vc=4), 1, "capacity"), (dict(count=None), 1, "count"),
-                            (dict(count=FAKE + 2), 1, "count"), (dict(A=17, Vc=20), 2, "A=17"),
+                            (dict(count=FAKE + 2), 1, "count"), (dict(A=17, Vc=20), 2, "A*r=544"),
                             (dict(slot=FAKE + 1), 1, "slot_out"), (dict(ws=None), 4, "work")]:
         a = dict(base)
         a.update(kw)

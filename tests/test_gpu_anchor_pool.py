@@ -27,7 +27,9 @@ def _host_pool(p, desc):
                                                ("f32", 128, 257, 5, 2, 8),
                                                ("bf16", 128, 300, 20, 4, 32),
                                                ("bf16", 128, 200, 32, 16, 16),
-                                               ("bf16", 64, 100, 1, 1, 8)])
+                                               ("bf16", 64, 100, 1, 1, 8),
+                                               ("bf16", 128, 150, 24, 20, 12),  # general
+                                               ("f32", 128, 120, 8, 4, 32)])    # general
 def test_pooled_correction_matches_the_oracle(dtype, dd, T, Vc, A, r):
     cfg = synth.CONFIGS["llama8b_t2048"].replace(L=2, H=4, T=T, d=dd, dtype=dtype, A=A, r=r,
                                                  seed=51 + Vc, fallback_prob=0.25)

@@ -12,8 +12,10 @@ from gpu_helpers import check_close, dev, pool_all, say
 pytestmark = pytest.mark.gpu
 
 
-def test_small_chain_every_segment():
-    cfg = synth.CONFIGS["chain_t32768"].replace(L=2, H=3, T=600, seed=31, fallback_prob=0.3)
+@pytest.mark.parametrize("dtype,A,r", [("bf16", 4, 32), ("bf16", 2, 128), ("f32", 4, 32)])
+def test_small_chain_every_segment(dtype, A, r):
+    cfg = synth.CONFIGS["chain_t32768"].replace(L=2, H=3, T=600, seed=31, fallback_prob=0.3,
+                                                dtype=dtype, A=A, r=r)
     say(f"[chain] L={cfg.L} H={cfg.H} T={cfg.T} edges={cfg.n_edges}")
     case = synth.generate(cfg)
     # descriptors of edge e are built on the oracle's pooled query of edge e's source, so the

@@ -70,6 +70,17 @@ SMALL = [
     ("f32", 128, 777, 3, 12),
     ("f32", 128, 64, 1, 64),
     ("f32", 64, 333, 8, 5),
+    # general correction: every shape with r <= d and A * r <= 256 outside the specialised
+    # kernel's budget (one contraction over the concatenated rank index)
+    ("bf16", 128, 700, 2, 128),   # r = d
+    ("f32", 128, 300, 4, 32),
+    ("bf16", 64, 500, 4, 64),     # r = d = 64, A * r = 256
+    ("bf16", 128, 333, 256, 1),   # 256 anchors of rank 1
+    ("bf16", 128, 200, 20, 12),   # A > 16, r not a multiple of 8
+    ("f32", 64, 129, 3, 64),
+    ("f32", 128, 257, 1, 128),
+    ("bf16", 128, 96, 9, 28),
+    ("f32", 64, 70, 17, 15),
 ]
 
 

@@ -31,7 +31,8 @@ def _fanout_inputs(cfg, with_fb):
 
 
 @pytest.mark.parametrize("dtype,d,T,A,r", [("bf16", 128, 600, 4, 32), ("bf16", 64, 1000, 3, 16),
-                                           ("f32", 128, 300, 2, 8)])
+                                           ("f32", 128, 300, 2, 8), ("bf16", 128, 300, 2, 128),
+                                           ("f32", 128, 200, 4, 32)])
 def test_fanout_matches_the_oracle(dtype, d, T, A, r):
     cfg = synth.CONFIGS["chain_t32768"].replace(L=2, H=3, T=T, d=d, dtype=dtype, A=A, r=r,
                                                 seed=41, fallback_prob=0.35, outliers=2)
