@@ -27,8 +27,6 @@ import torch
 
 __all__ = [
     "KvcError",
-    "KvcWaitError",
-    "check_mask",
     "CorrectResult",
     "FitResult",
     "lib",
@@ -75,7 +73,6 @@ _sz = ctypes.c_size_t
 _SIGS = {
     "kvc_version": (ctypes.c_char_p, []),
     "kvc_last_error": (ctypes.c_char_p, []),
-    "kvc_test_fused_wait": (None, [ctypes.c_longlong, _i]),
     "kvc_pool_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_pool_descriptor": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "kvc_correct_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -127,21 +124,6 @@ def lib() -> ctypes.CDLL:
 def _check(status: int) -> None:
     if status != 0:
         raise KvcError(status, lib().kvc_last_error().decode())
-
-
-class KvcWaitError(RuntimeError):
-    """A segment of the single-launch correction pass gave up waiting for its matching result
-    (mask value 2): the segment was copied through as for a fallback."""
-
-
-def check_mask(mask: torch.Tensor) -> torch.Tensor:
-    """Raise KvcWaitError if any segment of a correction's fallback mask carries the value 2
-    (see mask_out of kvc_correct in include/kvc.h).  Synchronises with the mask's stream."""
-    bad = (mask == 2).nonzero()
-    if bad.numel():
-        raise KvcWaitError(f"{bad.shape[0]} segment(s) gave up waiting in the single-launch "
-                           f"pass and were copied through, first (l, h) = {tuple(bad[0].tolist())}")
-    return mask
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -236,14 +218,11 @@ def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tenso
             K_fb: Optional[torch.Tensor] = None, V_fb: Optional[torch.Tensor] = None,
             K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
             want_score: bool = True, want_w: bool = True, want_q_next: bool = False,
-            workspace: Optional[torch.Tensor] = None, check: bool = True) -> CorrectResult:
+            workspace: Optional[torch.Tensor] = None) -> CorrectResult:
     """Correct a reused cache with its segments' anchors (see kvc_correct in include/kvc.h).
 
     K, V: [L, H, T, d]; desc: [L, H, A, 2d] float32; U: [2, L, H, A, T, r];
     W: [2, L, H, A, r, d] (cache dtype).  Pass K_out=K, V_out=V to correct in place.
-    check: raise KvcWaitError if a segment of the single-launch pass gave up waiting
-    (mask 2).  That check synchronises with the stream; pass False in a timed loop and call
-    check_mask(result.mask) afterwards.
     """
     L, H, T, d = K.shape
     dev = K.device
@@ -273,8 +252,6 @@ def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tenso
                              r, float(tau), _ptr(q_in), _ptr(K_fb), _ptr(V_fb), _ptr(Ko),
                              _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(qn), _ptr(ws),
                              _ws_bytes(ws), _stream(dev)))
-    if check and q_in is None:
-        check_mask(mask)
     return CorrectResult(Ko, Vo, mask, score, w, qn)
 
 
@@ -287,13 +264,11 @@ def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
 
 def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau: float, *,
                   outputs: Optional[Sequence[tuple]] = None,
-                  workspace: Optional[torch.Tensor] = None, check: bool = True) -> list:
+                  workspace: Optional[torch.Tensor] = None) -> list:
     """Chained correction A0 -> A1 -> ... (see kvc_correct_chain in include/kvc.h).
 
     ``edges``: one dict per edge with desc, U, W and optionally K_fb, V_fb.  ``outputs``:
     optional preallocated (K_out, V_out) per edge.  Returns one CorrectResult per edge.
-    check: raise KvcWaitError if a segment of edge 0's single-launch pass gave up waiting
-    (synchronises; see correct).
     """
     L, H, T, d = K0.shape
     dev = K0.device
@@ -334,18 +309,15 @@ def correct_chain(K0: torch.Tensor, V0: torch.Tensor, edges: Sequence[dict], tau
         _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
         _ptr(ws), _ws_bytes(ws), _stream(dev)))
-    if check:
-        check_mask(res[0].mask)
     return res
 
 
 def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau: float, *,
                    outputs: Optional[Sequence[tuple]] = None,
-                   workspace: Optional[torch.Tensor] = None, check: bool = True) -> list:
+                   workspace: Optional[torch.Tensor] = None) -> list:
     """Non-chained correction of one reference cache toward several agents (see
     kvc_correct_fanout in include/kvc.h).  ``agents``: one dict per agent with desc, U, W
-    and optionally K_fb, V_fb.  Returns one CorrectResult per agent.  check: as for
-    correct (a single agent takes the single-launch pass)."""
+    and optionally K_fb, V_fb.  Returns one CorrectResult per agent."""
     L, H, T, d = K.shape
     dev = K.device
     dt = _dtype_code(K)
@@ -385,8 +357,6 @@ def correct_fanout(K: torch.Tensor, V: torch.Tensor, agents: Sequence[dict], tau
         _ptr_array([x.K for x in res]), _ptr_array([x.V for x in res]),
         _ptr_array([x.mask for x in res]), _ptr_array([x.score for x in res]),
         _ptr(ws), _ws_bytes(ws), _stream(dev)))
-    if check and n == 1:
-        check_mask(res[0].mask)
     return res
 
 

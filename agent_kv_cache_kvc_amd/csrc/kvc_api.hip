@@ -86,9 +86,6 @@ const char* kvc_version(void) { return "kvc 0.1.0 gfx950"; }
 
 const char* kvc_last_error(void) { return g_err; }
 
-void kvc_test_fused_wait(long long wait_ticks, int withhold_segment) {
-  kvc::set_fused_wait_for_tests(wait_ticks, withhold_segment);
-}
 
 // --------------------------------------------------------------------------- pooling
 size_t kvc_pool_workspace_bytes(int L, int H, int T, int d) {
@@ -157,9 +154,6 @@ static kvc_status validate_correct(const void* K, const void* V, int L, int H, i
   return KVC_OK;
 }
 
-// One correction pass.  Without q_in or earlier chunk sums, pooling, matching and correction
-// run as one fused launch; with them the matching kernel reads q_in (or the chunk sums that
-// the previous pass of a chain left in the workspace) and the correction kernel follows.
 // The general correction (anchor shapes outside the specialised kernel): q from q_in, from the
 // previous pass's output chunk sums, or from a pooling pass; matching of any number of
 // anchors; the correction; then, if asked, the output's chunk sums by a pooling pass.
@@ -215,6 +209,10 @@ static kvc_status enqueue_correct_general(const void* K, const void* V, int L, i
   return KVC_OK;
 }
 
+// One correction pass: the pooled descriptor from q_in, from the chunk sums that the previous
+// pass of a chain left in the workspace, or from a pooling pass over (K, V); then the matching
+// kernel (cosines, softmax, score, flag) and the correction kernel, whose output chunk sums
+// serve the next pass when asked.
 static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, int T, int d,
                                   int dtype, const float* desc, const void* U, const void* W,
                                   int A, int r, float tau, const float* q_in,
@@ -249,21 +247,15 @@ static kvc_status enqueue_correct(const void* K, const void* V, int L, int H, in
   cl.V_out = V_out;
   cl.next_partials = want_next ? reinterpret_cast<float*>(base + c.off_next) : nullptr;
   cl.ctr = reinterpret_cast<int*>(base + c.off_ctr);
-  cl.fused = q_in == nullptr && next_partials_in == nullptr;
-  if (cl.fused) {
-    cl.pool_partials = pool;
-    cl.done = reinterpret_cast<int*>(base + c.off_done);
-    cl.desc = desc;
-    cl.tau = tau;
-    cl.mask_out = mask_out;
-    cl.score_out = score_out;
-    cl.w_out = w_out;
-  } else {
-    KVC_HIP(kvc::launch_score(next_partials_in, nc, T, q_in, desc, c.S, d, A, tau, cl.w_ws,
-                              reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
-                              mask_out, cl.ctr, st),
-            "score");
+  const float* part = next_partials_in;
+  if (q_in == nullptr && part == nullptr) {
+    KVC_HIP(kvc::launch_pool_partials(K, V, c.S, T, d, dtype, pool, nc, st), "pool");
+    part = pool;
   }
+  KVC_HIP(kvc::launch_score(part, nc, T, q_in, desc, c.S, d, A, tau, cl.w_ws,
+                            reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
+                            mask_out, cl.ctr, st),
+          "score");
   KVC_HIP(kvc::launch_correct(cl, st), "correct");
   return KVC_OK;
 }
@@ -394,7 +386,7 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
   }
   if (L * H == 0) return ok();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (n_agents == 1) {  // one agent: the fused single launch
+  if (n_agents == 1) {  // one agent: exactly kvc_correct
     KVC_TRY(enqueue_correct(K, V, L, H, T, d, dtype, desc[0], U[0], W[0], A, r, tau, nullptr,
                             nullptr, K_fb ? K_fb[0] : nullptr, V_fb ? V_fb[0] : nullptr,
                             K_out[0], V_out[0], mask_out[0], score_out ? score_out[0] : nullptr,

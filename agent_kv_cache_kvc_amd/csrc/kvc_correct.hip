@@ -10,9 +10,7 @@
 //   reduce_pool_kernel    chunk sums -> q (the pooling entry point)
 //   score_kernel          chunk sums or q -> cosines, softmax, score, mask  (one wave/segment)
 //   correct_kernel        X' = X + sum_a w_a U_a W_a on MFMA, or copy-through (HBM stream);
-//                         its fused form also pools and matches every segment in the same
-//                         work queue, so a whole correction step is one launch
-//   reset_kernel          zeroes the counters of the fused form
+//                         optionally the chunk sums of its output (the next pooled descriptor)
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -111,9 +109,8 @@ __device__ __forceinline__ void unpack_in(const u32x4& raw, float* v) {
 }
 
 // One wave's 32-token tile starting at token t0 of a [T, D] segment (zeros past T).  LAST: issued
-// as non-temporal loads, so single-use lines leave L2 first.  Every read of K, V and the fallback
-// caches in this file takes it, both reads of the fused pass included (temporal pooling reads,
-// meant to keep a chunk in L2 for the correction's second read, measured slower).
+// as non-temporal loads, so single-use lines leave L2 first (every read of K, V and the fallback
+// caches in this file is a single use).
 template <class Tr, int D, bool LAST = false>
 __device__ __forceinline__ void load_tile(const typename Tr::elem* __restrict__ X, int t0, int T,
                                           int lrow, int lcol, Tile<Tr, D>& tile) {
@@ -155,9 +152,9 @@ __device__ __forceinline__ void add_tile(const Tile<Tr, D>& tile, float (&qs)[D 
 
 // ------------------------------------------------------------------------- chunk sums
 // A lane adds its tokens in (tile, access) order, then the lanes sharing a channel are added
-// by a butterfly and the 4 waves in fixed order.  Every pooled sum in this file (inputs,
-// fused pooling, outputs) takes this order over the same chunks, so the pooled
-// descriptor of a cache does not depend on which pass computed it.
+// by a butterfly and the 4 waves in fixed order.  Every pooled sum in this file (inputs and
+// outputs) takes this order over the same chunks, so the pooled descriptor of a cache does
+// not depend on which pass computed it.
 template <class Tr, int D>
 __device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
                                              int tid) {
@@ -455,12 +452,6 @@ __global__ __launch_bounds__(kBlock) void select_kernel(
   }
 }
 
-__global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
-                                                       int* __restrict__ done, int S) {
-  if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) ctr[threadIdx.x] = 0;
-  for (int i = blockIdx.x * kBlock + threadIdx.x; i < S; i += gridDim.x * kBlock) done[i] = 0;
-}
-
 // ------------------------------------------------------------------------- correction
 // Persistent workgroups (4 waves) take work items from a counter.  A work item is
 // (segment, K|V, chunk of NT x 128 tokens); each wave owns NT tiles of 32 tokens, loads
@@ -474,41 +465,20 @@ __global__ __launch_bounds__(kBlock) void reset_kernel(int* __restrict__ ctr,
 // [g*rp/2, (g+1)*rp/2), MFMA step ks takes SLOT consecutive k from there.  The MFMA result
 // goes through a per-wave LDS tile [32][64 + 4] floats to meet the coalesced layout of X;
 // the next tile's U (double-buffered) is requested before the current tile's MFMAs.
-//
-// FUSED: the queues also hold pooling items (segment, K|V, chunk) that publish chunk sums and
-// count them per segment.  Workgroup b takes items from queue b mod nq, which holds the
-// segments q, q + nq, q + 2 nq, ... (one queue per XCD: a chunk is read twice on one XCD).
-// In each queue, items are grouped in slots of `batch` segments and the pooling slots run
-// `lead` slots ahead of the correction slots:
-//   P0 .. P(lead-1), C0, P(lead), C1, P(lead+1), ..., C(nb-1)
-// so a correction item only waits for pooling items taken from the queue before it; each of
-// those is held by a running workgroup that does not wait, hence every wait ends, with no
-// condition on how many workgroups are resident.  The segment's last pooling item to count
-// computes q, the weights and the fallback flag, publishes them and moves the count past n_ci
-// (by 1, or by 2 for a fallback); correction items issue their loads of X first and then
-// wait for that.  Published values are written with device-coherent stores whose completion
-// is awaited before the count moves, and read with device-coherent loads (device-scope
-// release/acquire fences would write back or invalidate the whole L2 at every item on this
-// target).  K and V are read twice (pooling, then correction): keeping a chunk in registers
-// between the two was measured slower, since every signal is a memory round trip of several
-// microseconds under a saturated memory system and two workgroups per CU cannot hide it.
+
 struct CorrectArgs {
   const void* K;
   const void* V;
   const void* U;
   const void* W;
-  float* w_ws;             // [S][A] weights (from score_kernel, or published when fused)
-  const uint8_t* mask;     // [S] fallback flags from score_kernel (not fused)
+  const float* w_ws;       // [S][A] weights (from the matching kernel)
+  const uint8_t* mask;     // [S] fallback flags (from the matching kernel)
   const void* K_fb;
   const void* V_fb;
   void* K_out;
   void* V_out;
   float* next_partials;    // chunk sums of the output, or null
-  int* ctr;                // work counters, one per queue
-  float* pool_partials;    // fused: [2][S][n_chunks][D] chunk sums of the source
-  int* done;               // fused: [S] items pooled, then n_ci + 1 (matched) or
-                           //        n_ci + 2 (matched, fallback)
-  const float* desc;       // fused: [S][A][2D] anchor descriptors
+  int* ctr;                // work counter (reset by the matching kernel)
   const int* slot_ws;      // SEL: [S][A] pool slot of each selected anchor
   int Vc;                  // SEL: pool slots per segment (U, W hold Vc anchors per segment)
   int n_t;                 // MT: targets corrected from one read of the source
@@ -518,59 +488,20 @@ struct CorrectArgs {
   void* tV[kMaxTargets];
   const void* tKfb[kMaxTargets];
   const void* tVfb[kMaxTargets];
-  uint8_t* mask_out;       // fused outputs
-  float* score_out;
-  float* w_out;
-  long long wait_ticks;    // fused: limit of a correction item's wait (constant-clock ticks)
-  int withhold;            // fused: segment whose matching is not published (tests), or -1
-  float tau;
   int T, S, A, r, rp, n_chunks, n_items;
-  int batch, lead;         // fused: segments per slot, pooling slots ahead of correction
-  int nq;                  // fused: queues (workgroup b serves queue b mod nq)
 };
-
-// Bounded wait of a correction item of the fused form: 0.2 s of the 100 MHz constant clock by
-// default.  A safety net that the queue order above never reaches.  An item that reaches it
-// sets kGaveUp in the segment's counter (only while the segment is still unmatched, by
-// compare-and-swap), writes mask value 2 and copies its tiles through; every later item of the
-// segment sees the flag and copies through too, and the matching item, whose publishing add
-// returns the flag, writes mask value 2 as well.  So a segment is either corrected (or falls
-// back) as a whole, or is copied through as a whole with mask 2.
-constexpr long long kWaitTicks = 20000000ll;
-constexpr int kGaveUp = 1 << 30;  // above any item count: the counters stay below 2^30
-
-// Test hook (kvc_test_fused_wait): the wait limit of later fused launches, and one segment
-// whose matching result is withheld so that its correction items reach that limit.
-static long long g_wait_ticks = kWaitTicks;
-static int g_withhold_segment = -1;
-
-void set_fused_wait_for_tests(long long ticks, int withhold_segment) {
-  g_wait_ticks = ticks > 0 ? ticks : kWaitTicks;
-  g_withhold_segment = withhold_segment;
-}
-
-__device__ __forceinline__ void order_stores_before_signal() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0): stores acknowledged
-}
-
-__device__ __forceinline__ void order_loads_after_signal() {
-  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // NA > 0: compile-time anchor count NA and MFMA steps per anchor KSC (r = 2 KSC SLOT);
 // NA == 0: runtime A and r with up to NFG register-resident fragments.
-// SEL (not fused): anchor a of segment s is pool slot slot_ws[s][a] of Vc slots per segment
+// SEL: anchor a of segment s is pool slot slot_ws[s][a] of Vc slots per segment
 // (the online anchor pool); otherwise anchor a is slot a of A.
-// MT (not fused): each item's tiles of the source are read once and corrected for n_t
+// MT: each item's tiles of the source are read once and corrected for n_t
 // targets in turn (one source, several agents), each with its own factors, weights, flag,
 // output and fallback cache.
-template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool FUSED, bool SEL = false,
+template <class Tr, int D, int NA, int KSC, int NFG, bool POOL_OUT, bool SEL = false,
           bool MT = false>
 __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
-  static_assert(!(SEL && FUSED), "pool slot selection runs in the matching kernel");
-  static_assert(!(MT && (FUSED || SEL || POOL_OUT)), "several targets: plain correction only");
+  static_assert(!(MT && (SEL || POOL_OUT)), "several targets: plain correction only");
   using elem = typename Tr::elem;
   using frag = typename Tr::frag;
   using TL = Tile<Tr, D>;
@@ -607,10 +538,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   __shared__ float wsh[kMaxA];
   __shared__ int ssl[kMaxA];
   __shared__ float red[4][D];
-  __shared__ float qsh[2 * D];
   __shared__ int s_item;
   __shared__ int s_mask;
-  __shared__ int s_last;
 
   elem* wt = reinterpret_cast<elem*>(smem_raw + 4 * 32 * SROW * sizeof(float));
   const int A = FIX ? NA : args.A;
@@ -628,14 +557,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   const bool uvec = FIX || (r % VEC) == 0;
   const int n_ci = 2 * n_chunks;             // items per segment
   const int nslot = SEL ? args.Vc : A;       // anchors stored per segment
-
-  // this workgroup's queue, its segments (q, q + nq, ...) and its item count
-  const int nq = FUSED ? args.nq : 1;
-  const int q = FUSED ? (int)(blockIdx.x % nq) : 0;
-  int* const ctr = args.ctr + q;
-  const int Sq = FUSED ? (S - q + nq - 1) / nq : S;
-  const int nbq = FUSED ? (Sq + args.batch - 1) / args.batch : 0;
-  const int n_items = FUSED ? 2 * nbq * args.batch * n_ci : args.n_items;
+  int* const ctr = args.ctr;
+  const int n_items = args.n_items;
   if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
   __syncthreads();
   int item = __builtin_amdgcn_readfirstlane(s_item);
@@ -656,37 +579,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const int lrow = lane / LPT;               // token within a coalesced access
     const int lcol = VEC * (lane % LPT);       // channel offset within a half row
 
-    bool pool_item = false;
-    int s, ci;
-    if constexpr (FUSED) {
-      const int per_slot = args.batch * n_ci;
-      const int k = item / per_slot, o = item - k * per_slot;
-      const int nb = nbq;
-      const int ld = min(args.lead, nb);
-      int b;
-      if (k < ld) {
-        pool_item = true;
-        b = k;
-      } else {
-        const int kk = k - ld, paired = nb - ld;  // C(j) then P(j + ld) while any P is left
-        if (kk < 2 * paired) {
-          b = kk >> 1;
-          if (kk & 1) {
-            pool_item = true;
-            b += ld;
-          }
-        } else {
-          b = paired + (kk - 2 * paired);
-        }
-      }
-      const int sq = b * args.batch + o / n_ci;  // segment within the queue
-      ci = o - (o / n_ci) * n_ci;
-      if (sq >= Sq) goto next_item;  // padding of the last slot
-      s = q + nq * sq;
-    } else {
-      s = item / n_ci;
-      ci = item - s * n_ci;
-    }
+    const int s = item / n_ci;
+    const int ci = item - s * n_ci;
     const int x = ci / n_chunks, chunk = ci - x * n_chunks;
     const size_t seg = (size_t)s * T * D;
     const elem* X = (x == 0 ? K : V) + seg;
@@ -698,85 +592,12 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 
     // ---- this wave's tiles of X, held in registers for the whole item (a segment already
     //      known to fall back to a fallback cache loads that cache instead)
-    const bool fb_known = !FUSED && !MT && Xfb != nullptr && args.mask[s] != 0;
+    const bool fb_known = !MT && Xfb != nullptr && args.mask[s] != 0;
     const elem* Xsrc = fb_known ? Xfb + seg : X;
     TL xr[NT];
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl)
       load_tile<Tr, D, true>(Xsrc, first + tl * kRowsPerPass, T, lrow, lcol, xr[tl]);
-
-    if (FUSED && pool_item) {
-      // fields used only here are read through an opaque pointer to the kernel arguments,
-      // so they are loaded when needed instead of holding scalar registers for the whole
-      // kernel
-      const __attribute__((address_space(4))) CorrectArgs* pa =
-          (const __attribute__((address_space(4))) CorrectArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-      asm volatile("" : "+s"(pa));
-      {
-        float qs[NH][VEC];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) qs[h][e] = 0.f;
-#pragma unroll
-        for (int tl = 0; tl < NT; ++tl) add_tile<Tr, D>(xr[tl], qs);
-        const float v = finish_sums<Tr, D>(qs, red, tid);
-        if (tid < D)
-          __hip_atomic_store(pa->pool_partials + (((size_t)x * S + s) * n_chunks + chunk) * D + tid,
-                             v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      order_stores_before_signal();
-      __syncthreads();
-      if (tid == 0)
-        s_last = (__hip_atomic_fetch_add(pa->done + s, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) & ~kGaveUp) == n_ci - 1;
-      __syncthreads();
-      if (s_last) {
-        // the segment's last item to count matches it: q (one thread per channel, chunk
-        // sums added in chunk order), then weights and flag
-        order_loads_after_signal();
-        if (tid < 2 * D) {
-          const float* p = pa->pool_partials + ((size_t)(tid / D) * S + s) * n_chunks * D + tid % D;
-          float sum = 0.f;
-          for (int c0 = 0; c0 < n_chunks; c0 += 8) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              v[u] = c0 + u < n_chunks
-                         ? __hip_atomic_load(p + (size_t)(c0 + u) * D, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (c0 + u < n_chunks) sum += v[u];
-          }
-          qsh[tid] = T > 0 ? sum / (float)T : 0.f;
-        }
-        __syncthreads();
-        if (wave == 0) {
-          float q[PER];
-#pragma unroll
-          for (int i = 0; i < PER; ++i) q[i] = qsh[lane + kWave * i];
-          float score;
-          uint8_t fall;
-          const float wv = segment_weights<D>(q, pa->desc, s, A, pa->tau, lane, score, fall);
-          if (lane < A) {
-            __hip_atomic_store(pa->w_ws + (size_t)s * A + lane, wv, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            if (pa->w_out) pa->w_out[(size_t)s * A + lane] = wv;
-          }
-          if (lane == 0 && pa->score_out) pa->score_out[s] = score;
-          order_stores_before_signal();
-          if (lane == 0 && s != pa->withhold) {
-            // publish; a correction item that gave up before this shows in the old value
-            const int old = __hip_atomic_fetch_add(pa->done + s, 1 + (int)fall, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            pa->mask_out[s] = (old & kGaveUp) ? 2 : fall;
-          }
-        }
-      }
-      goto next_item;
-    }
 
     float qs[NH][VEC];
     if constexpr (POOL_OUT) {
@@ -808,11 +629,9 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       __syncthreads();
     }
 
-    // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r);
-    //      in the fused form this overlaps the wait for the segment's weights.  Without the
-    //      fused pass the flag is known before the launch and a falling-back segment stages
-    //      nothing (its factors are not read).
-    const bool pre_masked = !FUSED && m_src[s] != 0;  // same address in every lane
+    // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r); a
+    //      falling-back segment stages nothing (its factors are not read)
+    const bool pre_masked = m_src[s] != 0;  // same address in every lane
     if (!pre_masked) {
       const elem* Wseg = Wt + ((size_t)x * S + s) * nslot * r * D;
       const int n_w = A * r * (D / VEC);
@@ -841,34 +660,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       }
     }
 
-    if constexpr (FUSED) {
-      if (tid == 0) {
-        int* done = args.done + s;
-        int v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v <= n_ci) {
-          const long long t_end = wall_clock64() + args.wait_ticks;
-          do {
-            __builtin_amdgcn_s_sleep(2);
-            v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } while (v <= n_ci && wall_clock64() < t_end);
-          // give up only while the segment is unmatched: each failed swap saw the count move,
-          // so the loop ends (the count is at most n_ci + 2)
-          while (v <= n_ci) {
-            if (__hip_atomic_compare_exchange_strong(done, &v, v | kGaveUp, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-              args.mask_out[s] = 2;
-              v |= kGaveUp;
-            }
-          }
-        }
-        order_loads_after_signal();
-        s_mask = v != n_ci + 1;  // fallback, or given up (flag set)
-        if (v == n_ci + 1)
-          for (int a = 0; a < A; ++a)
-            wsh[a] = __hip_atomic_load(args.w_ws + (size_t)s * A + a, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-      }
-    } else {
+    {
       if (tid == 0) s_mask = m_src[s];
       if (tid < A) wsh[tid] = w_src[(size_t)s * A + tid];
     }
@@ -1109,7 +901,6 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
       if (tid < D) args.next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
     }
     }
-  next_item:
     if (tid == 0) s_item = nxt;
     __syncthreads();  // LDS (W^T, weights, staging, chunk sums, item id) is free for the next item
     item = __builtin_amdgcn_readfirstlane(s_item);
@@ -1232,9 +1023,6 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   a.V_out = L.V_out;
   a.next_partials = L.next_partials;
   a.ctr = L.ctr;
-  a.pool_partials = L.pool_partials;
-  a.done = L.done;
-  a.desc = L.desc;
   a.slot_ws = L.slot_ws;
   a.Vc = L.Vc;
   a.n_t = L.n_t;
@@ -1246,12 +1034,6 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
     a.tKfb[j] = L.tKfb[j];
     a.tVfb[j] = L.tVfb[j];
   }
-  a.mask_out = L.mask_out;
-  a.score_out = L.score_out;
-  a.w_out = L.w_out;
-  a.wait_ticks = g_wait_ticks;
-  a.withhold = g_withhold_segment;
-  a.tau = L.tau;
   a.T = L.T;
   a.S = L.S;
   a.A = L.A;
@@ -1262,30 +1044,17 @@ static hipError_t correct_v(const CorrectLaunch& L, hipStream_t st) {
   const bool pool = L.next_partials != nullptr;
   void (*k)(CorrectArgs);
   if constexpr (SEL) {
-    k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, true>;
+    k = correct_kernel<Tr, D, NA, KSC, NFG, false, true>;
   } else if constexpr (MT) {
-    k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, false, true>;
+    k = correct_kernel<Tr, D, NA, KSC, NFG, false, false, true>;
   } else {
-    k = pool ? (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, true, true>
-                        : correct_kernel<Tr, D, NA, KSC, NFG, true, false>)
-             : (L.fused ? correct_kernel<Tr, D, NA, KSC, NFG, false, true>
-                        : correct_kernel<Tr, D, NA, KSC, NFG, false, false>);
+    k = pool ? correct_kernel<Tr, D, NA, KSC, NFG, true> : correct_kernel<Tr, D, NA, KSC, NFG, false>;
   }
   if (lds > 48 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  const int want = L.fused ? 2 * L.S * 2 * a.n_chunks : a.n_items;
   const int cap = resident_per_cu(reinterpret_cast<const void*>(k), lds) * device_cus();
-  const int grid = want < cap ? want : cap;
-  a.nq = 1;
-  if (L.fused) {
-    a.batch = fused_batch(a.n_chunks);
-    a.lead = fused_lead(a.batch * 2 * a.n_chunks);
-    a.nq = grid < kMaxQueues ? grid : kMaxQueues;  // every queue is served
-    hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(kBlock), 0, st, L.ctr, L.done, L.S);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const int grid = a.n_items < cap ? a.n_items : cap;
   hipLaunchKernelGGL(k, dim3(grid), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }

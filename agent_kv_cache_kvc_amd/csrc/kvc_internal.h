@@ -40,23 +40,6 @@ inline int chunks_of(int T, int d, int dtype) {
 // the most chunks any dtype gives (workspace sizes do not depend on the dtype)
 inline int max_chunks_of(int T) { return T > 0 ? ceil_div(T, kRowsPerPass) : 1; }
 
-// Fused correction: one queue per XCD (workgroup b serves queue b mod nq, the XCD that the
-// round-robin dispatch places it on) holding the segments s with s mod nq equal to it, so a
-// chunk's pooling and correction items run on one XCD and the second read of K and V can
-// hit that XCD's L2.  Each queue has slots of about kFusedSlotItems items (whole segments)
-// and pools about kFusedLeadItems items (at least four slots) ahead of its correction items.
-constexpr int kMaxQueues = 8;
-constexpr int kFusedSlotItems = 16;
-constexpr int kFusedLeadItems = 96;  // pooling items a queue runs ahead of its corrections
-inline int fused_lead(int slot_items) {
-  const int l = (kFusedLeadItems + slot_items - 1) / slot_items;
-  return l < 4 ? 4 : l;
-}
-inline int fused_batch(int n_chunks) {
-  const int n_ci = 2 * n_chunks;
-  return n_ci >= kFusedSlotItems ? 1 : kFusedSlotItems / n_ci;
-}
-
 // ---------------------------------------------------------------- correction workspace
 struct CorrectLayout {
   int S, T, d, A;
@@ -65,8 +48,7 @@ struct CorrectLayout {
   size_t off_next;    // float [2][S][n_chunks][d]   chunk sums of the output (pooled next)
   size_t off_w;       // float [S][A]
   size_t off_mask;    // uint8 [S]
-  size_t off_done;    // int [S]: per-segment counters of the fused pass
-  size_t off_ctr;     // int [kMaxQueues]: work counters of the correction pass
+  size_t off_ctr;     // int: work counter of the correction pass
   size_t off_slot;    // int [S][A]: pool slots of the selected anchors (pooled correction)
   size_t off_wmt;     // float [kMaxTargets][S][A]: weights of a multi-target launch
   size_t off_mmt;     // uint8 [kMaxTargets][S]: flags of a multi-target launch
@@ -87,8 +69,7 @@ inline CorrectLayout correct_layout(int L, int H, int T, int d, int A) {
   c.off_next = o;  o = align_up(o + sums, 256);
   c.off_w = o;     o = align_up(o + sizeof(float) * (size_t)c.S * A, 256);
   c.off_mask = o;  o = align_up(o + (size_t)c.S, 256);
-  c.off_done = o;  o = align_up(o + sizeof(int) * (size_t)c.S, 256);
-  c.off_ctr = o;   o = align_up(o + sizeof(int) * kMaxQueues, 256);
+  c.off_ctr = o;   o = align_up(o + sizeof(int), 256);
   c.off_slot = o;  o = align_up(o + sizeof(int) * (size_t)c.S * A, 256);
   c.off_wmt = o;   o = align_up(o + sizeof(float) * (size_t)kMaxTargets * c.S * A, 256);
   c.off_mmt = o;   o = align_up(o + (size_t)kMaxTargets * c.S, 256);
@@ -105,18 +86,14 @@ struct CorrectLaunch {
   const void* U;
   const void* W;
   int A, r, rp;
-  float* w_ws;              // weights (from launch_score, or published by the fused pass)
-  const uint8_t* mask_ws;   // fallback flags from launch_score (not fused)
+  float* w_ws;              // weights (from launch_score / launch_select)
+  const uint8_t* mask_ws;   // fallback flags (from launch_score / launch_select)
   const void* K_fb;
   const void* V_fb;
   void* K_out;
   void* V_out;
   float* next_partials;     // chunk sums of the output, or null
-  int* ctr;
-  bool fused;               // pooling + matching + correction in one launch
-  float* pool_partials;     // fused: chunk sums of the source
-  int* done;                // fused: per-segment counters
-  const float* desc;        // fused: anchor descriptors
+  int* ctr;                 // work counter, reset by launch_score / launch_select
   const int* slot_ws;       // pooled correction: [S][A] slots of Vc per segment, or null
   int Vc;
   int n_t;                  // multi-target correction: 0 (off) or the targets below (w_ws and
@@ -126,10 +103,6 @@ struct CorrectLaunch {
   void* tV[kMaxTargets];
   const void* tKfb[kMaxTargets];
   const void* tVfb[kMaxTargets];
-  float tau;
-  uint8_t* mask_out;        // fused: matching outputs
-  float* score_out;
-  float* w_out;
 };
 
 // ---------------------------------------------------------------- fit workspace
@@ -192,9 +165,7 @@ hipError_t launch_pool_insert(const uint8_t* mask, const float* U_new, const flo
                               const float* q, int S, int T, int d, int dtype, int Vc, int r,
                               void* U_pool, void* W_pool, float* desc_pool, int* count,
                               int* head, hipStream_t st);
-// Test hook of the fused pass's bounded wait (see kvc_test_fused_wait).
-void set_fused_wait_for_tests(long long ticks, int withhold_segment);
-// Correction (after launch_score), or the fused pass (resets its own counters).
+// Correction, after launch_score / launch_select (which reset its work counter).
 hipError_t launch_correct(const CorrectLaunch& L, hipStream_t st);
 // Anchor shapes the specialised correction kernel holds in registers and LDS.
 inline bool correct_specialised(int A, int r, int dtype) {

@@ -258,7 +258,7 @@ def headline_leg(dev, stream, steps: int, warmup: int):
 
     def chain():
         state["res"] = kvc.correct_chain(case.K0, case.V0, edges, cfg.tau, outputs=outs,
-                                         workspace=ws, check=False)
+                                         workspace=ws)
 
     def fit():
         state["fit"] = kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
@@ -266,7 +266,6 @@ def headline_leg(dev, stream, steps: int, warmup: int):
     chain()
     fit()
     torch.cuda.synchronize()
-    kvc.check_mask(state["res"][0].mask)
     masks = [x.mask.cpu().numpy() for x in state["res"]]
     errs, layer_errs = study_errors(state["res"], [(ed.exact_K, ed.exact_V) for ed in case.edges])
     k_eff = state["fit"].k_eff.cpu().numpy()
@@ -284,7 +283,6 @@ def headline_leg(dev, stream, steps: int, warmup: int):
         e2.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
-    kvc.check_mask(state["res"][0].mask)
     t_chain = np.array([a.elapsed_time(b) for a, b, _ in evs])
     t_fit = np.array([b.elapsed_time(c) for _, b, c in evs])
     t_step = np.array([a.elapsed_time(c) for a, _, c in evs])
@@ -366,7 +364,7 @@ def cpu_baseline_headline(case, edges, delta, n_seg: int = 6, n_mat: int = 12,
 
 def tiny_leg(dev, n: int = 200):
     """Latency of the tiny configuration (1 x 1 x 256 x 64 fp32, A = 2, r = 8): one kvc_correct
-    (single-launch pass) and one kvc_fit_anchor, each a median over n calls of per-call events."""
+    and one kvc_fit_anchor, each a median over n calls of per-call events."""
     cfg = synth.CONFIGS["tiny"]
     case = synth.generate(cfg, dev)
     desc = descriptors_on_device(case)
@@ -381,7 +379,7 @@ def tiny_leg(dev, n: int = 200):
 
     def corr():
         kvc.correct(case.K0, case.V0, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo,
-                    want_w=False, want_score=False, workspace=ws, check=False)
+                    want_w=False, want_score=False, workspace=ws)
 
     def fit():
         kvc.fit_anchor(delta, r=cfg.r, want_eig=False, workspace=fws)
@@ -413,8 +411,7 @@ def fanout_leg(dev, stream, n):
                                                           cfg.r), dtype=torch.uint8, device=dev)
 
     def run():
-        return kvc.correct_fanout(case.K0, case.V0, agents, cfg.tau, outputs=outs, workspace=ws,
-                                  check=False)
+        return kvc.correct_fanout(case.K0, case.V0, agents, cfg.tau, outputs=outs, workspace=ws)
 
     res = run()
     torch.cuda.synchronize()
@@ -490,7 +487,7 @@ def pool_leg(dev, stream, n, cfg, case):
 
 def vl_leg(dev, stream, n):
     """The vision-language-shaped cache (28 layers x 4 kv-heads x 9216 tokens x 128, 7000
-    high-variance visual tokens, A = 6, r = 32, tau = 0.6): kvc_correct (fused) and the fit."""
+    high-variance visual tokens, A = 6, r = 32, tau = 0.6): kvc_correct and the fit."""
     cfg = synth.CONFIGS["vl_t9216"]
     log(f"[bench] vl leg: generating {cfg.name}")
     case = synth.generate(cfg, dev)
@@ -502,16 +499,15 @@ def vl_leg(dev, stream, n):
 
     def step():
         return kvc.correct(case.K0, case.V0, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo,
-                           want_w=False, want_score=False, workspace=ws, check=False)
+                           want_w=False, want_score=False, workspace=ws)
 
     res = step()
     torch.cuda.synchronize()
-    mask = kvc.check_mask(res.mask).cpu().numpy()
+    mask = res.mask.cpu().numpy()
     nbytes = correct_bytes(cfg, mask)
     for _ in range(5):
         step()
     ms, _ = per_call_ms(step, n, stream)
-    kvc.check_mask(res.mask)
     delta = synth.fit_input(case)
     del case, Ko, Vo, res
     M, T = delta.shape[0], delta.shape[1]
@@ -572,7 +568,7 @@ def cpu_baseline_fit(delta, r, n_mat: int = 16, budget_s: float = 8.0):
 
 
 def llama8b_leg(dev, stream, steps: int, warmup: int):
-    """kvc_correct over the 8B shape at T = 2048 (single-launch pass), its base-cache rank,
+    """kvc_correct over the 8B shape at T = 2048, its base-cache rank,
     the anchor pool and the q-given form."""
     cfg = synth.CONFIGS["llama8b_t2048"]
     log(f"[bench] generating {cfg.name} on {dev}")
@@ -586,29 +582,28 @@ def llama8b_leg(dev, stream, steps: int, warmup: int):
 
     def step():
         return kvc.correct(K, V, desc, ed.U, ed.W, cfg.tau, K_out=Ko, V_out=Vo, want_w=False,
-                           want_score=False, workspace=ws, check=False)
+                           want_score=False, workspace=ws)
 
     res = step()
     torch.cuda.synchronize()
-    mask = kvc.check_mask(res.mask).cpu().numpy()
+    mask = res.mask.cpu().numpy()
     nbytes = correct_bytes(cfg, mask)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ms, ms_mean = per_call_ms(step, steps, stream)
-    kvc.check_mask(res.mask)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] llama8b_t2048 step {ms:.4f} ms, {gbs:.1f} GB/s, reuse {1 - mask.mean():.3f}")
     traffic = traffic_record(nbytes)
     out = {"workload": f"{cfg.name}: {cfg.L}x{cfg.H}x{cfg.T}x{cfg.d} bf16, A={cfg.A}, r={cfg.r}, "
-                       f"tau={cfg.tau}, one kvc_correct (single-launch pass)",
+                       f"tau={cfg.tau}, one kvc_correct (pooling, matching, correction)",
            "ms": round(ms, 5), "ms_mean": round(ms_mean, 5), "gbs": round(gbs, 2),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
            "tokens_layers_per_s": round(cfg.T * cfg.L / (ms * 1e-3), 1),
            "reuse_ratio": round(float(1 - mask.mean()), 4),
            "roofline": {"bound": "hbm",
-                        "kernel": "correct_kernel, fused form (pooling, matching and correction "
-                                  "in one launch; a one-workgroup counter reset precedes it)",
+                        "kernel": "correct_kernel (after the pooling and matching kernels); "
+                                  "achieved = the call's algorithmic bytes / its median time",
                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "traffic": traffic["bytes"] if traffic else None,
@@ -634,7 +629,7 @@ def llama8b_leg(dev, stream, steps: int, warmup: int):
 
     out["anchor_pool"] = pool_leg(dev, stream, max(10, steps // 2), cfg, case)
 
-    # the unfused form, for reference: matching kernel from a precomputed q, then correction
+    # with a precomputed q: matching kernel, then correction (no pooling pass)
     q = kvc.pool_descriptor(K, V)
     torch.cuda.synchronize()
 
@@ -647,7 +642,7 @@ def llama8b_leg(dev, stream, steps: int, warmup: int):
     ms_k, _ = per_call_ms(corr_q_in, steps, stream)
     log(f"[bench] with q_in (score + correct kernels) {ms_k:.4f} ms")
     out["with_q_in"] = {"ms": round(ms_k, 5), "gbs": round(nbytes / (ms_k * 1e-3) / 1e9, 2),
-                        "note": "q precomputed: matching kernel + unfused correction kernel"}
+                        "note": "q precomputed: matching kernel + correction kernel"}
     return out
 
 
@@ -768,8 +763,8 @@ def main():
         "algorithmic_bytes_per_step": head["bytes"],
         "roofline": {"bound": "hbm",
                      "kernel": "correct_kernel, the chain's correction passes (one launch per "
-                               "edge, 3 per step: single-launch pass with output pooling on edge "
-                               "0, matched from the previous output's chunk sums on edges 1-2); "
+                               "edge, 3 per step; edge 0 after a pooling pass over A0's cache, "
+                               "edges 1-2 matched from the previous pass's output chunk sums); "
                                "achieved = the chain's algorithmic bytes / its median time",
                      "achieved": cgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(cgbs / HBM_PEAK_GBS, 4),

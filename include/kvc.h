@@ -53,14 +53,6 @@ const char* kvc_version(void);
  * valid until that thread's next call); "" if none. */
 const char* kvc_last_error(void);
 
-/* Test hook of the single-launch correction pass's bounded wait (see mask_out of
- * kvc_correct).  For every later single-launch pass in this process: wait_ticks is the
- * wait limit in ticks of the 100 MHz constant clock (<= 0 restores the default of
- * 20,000,000 = 0.2 s), and the matching result of segment withhold_segment (l * H + h) is
- * never published (-1, the default: none), so that its correction items reach the limit,
- * give up and copy the segment through with mask 2.  Every kernel still runs to its end.
- * Process-wide, not thread-safe; meant for tests of the give-up path only. */
-void kvc_test_fused_wait(long long wait_ticks, int withhold_segment);
 
 /* ---------------------------------------------------------------------------------------
  * Pooled descriptor (Fig. 1(b): the current cache representation that is matched
@@ -91,20 +83,18 @@ kvc_status kvc_pool_descriptor(const void* K, const void* V, int L, int H, int T
  *   desc        : [L,H,A,2d] float32                   (anchor descriptors)
  *   U           : [2,L,H,A,T,r] dtype                  (left factors, index 0 = K)
  *   W           : [2,L,H,A,r,d] dtype                  (right factors)
- *   A, r        : 1 <= A, 1 <= r <= 64, A * ceil(r/16)*16 <= 256
+ *   A, r        : 1 <= A, 1 <= r <= d, A * r <= 256 (shapes outside the specialised
+ *                 kernel's budget -- bf16: A <= 16, r <= 64, A * ceil(r/16)*16 <= 256; fp32:
+ *                 A * ceil(r/8)*8 <= 64 -- run as a separate pooling, matching and general
+ *                 correction pass; results meet the same bars)
  *   tau         : reliability threshold (+inf: every segment falls back; -inf: none)
  *   q_in        : [L,H,2d] float32 or NULL: a precomputed pooled descriptor of (K, V);
- *                 when NULL it is computed in the same pass (pooling, matching and
- *                 correction run as one launch; q is bit-identical to the one
- *                 kvc_pool_descriptor returns)
+ *                 when NULL a pooling pass computes it first (bit-identical to the q that
+ *                 kvc_pool_descriptor returns); then one matching and one correction launch
  *   K_fb, V_fb  : [L,H,T,d] dtype or NULL (both or neither)
  *   K_out, V_out: [L,H,T,d] dtype, written; may equal K / V (in place); must not
  *                 otherwise overlap any input
- *   mask_out    : [L,H] uint8, 1 = fall back, written.  2 flags a segment whose
- *                 correction gave up waiting for its matching result in the single-launch
- *                 pass (a 0.2 s safety net that the pass's work order never reaches); the
- *                 whole segment is then written as for a fallback (X_fb if given, else X),
- *                 and its score and weights are undefined.  The Python binding raises on it.
+ *   mask_out    : [L,H] uint8, 1 = fall back, 0 = corrected, written
  *   score_out   : [L,H] float32 or NULL;  w_out: [L,H,A] float32 or NULL
  *   q_next_out  : [L,H,2d] float32 or NULL: pooled descriptor of (K_out, V_out)
  *   ws          : at least kvc_correct_workspace_bytes(L,H,T,d,A,r) bytes
@@ -146,8 +136,9 @@ kvc_status kvc_correct_chain(const void* K0, const void* V0, int L, int H, int T
  * the same.  The reference is pooled once (every agent is matched against the same pooled
  * descriptor, bit for bit); then one correction launch per group of up to 8 agents reads
  * each tile of the reference once and corrects it for every agent of the group (a single
- * agent takes kvc_correct's fused launch).  The same call serves one agent whose cache feeds
- * several successors on a workflow graph.
+ * agent is exactly kvc_correct; anchor shapes outside the specialised kernel are corrected
+ * agent by agent).  The same call serves one agent whose cache feeds several successors on a
+ * workflow graph.
  *   n_agents >= 1.  desc, U, W, K_out, V_out, mask_out: HOST arrays of n_agents DEVICE
  *   pointers laid out as for kvc_correct; K_fb / V_fb (the array or an entry, both or
  *   neither per agent) and score_out may be NULL.  No output may overlap the reference or

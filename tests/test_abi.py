@@ -234,3 +234,4 @@ def test_anchor_pool_rejects_bad_arguments():
         a.update(kw)
         assert lib.kvc_anchor_pool_insert(*a.values()) == status, (kw, lib.kvc_last_error())
     assert lib.kvc_anchor_pool_insert(*dict(base, L=0).values()) == 0  # no segment: no-op
+

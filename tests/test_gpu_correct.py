@@ -93,9 +93,9 @@ def test_small_shapes(dtype, d, T, A, r):
 
 
 @pytest.mark.parametrize("L,H,T", [(1, 13, 2048), (3, 3, 1500), (5, 7, 300)])
-def test_segment_counts_not_a_multiple_of_the_queues(L, H, T):
-    """The fused form spreads segments over up to eight queues (segment s to queue s mod 8);
-    segment counts that leave queues uneven or empty must not change any result."""
+def test_segment_counts_not_a_multiple_of_the_grid(L, H, T):
+    """Segment counts that leave the persistent grid's work uneven (prime segment counts,
+    fewer items than workgroups) must not change any result."""
     base = synth.CONFIGS["llama8b_t2048"]
     cfg = base.replace(name=f"queues_{L}x{H}_{T}", L=L, H=H, T=T, seed=2000 + L * H + T,
                        fallback_prob=0.3)
