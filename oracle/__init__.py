@@ -7,6 +7,7 @@ from .kvc_oracle import (  # noqa: F401
     chain,
     correct,
     correct_pooled,
+    correct_rank,
     cosine_scores,
     effective_rank,
     fanout,
@@ -17,7 +18,9 @@ from .kvc_oracle import (  # noqa: F401
     pool,
     pool_insert,
     project,
+    rank_descriptor,
     rank_error_curve,
+    rank_scores,
     reliability,
     rel_frobenius,
     round_to_bf16,

@@ -135,6 +135,31 @@ def reliability(s, tau):
 # --------------------------------------------------------------------------------------
 
 
+def _apply(K, V, s, U, W, tau, dtype, K_fb, V_fb) -> dict:
+    """Weights, decision and correction from given anchor scores s [L, H, A] (see ``correct``)."""
+    w = softmax_weights(s)
+    score, mask = reliability(s, tau)
+    outs = []
+    for x, (X, X_fb) in enumerate(((K, K_fb), (V, V_fb))):
+        delta = np.zeros_like(X)
+        for a in range(U.shape[3]):
+            delta += w[..., a, None, None] * np.matmul(U[x, :, :, a], W[x, :, :, a])
+        corrected = X + delta
+        keep = X if X_fb is None else np.asarray(X_fb, dtype=np.float64)
+        exact = np.where(mask[..., None, None].astype(bool), keep, corrected)
+        outs.append(exact)
+    return {
+        "K_exact": outs[0],
+        "V_exact": outs[1],
+        "K_out": round_to_dtype(outs[0], dtype),
+        "V_out": round_to_dtype(outs[1], dtype),
+        "s": s,
+        "w": w,
+        "score": score,
+        "mask": mask,
+    }
+
+
 def correct(K, V, desc, U, W, tau, dtype, K_fb=None, V_fb=None, q=None) -> dict:
     """Correct a reused cache with the similarity-weighted sum of the anchors' low-rank deltas.
 
@@ -156,29 +181,76 @@ def correct(K, V, desc, U, W, tau, dtype, K_fb=None, V_fb=None, q=None) -> dict:
     if q is None:
         q = pool(K, V)
     q = np.asarray(q, dtype=np.float64)
-    s = cosine_scores(q, desc)
-    w = softmax_weights(s)
-    score, mask = reliability(s, tau)
-    outs = []
-    for x, (X, X_fb) in enumerate(((K, K_fb), (V, V_fb))):
-        delta = np.zeros_like(X)
-        for a in range(U.shape[3]):
-            delta += w[..., a, None, None] * np.matmul(U[x, :, :, a], W[x, :, :, a])
-        corrected = X + delta
-        keep = X if X_fb is None else np.asarray(X_fb, dtype=np.float64)
-        exact = np.where(mask[..., None, None].astype(bool), keep, corrected)
-        outs.append(exact)
-    return {
-        "K_exact": outs[0],
-        "V_exact": outs[1],
-        "K_out": round_to_dtype(outs[0], dtype),
-        "V_out": round_to_dtype(outs[1], dtype),
-        "q": q,
-        "s": s,
-        "w": w,
-        "score": score,
-        "mask": mask,
-    }
+    out = _apply(K, V, cosine_scores(q, desc), U, W, tau, dtype, K_fb, V_fb)
+    out["q"] = q
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# matching on the rank-r_C representation of the cache
+# --------------------------------------------------------------------------------------
+
+
+def rank_descriptor(K, V, rC: int) -> dict:
+    """Rank-r_C representation of every cache segment (Fig. 13: base-cache rank r_C, 32 by
+    default; Fig. 2: effective rank of the base cache).  Reading: for X in {K, V} the segment
+    is represented by its rank-r_C truncated second-moment matrix G_r = sum_{i <= r_C}
+    sigma_i^2 v_i v_i^T (sigma_i, v_i: singular values and right singular vectors of the
+    T x d matrix X), stored as the factor F = diag(sigma_1..r_C) V_r^T (r_C x d), so that
+    G_r = F^T F; each row's largest-magnitude entry is positive (the sign does not enter
+    any similarity).  Returns F [2, L, H, rC, d] (index 0 = K) and the cache's effective rank
+    k_eff [2, L, H] at 90% energy (``effective_rank``)."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, H, T, d = K.shape
+    F = np.zeros((2, L, H, rC, d))
+    lam = np.zeros((2, L, H, d))
+    for x, X in enumerate((K, V)):
+        for l in range(L):
+            for h in range(H):
+                if T == 0:
+                    continue
+                _, sv, vt = np.linalg.svd(X[l, h], full_matrices=False)
+                k = sv.shape[0]
+                lam[x, l, h, :k] = sv * sv
+                rr = min(rC, k)
+                F[x, l, h, :rr] = sv[:rr, None] * _canonical_rows(vt[:rr])
+    return {"F": F, "k_eff": effective_rank(lam), "eig": lam}
+
+
+def rank_scores(Fq, Fa) -> np.ndarray:
+    """Similarity of rank-r_C representations: the cosine of the truncated second-moment
+    matrices of K and V taken together as one vector,
+        s_a = (<Gq_K, Ga_K> + <Gq_V, Ga_V>) / (||(Gq_K, Gq_V)|| ||(Ga_K, Ga_V)||),
+    with Frobenius inner products <G, G'> = ||F F'^T||_F^2 (G = F^T F) and 0 when either norm
+    is 0.  Sign flips and rotations of the factor rows leave it unchanged.  Reading of the
+    listing's Fig. 1(b) matching on the cache representation of Fig. 13 (r_C).
+    Fq: [2, L, H, rC, d]; Fa: [2, L, H, A, rC, d] -> s [L, H, A]."""
+    Fq = np.asarray(Fq, dtype=np.float64)
+    Fa = np.asarray(Fa, dtype=np.float64)
+    A = Fa.shape[3]
+    L, H = Fq.shape[1], Fq.shape[2]
+    s = np.zeros((L, H, A))
+    for l in range(L):
+        for h in range(H):
+            nq = sum(np.sum((Fq[x, l, h] @ Fq[x, l, h].T) ** 2) for x in range(2))
+            for a in range(A):
+                na = sum(np.sum((Fa[x, l, h, a] @ Fa[x, l, h, a].T) ** 2) for x in range(2))
+                dot = sum(np.sum((Fq[x, l, h] @ Fa[x, l, h, a].T) ** 2) for x in range(2))
+                den = np.sqrt(nq * na)
+                s[l, h, a] = 0.0 if den == 0 else dot / den
+    return s
+
+
+def correct_rank(K, V, Fq, Fa, U, W, tau, dtype, K_fb=None, V_fb=None) -> dict:
+    """``correct`` with the anchors matched on rank-r_C representations (``rank_scores``)
+    instead of the mean-pooled descriptor: softmax weights, reliability and correction as
+    in ``correct``."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return _apply(K, V, rank_scores(Fq, Fa), U, W, tau, dtype, K_fb, V_fb)
 
 
 def chain(K0, V0, edges, tau, dtype) -> list:
