@@ -10,6 +10,7 @@ Entry points (same names as the C ABI in include/kvc.h):
     correct(K, V, desc, U, W, tau, ...)                 -> CorrectResult
     correct_chain(K0, V0, edges, tau)                   -> list[CorrectResult]
     correct_fanout(K, V, agents, tau)                   -> list[CorrectResult]
+    rank_descriptor(K, V, rC) / correct_rank(...)       (matching on rank-rC representations)
     AnchorPool.empty(...) / correct_pooled / anchor_pool_insert   (online anchor pool)
     fit_anchor(delta, r=32, energy=0.9)                 -> FitResult
     gram_accumulate / fit_from_gram / project           (streaming fit)
@@ -35,6 +36,8 @@ __all__ = [
     "correct",
     "correct_chain",
     "correct_fanout",
+    "rank_descriptor",
+    "correct_rank",
     "AnchorPool",
     "correct_pooled",
     "anchor_pool_insert",
@@ -78,6 +81,10 @@ _SIGS = {
     "kvc_correct_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kvc_correct": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, ctypes.c_float,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_rank_descriptor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "kvc_rank_descriptor": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_correct_rank": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i, _i,
+                              ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kvc_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kvc_correct_chain": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -253,6 +260,59 @@ def correct(K: torch.Tensor, V: torch.Tensor, desc: torch.Tensor, U: torch.Tenso
                              _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(qn), _ptr(ws),
                              _ws_bytes(ws), _stream(dev)))
     return CorrectResult(Ko, Vo, mask, score, w, qn)
+
+
+def rank_descriptor(K: torch.Tensor, V: torch.Tensor, rC: int = 32, *,
+                    workspace: Optional[torch.Tensor] = None):
+    """Rank-rC representation of every segment of a cache [L, H, T, d]: (F float32
+    [2, L, H, rC, d], k_eff int32 [2, L, H]) -- see kvc_rank_descriptor in include/kvc.h."""
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    _need(K, "K", (L, H, T, d), K.dtype, dev)
+    _need(V, "V", (L, H, T, d), K.dtype, dev)
+    F = torch.empty(2, L, H, rC, d, dtype=torch.float32, device=dev)
+    k = torch.empty(2, L, H, dtype=torch.int32, device=dev)
+    ws = _ws(workspace, lib().kvc_rank_descriptor_workspace_bytes(L, H, T, d, rC), dev)
+    _check(lib().kvc_rank_descriptor(_ptr(K), _ptr(V), L, H, T, d, dt, int(rC), _ptr(F), _ptr(k),
+                                     _ptr(ws), _ws_bytes(ws), _stream(dev)))
+    return F, k
+
+
+def correct_rank(K: torch.Tensor, V: torch.Tensor, Fq: torch.Tensor, Fa: torch.Tensor,
+                 U: torch.Tensor, W: torch.Tensor, tau: float, *,
+                 K_fb: Optional[torch.Tensor] = None, V_fb: Optional[torch.Tensor] = None,
+                 K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> CorrectResult:
+    """kvc_correct with the anchors matched on rank-rC representations (see kvc_correct_rank in
+    include/kvc.h).  Fq: [2, L, H, rC, d]; Fa: [2, L, H, A, rC, d] float32."""
+    L, H, T, d = K.shape
+    dev = K.device
+    dt = _dtype_code(K)
+    A, rC = Fa.shape[3], Fa.shape[4]
+    r = U.shape[-1]
+    _need(K, "K", (L, H, T, d), K.dtype, dev)
+    _need(V, "V", (L, H, T, d), K.dtype, dev)
+    _need(Fq, "Fq", (2, L, H, rC, d), torch.float32, dev)
+    _need(Fa, "Fa", (2, L, H, A, rC, d), torch.float32, dev)
+    _need(U, "U", (2, L, H, A, T, r), K.dtype, dev)
+    _need(W, "W", (2, L, H, A, r, d), K.dtype, dev)
+    for name, t in (("K_fb", K_fb), ("V_fb", V_fb)):
+        if t is not None:
+            _need(t, name, (L, H, T, d), K.dtype, dev)
+    Ko = K_out if K_out is not None else torch.empty_like(K)
+    Vo = V_out if V_out is not None else torch.empty_like(V)
+    _need(Ko, "K_out", (L, H, T, d), K.dtype, dev)
+    _need(Vo, "V_out", (L, H, T, d), K.dtype, dev)
+    mask = torch.empty(L, H, dtype=torch.uint8, device=dev)
+    score = torch.empty(L, H, dtype=torch.float32, device=dev)
+    w = torch.empty(L, H, A, dtype=torch.float32, device=dev)
+    ws = _ws(workspace, correct_workspace_bytes(L, H, T, d, A, r), dev)
+    _check(lib().kvc_correct_rank(_ptr(K), _ptr(V), L, H, T, d, dt, _ptr(Fq), _ptr(Fa), int(rC),
+                                  _ptr(U), _ptr(W), A, r, float(tau), _ptr(K_fb), _ptr(V_fb),
+                                  _ptr(Ko), _ptr(Vo), _ptr(mask), _ptr(score), _ptr(w), _ptr(ws),
+                                  _ws_bytes(ws), _stream(dev)))
+    return CorrectResult(Ko, Vo, mask, score, w)
 
 
 def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):

@@ -456,6 +456,92 @@ kvc_status kvc_correct_fanout(const void* K, const void* V, int L, int H, int T,
   return ok();
 }
 
+// --------------------------------------------------------------------------- rank matching
+size_t kvc_rank_descriptor_workspace_bytes(int L, int H, int T, int d, int rC) {
+  if (L < 0 || H < 0 || T < 0 || d <= 0 || rC < 1) return 0;
+  const int S = L * H;
+  const size_t fit = kvc::fit_layout(2 * S, T, d, rC).bytes;
+  const size_t eig = kvc::align_up(sizeof(float) * 2ull * S * d, 256);
+  const size_t ke = kvc::align_up(sizeof(int32_t) * 2ull * S, 256);
+  return fit + eig + ke;
+}
+
+kvc_status kvc_rank_descriptor(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, int rC, float* F_out, int32_t* k_eff_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  if (rC < 1 || rC > d || rC > kvc::kMaxRankC)
+    return fail(KVC_ERR_ARG, "rC=%d (need 1 <= rC <= d)", rC);
+  const int S = L * H;
+  if (S == 0) return ok();
+  if (T > 0) {
+    KVC_TRY(check_tensor(K, "K"));
+    KVC_TRY(check_tensor(V, "V"));
+  }
+  KVC_TRY(check_tensor(F_out, "F_out"));
+  if (k_eff_out) KVC_TRY(check_tensor(k_eff_out, "k_eff_out", 4));
+  const size_t need = kvc_rank_descriptor_workspace_bytes(L, H, T, d, rC);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(KVC_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  char* base = static_cast<char*>(ws);
+  const size_t fit = kvc::fit_layout(2 * S, T, d, rC).bytes;
+  float* eig = reinterpret_cast<float*>(base + fit);
+  int32_t* ke = k_eff_out ? k_eff_out
+                          : reinterpret_cast<int32_t*>(
+                                base + fit + kvc::align_up(sizeof(float) * 2ull * S * d, 256));
+  KVC_HIP(kvc::launch_rank_descriptor(K, V, S, T, d, dtype, rC, F_out, ke, eig, base,
+                                      reinterpret_cast<hipStream_t>(stream)),
+          "rank descriptor");
+  return ok();
+}
+
+kvc_status kvc_correct_rank(const void* K, const void* V, int L, int H, int T, int d, int dtype,
+                            const float* Fq, const float* Fa, int rC, const void* U,
+                            const void* W, int A, int r, float tau, const void* K_fb,
+                            const void* V_fb, void* K_out, void* V_out, uint8_t* mask_out,
+                            float* score_out, float* w_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (L > 0 && H > 0) KVC_TRY(check_tensor(Fq, "Fq", 4));
+  KVC_TRY(validate_correct(K, V, L, H, T, d, dtype, Fq, U, W, A, r, nullptr, K_fb, V_fb, K_out,
+                           V_out, mask_out, ws, ws_bytes));
+  if (rC < 1 || rC > d || rC > kvc::kMaxRankC)
+    return fail(KVC_ERR_ARG, "rC=%d (need 1 <= rC <= d)", rC);
+  if (score_out) KVC_TRY(check_tensor(score_out, "score_out", 4));
+  if (w_out) KVC_TRY(check_tensor(w_out, "w_out", 4));
+  if (L * H == 0) return ok();
+  KVC_TRY(check_tensor(Fa, "Fa", 4));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const kvc::CorrectLayout c = kvc::correct_layout(L, H, T, d, A);
+  char* base = static_cast<char*>(ws);
+  kvc::CorrectLaunch cl{};
+  cl.K = K;
+  cl.V = V;
+  cl.S = c.S;
+  cl.T = T;
+  cl.d = d;
+  cl.dtype = dtype;
+  cl.U = U;
+  cl.W = W;
+  cl.A = A;
+  cl.r = r;
+  cl.w_ws = reinterpret_cast<float*>(base + c.off_w);
+  cl.mask_ws = reinterpret_cast<uint8_t*>(base + c.off_mask);
+  cl.K_fb = K_fb;
+  cl.V_fb = V_fb;
+  cl.K_out = K_out;
+  cl.V_out = V_out;
+  cl.ctr = reinterpret_cast<int*>(base + c.off_ctr);
+  KVC_HIP(kvc::launch_score_rank(Fq, Fa, c.S, d, A, rC, tau, cl.w_ws,
+                                 reinterpret_cast<uint8_t*>(base + c.off_mask), score_out, w_out,
+                                 mask_out, cl.ctr, st),
+          "rank matching");
+  if (kvc::correct_specialised(A, r, dtype))
+    KVC_HIP(kvc::launch_correct(cl, st), "correct");
+  else
+    KVC_HIP(kvc::launch_correct_general(cl, st), "correct");
+  return ok();
+}
+
 // --------------------------------------------------------------------------- anchor pool
 size_t kvc_correct_pooled_workspace_bytes(int L, int H, int T, int d, int A, int r) {
   return kvc_correct_workspace_bytes(L, H, T, d, A, r);

@@ -37,9 +37,9 @@ __constant__ int c_blk64[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
 // grid (nsplit, M).  Each slab of SLAB = 16384/D tokens is loaded as 8x8 bf16 blocks
 // (one per thread, 8 rows x 16 bytes, coalesced), transposed in registers and stored
 // channel-major in LDS, so an MFMA fragment (8 consecutive tokens of one channel) is a
-// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator;
-// the accumulator holds one slab (SLAB / 16 MFMA steps) and is then added to a float64 sum,
-// so rounding only ever affects the sum of one slab's products.  The partials are float64.
+// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator,
+// which holds the split's whole sum (chunk / 16 MFMA steps; the error bound of the effective
+// rank's certificate counts them); the partials are written as float64.
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __restrict__ delta,
                                                               int T, int chunk,
@@ -65,14 +65,10 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
     J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
   }
   floatx16 acc[3];
-  double sum[3][16];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc[b][i] = 0.f;
-      sum[b][i] = 0.0;
-    }
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 
   // ---- 8x8 block of this thread: rows ts + 8 rg + i, channels 8 cg .. 8 cg + 7; the next
   //      slab's block is requested before the current slab's MFMAs
@@ -116,14 +112,6 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
         }
       }
     }
-    // ---- the slab's float32 sums into the float64 sums
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sum[b][i] += (double)acc[b][i];
-        acc[b][i] = 0.f;
-      }
   }
   // ---- write this workgroup's blocks: [m][split][blk][reg][lane]
 #pragma unroll
@@ -131,14 +119,14 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
     if (I[b] >= 0) {
       double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = sum[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (double)acc[b][i];
     }
   }
 }
 
 // ------------------------------------------------------------------------- Gram, fp32
-// Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2; each
-// slab's float32 sums are added to float64 sums as in the bf16 kernel.
+// Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2; one float32
+// accumulator per element over the split, written as a float64 partial.
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __restrict__ delta,
                                                              int T, int chunk,
@@ -162,14 +150,10 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
     J[b] = D == 128 ? c_blk128[wave][b][1] : c_blk64[wave][b][1];
   }
   floatx16 acc[3];
-  double sum[3][16];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc[b][i] = 0.f;
-      sum[b][i] = 0.0;
-    }
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
   for (int ts = t_begin; ts < t_end; ts += SLAB) {
     __syncthreads();
     for (int q = tid; q < SLAB * C4; q += kBlock) {
@@ -190,20 +174,13 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
         }
       }
     }
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sum[b][i] += (double)acc[b][i];
-        acc[b][i] = 0.f;
-      }
   }
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (I[b] >= 0) {
       double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = sum[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (double)acc[b][i];
     }
   }
 }
@@ -1268,7 +1245,8 @@ constexpr int kExactSlab = 64;  // rows of delta staged per step of the Gram
 
 template <int D, int SRC>
 __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __restrict__ src,
-                                                                int T, double energy,
+                                                                const void* __restrict__ src2,
+                                                                int m_split, int T, double energy,
                                                                 int32_t* __restrict__ k_eff,
                                                                 float* __restrict__ eig_out) {
   constexpr int GS = D + 1;            // row stride of G in LDS (doubles)
@@ -1289,6 +1267,9 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
       Gs[i * GS + j] = 0.5 * (Gm[(size_t)i * D + j] + Gm[(size_t)j * D + i]);
     }
   } else {
+    // matrices m >= m_split are read from src2 (two buffers of matrices, e.g. K then V)
+    const void* sp = m < m_split ? src : src2;
+    const int mm = m < m_split ? m : m - m_split;
     float* stage = reinterpret_cast<float*>(Gs);  // [kExactSlab][D], exact copies of delta
     const int i0 = TR * (tid / 16), j0 = TC * (tid % 16);
     double acc[TR][TC];
@@ -1299,11 +1280,11 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
     for (int t0 = 0; t0 < T; t0 += kExactSlab) {
       const int n = min(kExactSlab, T - t0);
       for (int e = tid; e < n * D; e += kExactBlock) {
-        const size_t g = ((size_t)m * T + t0) * D + e;
+        const size_t g = ((size_t)mm * T + t0) * D + e;
         if constexpr (SRC == 0)
-          stage[e] = bf16_to_f32(static_cast<const uint16_t*>(src)[g]);
+          stage[e] = bf16_to_f32(static_cast<const uint16_t*>(sp)[g]);
         else
-          stage[e] = static_cast<const float*>(src)[g];
+          stage[e] = static_cast<const float*>(sp)[g];
       }
       __syncthreads();
       for (int t = 0; t < n; ++t) {
@@ -1386,12 +1367,16 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
     double lo = lo0 - pad, hi = hi0 + pad;
     for (int it = 0; it < 24; ++it) {
       const double x = lo + (double)(q + 1) * ((hi - lo) / 5.0);
-      // Sturm count: negative pivots of T - x I
+      // Sturm count: negative pivots of T - x I.  1 / pivot from the hardware reciprocal and
+      // two Newton steps (a relative error far below the ulps a Sturm count tolerates)
       double pv = dd[0] - x;
       if (fabs(pv) < pivmin) pv = -pivmin;
       int cnt = pv < 0.0;
       for (int j = 1; j < D; ++j) {
-        pv = (dd[j] - x) - (ee[j - 1] * ee[j - 1]) / pv;
+        double rp = __builtin_amdgcn_rcp(pv);
+        rp = rp * fma(-pv, rp, 2.0);
+        rp = rp * fma(-pv, rp, 2.0);
+        pv = (dd[j] - x) - (ee[j - 1] * ee[j - 1]) * rp;
         if (fabs(pv) < pivmin) pv = -pivmin;
         cnt += pv < 0.0;
       }
@@ -1580,26 +1565,28 @@ static void allow_dynamic_lds(K kernel, size_t bytes) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// Bound on the Gram error of the fast path per unit of trace (see keff_certain): each float32
-// accumulator holds one slab of products before it joins the float64 sum, so an element's
-// error is at most (steps + 2) roundings of the sum of the slab's |products| (steps = MFMA
-// steps per slab: SLAB / 16 for bf16, 2 products per step for fp32), doubled for safety.
-template <int D>
-static double gram_gamma(int dtype) {
-  const double steps = dtype == KVC_BF16 ? (16384.0 / D) / 16.0 : 2.0 * (8192.0 / D) / 2.0;
+// Bound on the Gram error of the fast path per unit of trace (see keff_certain): a split's
+// float32 accumulator takes `chunk` rows, so an element's error is at most (steps + 2)
+// float32 roundings of the sum of its |products| (steps = accumulations into it: chunk / 16
+// MFMA steps for bf16, chunk rounded products for fp32), doubled for safety; the float64 sum
+// of the splits adds nothing measurable.
+static double gram_gamma(int dtype, int chunk) {
+  const double steps = dtype == KVC_BF16 ? chunk / 16.0 : (double)chunk;
   return 2.0 * (steps + 2.0) * 0x1p-24;
 }
 
 // Flagged effective ranks (k_eff_out < 0) decided again in float64 (keff_exact_kernel).
 template <int D>
 static hipError_t launch_keff_exact(const void* src, int src_kind, int M, int T, double energy,
-                                    int32_t* k_eff, float* eig, hipStream_t st) {
+                                    int32_t* k_eff, float* eig, hipStream_t st,
+                                    const void* src2 = nullptr, int m_split = 1 << 30) {
   const size_t lds = (size_t)D * (D + 1) * sizeof(double);
-  void (*k)(const void*, int, double, int32_t*, float*) =
+  void (*k)(const void*, const void*, int, int, double, int32_t*, float*) =
       src_kind == 0 ? keff_exact_kernel<D, 0>
                     : (src_kind == 1 ? keff_exact_kernel<D, 1> : keff_exact_kernel<D, 2>);
   allow_dynamic_lds(k, lds);
-  hipLaunchKernelGGL(k, dim3(M), dim3(kExactBlock), lds, st, src, T, energy, k_eff, eig);
+  hipLaunchKernelGGL(k, dim3(M), dim3(kExactBlock), lds, st, src, src2, m_split, T, energy,
+                     k_eff, eig);
   return hipGetLastError();
 }
 
@@ -1608,7 +1595,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
                         float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                         hipStream_t st) {
   double* partials = reinterpret_cast<double*>(ws + f.off_gram);
-  const double gamma = gram_gamma<D>(dtype);
+  const double gamma = gram_gamma(dtype, f.chunk);
   uint16_t* whi = reinterpret_cast<uint16_t*>(ws + f.off_whi);
   uint16_t* wlo = reinterpret_cast<uint16_t*>(ws + f.off_wlo);
   int* sweeps = reinterpret_cast<int*>(ws + f.off_sweeps);
@@ -1777,6 +1764,72 @@ hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, con
   if (M == 0 || T == 0) return hipSuccess;
   return d == 128 ? project_t<128>(delta, M, T, dtype, W, r, U_out, ws, st)
                   : project_t<64>(delta, M, T, dtype, W, r, U_out, ws, st);
+}
+
+// ------------------------------------------------------------------------- rank descriptor
+// F[m][i][:] = sqrt(max(lambda_i, 0)) W[m][i][:]: the sigma-scaled rows of a fit's W.
+__global__ __launch_bounds__(kBlock) void scale_rows_kernel(float* __restrict__ F,
+                                                          const float* __restrict__ eig, int r,
+                                                          int D) {
+  const int m = blockIdx.y;
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= r * D) return;
+  const float lam = eig[(size_t)m * D + e / D];
+  F[(size_t)m * r * D + e] *= sqrtf(fmaxf(lam, 0.f));
+}
+
+// Rank-rC representation of every segment of a cache: the Gram matrices of the S segments of
+// K (matrices 0..S-1) and of V (S..2S-1), their eigen-decomposition (the fit's kernels), the
+// effective rank, and the top rC eigenvectors scaled by sqrt(lambda) into F [2][S][rC][D].
+template <int D>
+static hipError_t rank_descriptor_t(const void* K, const void* V, const FitLayout& f, int S,
+                                    int dtype, float* F, int32_t* k_eff, float* eig, char* ws,
+                                    hipStream_t st) {
+  constexpr int NBLK = (D / 32) * (D / 32 + 1) / 2;
+  double* partials = reinterpret_cast<double*>(ws + f.off_gram);
+  const double gamma = gram_gamma(dtype, f.chunk);
+  const dim3 g1(f.nsplit, S);
+  for (int x = 0; x < 2; ++x) {
+    double* px = partials + (size_t)x * S * f.nsplit * NBLK * 1024;
+    if (dtype == KVC_BF16)
+      hipLaunchKernelGGL((gram_bf16_kernel<D>), g1, dim3(kBlock), 0, st,
+                         (const uint16_t*)(x == 0 ? K : V), f.T, f.chunk, px);
+    else
+      hipLaunchKernelGGL((gram_f32_kernel<D>), g1, dim3(kBlock), 0, st,
+                         (const float*)(x == 0 ? K : V), f.T, f.chunk, px);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (f.r <= kEigMaxR) {
+    const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
+    allow_dynamic_lds(eig_kernel<D>, lds);
+    hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
+                       f.nsplit, (const double*)nullptr, f.r, 0.9, gamma, F, eig, k_eff,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, f.rpad);
+  } else {
+    const size_t lds = (size_t)D * (D + 4) * sizeof(float);
+    allow_dynamic_lds(jacobi_kernel<D>, lds);
+    const float tol = 2e-6f, eta = 1e-12f;
+    hipLaunchKernelGGL((jacobi_kernel<D>), dim3(f.M), dim3(kJacobiBlock), lds, st, partials,
+                       f.nsplit, (const double*)nullptr, f.r, 0.9, gamma, tol, eta, F, eig, k_eff,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, f.rpad, (int*)nullptr);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_keff_exact<D>(K, dtype == KVC_BF16 ? 0 : 1, f.M, f.T, 0.9, k_eff, eig, st, V, S);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scale_rows_kernel, dim3(ceil_div(f.r * D, kBlock), f.M), dim3(kBlock), 0, st,
+                     F, eig, f.r, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_descriptor(const void* K, const void* V, int S, int T, int d, int dtype,
+                                  int rC, float* F, int32_t* k_eff, float* eig, char* ws,
+                                  hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  const FitLayout f = fit_layout(2 * S, T, d, rC);
+  return d == 128 ? rank_descriptor_t<128>(K, V, f, S, dtype, F, k_eff, eig, ws, st)
+                  : rank_descriptor_t<64>(K, V, f, S, dtype, F, k_eff, eig, ws, st);
 }
 
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,

@@ -15,6 +15,7 @@ constexpr int kBlock = 256;           // 4 waves per workgroup everywhere
 constexpr int kRowsPerPass = 128;     // tokens of one 32-token tile per wave, 4 waves
 constexpr int kMaxA = 16;             // anchors per segment held in registers
 constexpr int kMaxAnchorsGeneral = 256;  // A * r <= 256: the general correction's bound
+constexpr int kMaxRankC = 128;        // rank of the cache representation (rank matching)
 constexpr int kMaxKSlots = 256;       // A * ceil16(r) bound of the LDS-staged factors
 constexpr int kMaxR = 64;             // rank bound of the correction kernel
 constexpr int kMaxPool = 32;          // slots of an online anchor pool per segment
@@ -179,6 +180,17 @@ hipError_t launch_score_general(const float* q, const float* desc, int S, int d,
                                 float tau, float* w_ws, uint8_t* mask_ws, float* score_out,
                                 float* w_out, uint8_t* mask_out, hipStream_t st);
 hipError_t launch_correct_general(const CorrectLaunch& L, hipStream_t st);
+// Rank-rC representation of a cache (kvc_fit.hip): F [2][S][rC][d] float32 (K then V),
+// effective rank k_eff [2][S] and eigenvalues eig [2][S][d] (descending) through the fit's
+// Gram and eigensolver kernels; ws holds fit_layout(2S, T, d, rC).
+hipError_t launch_rank_descriptor(const void* K, const void* V, int S, int T, int d, int dtype,
+                                  int rC, float* F, int32_t* k_eff, float* eig, char* ws,
+                                  hipStream_t st);
+// Matching on rank-rC representations (kvc_rank.hip): Fq [2][S][rC][d], Fa [2][S][A][rC][d]
+// -> weights, flags and outputs as launch_score; resets *ctr.
+hipError_t launch_score_rank(const float* Fq, const float* Fa, int S, int d, int A, int rC,
+                             float tau, float* w_ws, uint8_t* mask_ws, float* score_out,
+                             float* w_out, uint8_t* mask_out, int* ctr, hipStream_t st);
 hipError_t launch_fit(const void* delta, const FitLayout& f, int dtype, double energy,
                       float* U_out, float* W_out, int32_t* k_eff, float* eig, char* ws,
                       hipStream_t st);

@@ -627,6 +627,35 @@ def llama8b_leg(dev, stream, steps: int, warmup: int):
     log(f"[bench] base-cache fit {ms_b:.3f} ms, effective rank median {int(np.median(ke))}")
     del base, bf, eigs
 
+    # matching on the rank-32 representation of the cache (listing Fig. 13's r_C) instead of
+    # the mean-pooled descriptor: kvc_rank_descriptor, then kvc_correct_rank with anchor
+    # representations near the query's (the query's factors plus a Gaussian of relative size
+    # 0.15 .. 2.5 per anchor)
+    rC = 32
+    rws = torch.empty(kvc.lib().kvc_rank_descriptor_workspace_bytes(cfg.L, cfg.H, cfg.T, cfg.d, rC),
+                      dtype=torch.uint8, device=dev)
+    F, _ = kvc.rank_descriptor(K, V, rC, workspace=rws)
+    g = torch.Generator(device=dev).manual_seed(5)
+    scale = F.pow(2).mean(dim=(-1, -2), keepdim=True).sqrt()
+    Fa = torch.stack([F + e * scale * torch.randn(F.shape, generator=g, device=dev)
+                      for e in (0.15, 0.6, 1.2, 2.5)], dim=3).contiguous()
+    rres = kvc.correct_rank(K, V, F, Fa, ed.U, ed.W, 0.5, K_out=Ko, V_out=Vo, workspace=ws)
+    torch.cuda.synchronize()
+    rmask = rres.mask.cpu().numpy()
+    ms_rd, _ = per_call_ms(lambda: kvc.rank_descriptor(K, V, rC, workspace=rws), 5, stream)
+    ms_rc, _ = per_call_ms(lambda: kvc.correct_rank(K, V, F, Fa, ed.U, ed.W, 0.5, K_out=Ko,
+                                                    V_out=Vo, workspace=ws), steps, stream)
+    rbytes = correct_bytes(cfg, rmask) - cfg.L * cfg.H * cfg.A * 2 * cfg.d * 4 + \
+        (1 + cfg.A) * 2 * cfg.L * cfg.H * rC * cfg.d * 4
+    out["rank_matching"] = {
+        "workload": f"{cfg.name}: rank-{rC} representation of K and V per segment, anchors' "
+                    f"representations [2,L,H,{cfg.A},{rC},{cfg.d}], tau=0.5",
+        "descriptor_ms": round(ms_rd, 4), "correct_ms": round(ms_rc, 4),
+        "correct_gbs": round(rbytes / (ms_rc * 1e-3) / 1e9, 2),
+        "reuse_ratio": round(float(1 - rmask.mean()), 4)}
+    log(f"[bench] rank matching: descriptor {ms_rd:.3f} ms, correction {ms_rc:.4f} ms")
+    del F, Fa, rws, rres
+
     out["anchor_pool"] = pool_leg(dev, stream, max(10, steps // 2), cfg, case)
 
     # with a precomputed q: matching kernel, then correction (no pooling pass)

@@ -108,6 +108,42 @@ kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d,
                        void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Rank-rC representation of a cache (Fig. 13: the base cache is kept at rank r_C, 32 by
+ * default; Fig. 2: the effective rank of the base cache).  Per segment and for X in {K, V}:
+ * the rank-rC truncation of X^T X, stored as F = diag(sigma_1..rC) V_rC^T (the top rC right
+ * singular vectors of X scaled by the singular values; each row's largest-magnitude entry
+ * positive), computed with kvc_fit_anchor's Gram and eigensolver kernels.
+ *   K, V      : [L,H,T,d] dtype
+ *   rC        : 1 <= rC <= d
+ *   F_out     : [2,L,H,rC,d] float32 (index 0 = K), written
+ *   k_eff_out : [2,L,H] int32 or NULL: the effective rank at 90% energy (exact, as for
+ *               kvc_fit_anchor)
+ *   ws        : at least kvc_rank_descriptor_workspace_bytes(L,H,T,d,rC) bytes
+ * ------------------------------------------------------------------------------------- */
+size_t kvc_rank_descriptor_workspace_bytes(int L, int H, int T, int d, int rC);
+kvc_status kvc_rank_descriptor(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, int rC, float* F_out, int32_t* k_eff_out, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * kvc_correct with the anchors matched on rank-rC representations instead of the mean-pooled
+ * descriptor (Fig. 1(b) matching of the cache representation; Fig. 13 rank r_C):
+ *   s_a = (<Gq_K, Ga_K> + <Gq_V, Ga_V>) / (||(Gq_K, Gq_V)|| ||(Ga_K, Ga_V)||)
+ * with G = F^T F and <G, G'> = ||F F'^T||_F^2 (0 when either norm is 0): the cosine of the
+ * truncated second-moment matrices, independent of the signs and rotations of the factor
+ * rows.  Softmax weights, score, fallback and correction as in kvc_correct.
+ *   Fq : [2,L,H,rC,d] float32, the source cache's representation (kvc_rank_descriptor)
+ *   Fa : [2,L,H,A,rC,d] float32, the anchors' representations
+ *   other arguments and the workspace (kvc_correct_workspace_bytes) as for kvc_correct
+ * ------------------------------------------------------------------------------------- */
+kvc_status kvc_correct_rank(const void* K, const void* V, int L, int H, int T, int d, int dtype,
+                            const float* Fq, const float* Fa, int rC, const void* U,
+                            const void* W, int A, int r, float tau, const void* K_fb,
+                            const void* V_fb, void* K_out, void* V_out, uint8_t* mask_out,
+                            float* score_out, float* w_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Chained correction along a workflow A0 -> A1 -> ... (Fig. 1(c); Fig. 3(b): A0's cache
  * is exact).  Edge e corrects its source with its own anchors; the stored result is the
  * source of edge e+1; edge 0's source is (K0, V0), which is not modified.  The pooled

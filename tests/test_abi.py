@@ -235,3 +235,18 @@ def test_anchor_pool_rejects_bad_arguments():
         assert lib.kvc_anchor_pool_insert(*a.values()) == status, (kw, lib.kvc_last_error())
     assert lib.kvc_anchor_pool_insert(*dict(base, L=0).values()) == 0  # no segment: no-op
 
+
+def test_validation_paths_under_address_and_undefined_behaviour_sanitizers():
+    """kvc_api.hip's host code built with ASan and UBSan, driven through every entry point's
+    rejection paths (tests/abi_sanitize_main.cpp): no sanitizer report, every status right."""
+    import shutil
+
+    sanitize_abi = pytest.importorskip("sanitize_abi")
+
+    if shutil.which(sanitize_abi.HIPCC) is None and not os.path.exists(sanitize_abi.HIPCC):
+        pytest.skip("hipcc not available")
+    if not all(os.path.exists(os.path.join(sanitize_abi.OBJ, o)) for o in sanitize_abi.OTHER):
+        pytest.skip("library objects not built")
+    out = sanitize_abi.build_and_run()
+    assert "abi-sanitize ok" in out and "exit 0" in out, out
+    assert "ERROR: AddressSanitizer" not in out and "runtime error" not in out, out

@@ -226,3 +226,40 @@ def test_llama8b_t8192_full_size():
 
 def test_vl_t9216_full_size():
     _run_sampled(synth.CONFIGS["vl_t9216"], n_samples=12)
+
+
+def test_three_tilings_of_one_correction_agree():
+    """The same correction through three kernels: A = 2 anchors of rank 32 (the compile-time
+    variant), the same factors zero-padded to rank 40 (the runtime-shaped specialised kernel:
+    other k-steps, other accumulation groups) and to rank 80 (the general kernel: one
+    contraction over the concatenated rank index).  Zero factor columns add exact zeros, so the
+    three results differ only by float32 accumulation order (and the general kernel's hi + lo
+    split of the weighted factor), which flips a last bf16 place now and then: every pair
+    within 2e-4 relative Frobenius (each within the bars of the oracle); masks and weights
+    identical."""
+    base = synth.CONFIGS["llama8b_t2048"]
+    cfg = base.replace(name="tilings", L=3, H=2, T=777, A=2, r=32, seed=313, fallback_prob=0.3)
+    say(f"[tilings] {cfg.L}x{cfg.H}x{cfg.T} A=2, r = 32 / 40 / 80")
+    case = synth.generate(cfg, "cpu")
+    d = dev()
+    desc, _ = correct_inputs(case, d)
+    ed = case.edges[0]
+    K, V = case.K0.to(d), case.V0.to(d)
+    outs = []
+    for rr in (32, 40, 80):
+        U = torch.zeros(2, cfg.L, cfg.H, 2, cfg.T, rr, dtype=torch.bfloat16)
+        W = torch.zeros(2, cfg.L, cfg.H, 2, rr, cfg.d, dtype=torch.bfloat16)
+        U[..., :32] = ed.U
+        W[..., :32, :] = ed.W
+        outs.append(kvc.correct(K, V, desc, U.to(d), W.to(d), cfg.tau))
+    torch.cuda.synchronize()
+    ref = oracle.correct(synth.to_f64(case.K0), synth.to_f64(case.V0), synth.to_f64(desc),
+                         synth.to_f64(ed.U), synth.to_f64(ed.W), cfg.tau, cfg.dtype)
+    for i, o in enumerate(outs):
+        assert torch.equal(o.mask, outs[0].mask) and torch.equal(o.w, outs[0].w)
+        np.testing.assert_array_equal(o.mask.cpu().numpy(), ref["mask"])
+        check_close(f"K' tiling {i}", synth.to_f64(o.K), ref["K_out"])
+        for j in range(i):
+            e = oracle.rel_frobenius(synth.to_f64(o.K), synth.to_f64(outs[j].K))
+            say(f"  tilings {j} vs {i}: K' relative difference {e:.2e}")
+            assert e <= 2e-4
