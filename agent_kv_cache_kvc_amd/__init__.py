@@ -81,6 +81,9 @@ _SIGS = {
     "kvc_correct_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kvc_correct": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, ctypes.c_float,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kvc_correct_noalloc": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i,
+                                 ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp]),
     "kvc_rank_descriptor_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "kvc_rank_descriptor": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "kvc_correct_rank": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i, _i,

@@ -5,9 +5,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kvc.h"
 #include "kvc_internal.h"
+
+// Device workspace of kvc_correct_noalloc (see scratch_address below).
+static __device__ __align__(256) unsigned char scratch[KVC_SCRATCH_BYTES];
 
 namespace {
 
@@ -77,6 +81,29 @@ kvc_status check_anchors(int A, int r, int d) {
     hipError_t _e = (call);                          \
     if (_e != hipSuccess) return hip_fail(_e, what); \
   } while (0)
+
+// ---- workspace of kvc_correct_noalloc: one array per device, held until the process ends.
+// In host code `scratch` names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever handed to kernels.
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices] = {};
+std::mutex g_scratch_mu;
+
+kvc_status scratch_address(void** out) {
+  int dev = -1;
+  KVC_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(KVC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    KVC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(KVC_ERR_HIP, "scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
 
 }  // namespace
 
@@ -283,6 +310,26 @@ kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d,
             "q_next");
   }
   return ok();
+}
+
+kvc_status kvc_correct_noalloc(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, const float* desc, const void* U, const void* W, int A,
+                               int r, float tau, const float* q_in, const void* K_fb,
+                               const void* V_fb, void* K_out, void* V_out, uint8_t* mask_out,
+                               float* score_out, float* w_out, float* q_next_out,
+                               void* stream) {
+  KVC_TRY(check_cache_shape(L, H, T, d, dtype));
+  KVC_TRY(check_anchors(A, r, d));
+  const size_t need = kvc_correct_workspace_bytes(L, H, T, d, A, r);
+  if (need > (size_t)KVC_SCRATCH_BYTES)
+    return fail(KVC_ERR_UNSUPPORTED,
+                "needs %zu bytes of workspace, more than the %u-byte scratch array", need,
+                (unsigned)KVC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  KVC_TRY(scratch_address(&ws));
+  return kvc_correct(K, V, L, H, T, d, dtype, desc, U, W, A, r, tau, q_in, K_fb, V_fb, K_out,
+                     V_out, mask_out, score_out, w_out, q_next_out, ws, KVC_SCRATCH_BYTES,
+                     stream);
 }
 
 // --------------------------------------------------------------------------- chain

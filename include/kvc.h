@@ -108,6 +108,29 @@ kvc_status kvc_correct(const void* K, const void* V, int L, int H, int T, int d,
                        void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * kvc_correct for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments, computation and
+ * outputs as kvc_correct, except that the workspace is a library-owned device array of
+ * KVC_SCRATCH_BYTES (16 MiB) instead of a caller-provided one.  The call allocates nothing.
+ *   - Limit: shapes whose kvc_correct_workspace_bytes(L,H,T,d,A,r) exceeds KVC_SCRATCH_BYTES
+ *     return KVC_ERR_UNSUPPORTED before any HIP call (e.g. 32 x 8 x 2048 x 128 with A = 4
+ *     needs about 8.7 MiB and fits; the same cache at T = 8192 does not).
+ *   - Each device has its own array, kept until the process ends; its address is looked up
+ *     on the first call made with that device current.
+ *   - Every call on a device shares that device's array and its contents from the last
+ *     call (the kernels re-initialise everything they read).  Calls that overlap on one
+ *     device (two streams, or two host threads, without ordering between them) race on it:
+ *     the caller must order them.
+ * ------------------------------------------------------------------------------------- */
+#define KVC_SCRATCH_BYTES (16u << 20)
+kvc_status kvc_correct_noalloc(const void* K, const void* V, int L, int H, int T, int d,
+                               int dtype, const float* desc, const void* U, const void* W, int A,
+                               int r, float tau, const float* q_in, const void* K_fb,
+                               const void* V_fb, void* K_out, void* V_out, uint8_t* mask_out,
+                               float* score_out, float* w_out, float* q_next_out,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Rank-rC representation of a cache (Fig. 13: the base cache is kept at rank r_C, 32 by
  * default; Fig. 2: the effective rank of the base cache).  Per segment and for X in {K, V}:
  * the rank-rC truncation of X^T X, stored as F = diag(sigma_1..rC) V_rC^T (the top rC right

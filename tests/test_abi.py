@@ -236,6 +236,19 @@ def test_anchor_pool_rejects_bad_arguments():
     assert lib.kvc_anchor_pool_insert(*dict(base, L=0).values()) == 0  # no segment: no-op
 
 
+def test_noalloc_refuses_oversize_shapes_before_any_hip_call():
+    lib = kvc.lib()
+    # 32 x 8 x 8192 x 128, A = 4: about 33 MiB of workspace, more than the 16 MiB array
+    st = lib.kvc_correct_noalloc(FAKE, FAKE, 32, 8, 8192, 128, 0, FAKE, FAKE, FAKE, 4, 32,
+                                 ctypes.c_float(0.3), None, None, None, FAKE, FAKE, FAKE, None,
+                                 None, None, None)
+    assert st == 2 and "scratch" in lib.kvc_last_error().decode()
+    st = lib.kvc_correct_noalloc(FAKE, FAKE, 2, 2, 64, 96, 0, FAKE, FAKE, FAKE, 4, 32,
+                                 ctypes.c_float(0.3), None, None, None, FAKE, FAKE, FAKE, None,
+                                 None, None, None)
+    assert st == 2 and "d=96" in lib.kvc_last_error().decode()
+
+
 def test_validation_paths_under_address_and_undefined_behaviour_sanitizers():
     """kvc_api.hip's host code built with ASan and UBSan, driven through every entry point's
     rejection paths (tests/abi_sanitize_main.cpp): no sanitizer report, every status right."""
