@@ -155,9 +155,10 @@ __device__ __forceinline__ void add_tile(const Tile<Tr, D>& tile, float (&qs)[D 
 // by a butterfly and the 4 waves in fixed order.  Every pooled sum in this file (inputs and
 // outputs) takes this order over the same chunks, so the pooled descriptor of a cache does
 // not depend on which pass computed it.
+// The wave's sums of every channel into red[wave] (no barrier).
 template <class Tr, int D>
-__device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
-                                             int tid) {
+__device__ __forceinline__ void wave_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
+                                          int tid) {
   constexpr int NH = D / 64, VEC = Tr::VEC, LPT = Tr::LPT;
   const int lane = tid % kWave, wave = tid / kWave;
   const int lcol = VEC * (lane % LPT);
@@ -170,9 +171,21 @@ __device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float
       for (int off = LPT; off < kWave; off <<= 1) v += __shfl_xor(v, off, 64);
       if (lane < LPT) red[wave][64 * h + lcol + e] = v;
     }
+}
+
+// The four waves' sums of channel tid (after a barrier that follows wave_sums).
+template <int D>
+__device__ __forceinline__ float join_sums(const float (*red)[D], int tid) {
+  return ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+template <class Tr, int D>
+__device__ __forceinline__ float finish_sums(float (&qs)[D / 64][Tr::VEC], float (*red)[D],
+                                             int tid) {
+  wave_sums<Tr, D>(qs, red, tid);
   __syncthreads();
   float out = 0.f;
-  if (tid < D) out = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (tid < D) out = join_sums<D>(red, tid);
   return out;  // valid for tid < D; the caller synchronises before `red` is written again
 }
 
@@ -205,19 +218,20 @@ __global__ __launch_bounds__(kBlock) void pool_partials_kernel(
 
 // ------------------------------------------------------------------------- matching
 // Chunk sums -> pooled descriptor [mean K ; mean V]; one wave, lane holds channels
-// lane + 64 i.  The sums are added in chunk order; loads go out 8 chunks at a time.
+// lane + 64 i.  The sums are added in chunk order; loads go out 16 chunks at a time.
 template <int D>
 __device__ __forceinline__ void pooled_query(const float* __restrict__ partials, int n_chunks,
                                              int T, int s, int S, int lane,
                                              float (&q)[2 * D / kWave]) {
   constexpr int PER = 2 * D / kWave;
+  constexpr int kJoin = 16;  // chunk sums loaded per round trip
   float sum[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) sum[i] = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
-    float v[8][PER];
+  for (int c0 = 0; c0 < n_chunks; c0 += kJoin) {
+    float v[kJoin][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kJoin; ++u)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int c = lane + kWave * i;
@@ -227,7 +241,7 @@ __device__ __forceinline__ void pooled_query(const float* __restrict__ partials,
                       : 0.f;
       }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kJoin; ++u)
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         if (c0 + u < n_chunks) sum[i] += v[u][i];
@@ -562,10 +576,17 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
   __syncthreads();
   int item = __builtin_amdgcn_readfirstlane(s_item);
+  // POOL_OUT: an item leaves its waves' chunk sums in `red`; they are joined and stored after
+  // the item's closing barrier, at the top of the loop (before the next item's first barrier,
+  // after which `red` may be written again)
+  [[maybe_unused]] long long pend = -1;  // (x S + s) n_chunks + chunk of the item whose sums wait
   for (;;) {
     // lane-derived values are recomputed per item (kept out of the loop-carried registers)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
+    if constexpr (POOL_OUT) {
+      if (pend >= 0 && tid < D) args.next_partials[pend * D + tid] = join_sums<D>(red, tid);
+    }
     if (item >= n_items) break;
     // the next item is requested now and read at the end of this one (the counter's round
     // trip overlaps the item)
@@ -579,8 +600,11 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     const int lrow = lane / LPT;               // token within a coalesced access
     const int lcol = VEC * (lane % LPT);       // channel offset within a half row
 
-    const int s = item / n_ci;
-    const int ci = item - s * n_ci;
+    // items run through the segments (and each segment's chunks) in the reverse of the
+    // pooling kernel's order, so the first ones read what that kernel read last
+    const int rs = item / n_ci;
+    const int s = S - 1 - rs;
+    const int ci = n_ci - 1 - (item - rs * n_ci);
     const int x = ci / n_chunks, chunk = ci - x * n_chunks;
     const size_t seg = (size_t)s * T * D;
     const elem* X = (x == 0 ? K : V) + seg;
@@ -897,8 +921,8 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
 
     if constexpr (POOL_OUT) {
       // token sums of the stored output, in the order of the input chunk sums
-      const float v = finish_sums<Tr, D>(qs, red, tid);
-      if (tid < D) args.next_partials[(((size_t)x * S + s) * n_chunks + chunk) * D + tid] = v;
+      wave_sums<Tr, D>(qs, red, tid);
+      pend = ((long long)x * S + s) * n_chunks + chunk;
     }
     }
     if (tid == 0) s_item = nxt;

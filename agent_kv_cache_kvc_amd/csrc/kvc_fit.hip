@@ -646,24 +646,40 @@ __device__ __forceinline__ float dpp_fl(float x) {
 }
 
 // The ev-th smallest eigenvalue of the symmetric tridiagonal matrix (diagonal df, squared
-// off-diagonals e2f > 0) by P-point multisection on Sturm counts, P aligned lanes per
-// eigenvalue (q = lane within the group).  Each step splits [lo, hi] into P + 1 parts; the
-// new interval ends at the lowest point with more than ev eigenvalues below it and starts
-// at the highest point under that one, so it always brackets the eigenvalue even where
-// rounding makes the counts non-monotone.  4 points x 13 steps or 8 points x 10 steps
-// shrink the start interval more than 2^30 times.
+// off-diagonals shifted by one: e2s[j] = e_{j-1}^2 > 0, e2s[0] = 0) by P-point multisection on
+// Sturm counts, P aligned lanes per eigenvalue (q = lane within the group).  Each step splits
+// [lo, hi] into P + 1 parts; the new interval ends at the lowest point with more than ev
+// eigenvalues below it and starts at the highest point under that one, so it always brackets
+// the eigenvalue even where rounding makes the counts non-monotone.  4 points x 13 steps or
+// 8 points x 10 steps shrink the start interval more than 2^30 times.  The Sturm chain reads
+// the matrix 8 entries at a time (16-byte LDS reads), the next 8 loaded while the current 8
+// are used, so LDS latency stays off the chain.
 template <int P, int D>
-__device__ float multisect(int ev, float lo, float hi, const float* df, const float* e2f, int q) {
+__device__ float multisect(int ev, float lo, float hi, const float* df, const float* e2s, int q) {
   static_assert(P == 4 || P == 8, "groups of 4 or 8 lanes");
+  static_assert(D % 8 == 0, "chunks of 8");
   constexpr int NIT = P == 4 ? 13 : 10;
+  const float4* d4 = reinterpret_cast<const float4*>(df);
+  const float4* e4 = reinterpret_cast<const float4*>(e2s);
   for (int it = 0; it < NIT; ++it) {
     const float mid = lo + (float)(q + 1) * ((hi - lo) * (1.f / (P + 1)));
-    // Sturm count: the number of negative pivots of T - mid I
-    float qv = df[0] - mid;
-    int cnt = qv < 0.f;
-    for (int j = 1; j < D; ++j) {
-      qv = (df[j] - mid) - e2f[j - 1] * __builtin_amdgcn_rcpf(qv);
-      cnt += qv < 0.f;
+    // Sturm count: the number of negative pivots of T - mid I (the first pivot is
+    // df[0] - mid: its e2s term is 0 * rcp(1))
+    float qv = 1.f;
+    int cnt = 0;
+    float4 da = d4[0], db = d4[1], ea = e4[0], eb = e4[1];
+#pragma unroll 2
+    for (int jb = 0; jb < D; jb += 8) {
+      const int nx = jb + 8 < D ? jb / 4 + 2 : jb / 4;  // the last chunk reloads itself
+      const float4 nda = d4[nx], ndb = d4[nx + 1], nea = e4[nx], neb = e4[nx + 1];
+      const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+      const float ev2[8] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        qv = (dv[u] - mid) - ev2[u] * __builtin_amdgcn_rcpf(qv);
+        cnt += qv < 0.f;
+      }
+      da = nda; db = ndb; ea = nea; eb = neb;
     }
     float h = cnt > ev ? mid : hi;
     h = fminf(h, dpp_fl<0xB1>(h));
@@ -693,7 +709,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   __shared__ __align__(16) double xs[D], cs[D], bx[D], vv[D], ww[D], dd[D], ee[D], tau[D];
   __shared__ double red[2 * NW + 2];
   __shared__ float lamd[D];  // eigenvalues, descending
-  __shared__ float df[D], e2f[D];
+  __shared__ __align__(16) float df[D], e2s[D];  // e2s[j] = e_{j-1}^2 (e2s[0] = 0)
   __shared__ double coef[kEigMaxR];
   __shared__ double wyT[D / 4][16];  // per block of four reflectors: T (10), then column dots
   const int m = blockIdx.x, tid = threadIdx.x;
@@ -924,7 +940,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
     df[tid] = (float)dd[tid];
     // a zero off-diagonal is replaced by a tiny one: the Sturm recurrence then never forms
     // 0 * inf (the eigenvalues move by far less than float32 resolves)
-    e2f[tid] = tid < D - 1 ? fmaxf((float)(ee[tid] * ee[tid]), 1e-36f) : 0.f;
+    e2s[tid] = tid >= 1 ? fmaxf((float)(ee[tid - 1] * ee[tid - 1]), 1e-36f) : 0.f;
     ghi = dd[tid] + (tid > 0 ? fabs(ee[tid - 1]) : 0.0) + fabs(ee[tid]);
   }
   const float hi0 = (float)block_max_d(ghi, red);
@@ -937,7 +953,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   //      eigenvalues (4-point multisection) only when they are asked for or needed
   __shared__ int s_ke, s_all;
   if (tid < 8 * r) {
-    const float lam = multisect<8, D>(D - 1 - tid / 8, lo_start, hi_start, df, e2f, tid % 8);
+    const float lam = multisect<8, D>(D - 1 - tid / 8, lo_start, hi_start, df, e2s, tid % 8);
     if (tid % 8 == 0) lamd[tid / 8] = fmaxf(lam, 0.f);
   }
   __syncthreads();
@@ -959,7 +975,7 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   __syncthreads();
   if (s_all) {  // uniform
     if (tid < 4 * (D - r)) {
-      const float lam = multisect<4, D>(D - 1 - r - tid / 4, lo_start, hi_start, df, e2f, tid % 4);
+      const float lam = multisect<4, D>(D - 1 - r - tid / 4, lo_start, hi_start, df, e2s, tid % 4);
       if (tid % 4 == 0) lamd[r + tid / 4] = fmaxf(lam, 0.f);
     }
     __syncthreads();

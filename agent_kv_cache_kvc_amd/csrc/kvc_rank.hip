@@ -13,8 +13,10 @@
 // descriptor.
 //
 //   score_rank_kernel   one 256-thread workgroup per segment: the squared Frobenius norms of
-//                       the rC x rC products, 32 channels of both factors staged in LDS at a
-//                       time; each thread owns PAIRS (i, j) entries; fixed-order reductions
+//                       the rC x rC products, each 32 x 32 tile of a product one wave's
+//                       MFMA (fp32 32x32x2: lane (i, h) feeds row i of both factors over
+//                       the h-th half of the channels, so the MFMA steps run through every
+//                       channel once); per-wave sums joined in a fixed order
 #include <hip/hip_runtime.h>
 
 #include "kvc_device.h"
@@ -24,86 +26,99 @@ namespace kvc {
 
 namespace {
 
-constexpr int kRankChunk = 32;  // channels of the factors staged per step
-
 __device__ __forceinline__ float rank_wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-// ||F1 F2^T||_F^2 for two rC x D row-major factors (float32 sums, fixed order; every thread of
-// the workgroup returns the same value)
-template <int D, int PAIRS>
-__device__ float prod_sq(const float* __restrict__ F1, const float* __restrict__ F2, int rC,
-                         float (*t1)[kRankChunk + 1], float (*t2)[kRankChunk + 1], float* red) {
-  const int tid = threadIdx.x;
-  float acc[PAIRS];
+// sum of the squared entries of the 32 x 32 tile (bi, bj) of F1 F2^T, F1 and F2 rC x D
+// row-major (rows past rC are zero); every lane of the wave returns the same value
+template <int D>
+__device__ float tile_sq(const float* __restrict__ F1, const float* __restrict__ F2, int rC,
+                         int bi, int bj, int lane) {
+  constexpr int HK = D / 2;  // channels per half
+  const int i = lane & 31, h = lane >> 5;
+  const int r1 = bi * 32 + i, r2 = bj * 32 + i;
+  const float4* a = reinterpret_cast<const float4*>(F1 + (size_t)r1 * D + h * HK);
+  const float4* b = reinterpret_cast<const float4*>(F2 + (size_t)r2 * D + h * HK);
+  const bool va = r1 < rC, vb = r2 < rC;
+  floatx16 acc;
 #pragma unroll
-  for (int p = 0; p < PAIRS; ++p) acc[p] = 0.f;
-  for (int c0 = 0; c0 < D; c0 += kRankChunk) {
-    __syncthreads();
-    for (int e = tid; e < rC * kRankChunk; e += kBlock) {
-      const int i = e / kRankChunk, c = e % kRankChunk;
-      t1[i][c] = F1[(size_t)i * D + c0 + c];
-      t2[i][c] = F2[(size_t)i * D + c0 + c];
-    }
-    __syncthreads();
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int p = 0; p < PAIRS; ++p) {
-      const int pr = tid + kBlock * p;
-      if (pr < rC * rC) {
-        const int i = pr / rC, j = pr % rC;
-        float a = acc[p];
-#pragma unroll 8
-        for (int c = 0; c < kRankChunk; ++c) a += t1[i][c] * t2[j][c];
-        acc[p] = a;
-      }
-    }
+  for (int m = 0; m < HK / 4; ++m) {
+    const float4 x = va ? a[m] : float4{0.f, 0.f, 0.f, 0.f};
+    const float4 y = vb ? b[m] : float4{0.f, 0.f, 0.f, 0.f};
+    acc = mfma_f32(x.x, y.x, acc);
+    acc = mfma_f32(x.y, y.y, acc);
+    acc = mfma_f32(x.z, y.z, acc);
+    acc = mfma_f32(x.w, y.w, acc);
   }
   float sq = 0.f;
 #pragma unroll
-  for (int p = 0; p < PAIRS; ++p) sq += acc[p] * acc[p];
-  sq = rank_wave_sum(sq);
-  __syncthreads();
-  if (tid % kWave == 0) red[tid / kWave] = sq;
-  __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  for (int e = 0; e < 16; ++e) sq = fmaf(acc[e], acc[e], sq);
+  return rank_wave_sum(sq);
 }
 
 }  // namespace
 
-// Fq [2][S][rC][D], Fa [2][S][A][rC][D] float32.
-template <int D, int PAIRS>
+// Fq [2][S][rC][D], Fa [2][S][A][rC][D] float32.  Products per segment: p = 0, 1 the query's
+// own K and V products (||q||^2); per anchor a, p = 2 + 4a + {0, 1} its own (||a||^2) and
+// p = 2 + 4a + {2, 3} the query's with it (<q, a>).  Work unit u = (p, tile) goes to wave
+// u % 4; each wave adds its units' tile sums in increasing u, then the waves are added in
+// order.
+template <int D>
 __global__ __launch_bounds__(kBlock) void score_rank_kernel(
     const float* __restrict__ Fq, const float* __restrict__ Fa, int S, int A, int rC, float tau,
     float* __restrict__ w_ws, uint8_t* __restrict__ mask_ws, float* __restrict__ score_out,
     float* __restrict__ w_out, uint8_t* __restrict__ mask_out, int* __restrict__ ctr) {
-  __shared__ float t1[kMaxRankC][kRankChunk + 1];
-  __shared__ float t2[kMaxRankC][kRankChunk + 1];
-  __shared__ float red[kBlock / kWave];
+  constexpr int NW = kBlock / kWave;
+  __shared__ float part[NW][1 + 2 * kMaxAnchorsGeneral];  // [wave][||q||^2, ||a||^2, <q,a>]
   __shared__ float sc[kMaxAnchorsGeneral];
-  const int s = blockIdx.x, tid = threadIdx.x;
+  const int s = blockIdx.x, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   if (s == 0 && tid == 0) *ctr = 0;  // work counter of the correction that follows
+  const int nq = 1 + 2 * A;
+  for (int e = tid; e < NW * nq; e += kBlock) part[e / nq][e % nq] = 0.f;
+  __syncthreads();
   const size_t fsz = (size_t)rC * D;
-  const float* qK = Fq + (size_t)s * fsz;
-  const float* qV = Fq + ((size_t)S + s) * fsz;
-  const float nq = prod_sq<D, PAIRS>(qK, qK, rC, t1, t2, red) +
-                   prod_sq<D, PAIRS>(qV, qV, rC, t1, t2, red);
-  for (int a = 0; a < A; ++a) {
-    const float* aK = Fa + ((size_t)s * A + a) * fsz;
-    const float* aV = Fa + (((size_t)S + s) * A + a) * fsz;
-    const float na = prod_sq<D, PAIRS>(aK, aK, rC, t1, t2, red) +
-                     prod_sq<D, PAIRS>(aV, aV, rC, t1, t2, red);
-    const float dq = prod_sq<D, PAIRS>(qK, aK, rC, t1, t2, red) +
-                     prod_sq<D, PAIRS>(qV, aV, rC, t1, t2, red);
-    const float den = sqrtf(nq) * sqrtf(na);
-    if (tid == 0) sc[a] = den == 0.f ? 0.f : dq / den;
+  const float* qX[2] = {Fq + (size_t)s * fsz, Fq + ((size_t)S + s) * fsz};
+  const int nt = (rC + 31) / 32, nt2 = nt * nt;
+  const int n_units = (2 + 4 * A) * nt2;
+  for (int u = wave; u < n_units; u += NW) {  // uniform per wave
+    const int p = u / nt2, t = u - p * nt2;
+    const int bi = t / nt, bj = t - bi * nt;
+    const float* F1;
+    const float* F2;
+    int tgt;
+    if (p < 2) {
+      F1 = F2 = qX[p];
+      tgt = 0;
+    } else {
+      const int a = (p - 2) >> 2, k = (p - 2) & 3, x = k & 1;
+      const float* aX = Fa + (((size_t)x * S + s) * A + a) * fsz;
+      F1 = k < 2 ? aX : qX[x];
+      F2 = aX;
+      tgt = k < 2 ? 1 + a : 1 + A + a;
+    }
+    const float v = tile_sq<D>(F1, F2, rC, bi, bj, lane);
+    if (lane == 0) part[wave][tgt] += v;
+  }
+  __syncthreads();
+  for (int a = tid; a < A; a += kBlock) {
+    float nqq = 0.f, naa = 0.f, dqa = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      nqq += part[w][0];
+      naa += part[w][1 + a];
+      dqa += part[w][1 + A + a];
+    }
+    const float den = sqrtf(nqq) * sqrtf(naa);
+    sc[a] = den == 0.f ? 0.f : dqa / den;
   }
   __syncthreads();
   if (tid >= kWave) return;
   // wave 0: score, softmax (the lanes' anchors a = lane + 64 i, joined in a fixed order)
-  const int lane = tid;
   float best = -INFINITY;
   bool nan = false;
   for (int a = lane; a < A; a += kWave) {
@@ -134,19 +149,12 @@ hipError_t launch_score_rank(const float* Fq, const float* Fa, int S, int d, int
                              float tau, float* w_ws, uint8_t* mask_ws, float* score_out,
                              float* w_out, uint8_t* mask_out, int* ctr, hipStream_t st) {
   if (S == 0) return hipSuccess;
-  const int pairs = (rC * rC + kBlock - 1) / kBlock;  // rC <= 128: at most 64
-#define KVC_RANK_LAUNCH(DD, PP)                                                              \
-  hipLaunchKernelGGL((score_rank_kernel<DD, PP>), dim3(S), dim3(kBlock), 0, st, Fq, Fa, S, A, \
-                     rC, tau, w_ws, mask_ws, score_out, w_out, mask_out, ctr)
-  if (d == 128) {
-    if (pairs <= 4) KVC_RANK_LAUNCH(128, 4);
-    else if (pairs <= 16) KVC_RANK_LAUNCH(128, 16);
-    else KVC_RANK_LAUNCH(128, 64);
-  } else {
-    if (pairs <= 4) KVC_RANK_LAUNCH(64, 4);
-    else KVC_RANK_LAUNCH(64, 16);
-  }
-#undef KVC_RANK_LAUNCH
+  if (d == 128)
+    hipLaunchKernelGGL((score_rank_kernel<128>), dim3(S), dim3(kBlock), 0, st, Fq, Fa, S, A, rC,
+                       tau, w_ws, mask_ws, score_out, w_out, mask_out, ctr);
+  else
+    hipLaunchKernelGGL((score_rank_kernel<64>), dim3(S), dim3(kBlock), 0, st, Fq, Fa, S, A, rC,
+                       tau, w_ws, mask_ws, score_out, w_out, mask_out, ctr);
   return hipGetLastError();
 }
 

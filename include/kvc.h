@@ -300,7 +300,11 @@ kvc_status kvc_rank_error_curve(const float* eig, int M, int n, float* curve_out
  *   U = delta W^T (float32 accumulation),
  * and the effective rank k = min{k >= 1 : sum_{i<k} lambda_i >= energy * total} with
  * total = sum lambda = trace G = ||delta||_F^2 (0 for a zero delta), the running sum and
- * compare in float64 (Figs. 2, 7(a)).
+ * compare in float64 (Figs. 2, 7(a)).  k is exact (the value the exact eigenvalues of
+ * delta^T delta give, up to float64 rounding): the fast path keeps its k only when both
+ * running sums around the threshold clear a stated bound on its own error (float32 Gram
+ * sums, float32 eigenvalue brackets, float64 reduction); otherwise a float64 pass (Gram
+ * from delta in float64, Householder, multisection to float64 resolution) decides it.
  *   delta    : [M,T,d] dtype, read only
  *   r        : 1 <= r <= d
  *   energy   : in (0, 1], 0.9 in the pages
