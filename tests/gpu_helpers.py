@@ -139,3 +139,39 @@ def energy_margin(eig: np.ndarray, energy: float = 0.9) -> np.ndarray:
     tot = lam.sum(-1, keepdims=True)
     frac = np.cumsum(lam, -1) / np.where(tot > 0, tot, 1)
     return np.min(np.abs(frac - energy), axis=-1)
+
+
+def check_every_segment(name: str, got_K, got_V, ref_layer, L: int, mask=None) -> None:
+    """Corrected caches of every segment against the oracle, one layer at a time.
+    ref_layer(l) returns the oracle's result for layer l (a dict with K_out, V_out, mask of
+    shape [1, H, ...]); got_K, got_V are the library's [L, H, T, d] outputs; mask (if given)
+    is the expected [L, H] decision.  The bars apply to the whole tensors; the worst segment's
+    relative error is printed as well."""
+    acc = {x: [0.0, 0.0, 0.0, 0.0] for x in ("K", "V")}  # err^2, ref^2, max|diff|, max|ref|
+    worst = (0.0, None)
+    for l in range(L):
+        ref = ref_layer(l)
+        if mask is not None:
+            np.testing.assert_array_equal(ref["mask"][0], mask[l], err_msg=f"{name} layer {l}")
+        for x, got_t in (("K", got_K), ("V", got_V)):
+            got = synth.to_f64(got_t[l:l + 1])
+            want = ref[f"{x}_out"]
+            diff = got - want
+            a = acc[x]
+            a[0] += float(np.sum(diff ** 2))
+            a[1] += float(np.sum(want ** 2))
+            a[2] = max(a[2], float(np.max(np.abs(diff))) if diff.size else 0.0)
+            a[3] = max(a[3], float(np.max(np.abs(want))) if want.size else 0.0)
+            seg = np.sqrt(np.sum(diff ** 2, axis=(-2, -1)) /
+                          np.maximum(np.sum(want ** 2, axis=(-2, -1)), 1e-300))
+            h = int(np.argmax(seg[0]))
+            if seg[0, h] > worst[0]:
+                worst = (float(seg[0, h]), (x, l, h))
+    for x in ("K", "V"):
+        e2, r2, da, ra = acc[x]
+        rel = float(np.sqrt(e2 / r2)) if r2 > 0 else 0.0
+        say(f"  {name} {x}' every segment: rel-Frobenius {rel:.3e} (bar {REL_FROB:.0e}), "
+            f"max-abs {da:.3e} = {da / ra if ra > 0 else 0.0:.3e} x max|ref| (bar {MAX_ABS:.0e})")
+        assert rel <= REL_FROB, f"{name} {x}': relative Frobenius error {rel:.3e}"
+        assert da <= MAX_ABS * ra + 1e-30, f"{name} {x}': max-abs error {da:.3e}"
+    say(f"  {name} worst segment {worst[1]}: rel-Frobenius {worst[0]:.3e}")

@@ -9,8 +9,7 @@ import torch
 import agent_kv_cache_kvc_amd as kvc
 import oracle
 import synth
-from gpu_helpers import (check_close, correct_inputs, dev, oracle_correct_segments, pool_all,
-                         sample_segments, say)
+from gpu_helpers import check_close, check_every_segment, correct_inputs, dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -188,9 +187,10 @@ def test_deterministic_and_empty():
     assert float(out.q_next.abs().sum()) == 0.0
 
 
-def _run_sampled(cfg, n_samples=24):
-    """Full-size workload generated on the GPU; mask/score/weights compared for every
-    segment, caches for a sample of segments."""
+def _run_every_segment(cfg):
+    """Full-size workload generated on the GPU: mask and score of every segment against the
+    oracle's matching, and the corrected K', V' of every segment against the oracle's
+    correction, one layer at a time."""
     say(f"[correct-full] {cfg.name} L={cfg.L} H={cfg.H} T={cfg.T} A={cfg.A} r={cfg.r}")
     d = dev()
     case = synth.generate(cfg, d)
@@ -202,30 +202,25 @@ def _run_sampled(cfg, n_samples=24):
     score, mask = oracle.reliability(s, cfg.tau)
     np.testing.assert_array_equal(out.mask.cpu().numpy(), mask)
     np.testing.assert_allclose(out.score.cpu().numpy(), score, atol=2e-6)
-    rho = 1.0 - mask.mean()
-    say(f"  reuse ratio {rho:.3f}")
-    segs = sample_segments(cfg.L, cfg.H, mask, n_samples)
-    ref = oracle_correct_segments(case, desc, segs, cfg.tau)
-    ls = torch.tensor([x[0] for x in segs], device=d)
-    hs = torch.tensor([x[1] for x in segs], device=d)
-    np.testing.assert_array_equal(ref["mask"][:, 0], mask[[x[0] for x in segs], [x[1] for x in segs]])
-    eK = check_close("K'", synth.to_f64(out.K[ls, hs])[:, None], ref["K_out"])
-    eV = check_close("V'", synth.to_f64(out.V[ls, hs])[:, None], ref["V_out"])
-    say(f"  sampled {len(segs)} segments: rel-Frobenius K' {eK:.2e} V' {eV:.2e}")
+    say(f"  reuse ratio {1.0 - mask.mean():.3f}")
+    check_every_segment(cfg.name, out.K, out.V, lambda l: oracle.correct(
+        synth.to_f64(case.K0[l:l + 1]), synth.to_f64(case.V0[l:l + 1]),
+        synth.to_f64(desc[l:l + 1]), synth.to_f64(ed.U[:, l:l + 1]),
+        synth.to_f64(ed.W[:, l:l + 1]), cfg.tau, cfg.dtype), cfg.L, mask)
     del case, out
     torch.cuda.empty_cache()
 
 
 def test_llama8b_t2048_full_size():
-    _run_sampled(synth.CONFIGS["llama8b_t2048"])
+    _run_every_segment(synth.CONFIGS["llama8b_t2048"])
 
 
 def test_llama8b_t8192_full_size():
-    _run_sampled(synth.CONFIGS["llama8b_t8192_fit"], n_samples=12)
+    _run_every_segment(synth.CONFIGS["llama8b_t8192_fit"])
 
 
 def test_vl_t9216_full_size():
-    _run_sampled(synth.CONFIGS["vl_t9216"], n_samples=12)
+    _run_every_segment(synth.CONFIGS["vl_t9216"])
 
 
 def test_three_tilings_of_one_correction_agree():
