@@ -126,6 +126,10 @@ def test_streamed_blocks_match_the_oracle(dtype, d, blocks, r, M):
 
 
 def test_llama8b_t8192_streamed_in_four_blocks():
+    """The 8B delta at T = 8192 appended in four blocks of 2048 rows: the refit from the
+    accumulated G against the oracle's SVD of all rows (k_eff on every matrix, U = delta W^T,
+    W and eigenvalues on a sample of 32 matrices), and the same rank-32 subspace as the
+    one-call fit on every matrix."""
     cfg = synth.CONFIGS["llama8b_t8192_fit"]
     say(f"[stream] {cfg.name} in 4 blocks of {cfg.T // 4}")
     case = synth.generate(cfg, dev())
@@ -139,7 +143,8 @@ def test_llama8b_t8192_streamed_in_four_blocks():
     for i in range(4):
         G = kvc.gram_accumulate(delta[:, i * T // 4:(i + 1) * T // 4].contiguous(), G,
                                 workspace=ws)
-    fit = kvc.fit_from_gram(G, r=cfg.r, want_eig=False)
+    fit = kvc.fit_from_gram(G, r=cfg.r)
+    U = kvc.project(delta, fit.W)
     one = kvc.fit_anchor(delta, r=cfg.r, want_eig=False)
     torch.cuda.synchronize()
     assert torch.all(fit.k_eff == 11)
@@ -147,4 +152,13 @@ def test_llama8b_t8192_streamed_in_four_blocks():
     P1 = fit.W.double().transpose(1, 2) @ fit.W.double()
     P2 = one.W.double().transpose(1, 2) @ one.W.double()
     err = ((P1 - P2).norm(dim=(1, 2)) / P2.norm(dim=(1, 2))).max().item()
+    say(f"  W^T W against the one-call fit: max relative difference {err:.2e}")
     assert err < 1e-3, err
+    rng = np.random.default_rng(5)
+    idx = sorted(set([0, M - 1] + rng.choice(M, 30, replace=False).tolist()))
+    dh = synth.to_f64(delta[idx])
+    ref = oracle.fit_anchor(dh, cfg.r)
+    check_fit(f"stream-{cfg.name}", U[idx].cpu().double().numpy(),
+              fit.W[idx].cpu().double().numpy(), fit.k_eff[idx].cpu().numpy(),
+              fit.eig[idx].cpu().double().numpy(), ref, cfg.r, dh)
+    say(f"  {len(idx)} sampled matrices match the oracle's SVD of all rows")
