@@ -37,7 +37,10 @@ __constant__ int c_blk64[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
 // grid (nsplit, M).  Each slab of SLAB = 16384/D tokens is loaded as 8x8 bf16 blocks
 // (one per thread, 8 rows x 16 bytes, coalesced), transposed in registers and stored
 // channel-major in LDS, so an MFMA fragment (8 consecutive tokens of one channel) is a
-// single 16-byte LDS read.  Products of bf16 values are exact in the float32 accumulator,
+// single 16-byte LDS read.  The 16-byte chunks of channel row c sit at chunk ^ ((c >> 3) mod
+// chunks): the 16 lanes that store the same token chunk for channels 8 apart then reach
+// different banks (without it they all hit one bank group), and a fragment read stays one
+// access per lane.  Products of bf16 values are exact in the float32 accumulator,
 // which holds the split's whole sum (chunk / 16 MFMA steps; the error bound of the effective
 // rank's certificate counts them); the partials are written as float64.
 template <int D>
@@ -49,6 +52,8 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int CG = D / 8;  // 8-channel groups per row
+  constexpr int NCH = SLAB / 8;  // 16-byte token chunks per channel row
+  static_assert((NCH & (NCH - 1)) == 0 && NCH >= CG, "swizzle within the row");
   __shared__ __align__(16) uint16_t lt[D * SR];
   const int split = blockIdx.x, m = blockIdx.y, nsplit = gridDim.x;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
         const uint32_t a = in[2 * k][j >> 1], b = in[2 * k + 1][j >> 1];
         o[k] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
       }
-      *reinterpret_cast<u32x4*>(&lt[(8 * cg + j) * SR + 8 * rg]) = o;
+      *reinterpret_cast<u32x4*>(&lt[(8 * cg + j) * SR + 8 * (rg ^ (cg & (NCH - 1)))]) = o;
     }
     __syncthreads();
     if (ts + SLAB < t_end) load_block(ts + SLAB);
@@ -104,10 +109,11 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         if (I[b] >= 0) {
-          const u32x4 fa =
-              *reinterpret_cast<const u32x4*>(&lt[(I[b] * 32 + ln) * SR + 16 * ks + 8 * g]);
-          const u32x4 fb =
-              *reinterpret_cast<const u32x4*>(&lt[(J[b] * 32 + ln) * SR + 16 * ks + 8 * g]);
+          const int ra = I[b] * 32 + ln, rb = J[b] * 32 + ln;
+          const u32x4 fa = *reinterpret_cast<const u32x4*>(
+              &lt[ra * SR + 8 * ((2 * ks + g) ^ ((ra >> 3) & (NCH - 1)))]);
+          const u32x4 fb = *reinterpret_cast<const u32x4*>(
+              &lt[rb * SR + 8 * ((2 * ks + g) ^ ((rb >> 3) & (NCH - 1)))]);
           acc[b] = mfma_bf16(fa, fb, acc[b]);
         }
       }
