@@ -65,7 +65,9 @@ def _pick_tau(best):
 
 @pytest.mark.parametrize("dtype,d,T,A,r,rC", [("bf16", 128, 400, 4, 32, 32),
                                               ("f32", 64, 300, 3, 8, 8),
-                                              ("bf16", 128, 250, 2, 128, 16)])
+                                              ("bf16", 128, 250, 2, 128, 16),
+                                              ("bf16", 128, 300, 2, 32, 100),  # 4 x 4 tiles, ragged
+                                              ("f32", 64, 200, 5, 16, 40)])    # 2 x 2 tiles, ragged
 def test_correct_rank_matches_the_oracle(dtype, d, T, A, r, rC):
     """The same query representation (the oracle's, in float32) handed to both sides: masks
     exact, scores and weights to float32 accuracy, caches within the bars."""
