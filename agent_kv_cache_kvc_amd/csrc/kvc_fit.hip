@@ -1277,6 +1277,7 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
   constexpr int RT = kExactBlock / D;  // threads per row of a matrix-vector product
   extern __shared__ __align__(16) double Gs[];  // [D][GS]; the Gram stages delta here first
   __shared__ double vv[D], ww[D], dd[D], ee[D], red[NW];
+  __shared__ __align__(16) double dx[D], e2x[D];  // the diagonal and e_{j-1}^2 (e2x[0] = 0)
   __shared__ double lam[D];
   const int m = blockIdx.x, tid = threadIdx.x;
   if (k_eff[m] >= 0) return;  // uniform: only flagged matrices
@@ -1309,16 +1310,19 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
           stage[e] = static_cast<const float*>(sp)[g];
       }
       __syncthreads();
+      // rows in order; a thread's TR + TC values of a row come in 16-byte LDS reads
       for (int t = 0; t < n; ++t) {
-        double xa[TR], xb[TC];
+        float fa[TR], fb[TC];
 #pragma unroll
-        for (int a = 0; a < TR; ++a) xa[a] = (double)stage[t * D + i0 + a];
+        for (int a = 0; a < TR; a += 2)
+          *reinterpret_cast<float2*>(&fa[a]) = *reinterpret_cast<const float2*>(&stage[t * D + i0 + a]);
 #pragma unroll
-        for (int b = 0; b < TC; ++b) xb[b] = (double)stage[t * D + j0 + b];
+        for (int b = 0; b < TC; b += 4)
+          *reinterpret_cast<float4*>(&fb[b]) = *reinterpret_cast<const float4*>(&stage[t * D + j0 + b]);
 #pragma unroll
         for (int a = 0; a < TR; ++a)
 #pragma unroll
-          for (int b = 0; b < TC; ++b) acc[a][b] = fma(xa[a], xb[b], acc[a][b]);
+          for (int b = 0; b < TC; ++b) acc[a][b] = fma((double)fa[a], (double)fb[b], acc[a][b]);
       }
       __syncthreads();
     }
@@ -1360,9 +1364,12 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
     const double K = 0.5 * t * pdotv;
     if (tid < D) ww[tid] -= K * vv[tid];
     __syncthreads();
-    for (int e = tid; e < D * D; e += kExactBlock) {
-      const int i = e / D, j = e % D;
-      if (i > k && j > k) Gs[i * GS + j] -= vv[i] * ww[j] + ww[i] * vv[j];
+    {  // the trailing block (rows and columns k + 1 .. D - 1) only
+      const int nt = D - 1 - k;
+      for (int e = tid; e < nt * nt; e += kExactBlock) {
+        const int i = k + 1 + e / nt, j = k + 1 + e % nt;
+        Gs[i * GS + j] -= vv[i] * ww[j] + ww[i] * vv[j];
+      }
     }
     __syncthreads();
   }
@@ -1384,23 +1391,42 @@ __global__ __launch_bounds__(kExactBlock) void keff_exact_kernel(const void* __r
   }
   const double pivmin = 1e-290 * fmax(1.0, max_e2);
   const double pad = 1e-12 * fmax(fabs(lo0), fabs(hi0)) + 1e-290;
+  if (tid < D) {
+    dx[tid] = dd[tid];
+    e2x[tid] = tid >= 1 ? ee[tid - 1] * ee[tid - 1] : 0.0;
+  }
+  __syncthreads();
   if (tid < 4 * D) {
     const int ev = tid / 4, q = tid % 4;
     double lo = lo0 - pad, hi = hi0 + pad;
+    const double2* d2 = reinterpret_cast<const double2*>(dx);
+    const double2* e2 = reinterpret_cast<const double2*>(e2x);
     for (int it = 0; it < 24; ++it) {
       const double x = lo + (double)(q + 1) * ((hi - lo) / 5.0);
       // Sturm count: negative pivots of T - x I.  1 / pivot from the hardware reciprocal and
-      // two Newton steps (a relative error far below the ulps a Sturm count tolerates)
-      double pv = dd[0] - x;
+      // two Newton steps (a relative error far below the ulps a Sturm count tolerates).  The
+      // matrix is read four entries at a time, the next four in flight while these are used.
+      double pv = dx[0] - x;
       if (fabs(pv) < pivmin) pv = -pivmin;
       int cnt = pv < 0.0;
-      for (int j = 1; j < D; ++j) {
-        double rp = __builtin_amdgcn_rcp(pv);
-        rp = rp * fma(-pv, rp, 2.0);
-        rp = rp * fma(-pv, rp, 2.0);
-        pv = (dd[j] - x) - (ee[j - 1] * ee[j - 1]) * rp;
-        if (fabs(pv) < pivmin) pv = -pivmin;
-        cnt += pv < 0.0;
+      double2 da = d2[0], db = d2[1], ea = e2[0], eb = e2[1];
+#pragma unroll 1
+      for (int jb = 0; jb < D; jb += 4) {
+        const int nx = jb + 4 < D ? jb / 2 + 2 : jb / 2;  // the last chunk reloads itself
+        const double2 nda = d2[nx], ndb = d2[nx + 1], nea = e2[nx], neb = e2[nx + 1];
+        const double dv[4] = {da.x, da.y, db.x, db.y};
+        const double ev2[4] = {ea.x, ea.y, eb.x, eb.y};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (jb + u == 0) continue;  // the first pivot is dx[0] - x
+          double rp = __builtin_amdgcn_rcp(pv);
+          rp = rp * fma(-pv, rp, 2.0);
+          rp = rp * fma(-pv, rp, 2.0);
+          pv = (dv[u] - x) - ev2[u] * rp;
+          if (fabs(pv) < pivmin) pv = -pivmin;
+          cnt += pv < 0.0;
+        }
+        da = nda; db = ndb; ea = nea; eb = neb;
       }
       double h = cnt > ev ? x : hi;
       h = fmin(h, __shfl_xor(h, 1, 64));
