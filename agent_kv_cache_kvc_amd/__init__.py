@@ -47,6 +47,7 @@ __all__ = [
     "fit_workspace_bytes",
     "gram_accumulate",
     "fit_from_gram",
+    "refit_warm",
     "project",
     "segment_error",
     "rank_error_curve",
@@ -109,6 +110,7 @@ _SIGS = {
     "kvc_gram_workspace_bytes": (_sz, [_i, _i, _i]),
     "kvc_gram_accumulate": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "kvc_fit_from_gram": (_i, [_vp, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp]),
+    "kvc_refit_warm": (_i, [_vp, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
     "kvc_project_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "kvc_project": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _vp, _vp, _sz, _vp]),
 }
@@ -594,6 +596,27 @@ def fit_from_gram(G: torch.Tensor, r: int = 32, energy: float = 0.9, *,
     _check(lib().kvc_fit_from_gram(_ptr(G), M, d, int(r), float(energy), _ptr(W), _ptr(k),
                                    _ptr(eig), _stream(dev)))
     return FitResult(None, W, k, eig)
+
+
+def refit_warm(G: torch.Tensor, W_prev: torch.Tensor, energy: float = 0.9, *,
+               W_out: Optional[torch.Tensor] = None, want_warm: bool = True):
+    """Refit from an accumulated G [M, d, d] float64 starting from the previous W_prev
+    [M, r, d] float32 (kvc_refit_warm in include/kvc.h).  Returns (FitResult with W and
+    k_eff, warm [M] int32 or None: 1 where the warm result was kept).  W_out may be W_prev
+    itself (in-place update)."""
+    M, d, _ = G.shape
+    r = W_prev.shape[1]
+    dev = G.device
+    _need(G, "G", (M, d, d), torch.float64, dev)
+    _need(W_prev, "W_prev", (M, r, d), torch.float32, dev)
+    if W_out is None:
+        W_out = torch.empty(M, r, d, dtype=torch.float32, device=dev)
+    _need(W_out, "W_out", (M, r, d), torch.float32, dev)
+    k = torch.empty(M, dtype=torch.int32, device=dev)
+    warm = torch.empty(M, dtype=torch.int32, device=dev) if want_warm else None
+    _check(lib().kvc_refit_warm(_ptr(G), M, d, int(r), float(energy), _ptr(W_prev), _ptr(W_out),
+                                _ptr(k), _ptr(warm), _stream(dev)))
+    return FitResult(None, W_out, k, None), warm
 
 
 def project(delta: torch.Tensor, W: torch.Tensor, *,

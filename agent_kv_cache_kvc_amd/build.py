@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libkvc.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["kvc_api.hip", "kvc_correct.hip", "kvc_correct_general.hip", "kvc_fit.hip",
            "kvc_rank.hip", "kvc_metrics.hip",
-           "kvc_anchor_pool.hip"]
+           "kvc_anchor_pool.hip", "kvc_warm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

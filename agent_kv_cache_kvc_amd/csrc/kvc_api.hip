@@ -808,6 +808,24 @@ kvc_status kvc_fit_from_gram(const double* G, int M, int d, int r, double energy
   return ok();
 }
 
+kvc_status kvc_refit_warm(const double* G, int M, int d, int r, double energy,
+                          const float* W_prev, float* W_out, int32_t* k_eff_out,
+                          int32_t* warm_out, void* stream) {
+  KVC_TRY(validate_fit_shape(M, d, KVC_F32));
+  if (r < 1 || r > d) return fail(KVC_ERR_ARG, "r=%d (need 1 <= r <= d)", r);
+  if (!(energy > 0.0 && energy <= 1.0)) return fail(KVC_ERR_ARG, "energy must be in (0, 1]");
+  if (M == 0) return ok();
+  KVC_TRY(check_tensor(G, "G", 8));
+  KVC_TRY(check_tensor(W_prev, "W_prev"));
+  KVC_TRY(check_tensor(W_out, "W_out"));
+  KVC_TRY(check_tensor(k_eff_out, "k_eff_out", 4));
+  if (warm_out) KVC_TRY(check_tensor(warm_out, "warm_out", 4));
+  KVC_HIP(kvc::launch_refit_warm(G, M, d, r, energy, W_prev, W_out, k_eff_out, warm_out,
+                                 reinterpret_cast<hipStream_t>(stream)),
+          "refit_warm");
+  return ok();
+}
+
 size_t kvc_project_workspace_bytes(int M, int d, int r, int dtype) {
   if (M < 0 || d <= 0 || r < 1) return 0;
   return kvc::project_ws_bytes(M, d, r, dtype);

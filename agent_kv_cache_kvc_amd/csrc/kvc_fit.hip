@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvc_device.h"
+#include "kvc_eig_common.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -566,58 +567,9 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
 //     eigenvalues, null directions) two passes of Gram-Schmidt in descending order, with
 //     null directions completed by canonical basis vectors.  Then the canonical sign.
 constexpr int kEigBlock = 512;
-constexpr int kEigMaxR = 32;
 constexpr double kEigOrthoTol = 1e-7;
 
 __device__ __forceinline__ int pk(int i, int j) { return i * (i + 1) / 2 + j; }  // j <= i
-
-// lanes whose DPP source lies outside the row read 0
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double x) {
-  const int2 h = __builtin_bit_cast(int2, x);
-  int2 o;
-  o.x = __builtin_amdgcn_mov_dpp(h.x, CTRL, 0xf, 0xf, true);
-  o.y = __builtin_amdgcn_mov_dpp(h.y, CTRL, 0xf, 0xf, true);
-  return __builtin_bit_cast(double, o);
-}
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
-}
-
-// sum over aligned groups of N lanes (4, 8 or 16); every lane of the group gets it
-template <int N>
-__device__ __forceinline__ double group_sum_d(double v) {
-  v += dpp_d<0xB1>(v);  // quad_perm [1, 0, 3, 2]
-  v += dpp_d<0x4E>(v);  // quad_perm [2, 3, 0, 1]
-  if constexpr (N >= 8) v += dpp_d<0x141>(v);   // row_half_mirror
-  if constexpr (N >= 16) v += dpp_d<0x140>(v);  // row_mirror
-  return v;
-}
-
-__device__ __forceinline__ double readlane_d(double v, int lane) {
-  const int2 h = __builtin_bit_cast(int2, v);
-  int2 o;
-  o.x = __builtin_amdgcn_readlane(h.x, lane);
-  o.y = __builtin_amdgcn_readlane(h.y, lane);
-  return __builtin_bit_cast(double, o);
-}
-
-// a value that is the same on every lane, moved to scalar registers
-__device__ __forceinline__ double uniform_d(double v) {
-  const int2 h = __builtin_bit_cast(int2, v);
-  int2 o;
-  o.x = __builtin_amdgcn_readfirstlane(h.x);
-  o.y = __builtin_amdgcn_readfirstlane(h.y);
-  return __builtin_bit_cast(double, o);
-}
-
-// wavefront sum in a fixed order (rows of 16 lanes, then the four rows); uniform result
-__device__ __forceinline__ double wave_sum_d(double v) {
-  v = group_sum_d<16>(v);
-  return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
-}
 
 // deterministic workgroup sum (waves in fixed order); every thread gets it
 __device__ __forceinline__ double block_sum_d(double v, double* red) {
@@ -645,68 +597,12 @@ __device__ __forceinline__ double block_max_d(double v, double* red) {
   return s;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_fl(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf,
-                                                            0xf, true));
-}
-
-// The ev-th smallest eigenvalue of the symmetric tridiagonal matrix (diagonal df, squared
-// off-diagonals shifted by one: e2s[j] = e_{j-1}^2 > 0, e2s[0] = 0) by P-point multisection on
-// Sturm counts, P aligned lanes per eigenvalue (q = lane within the group).  Each step splits
-// [lo, hi] into P + 1 parts; the new interval ends at the lowest point with more than ev
-// eigenvalues below it and starts at the highest point under that one, so it always brackets
-// the eigenvalue even where rounding makes the counts non-monotone.  4 points x 13 steps or
-// 8 points x 10 steps shrink the start interval more than 2^30 times.  The Sturm chain reads
-// the matrix 8 entries at a time (16-byte LDS reads), the next 8 loaded while the current 8
-// are used, so LDS latency stays off the chain.
-template <int P, int D>
-__device__ float multisect(int ev, float lo, float hi, const float* df, const float* e2s, int q) {
-  static_assert(P == 4 || P == 8, "groups of 4 or 8 lanes");
-  static_assert(D % 8 == 0, "chunks of 8");
-  constexpr int NIT = P == 4 ? 13 : 10;
-  const float4* d4 = reinterpret_cast<const float4*>(df);
-  const float4* e4 = reinterpret_cast<const float4*>(e2s);
-  for (int it = 0; it < NIT; ++it) {
-    const float mid = lo + (float)(q + 1) * ((hi - lo) * (1.f / (P + 1)));
-    // Sturm count: the number of negative pivots of T - mid I (the first pivot is
-    // df[0] - mid: its e2s term is 0 * rcp(1))
-    float qv = 1.f;
-    int cnt = 0;
-    float4 da = d4[0], db = d4[1], ea = e4[0], eb = e4[1];
-#pragma unroll 2
-    for (int jb = 0; jb < D; jb += 8) {
-      const int nx = jb + 8 < D ? jb / 4 + 2 : jb / 4;  // the last chunk reloads itself
-      const float4 nda = d4[nx], ndb = d4[nx + 1], nea = e4[nx], neb = e4[nx + 1];
-      const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-      const float ev2[8] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        qv = (dv[u] - mid) - ev2[u] * __builtin_amdgcn_rcpf(qv);
-        cnt += qv < 0.f;
-      }
-      da = nda; db = ndb; ea = nea; eb = neb;
-    }
-    float h = cnt > ev ? mid : hi;
-    h = fminf(h, dpp_fl<0xB1>(h));
-    h = fminf(h, dpp_fl<0x4E>(h));
-    if constexpr (P == 8) h = fminf(h, dpp_fl<0x141>(h));
-    float l = mid < h ? mid : lo;
-    l = fmaxf(l, dpp_fl<0xB1>(l));
-    l = fmaxf(l, dpp_fl<0x4E>(l));
-    if constexpr (P == 8) l = fmaxf(l, dpp_fl<0x141>(l));
-    lo = l;
-    hi = h;
-  }
-  return 0.5f * (lo + hi);
-}
-
 template <int D>
 __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
     const double* __restrict__ partials, int nsplit, const double* __restrict__ G_in, int r,
     double energy, double gamma, float* __restrict__ W_out, float* __restrict__ eig_out,
     int32_t* __restrict__ k_eff_out, uint16_t* __restrict__ w_hi, uint16_t* __restrict__ w_lo,
-    int rpad) {
+    int rpad, int only_missed) {
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int NW = kEigBlock / kWave;
@@ -719,6 +615,8 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
   __shared__ double coef[kEigMaxR];
   __shared__ double wyT[D / 4][16];  // per block of four reflectors: T (10), then column dots
   const int m = blockIdx.x, tid = threadIdx.x;
+  // after a warm refit only the matrices it left open (uniform per workgroup)
+  if (only_missed && k_eff_out[m] != kWarmMiss) return;
 
   // ---- G = sum of the partials (fixed split order, float64), lower triangle; or G as given
   if (G_in != nullptr) {
@@ -1662,7 +1560,7 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
     hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
                        f.nsplit, (const double*)nullptr, f.r, energy, gamma, W_out, eig, k_eff,
                        dtype == KVC_BF16 ? whi : nullptr, dtype == KVC_BF16 ? wlo : nullptr,
-                       f.rpad);
+                       f.rpad, 0);
   } else {
     const size_t lds = (size_t)D * (D + 4) * sizeof(float);
     allow_dynamic_lds(jacobi_kernel<D>, lds);
@@ -1757,7 +1655,7 @@ static hipError_t eig_from_gram_t(const double* G, int M, int r, double energy, 
     allow_dynamic_lds(eig_kernel<D>, lds);
     hipLaunchKernelGGL((eig_kernel<D>), dim3(M), dim3(kEigBlock), lds, st,
                        (const double*)nullptr, 0, G, r, energy, 0.0, W_out, eig, k_eff,
-                       (uint16_t*)nullptr, (uint16_t*)nullptr, rpad);
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, rpad, 0);
   } else {
     const size_t lds = (size_t)D * (D + 4) * sizeof(float);
     allow_dynamic_lds(jacobi_kernel<D>, lds);
@@ -1769,6 +1667,33 @@ static hipError_t eig_from_gram_t(const double* G, int M, int r, double energy, 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_keff_exact<D>(G, 2, M, 0, energy, k_eff, eig, st);
+}
+
+// Warm refit: the warm kernel, then the full eigensolver for the matrices it left open
+// (k_eff = kWarmMiss), then the float64 decision of every flagged effective rank.  r > 32
+// (the Jacobi route) takes the full solve for every matrix.
+template <int D>
+static hipError_t refit_warm_t(const double* G, int M, int r, double energy,
+                               const float* W_prev, float* W_out, int32_t* k_eff, int32_t* warm,
+                               hipStream_t st) {
+  if (r > kEigMaxR) {
+    if (warm) {
+      const hipError_t e = launch_fill_i32(warm, M, 0, st);
+      if (e != hipSuccess) return e;
+    }
+    return eig_from_gram_t<D>(G, M, r, energy, W_out, k_eff, nullptr, st);
+  }
+  hipError_t e = launch_refit_warm_kernel(G, M, D, r, energy, W_prev, W_out, k_eff, warm, st);
+  if (e != hipSuccess) return e;
+  const int rpad = (r + 31) / 32 * 32;
+  const size_t lds = (size_t)D * (D + 1) / 2 * sizeof(double);
+  allow_dynamic_lds(eig_kernel<D>, lds);
+  hipLaunchKernelGGL((eig_kernel<D>), dim3(M), dim3(kEigBlock), lds, st, (const double*)nullptr,
+                     0, G, r, energy, 0.0, W_out, (float*)nullptr, k_eff, (uint16_t*)nullptr,
+                     (uint16_t*)nullptr, rpad, 1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_keff_exact<D>(G, 2, M, 0, energy, k_eff, nullptr, st);
 }
 
 template <int D>
@@ -1805,6 +1730,14 @@ hipError_t launch_fit_from_gram(const double* G, int M, int d, int r, double ene
   if (M == 0) return hipSuccess;
   return d == 128 ? eig_from_gram_t<128>(G, M, r, energy, W_out, k_eff, eig, st)
                   : eig_from_gram_t<64>(G, M, r, energy, W_out, k_eff, eig, st);
+}
+
+hipError_t launch_refit_warm(const double* G, int M, int d, int r, double energy,
+                             const float* W_prev, float* W_out, int32_t* k_eff, int32_t* warm,
+                             hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  return d == 128 ? refit_warm_t<128>(G, M, r, energy, W_prev, W_out, k_eff, warm, st)
+                  : refit_warm_t<64>(G, M, r, energy, W_prev, W_out, k_eff, warm, st);
 }
 
 hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
@@ -1853,7 +1786,7 @@ static hipError_t rank_descriptor_t(const void* K, const void* V, const FitLayou
     allow_dynamic_lds(eig_kernel<D>, lds);
     hipLaunchKernelGGL((eig_kernel<D>), dim3(f.M), dim3(kEigBlock), lds, st, partials,
                        f.nsplit, (const double*)nullptr, f.r, 0.9, gamma, F, eig, k_eff,
-                       (uint16_t*)nullptr, (uint16_t*)nullptr, f.rpad);
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, f.rpad, 0);
   } else {
     const size_t lds = (size_t)D * (D + 4) * sizeof(float);
     allow_dynamic_lds(jacobi_kernel<D>, lds);

@@ -21,6 +21,8 @@ constexpr int kMaxR = 64;             // rank bound of the correction kernel
 constexpr int kMaxPool = 32;          // slots of an online anchor pool per segment
 constexpr int kMaxTargets = 8;        // targets of one multi-target correction launch
 constexpr int kJacobiMaxSweeps = 40;  // hard cap: every workgroup leaves the sweep loop
+constexpr int kEigMaxR = 32;         // rank bound of the tridiagonal eigensolver route
+constexpr int32_t kWarmMiss = INT32_MIN;  // k_eff mark: the warm refit left the matrix open
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -203,6 +205,16 @@ hipError_t launch_fit_from_gram(const double* G, int M, int d, int r, double ene
                                 float* W_out, int32_t* k_eff, float* eig, hipStream_t st);
 hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
                           int r, float* U_out, char* ws, hipStream_t st);
+// Warm-started refit from a given G and the previous W (kvc_warm.hip: the warm kernel alone,
+// marking k_eff = kWarmMiss where it gives up; kvc_fit.hip: the whole refit, the full
+// eigensolver finishing the marked matrices).
+hipError_t launch_refit_warm_kernel(const double* G, int M, int d, int r, double energy,
+                                    const float* W_prev, float* W_out, int32_t* k_eff,
+                                    int32_t* warm, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+hipError_t launch_refit_warm(const double* G, int M, int d, int r, double energy,
+                             const float* W_prev, float* W_out, int32_t* k_eff, int32_t* warm,
+                             hipStream_t st);
 // Error measures (kvc_metrics.hip): per-segment float64 sums of (X - R)^2 and R^2 through
 // chunk partials (2 doubles per segment and 256-token chunk), and the rank-error curve.
 int segment_error_chunks(int T);

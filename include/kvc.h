@@ -349,6 +349,33 @@ size_t kvc_project_workspace_bytes(int M, int d, int r, int dtype);
 kvc_status kvc_project(const void* delta, int M, int T, int d, int dtype, const float* W, int r,
                        float* U_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Warm-started refit for the growing context (same passages as the streaming fit): after
+ * rows were appended and G accumulated, the new anchor is found starting from the previous
+ * W instead of from scratch.  Results as kvc_fit_from_gram (W = the top-r eigenvectors of G
+ * as rows with the canonical sign, k_eff exact for the given G), found by
+ *   Q0 = [W_prev^T, 48 - r fixed directions orthogonal to it], then at most three passes of
+ *   Z = G Q (first G Q0), Q = Cholesky-QR(Z), Rayleigh-Ritz on Q^T G Q (48 x 48, float64);
+ * the Ritz vectors are kept when each residual |G x - rho x| is within 2^-28 of the
+ * Gershgorin bound of G and they are orthonormal to 1e-10, and k_eff is kept when the Ritz
+ * values prove it (lower bound: Ky Fan; upper bound: the residual and the energy left outside
+ * the Ritz block; k_eff <= r).  Every other matrix (no convergence, k_eff not proven or above
+ * r, a zero G) is solved by the kvc_fit_from_gram path, so the outputs always meet that
+ * contract; r > 32 takes that path for every matrix.
+ *   G         : [M,d,d] float64 (lower triangle read), as for kvc_fit_from_gram
+ *   W_prev    : [M,r,d] float32, the previous W (e.g. the last kvc_fit_from_gram or
+ *               kvc_refit_warm output for the same r); any values are allowed: a poor start
+ *               only sends the matrix to the full solve
+ *   W_out     : [M,r,d] float32; may be the same buffer as W_prev (each matrix's W_prev is
+ *               read before its W_out is written)
+ *   k_eff_out : [M] int32
+ *   warm_out  : [M] int32 or NULL: 1 where the warm result was kept, 0 where the full solve ran
+ * No workspace.  Errors as for kvc_fit_from_gram.
+ * ------------------------------------------------------------------------------------- */
+kvc_status kvc_refit_warm(const double* G, int M, int d, int r, double energy,
+                          const float* W_prev, float* W_out, int32_t* k_eff_out,
+                          int32_t* warm_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

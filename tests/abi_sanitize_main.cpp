@@ -86,6 +86,12 @@ int main() {
   expect(kvc_fit_from_gram(reinterpret_cast<const double*>(P), 4, 128, 200, 0.9, Fo, K32,
                            nullptr, nullptr),
          KVC_ERR_ARG, "fit_from_gram: r > d");
+  expect(kvc_refit_warm(reinterpret_cast<const double*>(P), 4, 128, 0, 0.9, F, Fo, K32, nullptr,
+                        nullptr),
+         KVC_ERR_ARG, "refit_warm: r = 0");
+  expect(kvc_refit_warm(reinterpret_cast<const double*>(P), 4, 128, 32, 0.9, nullptr, Fo, K32,
+                        nullptr, nullptr),
+         KVC_ERR_ARG, "refit_warm: no W_prev");
   expect(kvc_gram_accumulate(P, 4, -3, 128, KVC_BF16, reinterpret_cast<double*>(P), P, 1 << 30,
                              nullptr),
          KVC_ERR_ARG, "gram: negative T");

@@ -13,7 +13,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 OTHER = ["kvc_correct.o", "kvc_correct_general.o", "kvc_fit.o", "kvc_rank.o", "kvc_metrics.o",
-         "kvc_anchor_pool.o"]
+         "kvc_anchor_pool.o", "kvc_warm.o"]
 
 
 def build_and_run() -> str:

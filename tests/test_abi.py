@@ -139,6 +139,16 @@ def test_streaming_fit_rejects_bad_arguments():
         a.update(kw)
         assert lib.kvc_fit_from_gram(*a.values()) == status, (kw, lib.kvc_last_error())
     assert lib.kvc_fit_from_gram(*dict(base, M=0, G=None, W=None, k=None).values()) == 0
+    # kvc_refit_warm(G, M, d, r, energy, W_prev, W_out, k, warm, stream)
+    base = dict(G=FAKE, M=4, d=128, r=32, energy=0.9, Wp=FAKE, W=FAKE, k=FAKE, warm=None,
+                st=None)
+    for kw, status in [(dict(r=0), 1), (dict(r=129), 1), (dict(energy=0.0), 1), (dict(d=96), 2),
+                       (dict(G=None), 1), (dict(Wp=None), 1), (dict(W=None), 1),
+                       (dict(k=None), 1), (dict(warm=FAKE + 2), 1), (dict(G=FAKE + 4), 1)]:
+        a = dict(base)
+        a.update(kw)
+        assert lib.kvc_refit_warm(*a.values()) == status, (kw, lib.kvc_last_error())
+    assert lib.kvc_refit_warm(*dict(base, M=0, G=None, Wp=None, W=None, k=None).values()) == 0
     # kvc_project(delta, M, T, d, dtype, W, r, U, ws, ws_bytes, stream)
     base = dict(delta=FAKE, M=4, T=64, d=128, dtype=0, W=FAKE, r=32, U=FAKE, ws=None, nb=0,
                 st=None)
