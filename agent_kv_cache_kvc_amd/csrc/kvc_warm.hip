@@ -51,8 +51,24 @@ constexpr int kWarmQS = 50;  // row stride (doubles) of the n x 48 block in LDS
 constexpr int kWarmSS = 49;  // row stride of the 48 x 48 block
 constexpr int kWarmMaxIt = 3;
 constexpr int kWarmRpl = kWarmM / 16;  // rows per lane of a 48-long vector (16 lanes)
+constexpr int kWarmNW = 8;             // waves of the largest workgroup (d = 128)
 
 typedef double double4v __attribute__((ext_vector_type(4)));
+
+// LDS of the refit (one matrix per workgroup).  The phases below are separate functions
+// (not inlined): each gets its own register allocation, and they hand their results to
+// each other through these arrays.
+extern __shared__ __align__(16) double w_lds[];  // QB [D][kWarmQS], then SM [48][kWarmSS]
+__shared__ double w_red[2 * kWarmNW];
+__shared__ double w_dvec[kWarmM], w_evec[kWarmM], w_tau[kWarmM], w_dsc[kWarmM], w_rdg[kWarmM];
+__shared__ __align__(16) double w_vs[kWarmM], w_ws[kWarmM];
+__shared__ __align__(16) float w_df[kWarmM], w_e2s[kWarmM];
+__shared__ float w_lam[kEigMaxR];
+__shared__ double w_col[kWarmNW][kEigMaxR];
+__shared__ double w_res2[kEigMaxR], w_rho[kEigMaxR];
+__shared__ double w_amax[kWarmNW][kEigMaxR];
+__shared__ int w_aidx[kWarmNW][kEigMaxR];
+__shared__ int w_flag[2];
 
 __device__ __forceinline__ double4v mfma64(double a, double b, double4v c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -68,27 +84,27 @@ __device__ __forceinline__ double warm_pattern(int i, int j) {
 }
 
 template <int NW>
-__device__ __forceinline__ double wg_sum(double v, double* red) {
+__device__ __forceinline__ double wg_sum(double v) {
   v = wave_sum_d(v);
   __syncthreads();
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  if (threadIdx.x % kWave == 0) w_red[threadIdx.x / kWave] = v;
   __syncthreads();
   double s = 0.0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) s += red[w];
+  for (int w = 0; w < NW; ++w) s += w_red[w];
   return s;
 }
 
 template <int NW>
-__device__ __forceinline__ double wg_max(double v, double* red) {
+__device__ __forceinline__ double wg_max(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   __syncthreads();
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  if (threadIdx.x % kWave == 0) w_red[threadIdx.x / kWave] = v;
   __syncthreads();
-  double s = red[0];
+  double s = w_red[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) s = fmax(s, red[w]);
+  for (int w = 1; w < NW; ++w) s = fmax(s, w_red[w]);
   return s;
 }
 
@@ -100,138 +116,107 @@ __device__ __forceinline__ void tri_ij(int e, int n, int& i, int& j) {
   j = a + e;
 }
 
-}  // namespace
-
+// G fragment for the A operand: lane (g, i0) of wave w holds G[16 w + i0][4 kb + g]; the lower
+// triangle of G defines the symmetric matrix
 template <int D>
-__global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
-    const double* __restrict__ G, const float* __restrict__ W_prev, int r, double energy,
-    float* __restrict__ W_out, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ warm_out) {
-  constexpr int NW = D / 16, NTH = kWave * NW, KB = D / 4;
-  constexpr int MQ = kWarmM, QS = kWarmQS, SS = kWarmSS, NTRI = MQ * (MQ + 1) / 2;
-  constexpr int OWN = (NTRI + NTH - 1) / NTH;  // upper-triangle elements per thread
-  constexpr int RPL = kWarmRpl;
-  extern __shared__ __align__(16) double lds[];
-  double* QB = lds;           // [D][QS]: Q0, Z, Q, then G Q
-  double* SM = lds + D * QS;  // [MQ][SS]: Gram, Cholesky factor, H, reflectors, Y, X^T G X
-  __shared__ double red[2 * NW];
-  __shared__ double dvec[MQ], evec[MQ], tauv[MQ], vs[MQ], wsv[MQ], dsc[MQ], rdg[MQ];
-  __shared__ __align__(16) float df[MQ], e2s[MQ];
-  __shared__ float lamf[kEigMaxR];
-  __shared__ double colred[NW][kEigMaxR];
-  __shared__ double res2[kEigMaxR], rho[kEigMaxR];
-  __shared__ int s_flag[2];
-  __shared__ double s_amax[NW][kEigMaxR];
-  __shared__ int s_aidx[NW][kEigMaxR];
+__device__ __forceinline__ double g_at(const double* Gm, int kb, int w, int g, int i0) {
+  const int row = 16 * w + i0, col = 4 * kb + g;
+  return Gm[row >= col ? row * D + col : col * D + row];
+}
 
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int w = tid / kWave, l = tid % kWave, g = l / 16, i0 = l % 16;
-  const double* Gm = G + (size_t)m * D * D;
-  const int NC = (r + 15) / 16;  // 16-column tiles of the Ritz block (1 or 2)
-
-  // G fragments for the A operand: lane (g, i0) of wave w holds G[16 w + i0][4 kb + g]; the
-  // lower triangle of G defines the symmetric matrix
-  auto g_at = [&](int kb, int w, int g, int i0) {
-    const int row = 16 * w + i0, col = 4 * kb + g;
-    return Gm[row >= col ? row * D + col : col * D + row];
-  };
-  // acc[J] = G Q for the three 16-column tiles, Q from QB (B operand: row 4 kb + g).  G is
-  // read again for every product (L2), so its 32 fragments live only here; the B operands
-  // are read two k-steps at a time (the memory clobber keeps the compiler from hoisting
-  // every LDS read of the loop ahead of the MFMAs)
-  auto product = [&](double4v (&acc)[3], int w, int g, int i0) {
-    double gA[KB];
+// acc[J] = G B for the first nt 16-column tiles of the block B in QB (B operand: row
+// 4 kb + g).  G is read from global memory (L2) for every product, eight fragments at a time
+// with the next eight in flight; the B operands are read two k-steps at a time (the memory
+// clobber keeps the compiler from hoisting every LDS read of the loop ahead of the MFMAs).
+template <int D>
+__device__ __forceinline__ void product(const double* Gm, double4v* acc, int nt) {
+  constexpr int KB = D / 4, NG = KB / 8, QS = kWarmQS;
+  const int w = threadIdx.x / kWave, g = (threadIdx.x % kWave) / 16, i0 = threadIdx.x % 16;
+  const double* QB = w_lds;
+  double gA[2][8];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) gA[kb] = g_at(kb, w, g, i0);
+  for (int u = 0; u < 8; ++u) gA[0][u] = g_at<D>(Gm, u, w, g, i0);
 #pragma unroll
-    for (int J = 0; J < 3; ++J) acc[J] = double4v{0.0, 0.0, 0.0, 0.0};
+  for (int J = 0; J < 3; ++J)
+    if (J < nt) acc[J] = double4v{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int k2 = 0; k2 < KB; k2 += 2) {
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + 1 < NG) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) gA[(gi + 1) & 1][u] = g_at<D>(Gm, 8 * (gi + 1) + u, w, g, i0);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 8; k2 += 2) {
+      const int kb = 8 * gi + k2;
       double b[2][3];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int J = 0; J < 3; ++J) b[u][J] = QB[(4 * (k2 + u) + g) * QS + 16 * J + i0];
+        for (int J = 0; J < 3; ++J)
+          b[u][J] = J < nt ? QB[(4 * (kb + u) + g) * QS + 16 * J + i0] : 0.0;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int J = 0; J < 3; ++J) acc[J] = mfma64(gA[k2 + u], b[u][J], acc[J]);
+        for (int J = 0; J < 3; ++J)
+          if (J < nt) acc[J] = mfma64(gA[gi & 1][k2 + u], b[u][J], acc[J]);
       asm volatile("" ::: "memory");
     }
-  };
+  }
+}
 
-  // SM tiles (I, J), I <= J, of P^T R summed over the waves in order: each wave's part is the
-  // product of its 16 rows of P and R (both in the result layout), three tiles at a time
-  auto sym_tiles_to_sm = [&](const double4v (&P)[3], const double4v (&R)[3], int w, int g,
-                             int i0) {
+// SM tiles (I, J), I <= J, of P^T R summed over the waves in order: each wave's part is the
+// product of its 16 rows of P and R (both in the result layout), three tiles at a time.
+template <int D>
+__device__ __forceinline__ void sym_tiles_to_sm(const double4v (&P)[3], const double4v (&R)[3]) {
+  constexpr int NW = D / 16, SS = kWarmSS;
+  const int w = threadIdx.x / kWave, g = (threadIdx.x % kWave) / 16, i0 = threadIdx.x % 16;
+  double* SM = w_lds + D * kWarmQS;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      double4v part[3];
+  for (int half = 0; half < 2; ++half) {
+    double4v part[3];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int t = 3 * half + q;  // tiles (0,0) (0,1) (0,2) | (1,1) (1,2) (2,2)
-        const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
-        part[q] = double4v{0.0, 0.0, 0.0, 0.0};
+    for (int q = 0; q < 3; ++q) {
+      const int t = 3 * half + q;  // tiles (0,0) (0,1) (0,2) | (1,1) (1,2) (2,2)
+      const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
+      part[q] = double4v{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) part[q] = mfma64(P[I][v], R[J][v], part[q]);
-      }
-      for (int ww = 0; ww < NW; ++ww) {
-        if (w == ww) {
+      for (int v = 0; v < 4; ++v) part[q] = mfma64(P[I][v], R[J][v], part[q]);
+    }
+    for (int ww = 0; ww < NW; ++ww) {
+      if (w == ww) {
 #pragma unroll
-          for (int q = 0; q < 3; ++q) {
-            const int t = 3 * half + q;
-            const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
+        for (int q = 0; q < 3; ++q) {
+          const int t = 3 * half + q;
+          const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              double* p = SM + (16 * I + g + 4 * v) * SS + 16 * J + i0;
-              *p = (ww == 0 ? 0.0 : *p) + part[q][v];
-            }
+          for (int v = 0; v < 4; ++v) {
+            double* p = SM + (16 * I + g + 4 * v) * SS + 16 * J + i0;
+            *p = (ww == 0 ? 0.0 : *p) + part[q][v];
           }
         }
-        __syncthreads();
       }
+      __syncthreads();
     }
-  };
-
-  // ---- statistics of G: |G|_F^2, trace, Gershgorin bound
-  double ss = 0.0, ra = 0.0;
-#pragma unroll 8
-  for (int kb = 0; kb < KB; ++kb) {
-    const double gv = g_at(kb, w, g, i0);
-    ss = fma(gv, gv, ss);
-    ra += fabs(gv);
   }
-  ra += __shfl_xor(ra, 16, 64);  // the row's four column groups
-  ra += __shfl_xor(ra, 32, 64);
-  const double gf2 = wg_sum<NW>(ss, red);
-  const double gersh = wg_max<NW>(ra, red);
-  const double trace = wg_sum<NW>(tid < D ? Gm[tid * D + tid] : 0.0, red);
-  bool miss = !(trace > 0.0) || !(gf2 < 1e300) || !(gersh < 1e300) || !(trace < 1e300);
+}
 
-  // ---- Q0 = [W_prev^T, E], E orthogonal to the rows of W_prev
-  const int ne = MQ - r;
-  if (!miss) {
-    for (int e = tid; e < MQ * D; e += NTH) {
-      const int j = e / D, i = e - j * D;
-      QB[i * QS + j] = j < r ? (double)W_prev[((size_t)m * r + j) * D + i] : warm_pattern(i, j);
-    }
-    __syncthreads();
-    for (int e = tid; e < r * ne; e += NTH) {  // C = W_prev E  (r x ne) -> SM
-      const int a = e / ne, b = e - a * ne;
-      double c = 0.0;
-#pragma unroll 4
-      for (int i = 0; i < D; ++i) c = fma(QB[i * QS + a], QB[i * QS + r + b], c);
-      SM[a * SS + b] = c;
-    }
-    __syncthreads();
-    for (int e = tid; e < D * ne; e += NTH) {  // E -= W_prev^T C
-      const int i = e / ne, b = e - i * ne;
-      double v = QB[i * QS + r + b];
-      for (int a = 0; a < r; ++a) v = fma(-QB[i * QS + a], SM[a * SS + b], v);
-      QB[i * QS + r + b] = v;
-    }
-    __syncthreads();
-  }
-
+// ---- phase 1: Z = G B with B the block in QB, then Cholesky QR of Z into QB (one pass, a
+//      second when the first factor's smallest pivot is below 1e-4).  Returns 0 when Z is
+//      numerically rank-deficient (uniform).
+template <int D>
+__device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
+  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  constexpr int NTRI = MQ * (MQ + 1) / 2, OWN = (NTRI + NTH - 1) / NTH;
+  const int tid = threadIdx.x, w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
+  double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  double4v acc[3];
+  product<D>(Gm, acc, 3);
+  __syncthreads();  // every wave has read QB as a B operand
+#pragma unroll
+  for (int J = 0; J < 3; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) QB[(16 * w + g + 4 * v) * QS + 16 * J + i0] = acc[J][v];
   int own_i[OWN], own_j[OWN];
 #pragma unroll
   for (int u = 0; u < OWN; ++u) {
@@ -239,178 +224,210 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     if (e < NTRI) tri_ij(e, MQ, own_i[u], own_j[u]);
     else { own_i[u] = -1; own_j[u] = -1; }
   }
-
-  double4v acc[3];   // the current block in the result layout (Z, then Q)
-  double4v yacc[3];  // G Q
-  if (!miss) {  // Z = G Q0
-    int tq = threadIdx.x;
-    asm volatile("" : "+v"(tq));
-    product(acc, tq / kWave, (tq % kWave) / 16, tq % 16);
-  }
-  bool done = false;
-  int k_cert = -1;
-#pragma unroll 1
-  for (int it = 0; it < kWarmMaxIt && !miss && !done; ++it) {
-    // the lane coordinates again behind an opaque move: addresses derived from them are
-    // formed inside each phase instead of being held in registers across the whole pass
-    int tq = threadIdx.x;
-    asm volatile("" : "+v"(tq));
-    const int tid = tq, w = tq / kWave, l = tq % kWave, g = l / 16, i0 = l % 16;
-    // ---- Cholesky QR of Z into QB (the first pass stores Z = G Q0; later passes find G Q
-    //      there already, each wave in its own rows)
-    __syncthreads();  // every wave has read QB as a B operand
-#pragma unroll
-    for (int J = 0; J < 3; ++J)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        double* p = QB + (16 * w + g + 4 * v) * QS + 16 * J + i0;
-        if (it == 0) *p = acc[J][v];
-        else acc[J][v] = *p;
-      }
-    for (int pass = 0; pass < 2; ++pass) {
-      // S = Z^T Z: each wave's 16 rows, the upper 16 x 16 tiles (I <= J), summed over the
-      // waves in order into SM (three tiles at a time)
-      sym_tiles_to_sm(acc, acc, w, g, i0);
-      // unit diagonal: S' = D S D with D = diag(S)^-1/2
-      if (tid < MQ) {
-        const double sd = SM[tid * SS + tid];
-        dsc[tid] = sd > 0.0 && sd < 1e300 ? 1.0 / sqrt(sd) : 0.0;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < OWN; ++u)
-        if (own_i[u] >= 0) SM[own_i[u] * SS + own_j[u]] *= dsc[own_i[u]] * dsc[own_j[u]];
-      __syncthreads();
-      // right-looking Cholesky on the upper triangle: row k stays U[k][j] = R[k][k] R[k][j]
-      #pragma unroll 1
-      for (int k = 0; k < MQ; ++k) {
-        const double inv = 1.0 / SM[k * SS + k];
-#pragma unroll
-        for (int u = 0; u < OWN; ++u) {
-          const int i = own_i[u], j = own_j[u];
-          if (i > k) SM[i * SS + j] -= SM[k * SS + i] * SM[k * SS + j] * inv;
-        }
-        __syncthreads();
-      }
-      // R = rows of U scaled by 1 / sqrt(U[k][k]); the smallest pivot decides the second pass
-      double pmin = 1.0;
-      if (tid < MQ) {
-        const double pv = SM[tid * SS + tid];
-        pmin = pv;
-        rdg[tid] = pv > 0.0 && pv < 1e300 ? 1.0 / sqrt(pv) : 0.0;
-      }
-      pmin = -wg_max<NW>(-(pmin == pmin ? pmin : -1.0), red);  // NaN counts as a failure
-#pragma unroll
-      for (int u = 0; u < OWN; ++u)
-        if (own_i[u] >= 0) SM[own_i[u] * SS + own_j[u]] *= rdg[own_i[u]];
-      __syncthreads();
-      if (!(pmin > 1e-18)) { miss = true; break; }  // (uniform) numerically rank-deficient
-      // q R = z D, row by row: four lanes per row of Z in place (wave w: its own 16 rows)
-      {
-        const int row = tid / 4, p = tid % 4;
-        double* qr = QB + row * QS;
-        #pragma unroll 1
-        for (int j = 0; j < MQ; ++j) {
-          double s = 0.0;
-          for (int k = p; k < j; k += 4) s = fma(qr[k], SM[k * SS + j], s);
-          s += dpp_d<0xB1>(s);
-          s += dpp_d<0x4E>(s);
-          const double q = (qr[j] * dsc[j] - s) * rdg[j];
-          if (p == 0) qr[j] = q;
-        }
-      }
-#pragma unroll
-      for (int J = 0; J < 3; ++J)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[J][v] = QB[(16 * w + g + 4 * v) * QS + 16 * J + i0];
-      if (pmin >= 1e-4) break;  // (uniform) orthonormal to about 1e-12 after one pass
-      __syncthreads();          // SM is rewritten by the second pass
+  for (int pass = 0; pass < 2; ++pass) {
+    // S = Z^T Z (upper tiles) in SM
+    sym_tiles_to_sm<D>(acc, acc);
+    // unit diagonal: S' = D S D with D = diag(S)^-1/2
+    if (tid < MQ) {
+      const double sd = SM[tid * SS + tid];
+      w_dsc[tid] = sd > 0.0 && sd < 1e300 ? 1.0 / sqrt(sd) : 0.0;
     }
-    if (miss) break;
-    __syncthreads();  // Q complete in QB
-
-    // ---- G Q, and H = Q^T G Q (Q in the result layout again from QB)
-    product(yacc, w, g, i0);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < OWN; ++u)
+      if (own_i[u] >= 0) SM[own_i[u] * SS + own_j[u]] *= w_dsc[own_i[u]] * w_dsc[own_j[u]];
+    __syncthreads();
+    // right-looking Cholesky on the upper triangle: row k stays U[k][j] = R[k][k] R[k][j]
+#pragma unroll 1
+    for (int k = 0; k < MQ; ++k) {
+      const double inv = 1.0 / SM[k * SS + k];
+#pragma unroll
+      for (int u = 0; u < OWN; ++u) {
+        const int i = own_i[u], j = own_j[u];
+        if (i > k) SM[i * SS + j] -= SM[k * SS + i] * SM[k * SS + j] * inv;
+      }
+      __syncthreads();
+    }
+    // R = rows of U scaled by 1 / sqrt(U[k][k]); the smallest pivot decides the second pass
+    double pmin = 1.0;
+    if (tid < MQ) {
+      const double pv = SM[tid * SS + tid];
+      pmin = pv;
+      w_rdg[tid] = pv > 0.0 && pv < 1e300 ? 1.0 / sqrt(pv) : 0.0;
+    }
+    pmin = -wg_max<NW>(-(pmin == pmin ? pmin : -1.0));  // NaN counts as a failure
+#pragma unroll
+    for (int u = 0; u < OWN; ++u)
+      if (own_i[u] >= 0) SM[own_i[u] * SS + own_j[u]] *= w_rdg[own_i[u]];
+    __syncthreads();
+    if (!(pmin > 1e-18)) return 0;  // (uniform) numerically rank-deficient
+    // q R = z D, row by row: four lanes per row of Z in place (wave w: its own 16 rows)
+    {
+      const int row = tid / 4, p = tid % 4;
+      double* qr = QB + row * QS;
+#pragma unroll 1
+      for (int j = 0; j < MQ; ++j) {
+        double s = 0.0;
+        for (int k = p; k < j; k += 4) s = fma(qr[k], SM[k * SS + j], s);
+        s += dpp_d<0xB1>(s);
+        s += dpp_d<0x4E>(s);
+        const double q = (qr[j] * w_dsc[j] - s) * w_rdg[j];
+        if (p == 0) qr[j] = q;
+      }
+    }
+    if (pmin >= 1e-4) break;  // (uniform) orthonormal to about 1e-12 after one pass
 #pragma unroll
     for (int J = 0; J < 3; ++J)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[J][v] = QB[(16 * w + g + 4 * v) * QS + 16 * J + i0];
-    {
-      sym_tiles_to_sm(acc, yacc, w, g, i0);
-      // the lower triangle from the upper one
-      for (int e = tid; e < MQ * MQ; e += NTH) {
-        const int i = e / MQ, j = e - i * MQ;
-        if (i > j) SM[i * SS + j] = SM[j * SS + i];
-      }
-      __syncthreads();
-    }
+    __syncthreads();  // SM is rewritten by the second pass
+  }
+  __syncthreads();  // Q complete in QB
+  return 1;
+}
 
-    // ---- Householder tridiagonalisation of H (one wave, lane i = row i); the reflector of
-    //      step k stays in column k below the diagonal
-    if (w == 0) {
-      const int i = l;
-      const bool row_ok = i < MQ;
-      #pragma unroll 1
-      for (int k = 0; k < MQ - 2; ++k) {
-        const bool act = row_ok && i > k;
-        const double x = act ? SM[i * SS + k] : 0.0;
-        const double nx2 = wave_sum_d(x * x);
-        const double x0 = readlane_d(x, k + 1);
-        double alpha = 0.0, t = 0.0;
-        if (nx2 > 0.0) {
-          const double nx = sqrt(nx2);
-          alpha = x0 >= 0.0 ? -nx : nx;
-          t = 1.0 / (nx * (nx + fabs(x0)));  // 2 / v.v
+// ---- phase 2: H = Q^T G Q into SM (both triangles)
+template <int D>
+__device__ __attribute__((noinline)) void warm_rayleigh(const double* Gm) {
+  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  const int tid = threadIdx.x, w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
+  const double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  double4v yacc[3], acc[3];
+  product<D>(Gm, yacc, 3);
+#pragma unroll
+  for (int J = 0; J < 3; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[J][v] = QB[(16 * w + g + 4 * v) * QS + 16 * J + i0];
+  sym_tiles_to_sm<D>(acc, yacc);
+  for (int e = tid; e < MQ * MQ; e += NTH) {
+    const int i = e / MQ, j = e - i * MQ;
+    if (i > j) SM[i * SS + j] = SM[j * SS + i];
+  }
+  __syncthreads();
+}
+
+// ---- phase 3: the r largest eigenpairs of H (SM): Householder tridiagonalisation (one wave,
+//      lane i = row i; the reflector of step k stays in column k below the diagonal; a step
+//      touches the trailing columns in batches of eight, the row entries and the broadcast
+//      v, w of a batch read together; v and w vanish left of column k + 1 and p is cleared at
+//      and above row k), 8-point multisection for the eigenvalues, inverse iteration and
+//      back-transformation for the vectors; Y_r (48 x 16 NC, zero past r) into SM.
+template <int D>
+__device__ __attribute__((noinline)) void warm_small_eig(int r) {
+  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, SS = kWarmSS, RPL = kWarmRpl;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  double* SM = w_lds + D * kWarmQS;
+  const int NC = (r + 15) / 16;
+  if (w == 0) {
+    const int i = l;
+    const bool row_ok = i < MQ;
+    double* hrow = SM + (row_ok ? i : 0) * SS;
+#pragma unroll 1
+    for (int k = 0; k < MQ - 2; ++k) {
+      // x = column k below the diagonal, broadcast; H x over the trailing columns, with
+      // x.x and x.Hx in one reduction (H v = H x - alpha H e_{k+1}, so no second pass)
+      const bool act = row_ok && i > k;
+      const double x = act ? hrow[k] : 0.0;
+      const double hk1 = act ? hrow[k + 1] : 0.0;  // H[i][k+1]
+      if (row_ok) w_vs[i] = x;
+      const int jb0 = (k + 1) & ~7;  // first batch holding a trailing column
+      double pa = 0.0, pb = 0.0;
+#pragma unroll 2
+      for (int jb = jb0; jb < MQ; jb += 8) {
+        double h[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h[u] = hrow[jb + u];
+        const double2 v01 = *reinterpret_cast<const double2*>(w_vs + jb);
+        const double2 v23 = *reinterpret_cast<const double2*>(w_vs + jb + 2);
+        const double2 v45 = *reinterpret_cast<const double2*>(w_vs + jb + 4);
+        const double2 v67 = *reinterpret_cast<const double2*>(w_vs + jb + 6);
+        pa = fma(h[0], v01.x, fma(h[2], v23.x, fma(h[4], v45.x, fma(h[6], v67.x, pa))));
+        pb = fma(h[1], v01.y, fma(h[3], v23.y, fma(h[5], v45.y, fma(h[7], v67.y, pb))));
+      }
+      const double hx = act ? pa + pb : 0.0;
+      double s1 = x * x, s2 = x * hx;  // both sums over the wave, rows of 16 first
+      s1 = group_sum_d<16>(s1);
+      s2 = group_sum_d<16>(s2);
+      const double nx2 = ((readlane_d(s1, 0) + readlane_d(s1, 16)) + readlane_d(s1, 32)) +
+                         readlane_d(s1, 48);
+      const double xhx = ((readlane_d(s2, 0) + readlane_d(s2, 16)) + readlane_d(s2, 32)) +
+                         readlane_d(s2, 48);
+      const double x0 = readlane_d(x, k + 1), hx0 = readlane_d(hx, k + 1);
+      const double b00 = readlane_d(hk1, k + 1);  // H[k+1][k+1]
+      // |x| and t = 2 / v.v = 1 / (|x| (|x| + |x_0|)) from the hardware reciprocal square
+      // root and reciprocal, two Newton steps each (x = 0: alpha = t = 0, no change)
+      double y = __builtin_amdgcn_rsq(nx2);
+      y = y * fma(-0.5 * nx2 * y, y, 1.5);
+      y = y * fma(-0.5 * nx2 * y, y, 1.5);
+      const double nx = nx2 * y;
+      const double den = nx + fabs(x0);
+      double rd = __builtin_amdgcn_rcp(den);
+      rd = rd * fma(-den, rd, 2.0);
+      rd = rd * fma(-den, rd, 2.0);
+      const double alpha = nx2 > 0.0 ? (x0 >= 0.0 ? -nx : nx) : 0.0;
+      const double t = nx2 > 0.0 ? y * rd : 0.0;
+      const double v = i == k + 1 ? x0 - alpha : x;
+      const double p = act ? t * (hx - alpha * hk1) : 0.0;
+      const double K = 0.5 * t * t * (xhx - 2.0 * alpha * hx0 + alpha * alpha * b00);
+      const double wv = p - K * v;
+      if (row_ok) {
+        w_vs[i] = v;
+        w_ws[i] = wv;
+      }
+      if (act) {
+#pragma unroll 2
+        for (int jb = jb0; jb < MQ; jb += 8) {
+          double h[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) h[u] = hrow[jb + u];
+          double vv[8], ww[8];
+#pragma unroll
+          for (int u = 0; u < 8; u += 2) {
+            const double2 a = *reinterpret_cast<const double2*>(w_vs + jb + u);
+            const double2 b = *reinterpret_cast<const double2*>(w_ws + jb + u);
+            vv[u] = a.x; vv[u + 1] = a.y; ww[u] = b.x; ww[u + 1] = b.y;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) hrow[jb + u] = h[u] - (v * ww[u] + wv * vv[u]);
         }
-        const double v = i == k + 1 ? x0 - alpha : x;
-        if (row_ok) vs[i] = v;
-        double p = 0.0;
-        if (act) {
-          for (int j = k + 1; j < MQ; ++j) p = fma(SM[i * SS + j], vs[j], p);
-          p *= t;
-        }
-        const double K = 0.5 * t * wave_sum_d(v * p);
-        const double wv = p - K * v;
-        if (row_ok) wsv[i] = wv;
-        if (act) {
-          for (int j = k + 1; j < MQ; ++j) SM[i * SS + j] -= v * wsv[j] + wv * vs[j];
-          SM[i * SS + k] = v;
-        }
-        if (i == 0) {
-          dvec[k] = SM[k * SS + k];
-          evec[k] = alpha;
-          tauv[k] = t;
-        }
+        hrow[k] = v;
       }
       if (i == 0) {
-        dvec[MQ - 2] = SM[(MQ - 2) * SS + MQ - 2];
-        evec[MQ - 2] = SM[(MQ - 1) * SS + MQ - 2];
-        dvec[MQ - 1] = SM[(MQ - 1) * SS + MQ - 1];
-        evec[MQ - 1] = 0.0;
-        tauv[MQ - 2] = 0.0;
-        tauv[MQ - 1] = 0.0;
+        w_dvec[k] = SM[k * SS + k];
+        w_evec[k] = alpha;
+        w_tau[k] = t;
       }
     }
-    __syncthreads();
+    if (i == 0) {
+      w_dvec[MQ - 2] = SM[(MQ - 2) * SS + MQ - 2];
+      w_evec[MQ - 2] = SM[(MQ - 1) * SS + MQ - 2];
+      w_dvec[MQ - 1] = SM[(MQ - 1) * SS + MQ - 1];
+      w_evec[MQ - 1] = 0.0;
+      w_tau[MQ - 2] = 0.0;
+      w_tau[MQ - 1] = 0.0;
+    }
+  }
+  __syncthreads();
 
-    // ---- the r largest eigenvalues of the tridiagonal matrix (8-point multisection)
-    double glo = 0.0, ghi = 0.0;
-    if (tid < MQ) {
-      df[tid] = (float)dvec[tid];
-      e2s[tid] = tid >= 1 ? fmaxf((float)(evec[tid - 1] * evec[tid - 1]), 1e-36f) : 0.f;
-      const double rad = (tid > 0 ? fabs(evec[tid - 1]) : 0.0) + fabs(evec[tid]);
-      glo = dvec[tid] - rad;
-      ghi = dvec[tid] + rad;
-    }
-    const double hmax = wg_max<NW>(tid < MQ ? ghi : -1e300, red);
-    const double hmin = -wg_max<NW>(tid < MQ ? -glo : -1e300, red);
-    const double span = fmax(hmax - hmin, 1e-300);
-    const float lo_s = (float)(hmin - 1e-6 * span), hi_s = (float)(hmax + 1e-6 * span);
-    if (tid < 8 * r) {
-      const float lam = multisect<8, MQ>(MQ - 1 - tid / 8, lo_s, hi_s, df, e2s, tid % 8);
-      if (tid % 8 == 0) lamf[tid / 8] = lam;
-    }
-    __syncthreads();
+  // the r largest eigenvalues of the tridiagonal matrix (8-point multisection)
+  double glo = 0.0, ghi = 0.0;
+  if (tid < MQ) {
+    w_df[tid] = (float)w_dvec[tid];
+    w_e2s[tid] = tid >= 1 ? fmaxf((float)(w_evec[tid - 1] * w_evec[tid - 1]), 1e-36f) : 0.f;
+    const double rad = (tid > 0 ? fabs(w_evec[tid - 1]) : 0.0) + fabs(w_evec[tid]);
+    glo = w_dvec[tid] - rad;
+    ghi = w_dvec[tid] + rad;
+  }
+  const double hmax = wg_max<NW>(tid < MQ ? ghi : -1e300);
+  const double hmin = -wg_max<NW>(tid < MQ ? -glo : -1e300);
+  const double span = fmax(hmax - hmin, 1e-300);
+  const float lo_s = (float)(hmin - 1e-6 * span), hi_s = (float)(hmax + 1e-6 * span);
+  if (tid < 8 * r) {
+    const float lam = multisect<8, MQ>(MQ - 1 - tid / 8, lo_s, hi_s, w_df, w_e2s, tid % 8);
+    if (tid % 8 == 0) w_lam[tid / 8] = lam;
+  }
+  __syncthreads();
 
     // ---- inverse iteration (16 lanes per vector, RPL rows per lane), back-transformation,
     //      Y_r into SM after every reflector has been read
@@ -422,13 +439,13 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     for (int bt = 0; bt < (kEigMaxR + VPB - 1) / VPB; ++bt) {
       const int vec = bt * VPB + tid / 16;
       if (bt * VPB >= r) break;  // uniform
-      const double lam = vec < r ? (double)lamf[vec] : 0.0;
-      const double tiny = 1e-300 + 1e-16 * fmax(fabs((double)lamf[0]), 1e-300);
+      const double lam = vec < r ? (double)w_lam[vec] : 0.0;
+      const double tiny = 1e-300 + 1e-16 * fmax(fabs((double)w_lam[0]), 1e-300);
       double Rrp[RPL], Rc1[RPL], Rml[RPL], Ry[RPL];
       unsigned sw = 0;
       auto rhs0 = [&](int j) { return 1.0 + 0.1 * (double)((j * (2 * vec + 3)) % 7); };
       {
-        double cb = dvec[0] - lam, cc = evec[0], ry = rhs0(0);
+        double cb = w_dvec[0] - lam, cc = w_evec[0], ry = rhs0(0);
 #pragma unroll 1
         for (int b = 0; b < 16; ++b) {
           const bool own = L == b;
@@ -436,13 +453,15 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
           for (int u = 0; u < RPL; ++u) {
             const int j = b * RPL + u;
             if (j < MQ - 1) {
-              const double na = evec[j], nb = dvec[j + 1] - lam;
-              const double nc = j + 1 < MQ - 1 ? evec[j + 1] : 0.0;
+              const double na = w_evec[j], nb = w_dvec[j + 1] - lam;
+              const double nc = j + 1 < MQ - 1 ? w_evec[j + 1] : 0.0;
               const double ny = rhs0(j + 1);
               const bool swp = fabs(na) > fabs(cb);
               const double piv = swp ? na : cb, oth = swp ? cb : na;
               const double pg = fabs(piv) > tiny ? piv : (piv < 0.0 ? -tiny : tiny);
-              const double rp = 1.0 / pg;
+              double rp = __builtin_amdgcn_rcp(pg);  // 1 / pivot, two Newton steps
+              rp = rp * fma(-pg, rp, 2.0);
+              rp = rp * fma(-pg, rp, 2.0);
               const double mlt = oth * rp;
               const double c1 = swp ? nb : cc, yj = swp ? ny : ry;
               const double nry = swp ? ry - mlt * ny : ny - mlt * ry;
@@ -468,7 +487,7 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
 #pragma unroll
           for (int u = RPL - 1; u >= 0; --u) {
             const int j = b * RPL + u;
-            const double c2 = ((sw >> u) & 1u) && j + 1 < MQ - 1 ? evec[j + 1] : 0.0;
+            const double c2 = ((sw >> u) & 1u) && j + 1 < MQ - 1 ? w_evec[j + 1] : 0.0;
             const double xj = (Ry[u] - Rc1[u] * x1 - c2 * x2) * Rrp[u];
             if (own) { Ry[u] = xj; sq += xj * xj; }
             x2 = x1;
@@ -517,7 +536,7 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
           vk[u] = j > k ? SM[j * SS + k] : 0.0;
           s = fma(vk[u], z[u], s);
         }
-        s = group_sum_d<16>(s) * tauv[k];
+        s = group_sum_d<16>(s) * w_tau[k];
 #pragma unroll
         for (int u = 0; u < RPL; ++u) z[u] = fma(-s, vk[u], z[u]);
       }
@@ -537,37 +556,48 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     }
     __syncthreads();
 
-    // ---- X = Q Y_r; then G Q over Q in QB (each wave its own rows) and G X = (G Q) Y_r
-    double4v xacc[2], gxacc[2];  // result layout; tile 1 only when r > 16
+}
+
+// ---- phase 4: X = Q Y_r (written over the first r columns of Q in QB), G X, X^T G X and
+//      X^T X, the residuals, the decision (convergence; the effective rank proven from the
+//      Ritz values), and when accepted W.  Returns 0 (not converged), 1 (converged; *k_out
+//      holds k or -1 when it is not proven).
+template <int D>
+__device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, double energy,
+                                                    double gf2, double gersh, double trace,
+                                                    float* W_m, int* k_out) {
+  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave, g = l / 16, i0 = l % 16;
+  double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  const int NC = (r + 15) / 16;
+  double4v xacc[2], gxacc[2];  // result layout; tile 1 only when r > 16
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    xacc[c] = double4v{0.0, 0.0, 0.0, 0.0};
+    gxacc[c] = double4v{0.0, 0.0, 0.0, 0.0};
+  }
+  {
+    const double* arow = QB + (16 * w + i0) * QS + g;
+#pragma unroll
+    for (int kb = 0; kb < MQ / 4; ++kb) {
+      const double a = arow[4 * kb];
+      const double* brow = SM + (4 * kb + g) * SS + i0;
+      xacc[0] = mfma64(a, brow[0], xacc[0]);
+      if (NC > 1) xacc[1] = mfma64(a, brow[16], xacc[1]);
+      asm volatile("" ::: "memory");
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      xacc[c] = double4v{0.0, 0.0, 0.0, 0.0};
-      gxacc[c] = double4v{0.0, 0.0, 0.0, 0.0};
+      if (c >= NC) continue;
+      const int col = 16 * c + i0;
+      if (col >= r) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) QB[(16 * w + g + 4 * v) * QS + col] = xacc[c][v];
     }
-    {
-      const double* arow = QB + (16 * w + i0) * QS + g;
-#pragma unroll
-      for (int kb = 0; kb < MQ / 4; ++kb) {
-        const double a = arow[4 * kb];
-        const double* brow = SM + (4 * kb + g) * SS + i0;
-        xacc[0] = mfma64(a, brow[0], xacc[0]);
-        if (NC > 1) xacc[1] = mfma64(a, brow[16], xacc[1]);
-        asm volatile("" ::: "memory");
-      }
-#pragma unroll
-      for (int J = 0; J < 3; ++J)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) QB[(16 * w + g + 4 * v) * QS + 16 * J + i0] = yacc[J][v];
-#pragma unroll
-      for (int kb = 0; kb < MQ / 4; ++kb) {
-        const double a = arow[4 * kb];
-        const double* brow = SM + (4 * kb + g) * SS + i0;
-        gxacc[0] = mfma64(a, brow[0], gxacc[0]);
-        if (NC > 1) gxacc[1] = mfma64(a, brow[16], gxacc[1]);
-        asm volatile("" ::: "memory");
-      }
-    }
-    __syncthreads();  // every wave has read Y_r from SM
+  }
+  __syncthreads();  // X complete in QB; every wave has read Y_r from SM
+  product<D>(Gm, gxacc, NC);
     // X^T G X (SM[0 ..]) and X^T X (SM[1024 ..]), NC x NC tiles of stride 32, each summed
     // over the waves in order
 #pragma unroll
@@ -602,14 +632,14 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
         __syncthreads();
       }
     }
-    if (tid < r) rho[tid] = SM[tid * 32 + tid];
+    if (tid < r) w_rho[tid] = SM[tid * 32 + tid];
     __syncthreads();
     // residual of each Ritz vector: |G x_c - rho_c x_c|^2 over the rows, then the waves
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       if (c >= NC) continue;
       const int col = 16 * c + i0;
-      const double rc = col < r ? rho[col] : 0.0;
+      const double rc = col < r ? w_rho[col] : 0.0;
       double s = 0.0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -618,13 +648,13 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
       }
       s += __shfl_xor(s, 16, 64);
       s += __shfl_xor(s, 32, 64);
-      if (g == 0 && col < r) colred[w][col] = s;
+      if (g == 0 && col < r) w_col[w][col] = s;
     }
     __syncthreads();
     if (tid < r) {
       double s = 0.0;
-      for (int ww = 0; ww < NW; ++ww) s += colred[ww][tid];
-      res2[tid] = s;
+      for (int ww = 0; ww < NW; ++ww) s += w_col[ww][tid];
+      w_res2[tid] = s;
     }
     // orthonormality defect of X, |X^T G X|_F^2 and its off-diagonal part
     double dx = 0.0, af = 0.0, ff = 0.0;
@@ -636,58 +666,67 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
       af = fma(av, av, af);
       if (a != b) ff = fma(av, av, ff);
     }
-    const double defect = wg_max<NW>(dx, red);
-    const double a_f2 = wg_sum<NW>(af, red);
-    const double f_f2 = wg_sum<NW>(ff, red);
+    const double defect = wg_max<NW>(dx);
+    const double a_f2 = wg_sum<NW>(af);
+    const double f_f2 = wg_sum<NW>(ff);
 
-    // ---- decision (thread 0, then shared)
-    if (tid == 0) {
-      int ok = 0, kk = -1;
-      double rmax = 0.0, rsum = 0.0;
-      for (int c = 0; c < r; ++c) {
-        rmax = fmax(rmax, res2[c] == res2[c] ? res2[c] : 1e300);
-        rsum += res2[c];
-      }
-      const bool conv = defect <= 1e-10 && sqrt(rmax) <= 0x1p-28 * gersh;
+    // ---- decision (wave 0, lane c for Ritz pair c, then shared): convergence, then the
+    //      effective rank from the Ritz values (see the header)
+    if (w == 0) {
+      const int c = l;
+      const bool on = c < r;
+      const double r2 = on ? w_res2[c] : 0.0;
+      const double rc = on ? w_rho[c] : 0.0;
+      double rmx = on ? (r2 == r2 ? r2 : 1e300) : 0.0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) rmx = fmax(rmx, __shfl_xor(rmx, off, 64));
+      const double rsum = wave_sum_d(r2);
+      const bool conv = defect <= 1e-8 && sqrt(rmx) <= 0x1p-28 * gersh;  // uniform
+      int kk = -1;
       if (conv) {
-        ok = 1;
-        // the effective rank from the Ritz vectors (see the header)
-        double rs[kEigMaxR];
-        for (int c = 0; c < r; ++c) {  // descending insertion sort
-          double x = rho[c];
-          int p = c;
-          while (p > 0 && rs[p - 1] < x) { rs[p] = rs[p - 1]; --p; }
-          rs[p] = x;
+        double* rsd = w_col[0];  // the Ritz values, descending
+        double* csum = w_col[1];  // their running sums
+        int rank = 0;
+        for (int c2 = 0; c2 < r; ++c2) {
+          const double o = w_rho[c2];
+          rank += (o > rc) || (o == rc && c2 < c);
         }
+        if (on) rsd[rank] = rc;
+        const double sv = on ? rsd[c] : 0.0;
+        double cum = sv;  // C_{c+1}: the c + 1 largest
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const double o = __shfl_up(cum, off, 64);
+          if (c >= off) cum += o;
+        }
+        if (on) csum[c] = cum;
         const double unit = (3.0 * r * defect + 1e-12) * gersh;
         const double need_hi = energy * trace * (1.0 + 1e-13);
         const double need_lo = energy * trace * (1.0 - 1e-13);
         const double mu = sqrt(fmax(gf2 - a_f2, 0.0) + (1e-13 + 4.0 * r * defect) * gf2);
         const double bres = sqrt(rsum) + 2.0 * sqrt(f_f2) + 2.0 * r * defect * gersh;
-        double cum = 0.0;
-        for (int k = 1; k <= r; ++k) {
-          cum += rs[k - 1];
-          if (cum - k * unit >= need_hi) { kk = k; break; }
-        }
-        if (kk > 0) {
-          const int j = kk - 1;
-          double best = -1e300;
-          for (int i = 0; i <= j; ++i) {
-            double c = 0.0;
-            for (int q = 0; q < j - i; ++q) c += rs[q];
-            best = fmax(best, c + i * mu);
-          }
-          const double up = best + sqrt((double)j) * bres + j * unit;
-          if (!(up < need_lo)) kk = -1;
+        const unsigned long long bal = __ballot(on && cum - (c + 1) * unit >= need_hi);
+        if (bal) {
+          const int k = __ffsll((long long)bal);  // the first lane that proves C_k >= need, + 1
+          const int j = k - 1;
+          double cand = -1e300;
+          if (c <= j) cand = (j - c == 0 ? 0.0 : csum[j - c - 1]) + c * mu;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) cand = fmax(cand, __shfl_xor(cand, off, 64));
+          const double up = cand + sqrt((double)j) * bres + j * unit;
+          kk = up < need_lo ? k : -1;
         }
       }
-      s_flag[0] = ok;
-      s_flag[1] = kk;
+      if (l == 0) {
+        w_flag[0] = conv ? 1 : 0;
+        w_flag[1] = kk;
+      }
     }
     __syncthreads();
-    if (s_flag[0]) {  // (uniform) converged: the Ritz vectors are the rows of W
-      done = true;
-      k_cert = s_flag[1];
+    if (!w_flag[0]) return 0;  // (uniform) not converged
+    {
+      const int k_cert = w_flag[1];
+      *k_out = k_cert;
       if (k_cert >= 0) {
         // canonical sign: the largest |entry| of each row positive (the first one on ties)
 #pragma unroll
@@ -709,9 +748,9 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
             if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; bval = ov; }
           }
           if (g == 0 && col < r) {
-            s_amax[w][col] = best;
-            s_aidx[w][col] = bidx;
-            colred[w][col] = bval;
+            w_amax[w][col] = best;
+            w_aidx[w][col] = bidx;
+            w_col[w][col] = bval;
           }
         }
         __syncthreads();
@@ -719,11 +758,11 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
           double best = -1.0, bval = 0.0;
           int bidx = D;
           for (int ww = 0; ww < NW; ++ww) {
-            const double a = s_amax[ww][tid];
-            const int ix = s_aidx[ww][tid];
-            if (a > best || (a == best && ix < bidx)) { best = a; bidx = ix; bval = colred[ww][tid]; }
+            const double a = w_amax[ww][tid];
+            const int ix = w_aidx[ww][tid];
+            if (a > best || (a == best && ix < bidx)) { best = a; bidx = ix; bval = w_col[ww][tid]; }
           }
-          rho[tid] = bval < 0.0 ? -1.0 : 1.0;  // rho is no longer needed: it holds the sign
+          w_rho[tid] = bval < 0.0 ? -1.0 : 1.0;  // rho is no longer needed: it holds the sign
         }
         __syncthreads();
 #pragma unroll
@@ -731,27 +770,91 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
           if (c >= NC) continue;
           const int col = 16 * c + i0;
           if (col >= r) continue;
-          const double sg = rho[col];
+          const double sg = w_rho[col];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int row = 16 * w + g + 4 * v;
-            W_out[((size_t)m * r + col) * D + row] = (float)(sg * xacc[c][v]);
+            W_m[(size_t)col * D + row] = (float)(sg * xacc[c][v]);
           }
         }
       }
     }
-  }
+  return 1;
+}
 
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
+    const double* __restrict__ G, const float* __restrict__ W_prev, int r, double energy,
+    float* __restrict__ W_out, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ warm_out) {
+  constexpr int NW = D / 16, NTH = kWave * NW, KB = D / 4, MQ = kWarmM, QS = kWarmQS;
+  constexpr int SS = kWarmSS;
+  double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
+  const double* Gm = G + (size_t)m * D * D;
+
+  // ---- statistics of G: |G|_F^2, trace, Gershgorin bound
+  double ss = 0.0, ra = 0.0;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const double gv = g_at<D>(Gm, kb, w, g, i0);
+    ss = fma(gv, gv, ss);
+    ra += fabs(gv);
+  }
+  ra += __shfl_xor(ra, 16, 64);  // the row's four column groups
+  ra += __shfl_xor(ra, 32, 64);
+  const double gf2 = wg_sum<NW>(ss);
+  const double gersh = wg_max<NW>(ra);
+  const double trace = wg_sum<NW>(tid < D ? Gm[tid * D + tid] : 0.0);
+  const bool bad = !(trace > 0.0) || !(gf2 < 1e300) || !(gersh < 1e300) || !(trace < 1e300);
+
+  int k_cert = -1;
+  if (!bad) {  // (uniform)
+    // ---- Q0 = [W_prev^T, E], E orthogonal to the rows of W_prev
+    const int ne = MQ - r;
+    for (int e = tid; e < MQ * D; e += NTH) {
+      const int j = e / D, i = e - j * D;
+      QB[i * QS + j] = j < r ? (double)W_prev[((size_t)m * r + j) * D + i] : warm_pattern(i, j);
+    }
+    __syncthreads();
+    for (int e = tid; e < r * ne; e += NTH) {  // C = W_prev E  (r x ne) -> SM
+      const int a = e / ne, b = e - a * ne;
+      double c = 0.0;
+#pragma unroll 4
+      for (int i = 0; i < D; ++i) c = fma(QB[i * QS + a], QB[i * QS + r + b], c);
+      SM[a * SS + b] = c;
+    }
+    __syncthreads();
+    for (int e = tid; e < D * ne; e += NTH) {  // E -= W_prev^T C
+      const int i = e / ne, b = e - i * ne;
+      double v = QB[i * QS + r + b];
+      for (int a = 0; a < r; ++a) v = fma(-QB[i * QS + a], SM[a * SS + b], v);
+      QB[i * QS + r + b] = v;
+    }
+    __syncthreads();
+    // ---- passes: Z = G B, Cholesky QR, Rayleigh-Ritz, check; B for the next pass is the
+    //      Ritz vectors of this one and the remaining columns of its Q (left in QB)
+#pragma unroll 1
+    for (int it = 0; it < kWarmMaxIt; ++it) {
+      if (!warm_zchol<D>(Gm)) break;
+      warm_rayleigh<D>(Gm);
+      warm_small_eig<D>(r);
+      int kc = -1;
+      if (warm_check<D>(Gm, r, energy, gf2, gersh, trace, W_out + (size_t)m * r * D, &kc)) {
+        k_cert = kc;
+        break;
+      }
+    }
+  }
   if (tid == 0) {
-    const bool keep = done && k_cert >= 0;
-    k_eff_out[m] = keep ? k_cert : kWarmMiss;
-    if (warm_out) warm_out[m] = keep ? 1 : 0;
+    k_eff_out[m] = k_cert >= 0 ? k_cert : kWarmMiss;
+    if (warm_out) warm_out[m] = k_cert >= 0 ? 1 : 0;
   }
 }
 
-// G [M][D][D] (float64, lower triangle read), W_prev [M][r][D] -> W_out (rows of matrices
-// whose refit converged and whose k_eff is certain), k_eff_out (k, or kWarmMiss), warm_out
-// (1 / 0, may be null).
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -763,6 +866,9 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
+// G [M][D][D] (float64, lower triangle read), W_prev [M][r][D] -> W_out (rows of matrices
+// whose refit converged and whose k_eff is proven), k_eff_out (k, or kWarmMiss), warm_out
+// (1 / 0, may be null).
 hipError_t launch_refit_warm_kernel(const double* G, int M, int d, int r, double energy,
                                     const float* W_prev, float* W_out, int32_t* k_eff,
                                     int32_t* warm, hipStream_t st) {
