@@ -50,7 +50,6 @@ constexpr int kWarmM = 48;   // columns of the iterated block
 constexpr int kWarmQS = 50;  // row stride (doubles) of the n x 48 block in LDS
 constexpr int kWarmSS = 49;  // row stride of the 48 x 48 block
 constexpr int kWarmMaxIt = 3;
-constexpr int kWarmRpl = kWarmM / 16;  // rows per lane of a 48-long vector (16 lanes)
 constexpr int kWarmNW = 8;             // waves of the largest workgroup (d = 128)
 
 typedef double double4v __attribute__((ext_vector_type(4)));
@@ -164,20 +163,29 @@ __device__ __forceinline__ void product(const double* Gm, double4v* acc, int nt)
   }
 }
 
-// SM tiles (I, J), I <= J, of P^T R summed over the waves in order: each wave's part is the
-// product of its 16 rows of P and R (both in the result layout), three tiles at a time.
-template <int D>
-__device__ __forceinline__ void sym_tiles_to_sm(const double4v (&P)[3], const double4v (&R)[3]) {
-  constexpr int NW = D / 16, SS = kWarmSS;
+// upper tile t (row-major over I <= J) of an NT x NT grid of 16 x 16 tiles
+template <int NT>
+__device__ __forceinline__ void tile_ij(int t, int& I, int& J) {
+  int a = 0;
+  while (t >= NT - a) { t -= NT - a; ++a; }
+  I = a;
+  J = a + t;
+}
+
+// SM tiles (I, J), I <= J < NT, of P^T R summed over the waves in order: each wave's part is
+// the product of its 16 rows of P and R (both in the result layout), three tiles at a time.
+template <int D, int NT>
+__device__ __forceinline__ void sym_tiles_to_sm(const double4v* P, const double4v* R) {
+  constexpr int NW = D / 16, SS = kWarmSS, NTILE = NT * (NT + 1) / 2;
   const int w = threadIdx.x / kWave, g = (threadIdx.x % kWave) / 16, i0 = threadIdx.x % 16;
   double* SM = w_lds + D * kWarmQS;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int t0 = 0; t0 < NTILE; t0 += 3) {
     double4v part[3];
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const int t = 3 * half + q;  // tiles (0,0) (0,1) (0,2) | (1,1) (1,2) (2,2)
-      const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
+      int I, J;
+      tile_ij<NT>(t0 + q, I, J);
       part[q] = double4v{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int v = 0; v < 4; ++v) part[q] = mfma64(P[I][v], R[J][v], part[q]);
@@ -186,8 +194,8 @@ __device__ __forceinline__ void sym_tiles_to_sm(const double4v (&P)[3], const do
       if (w == ww) {
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          const int t = 3 * half + q;
-          const int I = t < 3 ? 0 : (t < 5 ? 1 : 2), J = t < 3 ? t : (t < 5 ? t - 2 : 2);
+          int I, J;
+          tile_ij<NT>(t0 + q, I, J);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             double* p = SM + (16 * I + g + 4 * v) * SS + 16 * J + i0;
@@ -203,18 +211,18 @@ __device__ __forceinline__ void sym_tiles_to_sm(const double4v (&P)[3], const do
 // ---- phase 1: Z = G B with B the block in QB, then Cholesky QR of Z into QB (one pass, a
 //      second when the first factor's smallest pivot is below 1e-4).  Returns 0 when Z is
 //      numerically rank-deficient (uniform).
-template <int D>
+template <int D, int MQ>
 __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
-  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  constexpr int NW = D / 16, NTH = kWave * NW, NT = MQ / 16, QS = kWarmQS, SS = kWarmSS;
   constexpr int NTRI = MQ * (MQ + 1) / 2, OWN = (NTRI + NTH - 1) / NTH;
   const int tid = threadIdx.x, w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
   double* QB = w_lds;
   double* SM = w_lds + D * QS;
   double4v acc[3];
-  product<D>(Gm, acc, 3);
+  product<D>(Gm, acc, NT);
   __syncthreads();  // every wave has read QB as a B operand
 #pragma unroll
-  for (int J = 0; J < 3; ++J)
+  for (int J = 0; J < NT; ++J)
 #pragma unroll
     for (int v = 0; v < 4; ++v) QB[(16 * w + g + 4 * v) * QS + 16 * J + i0] = acc[J][v];
   int own_i[OWN], own_j[OWN];
@@ -226,7 +234,7 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
   }
   for (int pass = 0; pass < 2; ++pass) {
     // S = Z^T Z (upper tiles) in SM
-    sym_tiles_to_sm<D>(acc, acc);
+    sym_tiles_to_sm<D, NT>(acc, acc);
     // unit diagonal: S' = D S D with D = diag(S)^-1/2
     if (tid < MQ) {
       const double sd = SM[tid * SS + tid];
@@ -277,7 +285,7 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
     }
     if (pmin >= 1e-4) break;  // (uniform) orthonormal to about 1e-12 after one pass
 #pragma unroll
-    for (int J = 0; J < 3; ++J)
+    for (int J = 0; J < NT; ++J)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[J][v] = QB[(16 * w + g + 4 * v) * QS + 16 * J + i0];
     __syncthreads();  // SM is rewritten by the second pass
@@ -287,19 +295,19 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
 }
 
 // ---- phase 2: H = Q^T G Q into SM (both triangles)
-template <int D>
+template <int D, int MQ>
 __device__ __attribute__((noinline)) void warm_rayleigh(const double* Gm) {
-  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  constexpr int NW = D / 16, NTH = kWave * NW, NT = MQ / 16, QS = kWarmQS, SS = kWarmSS;
   const int tid = threadIdx.x, w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
   const double* QB = w_lds;
   double* SM = w_lds + D * QS;
   double4v yacc[3], acc[3];
-  product<D>(Gm, yacc, 3);
+  product<D>(Gm, yacc, NT);
 #pragma unroll
-  for (int J = 0; J < 3; ++J)
+  for (int J = 0; J < NT; ++J)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[J][v] = QB[(16 * w + g + 4 * v) * QS + 16 * J + i0];
-  sym_tiles_to_sm<D>(acc, yacc);
+  sym_tiles_to_sm<D, NT>(acc, yacc);
   for (int e = tid; e < MQ * MQ; e += NTH) {
     const int i = e / MQ, j = e - i * MQ;
     if (i > j) SM[i * SS + j] = SM[j * SS + i];
@@ -313,9 +321,9 @@ __device__ __attribute__((noinline)) void warm_rayleigh(const double* Gm) {
 //      v, w of a batch read together; v and w vanish left of column k + 1 and p is cleared at
 //      and above row k), 8-point multisection for the eigenvalues, inverse iteration and
 //      back-transformation for the vectors; Y_r (48 x 16 NC, zero past r) into SM.
-template <int D>
+template <int D, int MQ>
 __device__ __attribute__((noinline)) void warm_small_eig(int r) {
-  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, SS = kWarmSS, RPL = kWarmRpl;
+  constexpr int NW = D / 16, NTH = kWave * NW, SS = kWarmSS, RPL = MQ / 16;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   double* SM = w_lds + D * kWarmQS;
   const int NC = (r + 15) / 16;
@@ -562,11 +570,11 @@ __device__ __attribute__((noinline)) void warm_small_eig(int r) {
 //      X^T X, the residuals, the decision (convergence; the effective rank proven from the
 //      Ritz values), and when accepted W.  Returns 0 (not converged), 1 (converged; *k_out
 //      holds k or -1 when it is not proven).
-template <int D>
+template <int D, int MQ>
 __device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, double energy,
                                                     double gf2, double gersh, double trace,
                                                     float* W_m, int* k_out) {
-  constexpr int NW = D / 16, NTH = kWave * NW, MQ = kWarmM, QS = kWarmQS, SS = kWarmSS;
+  constexpr int NW = D / 16, NTH = kWave * NW, QS = kWarmQS, SS = kWarmSS;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave, g = l / 16, i0 = l % 16;
   double* QB = w_lds;
   double* SM = w_lds + D * QS;
@@ -837,13 +845,24 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     __syncthreads();
     // ---- passes: Z = G B, Cholesky QR, Rayleigh-Ritz, check; B for the next pass is the
     //      Ritz vectors of this one and the remaining columns of its Q (left in QB)
+    // the first pass uses 32 columns (the previous rows and, for r < 32, extra directions);
+    // later passes all 48
+    float* W_m = W_out + (size_t)m * r * D;
 #pragma unroll 1
     for (int it = 0; it < kWarmMaxIt; ++it) {
-      if (!warm_zchol<D>(Gm)) break;
-      warm_rayleigh<D>(Gm);
-      warm_small_eig<D>(r);
-      int kc = -1;
-      if (warm_check<D>(Gm, r, energy, gf2, gersh, trace, W_out + (size_t)m * r * D, &kc)) {
+      int kc = -1, conv = 0;
+      if (it == 0) {
+        if (!warm_zchol<D, 32>(Gm)) break;
+        warm_rayleigh<D, 32>(Gm);
+        warm_small_eig<D, 32>(r);
+        conv = warm_check<D, 32>(Gm, r, energy, gf2, gersh, trace, W_m, &kc);
+      } else {
+        if (!warm_zchol<D, kWarmM>(Gm)) break;
+        warm_rayleigh<D, kWarmM>(Gm);
+        warm_small_eig<D, kWarmM>(r);
+        conv = warm_check<D, kWarmM>(Gm, r, energy, gf2, gersh, trace, W_m, &kc);
+      }
+      if (conv) {
         k_cert = kc;
         break;
       }
