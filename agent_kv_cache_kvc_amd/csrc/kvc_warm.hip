@@ -269,19 +269,29 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
       if (own_i[u] >= 0) SM[own_i[u] * SS + own_j[u]] *= w_rdg[own_i[u]];
     __syncthreads();
     if (!(pmin > 1e-18)) return 0;  // (uniform) numerically rank-deficient
-    // q R = z D, row by row: four lanes per row of Z in place (wave w: its own 16 rows)
+    // q R = z D, row by row: four lanes per row of Z (wave w: its own 16 rows); lane p keeps
+    // the solved q_k of its residue class k = p mod 4 in registers, so only R is read from
+    // LDS (the same entries on every row: broadcast reads, independent of the solve)
     {
       const int row = tid / 4, p = tid % 4;
       double* qr = QB + row * QS;
-#pragma unroll 1
+      double z[MQ / 4], qk[MQ / 4];
+#pragma unroll
+      for (int u = 0; u < MQ / 4; ++u) z[u] = qr[4 * u + p];
+#pragma unroll
       for (int j = 0; j < MQ; ++j) {
         double s = 0.0;
-        for (int k = p; k < j; k += 4) s = fma(qr[k], SM[k * SS + j], s);
+#pragma unroll
+        for (int u = 0; u < MQ / 4; ++u)
+          if (4 * u < j) s = 4 * u + p < j ? fma(qk[u], SM[(4 * u + p) * SS + j], s) : s;
         s += dpp_d<0xB1>(s);
         s += dpp_d<0x4E>(s);
-        const double q = (qr[j] * w_dsc[j] - s) * w_rdg[j];
-        if (p == 0) qr[j] = q;
+        const double zj = __shfl(z[j / 4], (tid & ~3) + (j % 4), 64);  // z_j from its lane
+        const double q = (zj * w_dsc[j] - s) * w_rdg[j];
+        if (p == j % 4) qk[j / 4] = q;
       }
+#pragma unroll
+      for (int u = 0; u < MQ / 4; ++u) qr[4 * u + p] = qk[u];
     }
     if (pmin >= 1e-4) break;  // (uniform) orthonormal to about 1e-12 after one pass
 #pragma unroll
