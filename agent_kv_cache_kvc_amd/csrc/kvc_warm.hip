@@ -59,6 +59,7 @@ typedef double double4v __attribute__((ext_vector_type(4)));
 // each other through these arrays.
 extern __shared__ __align__(16) double w_lds[];  // QB [D][kWarmQS], then SM [48][kWarmSS]
 __shared__ double w_red[2 * kWarmNW];
+__shared__ double w_red3[kWarmNW][3];
 __shared__ double w_dvec[kWarmM], w_evec[kWarmM], w_tau[kWarmM], w_dsc[kWarmM], w_rdg[kWarmM];
 __shared__ __align__(16) double w_vs[kWarmM], w_ws[kWarmM];
 __shared__ __align__(16) float w_df[kWarmM], w_e2s[kWarmM];
@@ -105,6 +106,32 @@ __device__ __forceinline__ double wg_max(double v) {
 #pragma unroll
   for (int w = 1; w < NW; ++w) s = fmax(s, w_red[w]);
   return s;
+}
+
+// one pass over the workgroup for three values: a sum, a maximum and a sum (waves in order)
+template <int NW>
+__device__ __forceinline__ void wg_sum_max_sum(double& a, double& b, double& c) {
+  a = wave_sum_d(a);
+  c = wave_sum_d(c);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) b = fmax(b, __shfl_xor(b, off, 64));
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    const int w = threadIdx.x / kWave;
+    w_red3[w][0] = a;
+    w_red3[w][1] = b;
+    w_red3[w][2] = c;
+  }
+  __syncthreads();
+  a = w_red3[0][0];
+  b = w_red3[0][1];
+  c = w_red3[0][2];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    a += w_red3[w][0];
+    b = fmax(b, w_red3[w][1]);
+    c += w_red3[w][2];
+  }
 }
 
 // element e of the upper triangle (row-major, diagonal included) of an n x n matrix
@@ -206,6 +233,37 @@ __device__ __forceinline__ void sym_tiles_to_sm(const double4v* P, const double4
       __syncthreads();
     }
   }
+}
+
+// extra start directions: QB columns [c0, c1) get the fixed +-1 pattern, made orthogonal to
+// the columns [0, c0) (taken as orthonormal rows of a basis: E -= B (B^T E)); C = B^T E goes
+// through SM
+template <int D>
+__device__ __attribute__((noinline)) void warm_extras(int c0, int c1) {
+  constexpr int NW = D / 16, NTH = kWave * NW, QS = kWarmQS, SS = kWarmSS;
+  const int tid = threadIdx.x, ne = c1 - c0;
+  double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  for (int e = tid; e < ne * D; e += NTH) {
+    const int j = c0 + e / D, i = e % D;
+    QB[i * QS + j] = warm_pattern(i, j);
+  }
+  __syncthreads();
+  for (int e = tid; e < c0 * ne; e += NTH) {  // C = B^T E  (c0 x ne)
+    const int a = e / ne, b = e - a * ne;
+    double c = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < D; ++i) c = fma(QB[i * QS + a], QB[i * QS + c0 + b], c);
+    SM[a * SS + b] = c;
+  }
+  __syncthreads();
+  for (int e = tid; e < D * ne; e += NTH) {  // E -= B C
+    const int i = e / ne, b = e - i * ne;
+    double v = QB[i * QS + c0 + b];
+    for (int a = 0; a < c0; ++a) v = fma(-QB[i * QS + a], SM[a * SS + b], v);
+    QB[i * QS + c0 + b] = v;
+  }
+  __syncthreads();
 }
 
 // ---- phase 1: Z = G B with B the block in QB, then Cholesky QR of Z into QB (one pass, a
@@ -616,77 +674,90 @@ __device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, dou
   }
   __syncthreads();  // X complete in QB; every wave has read Y_r from SM
   product<D>(Gm, gxacc, NC);
-    // X^T G X (SM[0 ..]) and X^T X (SM[1024 ..]), NC x NC tiles of stride 32, each summed
-    // over the waves in order
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      double4v pp[2][2];
-#pragma unroll
-      for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          pp[c1][c2] = double4v{0.0, 0.0, 0.0, 0.0};
-          if (c1 < NC && c2 < NC) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              pp[c1][c2] = mfma64(xacc[c1][v], which == 0 ? gxacc[c2][v] : xacc[c2][v],
-                                  pp[c1][c2]);
-          }
-        }
-      for (int ww = 0; ww < NW; ++ww) {
-        if (w == ww) {
-#pragma unroll
-          for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-              if (c1 >= NC || c2 >= NC) continue;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                double* pa = SM + 1024 * which + (16 * c1 + g + 4 * v) * 32 + 16 * c2 + i0;
-                *pa = (ww == 0 ? 0.0 : *pa) + pp[c1][c2][v];
-              }
-            }
-        }
-        __syncthreads();
+  // X^T X (SM[1024 ..], stride 32): tile (c1, c2), c1 <= c2, from X in QB over all rows, one
+  // wave per tile
+  {
+    const int nt = NC * (NC + 1) / 2;
+    if (w < nt) {
+      const int c1 = w == 2 ? 1 : 0, c2 = w == 0 ? 0 : 1;
+      double4v t = double4v{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+      for (int kb = 0; kb < D / 4; ++kb) {
+        const double* row = QB + (4 * kb + g) * QS + i0;
+        t = mfma64(row[16 * c1], row[16 * c2], t);
       }
-    }
-    if (tid < r) w_rho[tid] = SM[tid * 32 + tid];
-    __syncthreads();
-    // residual of each Ritz vector: |G x_c - rho_c x_c|^2 over the rows, then the waves
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (c >= NC) continue;
-      const int col = 16 * c + i0;
-      const double rc = col < r ? w_rho[col] : 0.0;
-      double s = 0.0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const double d = gxacc[c][v] - rc * xacc[c][v];
-        s = fma(d, d, s);
+        SM[1024 + (16 * c1 + g + 4 * v) * 32 + 16 * c2 + i0] = t[v];
+        SM[1024 + (16 * c2 + i0) * 32 + 16 * c1 + g + 4 * v] = t[v];
       }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (g == 0 && col < r) w_col[w][col] = s;
     }
-    __syncthreads();
-    if (tid < r) {
-      double s = 0.0;
-      for (int ww = 0; ww < NW; ++ww) s += w_col[ww][tid];
-      w_res2[tid] = s;
+  }
+  // X^T G X (SM[0 ..], stride 32): each wave's rows, summed over the waves in order
+  {
+    double4v pp[2][2];
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        pp[c1][c2] = double4v{0.0, 0.0, 0.0, 0.0};
+        if (c1 < NC && c2 < NC) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) pp[c1][c2] = mfma64(xacc[c1][v], gxacc[c2][v], pp[c1][c2]);
+        }
+      }
+    for (int ww = 0; ww < NW; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            if (c1 >= NC || c2 >= NC) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              double* pa = SM + (16 * c1 + g + 4 * v) * 32 + 16 * c2 + i0;
+              *pa = (ww == 0 ? 0.0 : *pa) + pp[c1][c2][v];
+            }
+          }
+      }
+      __syncthreads();
     }
-    // orthonormality defect of X, |X^T G X|_F^2 and its off-diagonal part
-    double dx = 0.0, af = 0.0, ff = 0.0;
-    for (int e = tid; e < r * r; e += NTH) {
-      const int a = e / r, b = e - a * r;
-      const double xv = SM[1024 + a * 32 + b] - (a == b ? 1.0 : 0.0);
-      const double av = SM[a * 32 + b];
-      dx = fmax(dx, xv == xv ? fabs(xv) : 1e300);
-      af = fma(av, av, af);
-      if (a != b) ff = fma(av, av, ff);
+  }
+  // residual of each Ritz vector: |G x_c - rho_c x_c|^2 over the rows, then the waves
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c >= NC) continue;
+    const int col = 16 * c + i0;
+    const double rc = col < r ? SM[col * 32 + col] : 0.0;
+    double s = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const double d = gxacc[c][v] - rc * xacc[c][v];
+      s = fma(d, d, s);
     }
-    const double defect = wg_max<NW>(dx);
-    const double a_f2 = wg_sum<NW>(af);
-    const double f_f2 = wg_sum<NW>(ff);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (g == 0 && col < r) w_col[w][col] = s;
+  }
+  // |X^T G X|_F^2, the orthonormality defect of X, the off-diagonal part of X^T G X
+  double af = 0.0, dx = 0.0, ff = 0.0;
+  for (int e = tid; e < r * r; e += NTH) {
+    const int a = e / r, b = e - a * r;
+    const double xv = SM[1024 + a * 32 + b] - (a == b ? 1.0 : 0.0);
+    const double av = SM[a * 32 + b];
+    dx = fmax(dx, xv == xv ? fabs(xv) : 1e300);
+    af = fma(av, av, af);
+    if (a != b) ff = fma(av, av, ff);
+  }
+  wg_sum_max_sum<NW>(af, dx, ff);  // (its barriers also publish w_col)
+  const double a_f2 = af, defect = dx, f_f2 = ff;
+  if (tid < r) {
+    double s = 0.0;
+    for (int ww = 0; ww < NW; ++ww) s += w_col[ww][tid];
+    w_res2[tid] = s;
+    w_rho[tid] = SM[tid * 32 + tid];
+  }
+  __syncthreads();
 
     // ---- decision (wave 0, lane c for Ritz pair c, then shared): convergence, then the
     //      effective rank from the Ritz values (see the header)
@@ -806,10 +877,8 @@ template <int D>
 __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     const double* __restrict__ G, const float* __restrict__ W_prev, int r, double energy,
     float* __restrict__ W_out, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ warm_out) {
-  constexpr int NW = D / 16, NTH = kWave * NW, KB = D / 4, MQ = kWarmM, QS = kWarmQS;
-  constexpr int SS = kWarmSS;
+  constexpr int NW = D / 16, NTH = kWave * NW, KB = D / 4, QS = kWarmQS;
   double* QB = w_lds;
-  double* SM = w_lds + D * QS;
   const int m = blockIdx.x, tid = threadIdx.x;
   const int w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
   const double* Gm = G + (size_t)m * D * D;
@@ -824,35 +893,19 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
   }
   ra += __shfl_xor(ra, 16, 64);  // the row's four column groups
   ra += __shfl_xor(ra, 32, 64);
-  const double gf2 = wg_sum<NW>(ss);
-  const double gersh = wg_max<NW>(ra);
-  const double trace = wg_sum<NW>(tid < D ? Gm[tid * D + tid] : 0.0);
+  double gf2 = ss, gersh = ra, trace = tid < D ? Gm[tid * D + tid] : 0.0;
+  wg_sum_max_sum<NW>(gf2, gersh, trace);
   const bool bad = !(trace > 0.0) || !(gf2 < 1e300) || !(gersh < 1e300) || !(trace < 1e300);
 
   int k_cert = -1;
   if (!bad) {  // (uniform)
-    // ---- Q0 = [W_prev^T, E], E orthogonal to the rows of W_prev
-    const int ne = MQ - r;
-    for (int e = tid; e < MQ * D; e += NTH) {
+    // ---- Q0 = [W_prev^T, E] on 32 columns, E orthogonal to the rows of W_prev (r < 32)
+    for (int e = tid; e < r * D; e += NTH) {
       const int j = e / D, i = e - j * D;
-      QB[i * QS + j] = j < r ? (double)W_prev[((size_t)m * r + j) * D + i] : warm_pattern(i, j);
+      QB[i * QS + j] = (double)W_prev[((size_t)m * r + j) * D + i];
     }
     __syncthreads();
-    for (int e = tid; e < r * ne; e += NTH) {  // C = W_prev E  (r x ne) -> SM
-      const int a = e / ne, b = e - a * ne;
-      double c = 0.0;
-#pragma unroll 4
-      for (int i = 0; i < D; ++i) c = fma(QB[i * QS + a], QB[i * QS + r + b], c);
-      SM[a * SS + b] = c;
-    }
-    __syncthreads();
-    for (int e = tid; e < D * ne; e += NTH) {  // E -= W_prev^T C
-      const int i = e / ne, b = e - i * ne;
-      double v = QB[i * QS + r + b];
-      for (int a = 0; a < r; ++a) v = fma(-QB[i * QS + a], SM[a * SS + b], v);
-      QB[i * QS + r + b] = v;
-    }
-    __syncthreads();
+    if (r < 32) warm_extras<D>(r, 32);
     // ---- passes: Z = G B, Cholesky QR, Rayleigh-Ritz, check; B for the next pass is the
     //      Ritz vectors of this one and the remaining columns of its Q (left in QB)
     // the first pass uses 32 columns (the previous rows and, for r < 32, extra directions);
@@ -867,6 +920,7 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
         warm_small_eig<D, 32>(r);
         conv = warm_check<D, 32>(Gm, r, energy, gf2, gersh, trace, W_m, &kc);
       } else {
+        if (it == 1) warm_extras<D>(32, kWarmM);  // the block grows to 48 columns
         if (!warm_zchol<D, kWarmM>(Gm)) break;
         warm_rayleigh<D, kWarmM>(Gm);
         warm_small_eig<D, kWarmM>(r);
