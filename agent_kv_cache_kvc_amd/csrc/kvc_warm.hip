@@ -266,6 +266,32 @@ __device__ __attribute__((noinline)) void warm_extras(int c0, int c1) {
   __syncthreads();
 }
 
+// SM tiles (I, J), I <= J < NT, of B^T B for the block B in QB (MQ = 16 NT columns), each tile
+// by one wave over all D rows (no cross-wave sum); both triangles of SM are written
+template <int D, int NT>
+__device__ __forceinline__ void gram_tiles_from_qb() {
+  constexpr int NW = D / 16, QS = kWarmQS, SS = kWarmSS, NTILE = NT * (NT + 1) / 2;
+  const int w = threadIdx.x / kWave, g = (threadIdx.x % kWave) / 16, i0 = threadIdx.x % 16;
+  const double* QB = w_lds;
+  double* SM = w_lds + D * QS;
+  for (int t = w; t < NTILE; t += NW) {
+    int I, J;
+    tile_ij<NT>(t, I, J);
+    double4v acc = double4v{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int kb = 0; kb < D / 4; ++kb) {
+      const double* row = QB + (4 * kb + g) * QS + i0;
+      acc = mfma64(row[16 * I], row[16 * J], acc);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      SM[(16 * I + g + 4 * v) * SS + 16 * J + i0] = acc[v];
+      SM[(16 * J + i0) * SS + 16 * I + g + 4 * v] = acc[v];
+    }
+  }
+  __syncthreads();
+}
+
 // ---- phase 1: Z = G B with B the block in QB, then Cholesky QR of Z into QB (one pass, a
 //      second when the first factor's smallest pivot is below 1e-4).  Returns 0 when Z is
 //      numerically rank-deficient (uniform).
@@ -290,9 +316,10 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
     if (e < NTRI) tri_ij(e, MQ, own_i[u], own_j[u]);
     else { own_i[u] = -1; own_j[u] = -1; }
   }
+  __syncthreads();  // Z complete in QB
   for (int pass = 0; pass < 2; ++pass) {
-    // S = Z^T Z (upper tiles) in SM
-    sym_tiles_to_sm<D, NT>(acc, acc);
+    // S = Z^T Z in SM
+    gram_tiles_from_qb<D, NT>();
     // unit diagonal: S' = D S D with D = diag(S)^-1/2
     if (tid < MQ) {
       const double sd = SM[tid * SS + tid];
