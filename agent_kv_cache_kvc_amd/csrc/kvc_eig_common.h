@@ -70,11 +70,10 @@ __device__ __forceinline__ float dpp_fl(float x) {
 // 8 points x 10 steps shrink the start interval more than 2^30 times.  The Sturm chain reads
 // the matrix 8 entries at a time (16-byte LDS reads), the next 8 loaded while the current 8
 // are used, so LDS latency stays off the chain.
-template <int P, int D>
+template <int P, int D, int NIT = (P == 4 ? 13 : 10)>
 __device__ float multisect(int ev, float lo, float hi, const float* df, const float* e2s, int q) {
   static_assert(P == 4 || P == 8, "groups of 4 or 8 lanes");
   static_assert(D % 8 == 0, "chunks of 8");
-  constexpr int NIT = P == 4 ? 13 : 10;
   const float4* d4 = reinterpret_cast<const float4*>(df);
   const float4* e4 = reinterpret_cast<const float4*>(e2s);
   for (int it = 0; it < NIT; ++it) {

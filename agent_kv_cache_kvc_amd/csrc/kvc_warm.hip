@@ -60,6 +60,7 @@ typedef double double4v __attribute__((ext_vector_type(4)));
 extern __shared__ __align__(16) double w_lds[];  // QB [D][kWarmQS], then SM [48][kWarmSS]
 __shared__ double w_red[2 * kWarmNW];
 __shared__ double w_red3[kWarmNW][3];
+__shared__ double w_stat[3];  // |G|_F^2, Gershgorin bound, trace
 __shared__ double w_dvec[kWarmM], w_evec[kWarmM], w_tau[kWarmM], w_dsc[kWarmM], w_rdg[kWarmM];
 __shared__ __align__(16) double w_vs[kWarmM], w_ws[kWarmM];
 __shared__ __align__(16) float w_df[kWarmM], w_e2s[kWarmM];
@@ -154,8 +155,9 @@ __device__ __forceinline__ double g_at(const double* Gm, int kb, int w, int g, i
 // 4 kb + g).  G is read from global memory (L2) for every product, eight fragments at a time
 // with the next eight in flight; the B operands are read two k-steps at a time (the memory
 // clobber keeps the compiler from hoisting every LDS read of the loop ahead of the MFMAs).
-template <int D>
-__device__ __forceinline__ void product(const double* Gm, double4v* acc, int nt) {
+template <int D, bool STATS = false>
+__device__ __forceinline__ void product(const double* Gm, double4v* acc, int nt,
+                                        double* ss = nullptr, double* ra = nullptr) {
   constexpr int KB = D / 4, NG = KB / 8, QS = kWarmQS;
   const int w = threadIdx.x / kWave, g = (threadIdx.x % kWave) / 16, i0 = threadIdx.x % 16;
   const double* QB = w_lds;
@@ -170,6 +172,13 @@ __device__ __forceinline__ void product(const double* Gm, double4v* acc, int nt)
     if (gi + 1 < NG) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) gA[(gi + 1) & 1][u] = g_at<D>(Gm, 8 * (gi + 1) + u, w, g, i0);
+    }
+    if constexpr (STATS) {  // |G|_F^2 and this lane's share of its row's absolute sum
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        *ss = fma(gA[gi & 1][u], gA[gi & 1][u], *ss);
+        *ra += fabs(gA[gi & 1][u]);
+      }
     }
 #pragma unroll
     for (int k2 = 0; k2 < 8; k2 += 2) {
@@ -295,7 +304,7 @@ __device__ __forceinline__ void gram_tiles_from_qb() {
 // ---- phase 1: Z = G B with B the block in QB, then Cholesky QR of Z into QB (one pass, a
 //      second when the first factor's smallest pivot is below 1e-4).  Returns 0 when Z is
 //      numerically rank-deficient (uniform).
-template <int D, int MQ>
+template <int D, int MQ, bool FIRST>
 __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
   constexpr int NW = D / 16, NTH = kWave * NW, NT = MQ / 16, QS = kWarmQS, SS = kWarmSS;
   constexpr int NTRI = MQ * (MQ + 1) / 2, OWN = (NTRI + NTH - 1) / NTH;
@@ -303,7 +312,25 @@ __device__ __attribute__((noinline)) int warm_zchol(const double* Gm) {
   double* QB = w_lds;
   double* SM = w_lds + D * QS;
   double4v acc[3];
-  product<D>(Gm, acc, NT);
+  if constexpr (FIRST) {
+    // the statistics of G ride on the first product: |G|_F^2, the Gershgorin bound (row sums
+    // of |G|: a lane holds a quarter of its row), the trace; published in w_stat
+    double ss = 0.0, ra = 0.0;
+    double tr = tid < D ? Gm[tid * D + tid] : 0.0;  // issued before the product's loads
+    product<D, true>(Gm, acc, NT, &ss, &ra);
+    ra += __shfl_xor(ra, 16, 64);
+    ra += __shfl_xor(ra, 32, 64);
+    wg_sum_max_sum<NW>(ss, ra, tr);
+    if (tid == 0) {
+      w_stat[0] = ss;
+      w_stat[1] = ra;
+      w_stat[2] = tr;
+    }
+    // a zero, infinite or NaN G is left to the full eigensolver (uniform)
+    if (!(tr > 0.0) || !(ss < 1e300) || !(ra < 1e300) || !(tr < 1e300)) return 0;
+  } else {
+    product<D>(Gm, acc, NT);
+  }
   __syncthreads();  // every wave has read QB as a B operand
 #pragma unroll
   for (int J = 0; J < NT; ++J)
@@ -527,7 +554,9 @@ __device__ __attribute__((noinline)) void warm_small_eig(int r) {
   const double span = fmax(hmax - hmin, 1e-300);
   const float lo_s = (float)(hmin - 1e-6 * span), hi_s = (float)(hmax + 1e-6 * span);
   if (tid < 8 * r) {
-    const float lam = multisect<8, MQ>(MQ - 1 - tid / 8, lo_s, hi_s, w_df, w_e2s, tid % 8);
+    // 11 steps: 9^11 > 2^34 times below the Gershgorin width (the inverse iteration's
+    // vectors for close eigenvalues stay orthogonal to about 1e-11)
+    const float lam = multisect<8, MQ, 11>(MQ - 1 - tid / 8, lo_s, hi_s, w_df, w_e2s, tid % 8);
     if (tid % 8 == 0) w_lam[tid / 8] = lam;
   }
   __syncthreads();
@@ -904,28 +933,13 @@ template <int D>
 __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     const double* __restrict__ G, const float* __restrict__ W_prev, int r, double energy,
     float* __restrict__ W_out, int32_t* __restrict__ k_eff_out, int32_t* __restrict__ warm_out) {
-  constexpr int NW = D / 16, NTH = kWave * NW, KB = D / 4, QS = kWarmQS;
+  constexpr int NTH = kWave * (D / 16), QS = kWarmQS;
   double* QB = w_lds;
   const int m = blockIdx.x, tid = threadIdx.x;
-  const int w = tid / kWave, g = (tid % kWave) / 16, i0 = tid % 16;
   const double* Gm = G + (size_t)m * D * D;
 
-  // ---- statistics of G: |G|_F^2, trace, Gershgorin bound
-  double ss = 0.0, ra = 0.0;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const double gv = g_at<D>(Gm, kb, w, g, i0);
-    ss = fma(gv, gv, ss);
-    ra += fabs(gv);
-  }
-  ra += __shfl_xor(ra, 16, 64);  // the row's four column groups
-  ra += __shfl_xor(ra, 32, 64);
-  double gf2 = ss, gersh = ra, trace = tid < D ? Gm[tid * D + tid] : 0.0;
-  wg_sum_max_sum<NW>(gf2, gersh, trace);
-  const bool bad = !(trace > 0.0) || !(gf2 < 1e300) || !(gersh < 1e300) || !(trace < 1e300);
-
   int k_cert = -1;
-  if (!bad) {  // (uniform)
+  {
     // ---- Q0 = [W_prev^T, E] on 32 columns, E orthogonal to the rows of W_prev (r < 32)
     for (int e = tid; e < r * D; e += NTH) {
       const int j = e / D, i = e - j * D;
@@ -942,16 +956,16 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
     for (int it = 0; it < kWarmMaxIt; ++it) {
       int kc = -1, conv = 0;
       if (it == 0) {
-        if (!warm_zchol<D, 32>(Gm)) break;
+        if (!warm_zchol<D, 32, true>(Gm)) break;
         warm_rayleigh<D, 32>(Gm);
         warm_small_eig<D, 32>(r);
-        conv = warm_check<D, 32>(Gm, r, energy, gf2, gersh, trace, W_m, &kc);
+        conv = warm_check<D, 32>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc);
       } else {
         if (it == 1) warm_extras<D>(32, kWarmM);  // the block grows to 48 columns
-        if (!warm_zchol<D, kWarmM>(Gm)) break;
+        if (!warm_zchol<D, kWarmM, false>(Gm)) break;
         warm_rayleigh<D, kWarmM>(Gm);
         warm_small_eig<D, kWarmM>(r);
-        conv = warm_check<D, kWarmM>(Gm, r, energy, gf2, gersh, trace, W_m, &kc);
+        conv = warm_check<D, kWarmM>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc);
       }
       if (conv) {
         k_cert = kc;
