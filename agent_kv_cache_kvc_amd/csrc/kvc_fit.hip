@@ -43,11 +43,12 @@ __constant__ int c_blk64[4][3][2] = {{{0, 0}, {-1, -1}, {-1, -1}},
 // different banks (without it they all hit one bank group), and a fragment read stays one
 // access per lane.  Products of bf16 values are exact in the float32 accumulator,
 // which holds the split's whole sum (chunk / 16 MFMA steps; the error bound of the effective
-// rank's certificate counts them); the partials are written as float64.
-template <int D>
+// rank's certificate counts them); the partials are written as float64 (P = double, read by
+// the fit's eigensolver) or float32 (P = float, the streaming accumulation: the same values).
+template <int D, typename P = double>
 __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __restrict__ delta,
                                                               int T, int chunk,
-                                                              double* __restrict__ partials) {
+                                                              P* __restrict__ partials) {
   constexpr int SLAB = 16384 / D;
   constexpr int SR = SLAB + 8;  // LDS row stride (bf16 elements), 16-byte pad
   constexpr int NB = D / 32;
@@ -124,20 +125,20 @@ __global__ __launch_bounds__(kBlock, 2) void gram_bf16_kernel(const uint16_t* __
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (I[b] >= 0) {
-      double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+      P* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (double)acc[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (P)acc[b][i];
     }
   }
 }
 
 // ------------------------------------------------------------------------- Gram, fp32
 // Same block ownership; slab of 8192/D tokens staged row-major; fp32 MFMA 32x32x2; one float32
-// accumulator per element over the split, written as a float64 partial.
-template <int D>
+// accumulator per element over the split, written as a float64 (or float32) partial.
+template <int D, typename P = double>
 __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __restrict__ delta,
                                                              int T, int chunk,
-                                                             double* __restrict__ partials) {
+                                                             P* __restrict__ partials) {
   constexpr int SLAB = 8192 / D;
   constexpr int SR = D + 4;
   constexpr int NB = D / 32;
@@ -185,9 +186,9 @@ __global__ __launch_bounds__(kBlock, 2) void gram_f32_kernel(const float* __rest
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
     if (I[b] >= 0) {
-      double* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
+      P* dst = partials + (((size_t)m * nsplit + split) * NBLK + blk_index(I[b], J[b], NB)) * 1024;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (double)acc[b][i];
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = (P)acc[b][i];
     }
   }
 }
@@ -1586,30 +1587,45 @@ static hipError_t fit_t(const void* delta, const FitLayout& f, int dtype, double
 }
 
 // ------------------------------------------------------------------------- streaming fit
-// G += delta^T delta from the Gram partials of one block of rows: each element of the upper
-// blocks is summed over the splits in fixed order (float64, from 0) and added to both
-// triangles of G, so a block accumulated onto G = 0 gives exactly the G of the one-call fit.
+// G += delta^T delta from the float32 Gram partials of one block of rows.  One workgroup per
+// upper 32x32 block (I, J) of one matrix: each element's partials are summed over the splits
+// in fixed order (float64, from 0) and added to the upper element of G; the new upper block
+// is then written transposed into the lower triangle through LDS (G stays symmetric; the
+// lower triangle on entry is not read).  A block accumulated onto G = 0 gives exactly the G of
+// the one-call fit, whose eigensolver sums the same partials in the same order.
 template <int D>
-__global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const double* __restrict__ partials,
+__global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const float* __restrict__ partials,
                                                                int nsplit,
                                                                double* __restrict__ G) {
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
-  const int m = blockIdx.y, e = blockIdx.x * kBlock + threadIdx.x;
-  if (e >= NBLK * 1024) return;
-  const int blk = e / 1024, i = (e / 64) % 16, l = e % 64;
+  __shared__ double tile[32][33];
+  const int blk = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
   int I = 0, rem = blk;
   while (rem >= NB - I) { rem -= NB - I; ++I; }
   const int J = I + rem;
-  const int row = I * 32 + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
-  const int col = J * 32 + (l % 32);
-  if (row > col) return;  // a diagonal block's lower half holds no new element
-  const double* Pm = partials + (size_t)m * nsplit * NBLK * 1024 + e;
-  double v = 0.0;
-  for (int sp = 0; sp < nsplit; ++sp) v += Pm[(size_t)sp * NBLK * 1024];
+  const float* Pm = partials + ((size_t)m * nsplit * NBLK + blk) * 1024;
   double* Gm = G + (size_t)m * D * D;
-  Gm[row * D + col] += v;
-  if (row != col) Gm[col * D + row] += v;
+#pragma unroll
+  for (int q = 0; q < 1024 / kBlock; ++q) {
+    const int e = q * kBlock + tid, i = e / 64, l = e % 64;
+    const int row = 8 * (i / 4) + 4 * (l / 32) + (i % 4), col = l % 32;  // MFMA 32x32 layout
+    if (I == J && row > col) continue;
+    double v = 0.0;
+    for (int sp = 0; sp < nsplit; ++sp) v += (double)Pm[(size_t)sp * NBLK * 1024 + e];
+    double* g = Gm + (size_t)(I * 32 + row) * D + J * 32 + col;
+    const double nv = *g + v;
+    *g = nv;
+    tile[row][col] = nv;
+  }
+  __syncthreads();
+  // lower triangle: G[J*32 + a][I*32 + b] = new G[I*32 + b][J*32 + a]
+#pragma unroll
+  for (int q = 0; q < 1024 / kBlock; ++q) {
+    const int e = q * kBlock + tid, a = e / 32, b = e % 32;
+    if (I == J && b >= a) continue;
+    Gm[(size_t)(J * 32 + a) * D + I * 32 + b] = tile[b][a];
+  }
 }
 
 // W (float32, [M][r][D]) -> bf16 hi + lo rows for the projection ([M][rpad][D], rows >= r zero)
@@ -1631,18 +1647,18 @@ template <int D>
 static hipError_t gram_t(const void* delta, const FitLayout& f, int dtype, double* G, char* ws,
                          hipStream_t st) {
   constexpr int NBLK = (D / 32) * (D / 32 + 1) / 2;
-  double* partials = reinterpret_cast<double*>(ws + f.off_gram);
+  float* partials = reinterpret_cast<float*>(ws + f.off_gram);
   const dim3 g1(f.nsplit, f.M);
   if (dtype == KVC_BF16)
-    hipLaunchKernelGGL((gram_bf16_kernel<D>), g1, dim3(kBlock), 0, st,
+    hipLaunchKernelGGL((gram_bf16_kernel<D, float>), g1, dim3(kBlock), 0, st,
                        (const uint16_t*)delta, f.T, f.chunk, partials);
   else
-    hipLaunchKernelGGL((gram_f32_kernel<D>), g1, dim3(kBlock), 0, st, (const float*)delta,
+    hipLaunchKernelGGL((gram_f32_kernel<D, float>), g1, dim3(kBlock), 0, st, (const float*)delta,
                        f.T, f.chunk, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gram_accumulate_kernel<D>), dim3(NBLK * 1024 / kBlock, f.M), dim3(kBlock),
-                     0, st, partials, f.nsplit, G);
+  hipLaunchKernelGGL((gram_accumulate_kernel<D>), dim3(NBLK, f.M), dim3(kBlock), 0, st, partials,
+                     f.nsplit, G);
   return hipGetLastError();
 }
 

@@ -222,7 +222,10 @@ hipError_t launch_segment_error(const void* X, const void* R, int S, int T, int 
                                 double* partials, double* out, hipStream_t st);
 hipError_t launch_rank_error_curve(const float* eig, int M, int n, float* curve, hipStream_t st);
 int rank_error_curve_max_n();  // eigenvalues per matrix the curve kernel stages
-inline size_t gram_ws_bytes(const FitLayout& f) { return f.off_whi; }  // partials lead
+// Streaming Gram workspace: float32 partials [M][nsplit][nblk][16][64].
+inline size_t gram_ws_bytes(const FitLayout& f) {
+  return align_up(sizeof(float) * (size_t)f.M * f.nsplit * f.nblk * 1024, 256);
+}
 inline size_t project_ws_bytes(int M, int d, int r, int dtype) {
   return dtype == KVC_BF16 ? 2ull * 2ull * M * ((r + 31) / 32 * 32) * d : 0;
 }

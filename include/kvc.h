@@ -329,7 +329,8 @@ kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int
  *   delta   : [M,T,d] dtype, read only (the appended rows; T = 0 leaves G unchanged)
  *   G_inout : [M,d,d] float64, full symmetric, 8-byte aligned; the caller zeroes it first
  *             (products of the inputs are exact, summed in float32 per split of T, the
- *             splits in a fixed order in float64)
+ *             splits in a fixed order in float64); the upper triangle is read and the sum
+ *             written to both triangles (the lower triangle on entry is not read)
  *   ws      : at least kvc_gram_workspace_bytes(M,T,d) bytes, 256-byte aligned
  * kvc_fit_from_gram: eigen-decomposition of G and the factors of kvc_fit_anchor.
  *   G       : [M,d,d] float64 as accumulated; r, energy, W_out, k_eff_out, eig_out as in
