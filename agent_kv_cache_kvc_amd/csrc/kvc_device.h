@@ -23,6 +23,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two float32 -> bfloat16 with the conversion instruction (round to nearest, ties to even),
+// packed a | b << 16.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+}
+
+// a = hi + lo (and b) in bfloat16 to about 16 bits: hi the nearest bfloat16, lo the nearest
+// bfloat16 to the exact remainder; both pairs packed as in cvt_pk_bf16.
+__device__ __forceinline__ void split_bf16_pk(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_pk_bf16(a, b);
+  lo = cvt_pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // Row m of a 32-row MFMA operand block -> channel within the block, chosen so that the
 // 16 accumulator registers of lane l of a 32x32 result hold 16 consecutive channels
 // (16 * (l / 32) + i).  The result layout of the 32x32 MFMAs puts register i of lane l

@@ -539,10 +539,10 @@ __global__ __launch_bounds__(kJacobiBlock, 2) void jacobi_kernel(
       W_out[((size_t)m * r + k) * D + c] = wv;
     }
     if (w_hi) {
-      const uint16_t hi = f32_to_bf16(wv);
-      const uint16_t lo = f32_to_bf16(wv - bf16_to_f32(hi));
-      w_hi[((size_t)m * rpad + k) * D + c] = hi;
-      w_lo[((size_t)m * rpad + k) * D + c] = lo;
+      uint32_t hi, lo;
+      split_bf16_pk(wv, 0.f, hi, lo);
+      w_hi[((size_t)m * rpad + k) * D + c] = (uint16_t)hi;
+      w_lo[((size_t)m * rpad + k) * D + c] = (uint16_t)lo;
     }
   }
 }
@@ -1140,10 +1140,10 @@ __global__ __launch_bounds__(kEigBlock, D == 128 ? 4 : 2) void eig_kernel(
       W_out[((size_t)m * r + kk) * D + c] = wv;
     }
     if (w_hi) {
-      const uint16_t hi = f32_to_bf16(wv);
-      const uint16_t lo = f32_to_bf16(wv - bf16_to_f32(hi));
-      w_hi[((size_t)m * rpad + kk) * D + c] = hi;
-      w_lo[((size_t)m * rpad + kk) * D + c] = lo;
+      uint32_t hi, lo;
+      split_bf16_pk(wv, 0.f, hi, lo);
+      w_hi[((size_t)m * rpad + kk) * D + c] = (uint16_t)hi;
+      w_lo[((size_t)m * rpad + kk) * D + c] = (uint16_t)lo;
     }
   }
 }
@@ -1367,13 +1367,15 @@ constexpr int kProjIters = 4;
 // bf16 delta: per iteration the workgroup loads a 128-token tile with coalesced 16-byte
 // accesses into LDS (row stride d + 8 bf16); each wave reads its B fragments (token l % 32,
 // channels 16 ks + 8 (l / 32) ...) from there; W is split as W = hi + lo in bf16 and both
-// halves are multiplied (float32 accumulation).  U is staged per wave in LDS and written
-// with coalesced 16-byte stores.  The next tile is requested before the current one is
-// computed.
-template <int D>
+// halves are multiplied (float32 accumulation).  The halves come split (w_hi, w_lo: [M][rpad]
+// [D], rows >= r zero) or, with WF, are split here from the float32 W [M][r][D].  U is staged
+// per wave in LDS and written with coalesced 16-byte stores.  The next tile is requested
+// before the current one is computed.
+template <int D, bool WF = false>
 __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
     const uint16_t* __restrict__ delta, const uint16_t* __restrict__ w_hi,
-    const uint16_t* __restrict__ w_lo, int T, int r, int rpad, float* __restrict__ U_out) {
+    const uint16_t* __restrict__ w_lo, int T, int r, int rpad, float* __restrict__ U_out,
+    const float* __restrict__ wf = nullptr) {
   constexpr int KS = D / 16;            // MFMA steps over d
   constexpr int DR = D + 8;             // LDS row stride of the delta tile (bf16)
   constexpr int UR = 36;                // LDS row stride of the U staging tile (floats)
@@ -1394,9 +1396,25 @@ __global__ __launch_bounds__(kBlock, 2) void project_bf16_kernel(
     u32x4 ah[KS], al[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const size_t off = ((size_t)m * rpad + jrow) * D + 16 * ks + 8 * g;
-      ah[ks] = *reinterpret_cast<const u32x4*>(w_hi + off);
-      al[ks] = *reinterpret_cast<const u32x4*>(w_lo + off);
+      if constexpr (WF) {  // 8 channels of row jrow as bf16 hi + lo pairs, packed 2 per word
+        floatx4 x[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (jrow < r) {
+          const float* wp = wf + ((size_t)m * r + jrow) * D + 16 * ks + 8 * g;
+          x[0] = *reinterpret_cast<const floatx4*>(wp);
+          x[1] = *reinterpret_cast<const floatx4*>(wp + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t hi, lo;
+          split_bf16_pk(x[k / 2][2 * (k % 2)], x[k / 2][2 * (k % 2) + 1], hi, lo);
+          ah[ks][k] = hi;
+          al[ks][k] = lo;
+        }
+      } else {
+        const size_t off = ((size_t)m * rpad + jrow) * D + 16 * ks + 8 * g;
+        ah[ks] = *reinterpret_cast<const u32x4*>(w_hi + off);
+        al[ks] = *reinterpret_cast<const u32x4*>(w_lo + off);
+      }
     }
     u32x4 ld[LD];
     auto load_tile = [&](int t0) {
@@ -1628,21 +1646,6 @@ __global__ __launch_bounds__(kBlock) void gram_accumulate_kernel(const float* __
   }
 }
 
-// W (float32, [M][r][D]) -> bf16 hi + lo rows for the projection ([M][rpad][D], rows >= r zero)
-template <int D>
-__global__ __launch_bounds__(kBlock) void split_w_kernel(const float* __restrict__ W, int r,
-                                                       int rpad, uint16_t* __restrict__ w_hi,
-                                                       uint16_t* __restrict__ w_lo) {
-  const int m = blockIdx.y;
-  const int e = blockIdx.x * kBlock + threadIdx.x;
-  if (e >= rpad * D) return;
-  const int k = e / D;
-  const float wv = k < r ? W[(size_t)m * r * D + e] : 0.f;
-  const uint16_t hi = f32_to_bf16(wv);
-  w_hi[(size_t)m * rpad * D + e] = hi;
-  w_lo[(size_t)m * rpad * D + e] = f32_to_bf16(wv - bf16_to_f32(hi));
-}
-
 template <int D>
 static hipError_t gram_t(const void* delta, const FitLayout& f, int dtype, double* G, char* ws,
                          hipStream_t st) {
@@ -1719,14 +1722,9 @@ static hipError_t project_t(const void* delta, int M, int T, int dtype, const fl
   const int n_tiles = ceil_div(T, kRowsPerPass * kProjIters);
   const dim3 g3(n_tiles, M);
   if (dtype == KVC_BF16) {
-    uint16_t* whi = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* wlo = whi + (size_t)M * rpad * D;
-    hipLaunchKernelGGL((split_w_kernel<D>), dim3(ceil_div(rpad * D, kBlock), M), dim3(kBlock),
-                       0, st, W, r, rpad, whi, wlo);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((project_bf16_kernel<D>), g3, dim3(kBlock), 0, st,
-                       (const uint16_t*)delta, whi, wlo, T, r, rpad, U_out);
+    hipLaunchKernelGGL((project_bf16_kernel<D, true>), g3, dim3(kBlock), 0, st,
+                       (const uint16_t*)delta, (const uint16_t*)nullptr, (const uint16_t*)nullptr,
+                       T, r, rpad, U_out, W);
   } else {
     hipLaunchKernelGGL((project_f32_kernel<D>), g3, dim3(kBlock), 0, st, (const float*)delta, W,
                        T, r, rpad, U_out);

@@ -226,8 +226,7 @@ int rank_error_curve_max_n();  // eigenvalues per matrix the curve kernel stages
 inline size_t gram_ws_bytes(const FitLayout& f) {
   return align_up(sizeof(float) * (size_t)f.M * f.nsplit * f.nblk * 1024, 256);
 }
-inline size_t project_ws_bytes(int M, int d, int r, int dtype) {
-  return dtype == KVC_BF16 ? 2ull * 2ull * M * ((r + 31) / 32 * 32) * d : 0;
-}
+// The projection splits W into bf16 halves inside its kernel: no workspace for either dtype.
+inline size_t project_ws_bytes(int, int, int, int) { return 0; }
 
 }  // namespace kvc

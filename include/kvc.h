@@ -338,7 +338,7 @@ kvc_status kvc_fit_anchor(const void* delta, int M, int T, int d, int dtype, int
  * kvc_project: U = delta W^T for any block of rows (e.g. only the appended ones).
  *   W       : [M,r,d] float32 (from kvc_fit_from_gram or kvc_fit_anchor)
  *   U_out   : [M,T,r] float32
- *   ws      : kvc_project_workspace_bytes(M,d,r,dtype) bytes (0 for float32 deltas: NULL ok)
+ *   ws      : kvc_project_workspace_bytes(M,d,r,dtype) bytes (0 for both dtypes: NULL ok)
  * Errors as for kvc_fit_anchor; nothing is enqueued when validation fails.
  * ------------------------------------------------------------------------------------- */
 size_t kvc_gram_workspace_bytes(int M, int T, int d);

@@ -152,12 +152,13 @@ def test_streaming_fit_rejects_bad_arguments():
     # kvc_project(delta, M, T, d, dtype, W, r, U, ws, ws_bytes, stream)
     base = dict(delta=FAKE, M=4, T=64, d=128, dtype=0, W=FAKE, r=32, U=FAKE, ws=None, nb=0,
                 st=None)
-    for kw, status in [(dict(r=0), 1), (dict(d=64, r=65), 1), (dict(U=None), 1), (dict(), 4)]:
+    for kw, status in [(dict(r=0), 1), (dict(d=64, r=65), 1), (dict(U=None), 1),
+                       (dict(W=FAKE + 4), 1), (dict(dtype=7), 1)]:
         a = dict(base)
         a.update(kw)
         assert lib.kvc_project(*a.values()) == status, (kw, lib.kvc_last_error())
-    assert lib.kvc_project_workspace_bytes(4, 128, 32, 1) == 0  # float32 deltas need none
-    assert lib.kvc_project_workspace_bytes(4, 128, 32, 0) == 2 * 2 * 4 * 32 * 128
+    assert lib.kvc_project_workspace_bytes(4, 128, 32, 1) == 0  # W is split in the kernel
+    assert lib.kvc_project_workspace_bytes(4, 128, 32, 0) == 0
     assert lib.kvc_gram_workspace_bytes(512, 8192, 128) > lib.kvc_gram_workspace_bytes(1, 128, 128) > 0
 
 
