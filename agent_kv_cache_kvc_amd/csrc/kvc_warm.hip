@@ -6,19 +6,22 @@
 // little and its new top-r eigenvectors lie close to the previous W.  This kernel starts from
 // that W instead of solving the d x d eigenproblem from scratch:
 //
-//   Q0   = [W_prev^T, E]: the previous rows plus 48 - r fixed +-1 directions made orthogonal
-//          to them (the 48-column block holds the convergence of the r wanted vectors
-//          against the next ones);
+//   Q0   = [W_prev^T, E] on 32 columns: the previous rows plus, for r < 32, fixed +-1
+//          directions made orthogonal to them;
 //   loop (at most kWarmMaxIt times):
-//     Z  = G Q (the first pass: G Q0; later passes: the previous G Q)
+//     Z  = G Q (the first pass: G Q0; later passes: G times the previous pass's Ritz vectors
+//          and the rest of its Q)
 //     Q  = Z R^-1 with R^T R = Z^T Z (Cholesky QR after scaling the columns to unit norm,
 //          a second pass when the first Cholesky factor is poorly conditioned)
-//     H  = Q^T G Q (48 x 48), its r largest eigenpairs (Householder tridiagonalisation in
-//          float64, float32 multisection on Sturm counts, float64 inverse iteration,
+//     H  = Q^T G Q, its r largest eigenpairs (Householder tridiagonalisation in float64,
+//          float32 multisection on Sturm counts, float64 inverse iteration,
 //          back-transformation)
 //     X  = Q Y_r (Ritz vectors), G X = (G Q) Y_r
 //     accept when every Ritz vector's residual |G x_i - rho_i x_i| is within 2^-28 of the
-//     Gershgorin bound of G and X^T X = I to 1e-10; otherwise iterate from G Q.
+//     Gershgorin bound of G and X^T X = I to 1e-8 (W is stored in float32; the bounds below
+//     carry the measured defect); otherwise iterate.  After the first pass the block grows
+//     to 48 columns (16 more fixed directions orthogonal to it), which sets the convergence
+//     of the r wanted vectors against the next ones.
 //
 // The effective rank is then decided from the Ritz vectors alone and must be certain
 // (rho_i = x_i^T G x_i, C_k = sum of the k largest eigenvalues of G, need = energy trace G):

@@ -355,10 +355,11 @@ kvc_status kvc_project(const void* delta, int M, int T, int d, int dtype, const 
  * rows were appended and G accumulated, the new anchor is found starting from the previous
  * W instead of from scratch.  Results as kvc_fit_from_gram (W = the top-r eigenvectors of G
  * as rows with the canonical sign, k_eff exact for the given G), found by
- *   Q0 = [W_prev^T, 48 - r fixed directions orthogonal to it], then at most three passes of
- *   Z = G Q (first G Q0), Q = Cholesky-QR(Z), Rayleigh-Ritz on Q^T G Q (48 x 48, float64);
+ *   Q0 = [W_prev^T, 32 - r fixed directions orthogonal to it], then at most three passes of
+ *   Z = G Q (first G Q0), Q = Cholesky-QR(Z), Rayleigh-Ritz on Q^T G Q (float64; 32 columns
+ *   in the first pass, 48 in later ones);
  * the Ritz vectors are kept when each residual |G x - rho x| is within 2^-28 of the
- * Gershgorin bound of G and they are orthonormal to 1e-10, and k_eff is kept when the Ritz
+ * Gershgorin bound of G and they are orthonormal to 1e-8, and k_eff is kept when the Ritz
  * values prove it (lower bound: Ky Fan; upper bound: the residual and the energy left outside
  * the Ritz block; k_eff <= r).  Every other matrix (no convergence, k_eff not proven or above
  * r, a zero G) is solved by the kvc_fit_from_gram path, so the outputs always meet that
