@@ -656,7 +656,31 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
     // ---- stage W_a^T of this segment in LDS, rows in MFMA operand order (zero for k >= r); a
     //      falling-back segment stages nothing (its factors are not read)
     const bool pre_masked = m_src[s] != 0;  // same address in every lane
-    if (!pre_masked) {
+    if (FIX && SLOT == 8 && !pre_masked) {
+      // bf16, r a multiple of 8: each step takes an 8 x 8 block (rank indices 8 kb .., channels
+      // 8 cg ..; 16-byte coalesced loads along the channels), transposes it in registers and
+      // writes 8 operand rows of 8 rank indices as 16-byte LDS stores
+      const elem* Wseg = Wt + ((size_t)x * S + s) * nslot * r * D;
+      constexpr int CGN = D / 8, KBN = FIX ? 2 * KSC * SLOT / 8 : 1;
+      for (int q = tid; q < NA * KBN * CGN; q += kBlock) {
+        const int cg = q % CGN, kb = (q / CGN) % KBN, a = q / (CGN * KBN);
+        const elem* src = Wseg + ((size_t)(SEL ? ssl[a] : a) * r + 8 * kb) * D + 8 * cg;
+        u32x4 in[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const u32x4*>(src + (size_t)i * D);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = in[2 * k][j >> 1], hi = in[2 * k + 1][j >> 1];
+            o[k] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          const int c = 8 * cg + j;
+          *reinterpret_cast<u32x4*>(&wt[widx(a * D + (c & ~31) + cinv32(c & 31), 8 * kb)]) = o;
+        }
+      }
+    } else if (!pre_masked) {
       const elem* Wseg = Wt + ((size_t)x * S + s) * nslot * r * D;
       const int n_w = A * r * (D / VEC);
       for (int q = tid; q < n_w; q += kBlock) {
@@ -857,8 +881,10 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
                   for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
                   const u32x4 o = pack_out<Tr>(dv);
                   if (full || tok < T) {
-                    __builtin_nontemporal_store(
-                        o, reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol));
+                    // an ordinary store: the two 64-byte halves of each 128-byte line are
+                    // written by the two blocks and meet in L2 (as non-temporal stores they
+                    // went out as separate half-line writes, measured 5% slower)
+                    *reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol) = o;
                     if constexpr (POOL_OUT) {
                       float fo[VEC];
                       unpack_in<Tr>(o, fo);
