@@ -30,9 +30,10 @@
 //   C_j <= max_i [sum of the j - i largest rho + i mu] + sqrt(j) (|G X - X diag(rho)|_F +
 //          2 |F|_F)                                          with F the off-diagonal part of
 //          X^T G X and mu >= the largest eigenvalue of G on the complement of X
-//          (mu^2 <= |G|_F^2 - |X^T G X|_F^2),
+//          (mu^2 <= |G|_F^2 - |X^T G X|_F^2, taken with (1e-13 + 4 r defect) |G|_F^2 added;
+//          the residual term with 2 r defect times the Gershgorin bound added),
 // each side widened by k (3 r defect(X) + 1e-12) times the Gershgorin bound for rounding and
-// for X being orthonormal only to its measured defect.  k is kept when C_k >= need is proven
+// for X being orthonormal only to its measured defect (max |X^T X - I|).  k is kept when C_k >= need is proven
 // and C_{k-1} < need is proven (k <= r); otherwise, or when the iteration does not converge,
 // the matrix is marked (kWarmMiss) and the full eigensolver of the fit decides it.
 //
