@@ -74,6 +74,7 @@ __shared__ double w_res2[kEigMaxR], w_rho[kEigMaxR];
 __shared__ double w_amax[kWarmNW][kEigMaxR];
 __shared__ int w_aidx[kWarmNW][kEigMaxR];
 __shared__ int w_flag[2];
+__shared__ double w_resp;  // the previous pass's largest residual norm
 
 __device__ __forceinline__ double4v mfma64(double a, double b, double4v c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -696,12 +697,17 @@ __device__ __attribute__((noinline)) void warm_small_eig(int r) {
 
 // ---- phase 4: X = Q Y_r (written over the first r columns of Q in QB), G X, X^T G X and
 //      X^T X, the residuals, the decision (convergence; the effective rank proven from the
-//      Ritz values), and when accepted W.  Returns 0 (not converged), 1 (converged; *k_out
-//      holds k or -1 when it is not proven).
+//      Ritz values), and when accepted W.  Returns 0 (not converged: iterate), 1 (converged;
+//      *k_out holds k or -1 when it is not proven) or 2 (not converged and not worth another
+//      pass: the sum of the r Ritz values, a lower bound on that of the r largest eigenvalues,
+//      stays 0.1% short of the energy threshold, so k_eff > r or the block is far off; or the
+//      residual, shrinking at the rate of the last two passes, would not reach the tolerance
+//      in the passes left).  Giving up only saves time: such a matrix takes the full solve,
+//      as does one that runs out of passes.
 template <int D, int MQ>
 __device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, double energy,
                                                     double gf2, double gersh, double trace,
-                                                    float* W_m, int* k_out) {
+                                                    float* W_m, int* k_out, int it) {
   constexpr int NW = D / 16, NTH = kWave * NW, QS = kWarmQS, SS = kWarmSS;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave, g = l / 16, i0 = l % 16;
   double* QB = w_lds;
@@ -830,8 +836,21 @@ __device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, dou
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) rmx = fmax(rmx, __shfl_xor(rmx, off, 64));
       const double rsum = wave_sum_d(r2);
-      const bool conv = defect <= 1e-8 && sqrt(rmx) <= 0x1p-28 * gersh;  // uniform
+      const double tol = 0x1p-28 * gersh;
+      const bool conv = defect <= 1e-8 && sqrt(rmx) <= tol;  // uniform
       int kk = -1;
+      bool give_up = false;
+      if (!conv) {
+        const double rho_r = wave_sum_d(rc);  // the r Ritz values
+        const double res = sqrt(rmx);
+        give_up = rho_r < (1.0 - 1e-3) * energy * trace;
+        if (it >= 1 && !give_up) {
+          double pred = res;  // after the passes left, at the last pass's rate
+          for (int q = it + 1; q < kWarmMaxIt; ++q) pred *= res / fmax(w_resp, 1e-300);
+          give_up = pred > tol;
+        }
+        if (l == 0) w_resp = res;
+      }
       if (conv) {
         double* rsd = w_col[0];  // the Ritz values, descending
         double* csum = w_col[1];  // their running sums
@@ -867,12 +886,12 @@ __device__ __attribute__((noinline)) int warm_check(const double* Gm, int r, dou
         }
       }
       if (l == 0) {
-        w_flag[0] = conv ? 1 : 0;
+        w_flag[0] = conv ? 1 : (give_up ? 2 : 0);
         w_flag[1] = kk;
       }
     }
     __syncthreads();
-    if (!w_flag[0]) return 0;  // (uniform) not converged
+    if (w_flag[0] != 1) return w_flag[0];  // (uniform) not converged: iterate or give up
     {
       const int k_cert = w_flag[1];
       *k_out = k_cert;
@@ -963,18 +982,20 @@ __global__ __launch_bounds__(4 * D, D == 128 ? 4 : 2) void refit_warm_kernel(
         if (!warm_zchol<D, 32, true>(Gm)) break;
         warm_rayleigh<D, 32>(Gm);
         warm_small_eig<D, 32>(r);
-        conv = warm_check<D, 32>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc);
+        conv = warm_check<D, 32>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc, it);
       } else {
         if (it == 1) warm_extras<D>(32, kWarmM);  // the block grows to 48 columns
         if (!warm_zchol<D, kWarmM, false>(Gm)) break;
         warm_rayleigh<D, kWarmM>(Gm);
         warm_small_eig<D, kWarmM>(r);
-        conv = warm_check<D, kWarmM>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc);
+        conv = warm_check<D, kWarmM>(Gm, r, energy, w_stat[0], w_stat[1], w_stat[2], W_m, &kc,
+                                     it);
       }
-      if (conv) {
+      if (conv == 1) {
         k_cert = kc;
         break;
       }
+      if (conv == 2) break;  // not worth another pass: the full solve takes it
     }
   }
   if (tid == 0) {

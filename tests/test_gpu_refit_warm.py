@@ -15,13 +15,13 @@ from test_gpu_stream_fit import _planted_delta
 pytestmark = pytest.mark.gpu
 
 
-def _check_against_oracle(name, G, W, k, r):
+def _check_against_oracle(name, G, W, k, r, energy=0.9):
     """k_eff on every matrix; W where the top-r gaps are resolved; the rank-r projector where
     only the subspace is unique."""
     Gh = G.cpu().numpy()
-    ref = oracle.fit_from_gram(Gh, r)
+    ref = oracle.fit_from_gram(Gh, r, energy)
     got_k = k.cpu().numpy()
-    margin = energy_margin(ref["eig"], 0.9)
+    margin = energy_margin(ref["eig"], energy)
     say(f"  {name}: min energy margin {margin.min():.2e}")
     assert np.all(margin > 1e-11)
     np.testing.assert_array_equal(got_k, ref["k_eff"], err_msg=f"{name}: effective rank")
@@ -95,6 +95,43 @@ def test_llama8b_t8192_appended_block_every_matrix():
     _check_against_oracle("warm-llama8b", G, fit.W, fit.k_eff, cfg.r)
     assert kept >= 0.9 * M
     del delta, G
+
+
+def _sweep_cases(n):
+    """Seeded random configurations: dtype, d, rows before and after the append, r, energy,
+    spectral decay of the planted delta."""
+    rng = np.random.default_rng(2026)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        out.append(("bf16" if rng.random() < 0.6 else "f32", d, int(rng.integers(200, 1500)),
+                    int(rng.integers(20, 600)), int(rng.integers(1, 33)),
+                    float(rng.choice([0.5, 0.8, 0.9, 0.99])), float(rng.choice([0.8, 0.9, 0.95])),
+                    100 + i))
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,t_old,t_new,r,energy,decay,seed", _sweep_cases(12))
+def test_random_configurations_match_the_oracle(dtype, d, t_old, t_new, r, energy, decay, seed):
+    """A seeded sweep over shapes, ranks, energies and spectra: k_eff exact on every matrix
+    (the warm certificate or the full path, whichever decided it), W within the bars, and the
+    matrices the warm path left open equal to the full path bit for bit."""
+    M = 4
+    say(f"[warm] sweep {dtype} d={d} {t_old}+{t_new} rows r={r} energy={energy} decay={decay}")
+    delta = _planted_delta(M, t_old + t_new, d, dtype, seed, decay).to(dev())
+    G = kvc.gram_accumulate(delta[:, :t_old].contiguous())
+    W_old = kvc.fit_from_gram(G, r=r, energy=energy, want_eig=False).W
+    G = kvc.gram_accumulate(delta[:, t_old:].contiguous(), G)
+    fit, warm = kvc.refit_warm(G, W_old, energy)
+    full = kvc.fit_from_gram(G, r=r, energy=energy, want_eig=False)
+    torch.cuda.synchronize()
+    w = warm.cpu().numpy()
+    say(f"  warm kept on {int(w.sum())} of {M}")
+    _check_against_oracle(f"sweep-{seed}", G, fit.W, fit.k_eff, r, energy)
+    assert torch.equal(full.k_eff, fit.k_eff)
+    for m in range(M):
+        if w[m] == 0:
+            assert torch.equal(fit.W[m], full.W[m]), f"sweep-{seed}[{m}]: W differs from the full path"
 
 
 def _flat_gram(M, T, d, seed):
