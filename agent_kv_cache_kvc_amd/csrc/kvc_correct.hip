@@ -914,7 +914,7 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
             for (int e = 0; e < VEC; ++e) dv[e] += xv[e];
             const u32x4 o = pack_out<Tr>(dv);
             if (full || tok < T) {
-              __builtin_nontemporal_store(  // L2 keeps the source for the second read
+              __builtin_nontemporal_store(  // the output is not read again here
                   o, reinterpret_cast<u32x4*>(Yt + (size_t)tok * D + 64 * h + lcol));
               if constexpr (POOL_OUT) {
                 float fo[VEC];
