@@ -55,6 +55,36 @@ def test_gram_matches_the_oracle():
     assert oracle.rel_frobenius(got, ref) < 1e-6
 
 
+@pytest.mark.parametrize("dtype,d,T,M", [
+    ("bf16", 128, 40000, 1),  # 313 splits of 128 rows
+    ("f32", 64, 20000, 2),    # 79 splits of 256 rows
+])
+def test_gram_fold_over_many_splits(dtype, d, T, M):
+    """Few matrices and many rows: the fold sums hundreds of split partials per element.
+    Onto zero it equals the one-call fit's G (same W, k_eff and eigenvalues, bit for bit);
+    onto a non-zero G it matches the oracle's float64 sum and stays symmetric."""
+    say(f"[stream] many splits {dtype} d={d} T={T} M={M}")
+    delta = _planted_delta(M, T, d, dtype, 17 + M).to(dev())
+    G = kvc.gram_accumulate(delta)
+    a = kvc.fit_from_gram(G, r=16)
+    b = kvc.fit_anchor(delta, r=16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.W, b.W) and torch.equal(a.k_eff, b.k_eff) and torch.equal(a.eig, b.eig)
+    head = delta[:, : T // 3].contiguous()
+    G2 = kvc.gram_accumulate(delta[:, T // 3:].contiguous(), kvc.gram_accumulate(head))
+    torch.cuda.synchronize()
+    dh = synth.to_f64(delta.cpu())
+    ref = oracle.gram(dh)
+    trace = np.trace(ref, axis1=1, axis2=2)
+    bar = gram_gamma(dtype, 256)  # |E|_F <= gamma trace (splits of at most 256 rows)
+    for name, got in (("one block", G.cpu().numpy()), ("two blocks", G2.cpu().numpy())):
+        np.testing.assert_array_equal(got, np.swapaxes(got, 1, 2))
+        e = np.linalg.norm(got - ref, axis=(1, 2)) / trace
+        say(f"  {name}: |G - G_oracle|_F / trace worst {e.max():.3e} (bar {bar:.1e}), "
+            f"rel-Frobenius {oracle.rel_frobenius(got, ref):.3e}")
+        assert np.all(e <= bar)
+
+
 def gram_gamma(dtype, rows):
     """Error bound of an accumulated Gram per unit of trace for blocks of at most `rows` rows:
     (steps + 2) float32 roundings of a split's sum, doubled (steps: rows / 16 MFMA steps for
