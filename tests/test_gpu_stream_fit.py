@@ -85,6 +85,32 @@ def test_gram_fold_over_many_splits(dtype, d, T, M):
         assert np.all(e <= bar)
 
 
+@pytest.mark.parametrize("dtype,d,T,r,M", [
+    ("bf16", 128, 1, 1, 2),
+    ("bf16", 128, 700, 33, 3),
+    ("bf16", 64, 37, 5, 4),
+    ("bf16", 128, 513, 100, 2),
+    ("f32", 128, 260, 64, 2),
+    ("f32", 64, 129, 17, 3),
+])
+def test_projection_matches_the_oracle(dtype, d, T, r, M):
+    """U = delta W^T for any float32 W (not only orthonormal rows), any r <= d and ragged T:
+    the bf16 path splits W into bf16 halves in the kernel (rows >= r read as zero)."""
+    say(f"[stream] projection {dtype} d={d} T={T} r={r} M={M}")
+    g = torch.Generator().manual_seed(1000 + T + r)
+    delta = torch.randn(M, T, d, generator=g, dtype=torch.float64)
+    W = torch.randn(M, r, d, generator=g, dtype=torch.float64).float()
+    delta = delta.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    U = kvc.project(delta.to(dev()), W.to(dev()))
+    torch.cuda.synchronize()
+    want = oracle.project(synth.to_f64(delta), W.double().numpy())
+    got = U.cpu().double().numpy()
+    e = oracle.rel_frobenius(got, want)
+    mx = np.abs(got - want).max() / np.abs(want).max()
+    say(f"  U rel-Frobenius {e:.3e}, max |diff| / max |U| {mx:.3e} (bar 1e-4)")
+    assert e <= 1e-4 and mx <= 1e-4
+
+
 def gram_gamma(dtype, rows):
     """Error bound of an accumulated Gram per unit of trace for blocks of at most `rows` rows:
     (steps + 2) float32 roundings of a split's sum, doubled (steps: rows / 16 MFMA steps for
