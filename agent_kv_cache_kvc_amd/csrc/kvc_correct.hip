@@ -528,7 +528,6 @@ __global__ __launch_bounds__(kBlock, 2) void correct_kernel(CorrectArgs args) {
   constexpr int TPI = TL::TPI;
   constexpr int NH = TL::NH, JN = TL::JN;
   constexpr int PADK = 16 / sizeof(elem);
-  constexpr int PER = 2 * D / kWave;
   // CMP (compact LDS, bf16 anchor counts of 6 and more at r = 32): W^T rows are stored
   // unpadded with their 16-byte chunks XOR-swizzled by bits 2-3 of the row (the 16 rows that
   // one quarter-wave reads then fall into 16 distinct bank groups), and the MFMA results are

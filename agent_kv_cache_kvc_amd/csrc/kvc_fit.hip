@@ -1717,7 +1717,7 @@ static hipError_t refit_warm_t(const double* G, int M, int r, double energy,
 
 template <int D>
 static hipError_t project_t(const void* delta, int M, int T, int dtype, const float* W, int r,
-                            float* U_out, char* ws, hipStream_t st) {
+                            float* U_out, hipStream_t st) {
   const int rpad = (r + 31) / 32 * 32;
   const int n_tiles = ceil_div(T, kRowsPerPass * kProjIters);
   const dim3 g3(n_tiles, M);
@@ -1757,8 +1757,9 @@ hipError_t launch_refit_warm(const double* G, int M, int d, int r, double energy
 hipError_t launch_project(const void* delta, int M, int T, int d, int dtype, const float* W,
                           int r, float* U_out, char* ws, hipStream_t st) {
   if (M == 0 || T == 0) return hipSuccess;
-  return d == 128 ? project_t<128>(delta, M, T, dtype, W, r, U_out, ws, st)
-                  : project_t<64>(delta, M, T, dtype, W, r, U_out, ws, st);
+  (void)ws;  // the bf16 path splits W into bf16 halves itself: no workspace
+  return d == 128 ? project_t<128>(delta, M, T, dtype, W, r, U_out, st)
+                  : project_t<64>(delta, M, T, dtype, W, r, U_out, st);
 }
 
 // ------------------------------------------------------------------------- rank descriptor
